@@ -1,0 +1,85 @@
+"""Flop and byte accounting for the tiled attention path (host arithmetic only).
+
+Algorithmic flops per kept (query, key) pair: the forward's two contractions
+(S = Q K^T and O = P V) are 2 * d each, so 4 * d; the backward's five
+contractions (recomputed S, dV, dP, dK, dQ) are 10 * d, so 14 * d for a forward
+plus backward.  A pair is kept when the causal, key-padding and block masks all
+keep it.
+
+Compulsory HBM bytes of one head (s = bytes per element): the forward reads
+Q, K, V and writes O and the fp32 logsumexp; the backward reads Q, K, V, O, dO
+and the logsumexp and writes dQ, dK, dV, plus its fp32 D vector.
+"""
+
+import numpy as np
+
+ELEM_BYTES = {"fp32": 4, "fp16": 2, "bf16": 2}
+
+
+def kept_pairs_head(n, causal=False, key_len=None, block_mask=None, block_size=128):
+    """Number of visible (query, key) pairs in one head, without forming N x N."""
+    n = int(n)
+    i = np.arange(n)
+    limit = np.full(n, n, dtype=np.int64)            # keys [0, limit_i) pass causal/len
+    if causal:
+        limit = np.minimum(limit, i + 1)
+    if key_len is not None:
+        limit = np.minimum(limit, max(0, min(int(key_len), n)))
+    if block_mask is None:
+        return int(limit.sum())
+    bm = (np.asarray(block_mask) != 0).astype(np.int64)
+    nb = bm.shape[1]
+    starts = np.arange(nb, dtype=np.int64) * block_size
+    total = 0
+    for blk in range(-(-n // block_size)):
+        rows = slice(blk * block_size, min(n, (blk + 1) * block_size))
+        lim = limit[rows][:, None]                    # rows x 1
+        per_block = np.clip(lim - starts[None, :], 0, block_size)   # rows x nb
+        total += int((per_block * bm[blk][None, :]).sum())
+    return total
+
+
+def kept_pairs(prob):
+    """Kept pairs summed over every (b, h) head of a Problem."""
+    total = 0
+    for b in range(prob.B):
+        kl = None if prob.key_lens is None else int(prob.key_lens[b])
+        total += prob.H * kept_pairs_head(prob.N, prob.causal, kl, prob.block_mask,
+                                          prob.block_size)
+    return total
+
+
+def flops(prob, which):
+    """Algorithmic flops: which in {'fwd', 'bwd', 'fwd+bwd'}."""
+    per = {"fwd": 4, "bwd": 10, "fwd+bwd": 14}[which]
+    return per * prob.d * kept_pairs(prob)
+
+
+def compulsory_bytes(prob, which):
+    s = ELEM_BYTES[prob.dtype]
+    heads = prob.B * prob.H
+    n, d = prob.N, prob.d
+    fwd = heads * (4 * n * d * s + 4 * n)
+    bwd = heads * (8 * n * d * s + 12 * n)
+    return {"fwd": fwd, "bwd": bwd, "fwd+bwd": fwd + bwd}[which]
+
+
+def standard_attention_bytes(prob):
+    """HBM bytes of a forward that materialises S and P (write S, read S, write
+    P, read P) plus reading Q, K, V and writing O: the Theta(N d + N^2) model."""
+    s = ELEM_BYTES[prob.dtype]
+    heads = prob.B * prob.H
+    n, d = prob.N, prob.d
+    return heads * (4 * n * n * s + 4 * n * d * s)
+
+
+def tiled_forward_bytes(prob, block_rows):
+    """HBM bytes of the tiled forward when every Q tile of ``block_rows`` rows
+    reads the K and V tiles it keeps: the Theta(N^2 d^2 / M) model's re-read
+    term plus the compulsory traffic."""
+    s = ELEM_BYTES[prob.dtype]
+    n, d = prob.N, prob.d
+    dense = prob.B * prob.H * n * n
+    frac = kept_pairs(prob) / dense if dense else 0.0
+    tiles = -(-n // block_rows)
+    return compulsory_bytes(prob, "fwd") + prob.B * prob.H * tiles * 2 * frac * n * d * s

@@ -1,0 +1,118 @@
+"""Seeded synthetic inputs for tiled exact attention.
+
+This module draws and rounds numbers; it performs none of the attention
+arithmetic.  Both the HIP path (through its tests and the bench) and the fp64
+oracle take their inputs from here, and from nowhere else.
+
+Recipe (the pages fix no data; their workloads are GPT-2, BERT-large, Long
+Range Arena and Path-X/Path-256 training, which only lend their attention
+shapes here):
+
+* ``numpy.random.default_rng(seed)`` draws Q, K, V, dO in that order, each as
+  float32 standard normal in C order [B, H, N, d];
+* every value is rounded to the compute dtype with round-to-nearest-even, so
+  the float32 arrays returned hold exactly what the GPU receives;
+* per-batch key lengths (key padding) come from
+  ``default_rng(seed + 1_000_003).integers(lo, hi + 1, B)`` (inclusive range);
+* the block mask comes from ``default_rng(seed + 2_000_003).random((nb, nb))
+  < p`` with the diagonal forced to 1, nb = ceil(N / block_size).
+"""
+
+from dataclasses import dataclass, field
+from typing import Optional
+
+import numpy as np
+
+DTYPES = ("fp32", "fp16", "bf16")
+
+
+def round_to_dtype(x, dtype):
+    """Round float32 values to ``dtype`` (round to nearest, ties to even) and
+    return them as float32 again."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    if dtype == "fp32":
+        return x
+    if dtype == "fp16":
+        return x.astype(np.float16).astype(np.float32)
+    if dtype == "bf16":
+        u = x.view(np.uint32).astype(np.uint64)
+        u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+        return u.astype(np.uint32).view(np.float32)
+    raise ValueError(f"unknown dtype {dtype!r}")
+
+
+@dataclass
+class Problem:
+    """One attention problem: inputs, masks and the softmax scale."""
+    B: int
+    H: int
+    N: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: np.float32
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    do: np.ndarray
+    key_lens: Optional[np.ndarray] = None       # int32 [B]
+    block_mask: Optional[np.ndarray] = None     # uint8 [nb, nb]
+    block_size: int = 128
+    seed: int = 0
+    name: str = ""
+    meta: dict = field(default_factory=dict)
+
+
+def make_problem(B, H, N, d, dtype, seed, causal=False, scale=None,
+                 key_len_range=None, block_keep_p=None, block_size=128, name=""):
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    shape = (B, H, N, d)
+    q, k, v, do = (round_to_dtype(rng.standard_normal(shape, dtype=np.float32), dtype)
+                   for _ in range(4))
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    key_lens = None
+    if key_len_range is not None:
+        lo, hi = key_len_range
+        key_lens = np.random.default_rng(seed + 1_000_003).integers(
+            lo, hi + 1, B).astype(np.int32)
+    block_mask = None
+    if block_keep_p is not None:
+        nb = -(-N // block_size)
+        bm = np.random.default_rng(seed + 2_000_003).random((nb, nb)) < block_keep_p
+        np.fill_diagonal(bm, True)
+        block_mask = bm.astype(np.uint8)
+    return Problem(B, H, N, d, dtype, bool(causal), np.float32(scale), q, k, v, do,
+                   key_lens, block_mask, block_size, seed, name)
+
+
+# The five workloads.  Shapes follow GPT-2-small, BERT-large, long-context
+# (Long Range Arena / Path-X lengths) and long-context block-sparse attention.
+LONG_POINTS = [(n, d) for n in (2048, 4096, 8192, 16384) for d in (64, 128)]
+
+
+def config(name, n=None, d=None):
+    """Return the keyword arguments of ``make_problem`` for a named workload."""
+    if name == "tiny":
+        return dict(B=1, H=2, N=128, d=64, dtype="fp32", seed=1, causal=False,
+                    scale=1 / 8, name=name)
+    if name == "gpt2_small":
+        return dict(B=8, H=12, N=1024, d=64, dtype="bf16", seed=2, causal=True,
+                    scale=1 / 8, name=name)
+    if name == "bert_large_padded":
+        return dict(B=16, H=16, N=512, d=64, dtype="fp16", seed=3, causal=False,
+                    scale=1 / 8, key_len_range=(128, 512), name=name)
+    if name == "long_causal":
+        idx = LONG_POINTS.index((n, d))
+        return dict(B=2, H=8, N=n, d=d, dtype="bf16", seed=4 + 10 * idx, causal=True,
+                    scale=1 / np.sqrt(d), name=f"long_causal_N{n}_d{d}")
+    if name == "block_sparse":
+        return dict(B=1, H=8, N=16384, d=64, dtype="bf16", seed=5, causal=False,
+                    scale=1 / 8, block_keep_p=1 / 8, block_size=128, name=name)
+    raise KeyError(name)
+
+
+def workload(name, n=None, d=None):
+    return make_problem(**config(name, n, d))

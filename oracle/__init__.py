@@ -1,0 +1,8 @@
+"""fp64 CPU oracle for tiled exact attention.  Test infrastructure only: the
+product path never imports it (see attention.py's header)."""
+
+from .attention import (visibility, head_forward, head_backward, head_probabilities,
+                        forward, backward)
+
+__all__ = ["visibility", "head_forward", "head_backward", "head_probabilities",
+           "forward", "backward"]

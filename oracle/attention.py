@@ -1,0 +1,180 @@
+"""Plain fp64 CPU attention: the correctness oracle for the tiled GPU kernels.
+
+TEST INFRASTRUCTURE ONLY.  Nothing in the product path may import or call this
+module; only the tests, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` use it.  It shares no code with the HIP library.
+
+What it computes is standard attention written out with the full N x N score
+matrix materialised, the formulation that the IO-aware method is exact with
+respect to:
+
+* review page, "Problem": standard attention materialises the N-by-N matrix;
+* visual guide, "standard attention" and the closing results table: the tiled
+  method gives the same outputs ("exact", no change to the model math);
+* review page, "Method" and claim C7: the forward keeps only the output and
+  small normalisation values, the backward recomputes the attention matrix
+  from them.  The normalisation value kept here is the per-row logsumexp
+  (natural log), which carries the running max m and denominator l of the
+  slides' "action grammar" card as LSE = m + ln(l);
+* visual guide, block-sparse paragraph: masking whole blocks.  The block-masked
+  result is exact with respect to the block mask and approximate with respect
+  to dense attention (review page, caveats), so the sparse reference is dense
+  attention with the same mask applied.
+
+The backward pass is the closed form of the gradient of L = sum(dO * O):
+D = rowsum(dO * O), dV = P^T dO, dP = dO V^T, dS = P * (dP - D),
+dQ = scale * dS K, dK = scale * dS^T Q.
+
+Readings where the pages are silent (each is also listed in the design notes):
+* layout [B, H, N, d], d innermost; one (b, h) head at a time;
+* causal means key j is visible to query i iff j <= i (top-left aligned);
+* key padding masks keys only: key j of batch b is visible iff j < key_lens[b];
+  padded query rows are computed like any other row;
+* the block mask is one uint8 [ceil(N/bs), ceil(N/bs)] array shared by every
+  (b, h); entry (I, J) nonzero keeps every (i, j) with i // bs == I and
+  j // bs == J; masks combine by logical AND;
+* a query row that sees no key at all has O = 0, LSE = -inf and contributes
+  nothing to any gradient.
+
+Everything is float64.  Inputs are the dtype-rounded values the GPU receives,
+upcast; ``scale`` is the float32 value handed to the GPU, upcast.
+"""
+
+import numpy as np
+
+
+def visibility(n, causal=False, key_len=None, block_mask=None, block_size=128):
+    """Boolean [n, n] matrix: entry (i, j) is True iff query i may attend key j.
+
+    Combines the three masks of the method (causal, key padding, block mask)
+    by logical AND, as read above.
+    """
+    i = np.arange(n)[:, None]
+    j = np.arange(n)[None, :]
+    vis = np.ones((n, n), dtype=bool)
+    if causal:
+        vis &= j <= i
+    if key_len is not None:
+        vis &= j < int(key_len)
+    if block_mask is not None:
+        bm = np.asarray(block_mask) != 0
+        vis &= bm[i // block_size, j // block_size]
+    return vis
+
+
+def _head_forward(q, k, v, scale, vis):
+    """One head (or a group of its query rows).  Returns (O, LSE, P).
+
+    Softmax over the visible keys of each row, with the row max m subtracted
+    before exponentiating and the denominator l = sum exp(S - m):
+    P = exp(S - m) / l and LSE = m + ln(l).
+    """
+    s = scale * (q @ k.T)                       # score matrix S, rows x N
+    s = np.where(vis, s, -np.inf)
+    seen = vis.any(axis=1)
+    m = np.where(seen, s.max(axis=1, initial=-np.inf), 0.0)
+    ex = np.where(vis, np.exp(s - m[:, None]), 0.0)
+    l = ex.sum(axis=1)
+    l_safe = np.where(seen, l, 1.0)
+    p = ex / l_safe[:, None]
+    lse = np.where(seen, m + np.log(l_safe), -np.inf)
+    o = p @ v
+    return o, lse, p
+
+
+def _row_chunks(n, row_chunk):
+    step = n if not row_chunk else max(1, int(row_chunk))
+    for r0 in range(0, n, step):
+        yield r0, min(n, r0 + step)
+
+
+def head_forward(q, k, v, scale, causal=False, key_len=None, block_mask=None,
+                 block_size=128, row_chunk=None):
+    """Forward for one head: q, k, v are [N, d] float64.  Returns (O, LSE).
+
+    Query rows are independent in the definition (each row's softmax sees all
+    its visible keys), so ``row_chunk`` only bounds memory: rows are handled
+    in groups, each group with its full set of keys.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    scale = float(scale)
+    n = q.shape[0]
+    vis_all = visibility(n, causal, key_len, block_mask, block_size)
+    o = np.zeros((n, v.shape[1]))
+    lse = np.zeros(n)
+    for r0, r1 in _row_chunks(n, row_chunk):
+        o[r0:r1], lse[r0:r1], _ = _head_forward(q[r0:r1], k, v, scale, vis_all[r0:r1])
+    return o, lse
+
+
+def head_probabilities(q, k, scale, causal=False, key_len=None, block_mask=None,
+                       block_size=128):
+    """The attention matrix P of one head (rows sum to 1 over visible keys)."""
+    q, k = (np.asarray(x, dtype=np.float64) for x in (q, k))
+    vis = visibility(q.shape[0], causal, key_len, block_mask, block_size)
+    return _head_forward(q, k, np.zeros((k.shape[0], 1)), float(scale), vis)[2]
+
+
+def head_backward(q, k, v, do, scale, causal=False, key_len=None, block_mask=None,
+                  block_size=128, row_chunk=None):
+    """Backward for one head from the closed form.  Returns (dQ, dK, dV).
+
+    Runs its own forward (never a GPU result).  dK and dV are sums over query
+    rows, so they accumulate across row groups.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    scale = float(scale)
+    n = q.shape[0]
+    vis_all = visibility(n, causal, key_len, block_mask, block_size)
+    dq = np.zeros_like(q)
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    for r0, r1 in _row_chunks(n, row_chunk):
+        o, _, p = _head_forward(q[r0:r1], k, v, scale, vis_all[r0:r1])
+        d_row = (do[r0:r1] * o).sum(axis=1)     # D = rowsum(dO * O)
+        dv += p.T @ do[r0:r1]                   # dV = P^T dO
+        dp = do[r0:r1] @ v.T                    # dP = dO V^T
+        ds = p * (dp - d_row[:, None])          # dS = P * (dP - D)
+        dq[r0:r1] = scale * (ds @ k)            # dQ = scale * dS K
+        dk += scale * (ds.T @ q[r0:r1])         # dK = scale * dS^T Q
+    return dq, dk, dv
+
+
+def _heads(x):
+    x = np.asarray(x)
+    assert x.ndim == 4, "expected [B, H, N, d]"
+    return x.shape
+
+
+def forward(q, k, v, scale, causal=False, key_lens=None, block_mask=None,
+            block_size=128, row_chunk=None, heads=None):
+    """Batched forward over [B, H, N, d].  Returns (O [B,H,N,d], LSE [B,H,N]).
+
+    ``heads``: optional list of (b, h) pairs; only those heads are computed
+    and the others are left as NaN (used to check sampled heads at full size).
+    """
+    B, H, N, d = _heads(q)
+    o = np.full((B, H, N, v.shape[-1]), np.nan)
+    lse = np.full((B, H, N), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        kl = None if key_lens is None else int(key_lens[b])
+        o[b, h], lse[b, h] = head_forward(q[b, h], k[b, h], v[b, h], scale, causal, kl,
+                                          block_mask, block_size, row_chunk)
+    return o, lse
+
+
+def backward(q, k, v, do, scale, causal=False, key_lens=None, block_mask=None,
+             block_size=128, row_chunk=None, heads=None):
+    """Batched backward over [B, H, N, d].  Returns (dQ, dK, dV)."""
+    B, H, N, d = _heads(q)
+    dq = np.full(q.shape, np.nan)
+    dk = np.full(k.shape, np.nan)
+    dv = np.full(v.shape, np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        kl = None if key_lens is None else int(key_lens[b])
+        dq[b, h], dk[b, h], dv[b, h] = head_backward(
+            q[b, h], k[b, h], v[b, h], do[b, h], scale, causal, kl, block_mask,
+            block_size, row_chunk)
+    return dq, dk, dv
