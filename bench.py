@@ -1,0 +1,254 @@
+"""Benchmark of the tiled attention hot path on one MI355X.
+
+One step = one forward (fa_forward) plus one backward (fa_backward) over one
+batch of synthetic inputs already resident in HBM.  The default workload is
+GPT-2-small-shaped causal self-attention (B=8, H=12, N=1024, d=64, bf16).
+
+    python bench.py [--steps K] [--warmup W] [--config NAME [--n N --d D]]
+
+Prints one JSON line.  ``value`` is algorithmic forward+backward TFLOP/s
+(14 * d flops per kept query-key pair) of the whole job.  ``roofline``
+describes the kernel that takes most of the step, timed with the library's
+per-launch HIP events over a second pass of the same K steps; ``cpu_baseline``
+times the fp64 oracle on the host on a bounded sample of the same workload.
+"""
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
+                                   fa_forward, fa_forward_blocksparse, fa_kernel_name,
+                                   fa_timing_enable, fa_timing_read, inputs)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X
+PEAK_HBM_GBS = 8000.0
+TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16}
+# Algorithmic flops per kept pair, in units of d, that each kernel performs:
+# forward S and PV; the dK/dV pass does the recomputed S, dP, dV and dK; the
+# dQ pass contributes the dQ product only (its S and dP repeat the dK/dV pass).
+KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+KERNEL_SOURCES = {
+    "fwd": ["fa_fwd.hip", "fa_common.h"],
+    "bwd_pre": ["fa_bwd.hip", "fa_common.h"],
+    "bwd_dkdv": ["fa_bwd.hip", "fa_common.h"],
+    "bwd_dq": ["fa_bwd.hip", "fa_common.h"],
+}
+
+
+def source_hash(kind):
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "exact_io_aware_52_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(kernel, workload):
+    """HBM bytes per launch from a committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    for line in open(path):
+        if ":" in line:
+            k, v = line.split(":", 1)
+            fields[k.strip()] = v.strip()
+    kind = {v: k for k, v in KERNEL_NAMES.items()}.get(kernel)
+    if kind is None or fields.get("source_sha256") != source_hash(kind):
+        return None
+    try:
+        return float(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+KERNEL_NAMES = {}
+
+
+def make_workload(args):
+    if args.config == "long_causal":
+        return inputs.workload("long_causal", args.n, args.d)
+    return inputs.workload(args.config)
+
+
+def cpu_baseline(prob, budget_s):
+    """Time the fp64 oracle (forward + backward, one head at a time) on the
+    host for about ``budget_s`` seconds of work; report TFLOP/s."""
+    import oracle   # test infrastructure; used only for this reported baseline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:   # pragma: no cover
+        threads = os.cpu_count()
+    heads = [(b, h) for b in range(prob.B) for h in range(prob.H)]
+    done = 0
+    pairs = 0
+    t0 = time.perf_counter()
+    while done < len(heads) and (done == 0 or time.perf_counter() - t0 < budget_s):
+        b, h = heads[done]
+        kl = None if prob.key_lens is None else int(prob.key_lens[b])
+        q, k, v, do = (x[b, h].astype(np.float64) for x in (prob.q, prob.k, prob.v, prob.do))
+        kw = dict(causal=prob.causal, key_len=kl, block_mask=prob.block_mask,
+                  block_size=prob.block_size, row_chunk=2048)
+        oracle.head_forward(q, k, v, float(prob.scale), **kw)
+        oracle.head_backward(q, k, v, do, float(prob.scale), **kw)
+        pairs += accounting.kept_pairs_head(prob.N, prob.causal, kl, prob.block_mask,
+                                            prob.block_size)
+        done += 1
+    dt = time.perf_counter() - t0
+    flops = 14 * prob.d * pairs
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} of {len(heads)} heads of the same workload, fp64 forward+backward, "
+                      f"{dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--config", default="gpt2_small",
+                    choices=["tiny", "gpt2_small", "bert_large_padded", "long_causal",
+                             "block_sparse"])
+    ap.add_argument("--n", type=int, default=4096)
+    ap.add_argument("--d", type=int, default=64)
+    ap.add_argument("--cpu-budget", type=float, default=12.0,
+                    help="seconds of host work for the oracle baseline (0 disables)")
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="run only a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE {world}): "
+              "(b, h) heads are independent, so a multi-GPU run would shard heads with no "
+              "communication; this build measures the single-GPU kernel.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+
+    if args.copy_calib:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30}))
+        return
+
+    for k in ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"):
+        KERNEL_NAMES[k] = fa_kernel_name(k)
+
+    prob = make_workload(args)
+    dt = TORCH_DT[prob.dtype]
+    q, k, v, do = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v, prob.do))
+    kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).to(dev)
+    bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa_backward_workspace_bytes(prob.B, prob.H, prob.N, prob.d),
+                     dtype=torch.uint8, device=dev)
+    scale = float(prob.scale)
+
+    def fwd():
+        if bm is not None:
+            fa_forward_blocksparse(q, k, v, bm, prob.block_size, scale=scale, causal=prob.causal,
+                                   key_lens=kl, o=o, lse=lse)
+        else:
+            fa_forward(q, k, v, scale=scale, causal=prob.causal, key_lens=kl, o=o, lse=lse)
+
+    def step():
+        fwd()
+        fa_backward(q, k, v, o, do, lse, scale=scale, causal=prob.causal, key_lens=kl,
+                    block_mask=bm, block_size=prob.block_size, dq=dq, dk=dk, dv=dv,
+                    workspace=ws)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    for _ in range(args.warmup):
+        step()
+    ms_step = timed(step, args.steps)
+    ms_fwd = timed(fwd, args.steps)
+
+    # Second pass with per-launch HIP events (recorded on the launch stream).
+    fa_timing_enable(True)
+    for kind in KERNEL_NAMES:
+        fa_timing_read(kind)
+    timed(step, args.steps)
+    fa_timing_enable(False)
+    kernels = {}
+    for kind in KERNEL_NAMES:
+        total, n = fa_timing_read(kind)
+        kernels[kind] = {"name": KERNEL_NAMES[kind], "avg_us": 1e3 * total / max(n, 1),
+                         "launches": n}
+
+    pairs = accounting.kept_pairs(prob)
+    flops_step = 14 * prob.d * pairs
+    value = flops_step / (ms_step * 1e-3) / 1e12
+    dom = max((k for k in kernels if kernels[k]["launches"]), key=lambda k: kernels[k]["avg_us"])
+    if dom in KERNEL_FLOPS_PER_PAIR_D:
+        work = KERNEL_FLOPS_PER_PAIR_D[dom] * prob.d * pairs
+        achieved = work / (kernels[dom]["avg_us"] * 1e-6) / 1e12
+        peak = PEAK_TFLOPS[prob.dtype]
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+                "frac": round(achieved / peak, 4)}
+    else:
+        work = accounting.ELEM_BYTES[prob.dtype] * 2 * prob.B * prob.H * prob.N * prob.d
+        achieved = work / (kernels[dom]["avg_us"] * 1e-6) / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    roof["traffic"] = read_traffic(KERNEL_NAMES[dom], prob.name)
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["kernel_avg_us"] = round(kernels[dom]["avg_us"], 2)
+
+    result = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob.dtype,
+        "data": "synthetic",
+        "config": {"workload": prob.name, "B": prob.B, "H": prob.H, "N": prob.N, "d": prob.d,
+                   "causal": prob.causal,
+                   "key_padding": prob.key_lens is not None,
+                   "block_sparse": prob.block_mask is not None, "parallelism": "none"},
+        "fwd_ms": round(ms_fwd, 4),
+        "fwd_tflops": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12, 2),
+        "frac_of_peak_fwd_bwd": round(value / PEAK_TFLOPS[prob.dtype], 4),
+        "kernels_us": {v["name"]: round(v["avg_us"], 2) for v in kernels.values()},
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

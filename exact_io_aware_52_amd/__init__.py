@@ -1,0 +1,15 @@
+"""Tiled exact attention for AMD Instinct MI355X (gfx950).
+
+The compute lives in ``libfa.so`` (hand-written HIP kernels behind a C ABI,
+declared in ``include/fa.h``); this package only marshals torch tensors
+(device memory and the current stream) into those calls.
+
+    from exact_io_aware_52_amd import fa_forward, fa_backward, fa_forward_blocksparse
+"""
+
+from ._binding import (  # noqa: F401
+    FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP,
+    FaError, library_path, load_library, fa_forward, fa_forward_blocksparse, fa_backward,
+    fa_backward_workspace_bytes, fa_timing_enable, fa_timing_read, fa_kernel_name,
+    KERNEL_KINDS,
+)

@@ -1,0 +1,211 @@
+"""ctypes binding of libfa.so: same entry-point names as the C ABI.
+
+Argument marshalling only: torch supplies device memory and the current HIP
+stream; every step of the attention computation runs in the library's
+kernels.  There is no fallback: if libfa.so is missing or a call fails, an
+exception is raised.
+"""
+
+import ctypes
+import math
+import os
+
+import torch
+
+FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
+_DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
+KERNEL_KINDS = {"fwd": 0, "bwd_pre": 1, "bwd_dkdv": 2, "bwd_dq": 3}
+
+_LIB = None
+
+
+class FaError(RuntimeError):
+    def __init__(self, fn, status, detail):
+        self.status = status
+        super().__init__(f"{fn} failed: {_status_name(status)}: {detail}")
+
+
+def library_path():
+    return os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
+
+
+def load_library():
+    """Load libfa.so (once) and declare the C signatures."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with "
+                           "`python -m exact_io_aware_52_amd.build_lib`")
+    lib = ctypes.CDLL(path)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.fa_forward.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, I, P]
+    lib.fa_forward_blocksparse.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P]
+    lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
+    lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
+    lib.fa_backward_workspace_bytes.restype = Z
+    lib.fa_status_string.argtypes = [I]
+    lib.fa_status_string.restype = ctypes.c_char_p
+    lib.fa_last_error_detail.argtypes = []
+    lib.fa_last_error_detail.restype = ctypes.c_char_p
+    lib.fa_timing_enable.argtypes = [I]
+    lib.fa_timing_read.argtypes = [I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
+    lib.fa_kernel_name.argtypes = [I]
+    lib.fa_kernel_name.restype = ctypes.c_char_p
+    for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_backward,
+               lib.fa_timing_enable, lib.fa_timing_read):
+        fn.restype = I
+    _LIB = lib
+    return lib
+
+
+def _status_name(status):
+    return load_library().fa_status_string(int(status)).decode()
+
+
+def _check(fn, status):
+    if status != FA_OK:
+        raise FaError(fn, status, load_library().fa_last_error_detail().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _shape(q, k, v):
+    if q.dim() != 4:
+        raise ValueError("q, k, v must be [B, H, N, d]")
+    for name, t in (("k", k), ("v", v)):
+        if t.shape != q.shape or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must match q in shape, dtype and device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device (the library has no CPU path)")
+    return q.shape
+
+
+def _like(name, t, ref, shape=None, dtype=None):
+    """Check a caller-supplied tensor: device, shape, dtype, contiguity."""
+    if t.device != ref.device:
+        raise ValueError(f"{name} must be on {ref.device}")
+    if tuple(t.shape) != tuple(ref.shape if shape is None else shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}")
+    if t.dtype != (ref.dtype if dtype is None else dtype):
+        raise ValueError(f"{name} has dtype {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _lens(key_lens, B, device):
+    if key_lens is None:
+        return None
+    kl = torch.as_tensor(key_lens).to(device=device, dtype=torch.int32).contiguous()
+    if kl.shape != (B,):
+        raise ValueError("key_lens must have shape [B]")
+    return kl
+
+
+def _mask(block_mask, N, block_size, device):
+    if block_mask is None:
+        return None
+    bm = torch.as_tensor(block_mask).to(device=device, dtype=torch.uint8).contiguous()
+    nb = -(-N // int(block_size)) if block_size > 0 else -1
+    if tuple(bm.shape) != (nb, nb):
+        raise ValueError(f"block_mask must have shape ({nb}, {nb}) for N={N}, "
+                         f"block_size={block_size}")
+    return bm
+
+
+def _scale(scale, d):
+    return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
+
+
+def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, lse):
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    o = torch.empty_like(q) if o is None else _like("o", o, q)
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _like("lse", lse, q, (B, H, N), torch.float32))
+    kl = _lens(key_lens, B, q.device)
+    args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
+            _scale(scale, d), int(bool(causal)), _ptr(kl)]
+    if name == "fa_forward_blocksparse":
+        bm = _mask(block_mask, N, block_size, q.device)
+        args += [_ptr(bm), int(block_size)]
+    args += [_DTYPE_CODE[q.dtype], _stream(q.device)]
+    _check(name, getattr(lib, name)(*args))
+    return o, lse
+
+
+def fa_forward(q, k, v, scale=None, causal=False, key_lens=None, o=None, lse=None):
+    """Forward pass: returns (O [B,H,N,d] in q.dtype, LSE [B,H,N] float32)."""
+    return _forward("fa_forward", q, k, v, scale, causal, key_lens, None, 128, o, lse)
+
+
+def fa_forward_blocksparse(q, k, v, block_mask, block_size=128, scale=None, causal=False,
+                           key_lens=None, o=None, lse=None):
+    """Block-sparse forward: block_mask is uint8 [ceil(N/bs), ceil(N/bs)]."""
+    if block_mask is None:
+        raise ValueError("block_mask is required")
+    return _forward("fa_forward_blocksparse", q, k, v, scale, causal, key_lens, block_mask,
+                    block_size, o, lse)
+
+
+def fa_backward_workspace_bytes(B, H, N, d):
+    return int(load_library().fa_backward_workspace_bytes(B, H, N, d))
+
+
+def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
+                block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass: returns (dQ, dK, dV) in q.dtype."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    _like("o", o, q)
+    _like("dout", dout, q)
+    _like("lse", lse, q, (B, H, N), torch.float32)
+    dq = torch.empty_like(q) if dq is None else _like("dq", dq, q)
+    dk = torch.empty_like(q) if dk is None else _like("dk", dk, q)
+    dv = torch.empty_like(q) if dv is None else _like("dv", dv, q)
+    need = fa_backward_workspace_bytes(B, H, N, d)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    kl = _lens(key_lens, B, q.device)
+    bm = _mask(block_mask, N, block_size, q.device)
+    st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
+                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
+                         int(bool(causal)), _ptr(kl), _ptr(bm), int(block_size),
+                         _DTYPE_CODE[q.dtype], _ptr(workspace),
+                         workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("fa_backward", st)
+    return dq, dk, dv
+
+
+def fa_timing_enable(enable=True):
+    _check("fa_timing_enable", load_library().fa_timing_enable(int(bool(enable))))
+
+
+def fa_timing_read(kind):
+    """(total_ms, launches) of one kernel kind since the last read."""
+    lib = load_library()
+    ms = ctypes.c_double()
+    n = ctypes.c_int()
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    _check("fa_timing_read", lib.fa_timing_read(k, ctypes.byref(ms), ctypes.byref(n)))
+    return ms.value, n.value
+
+
+def fa_kernel_name(kind):
+    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
+    return load_library().fa_kernel_name(k).decode()

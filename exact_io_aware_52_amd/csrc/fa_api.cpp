@@ -1,0 +1,229 @@
+// C ABI of the tiled attention library: argument validation, dispatch to the
+// kernel launchers, status strings and the optional kernel timing hooks.
+// Every check runs on the host before any HIP call, so a rejected call has
+// launched nothing.
+
+#include "fa.h"
+
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <vector>
+
+#include "fa_internal.h"
+
+namespace {
+
+thread_local char g_detail[256] = "";
+
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_detail, sizeof(g_detail), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// ---------------------------------------------------------------- timing hooks
+struct EventPair {
+  hipEvent_t start = nullptr, stop = nullptr;
+};
+struct KindTimes {
+  std::vector<EventPair> pool;  // events created so far (reused after a read)
+  size_t used = 0;              // pairs recorded since the last read
+};
+bool g_timing = false;
+KindTimes g_times[fa::kNumKernelKinds];
+
+}  // namespace
+
+namespace fa {
+
+void timing_begin(KernelKind kind, hipStream_t stream) {
+  if (!g_timing) return;
+  KindTimes& t = g_times[kind];
+  if (t.used == t.pool.size()) {
+    EventPair e;
+    if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess) return;
+    t.pool.push_back(e);
+  }
+  (void)hipEventRecord(t.pool[t.used].start, stream);
+}
+
+void timing_end(KernelKind kind, hipStream_t stream) {
+  if (!g_timing) return;
+  KindTimes& t = g_times[kind];
+  if (t.used < t.pool.size()) {
+    (void)hipEventRecord(t.pool[t.used].stop, stream);
+    ++t.used;
+  }
+}
+
+}  // namespace fa
+
+namespace {
+
+int check_common(int B, int H, int N, int d, float scale, fa_dtype dtype, bool* empty) {
+  if (B < 0 || H < 0 || N < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size B=%d H=%d N=%d", B, H, N);
+  *empty = (B == 0 || H == 0 || N == 0);
+  if (dtype != FA_F32 && dtype != FA_F16 && dtype != FA_BF16)
+    return fail(FA_ERR_INVALID_ARG, "unknown dtype %d", (int)dtype);
+  if (d != 64 && d != 128) return fail(FA_ERR_UNSUPPORTED, "head dim d=%d (supported: 64, 128)", d);
+  if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
+  if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "negative scale %g", (double)scale);
+  if (*empty) return FA_OK;
+  // One work-group per 128 query rows (forward) or 128 keys (backward) per head.
+  const long long tiles = ((long long)N + 127) / 128;
+  if ((long long)B * H * tiles > 0x7fffffffLL)
+    return fail(FA_ERR_INVALID_ARG, "problem too large: B*H*ceil(N/128) exceeds 2^31-1");
+  if ((long long)N * d > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "N*d exceeds 2^31-1");
+  return FA_OK;
+}
+
+int check_tensor(const void* p, const char* name, size_t align) {
+  if (!p) return fail(FA_ERR_INVALID_ARG, "%s is NULL", name);
+  if (!aligned(p, align)) return fail(FA_ERR_INVALID_ARG, "%s is not %zu-byte aligned", name, align);
+  return FA_OK;
+}
+
+int check_block(const uint8_t* block_mask, int block_size, bool required) {
+  if (!block_mask) {
+    if (required) return fail(FA_ERR_INVALID_ARG, "block_mask is NULL");
+    return FA_OK;
+  }
+  if (block_size != 128)
+    return fail(FA_ERR_UNSUPPORTED, "block_size=%d (supported: 128)", block_size);
+  return FA_OK;
+}
+
+int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                 int N, int d, float scale, int causal, const int32_t* key_lens,
+                 const uint8_t* block_mask, int block_size, bool sparse, fa_dtype dtype,
+                 hipStream_t stream) {
+  g_detail[0] = 0;
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_block(block_mask, block_size, sparse)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
+      (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||
+      (st = check_tensor(lse, "lse", 4)))
+    return st;
+  if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
+  fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
+  fa::FwdTensors t{q, k, v, o, lse};
+  hipError_t e = fa::launch_forward(p, t);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+extern "C" {
+
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+               int N, int d, float scale, int causal, const int32_t* key_lens, fa_dtype dtype,
+               hipStream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, nullptr, 128, false,
+                      dtype, stream);
+}
+
+int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o, float* lse,
+                           int B, int H, int N, int d, float scale, int causal,
+                           const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                           fa_dtype dtype, hipStream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
+                      block_size, true, dtype, stream);
+}
+
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
+  return round_up((size_t)B * H * N * sizeof(float), 256);
+}
+
+int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
+                int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream) {
+  g_detail[0] = 0;
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_block(block_mask, block_size, false)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
+      (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||
+      (st = check_tensor(dout, "dout", 16)) || (st = check_tensor(lse, "lse", 4)) ||
+      (st = check_tensor(dq, "dq", 16)) || (st = check_tensor(dk, "dk", 16)) ||
+      (st = check_tensor(dv, "dv", 16)))
+    return st;
+  if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
+  const size_t need = fa_backward_workspace_bytes(B, H, N, d);
+  if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
+  fa::BwdTensors t{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace)};
+  hipError_t e = fa::launch_backward(p, t);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
+const char* fa_status_string(int status) {
+  switch (status) {
+    case FA_OK: return "FA_OK";
+    case FA_ERR_INVALID_ARG: return "FA_ERR_INVALID_ARG";
+    case FA_ERR_UNSUPPORTED: return "FA_ERR_UNSUPPORTED";
+    case FA_ERR_WORKSPACE: return "FA_ERR_WORKSPACE";
+    case FA_ERR_HIP: return "FA_ERR_HIP";
+  }
+  return "FA_ERR_UNKNOWN";
+}
+
+const char* fa_last_error_detail(void) { return g_detail; }
+
+int fa_timing_enable(int enable) {
+  g_timing = enable != 0;
+  return FA_OK;
+}
+
+int fa_timing_read(int kernel, double* total_ms, int* launches) {
+  if (kernel < 0 || kernel >= fa::kNumKernelKinds || !total_ms || !launches)
+    return fail(FA_ERR_INVALID_ARG, "bad timing query");
+  KindTimes& t = g_times[kernel];
+  double total = 0.0;
+  for (size_t i = 0; i < t.used; ++i) {
+    if (hipEventSynchronize(t.pool[i].stop) != hipSuccess)
+      return fail(FA_ERR_HIP, "hipEventSynchronize failed");
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, t.pool[i].start, t.pool[i].stop) != hipSuccess)
+      return fail(FA_ERR_HIP, "hipEventElapsedTime failed");
+    total += ms;
+  }
+  *total_ms = total;
+  *launches = (int)t.used;
+  t.used = 0;
+  return FA_OK;
+}
+
+const char* fa_kernel_name(int kernel) {
+  switch (kernel) {
+    case fa::kFwd: return "fa_fwd_kernel";
+    case fa::kBwdPre: return "fa_bwd_preprocess_kernel";
+    case fa::kBwdDkDv: return "fa_bwd_dkdv_kernel";
+    case fa::kBwdDq: return "fa_bwd_dq_kernel";
+  }
+  return "unknown";
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// Host-side interface between the C ABI layer (fa_api.cpp) and the kernel
+// launchers (fa_fwd.hip, fa_bwd.hip).  Arguments arrive here validated.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum KernelKind { kFwd = 0, kBwdPre = 1, kBwdDkDv = 2, kBwdDq = 3, kNumKernelKinds = 4 };
+
+struct Problem {
+  int B, H, N, d;
+  float scale;
+  int causal;
+  const int32_t* key_lens;    // device, may be null
+  const uint8_t* block_mask;  // device, may be null
+  int dtype;                  // fa_dtype
+  hipStream_t stream;
+};
+
+struct FwdTensors {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+};
+
+struct BwdTensors {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dvec;  // D = rowsum(dO * O), float32 [B, H, N], in the caller's workspace
+};
+
+// Event bracketing of launches (active only while timing is enabled).
+void timing_begin(KernelKind kind, hipStream_t stream);
+void timing_end(KernelKind kind, hipStream_t stream);
+
+hipError_t launch_forward(const Problem& p, const FwdTensors& t);
+hipError_t launch_backward(const Problem& p, const BwdTensors& t);
+
+}  // namespace fa

@@ -1,0 +1,137 @@
+/*
+ * fa.h - tiled exact attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libfa.so.  Every tensor argument is a DEVICE pointer owned by the
+ * caller; the library never allocates, frees or synchronises memory it was
+ * handed, and it launches all work asynchronously on the caller's stream.
+ * Asynchronous kernel faults surface at the caller's next synchronisation.
+ *
+ * Method (FlashAttention, as summarised by the review page "FlashAttention"
+ * of agent-readings, section "Method", and the slides' steps 01-04): exact
+ * softmax(scale * Q K^T) V is computed tile by tile.  Q, K and V are cut into
+ * blocks that fit in on-chip memory, each score tile is formed on chip, a
+ * running row maximum and denominator (online softmax, visual guide,
+ * "online softmax" paragraph) rescale the partial outputs, and only the
+ * output O and one normalisation value per row (the logsumexp) reach HBM.
+ * The backward pass recomputes score tiles from that logsumexp instead of
+ * reading an N x N matrix (review page, claim C7).
+ *
+ * Common conventions
+ *   Layout     Q, K, V, O, dO, dQ, dK, dV: [B, H, N, d] contiguous, d fastest.
+ *              LSE: [B, H, N] float32, natural log: LSE_i = ln sum_j exp(S_ij)
+ *              over the keys visible to query i, S = scale * Q K^T.
+ *   dtype      FA_F32, FA_F16 or FA_BF16 for all of Q, K, V, O, dO, dQ, dK, dV.
+ *              16-bit inputs use bf16/fp16 matrix cores with fp32 accumulation;
+ *              probabilities are rounded to the input dtype (round to nearest
+ *              even) before the P V product.  FA_F32 computes in fp32 only.
+ *   d          64 or 128.
+ *   scale      finite and >= 0 (the usual value is 1/sqrt(d)).
+ *   causal     nonzero: key j is visible to query i only if j <= i.
+ *   key_lens   int32[B] on the device, or NULL.  Key j of batch b is visible
+ *              only if j < key_lens[b] (values are clamped to [0, N]); query
+ *              rows are never masked by it.
+ *   block_mask uint8[nb][nb] on the device, nb = ceil(N / block_size), one
+ *              mask shared by every (b, h); entry (I, J) != 0 keeps the keys
+ *              of block J for the queries of block I (visual guide,
+ *              block-sparse paragraph).  block_size must be 128.
+ *   Masks combine by logical AND.  A query row with no visible key gets
+ *   O = 0 and LSE = -inf and contributes nothing to any gradient.
+ *   Empty problems (B, H or N equal to 0) return FA_OK and launch nothing.
+ *   Alignment  tensors of the input dtype and the workspace: 16 bytes;
+ *              LSE, key_lens: 4 bytes.
+ *
+ * Errors: every argument is checked on the host before any HIP call.  A bad
+ * argument returns FA_ERR_INVALID_ARG or FA_ERR_UNSUPPORTED and nothing is
+ * launched; a failed launch returns FA_ERR_HIP.  fa_last_error_detail() then
+ * describes the failure (thread-local text, valid until the next call on the
+ * same thread).  No C++ exception crosses this interface.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_F32 = 0, FA_F16 = 1, FA_BF16 = 2 } fa_dtype;
+
+typedef enum {
+  FA_OK = 0,
+  FA_ERR_INVALID_ARG = 1,   /* null pointer, negative size, misalignment, ... */
+  FA_ERR_UNSUPPORTED = 2,   /* well-formed but not provided: d, block_size, scale < 0 */
+  FA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required */
+  FA_ERR_HIP = 4            /* the HIP runtime reported an error */
+} fa_status;
+
+/*
+ * Forward pass (review page, "Method": tiles of Q, K, V in on-chip memory,
+ * online softmax, write only the output and small normalisation values).
+ * Reads q, k, v; writes o [B,H,N,d] (dtype) and lse [B,H,N] (float32).
+ */
+int fa_forward(const void* q, const void* k, const void* v, void* o, float* lse,
+               int B, int H, int N, int d, float scale, int causal,
+               const int32_t* key_lens, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Block-sparse forward (visual guide, block-sparse paragraph; review page,
+ * "Method", last step): as fa_forward, with key/value tiles whose block_mask
+ * entry is zero never loaded.  block_mask must not be NULL.  The result is
+ * exact attention under the block mask.
+ */
+int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
+                           float* lse, int B, int H, int N, int d, float scale,
+                           int causal, const int32_t* key_lens,
+                           const uint8_t* block_mask, int block_size,
+                           fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Backward pass (review page, "Method" and claim C7: recompute the attention
+ * tiles on chip from the saved normalisation values).  Gradient of
+ * L = sum(dout * o): with P = exp(S - LSE), D = rowsum(dout * o),
+ * dV = P^T dout, dP = dout V^T, dS = P * (dP - D), dQ = scale * dS K,
+ * dK = scale * dS^T Q.
+ * o and lse must come from fa_forward / fa_forward_blocksparse called with
+ * the same q, k, v, sizes, scale and masks.  block_mask may be NULL (dense);
+ * block_size is ignored then.  Overwrites dq, dk, dv (dtype).
+ * workspace: device memory of at least fa_backward_workspace_bytes(B,H,N,d)
+ * bytes, 16-byte aligned, owned by the caller, contents need not be
+ * initialised; it holds D as float32 [B,H,N].  Calls that share a workspace
+ * must be ordered on one stream.
+ */
+int fa_backward(const void* q, const void* k, const void* v, const void* o,
+                const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                int B, int H, int N, int d, float scale, int causal,
+                const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                hipStream_t stream);
+
+/* Workspace bytes fa_backward needs for these sizes (0 for an empty problem). */
+size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
+
+/* Name of a status code; never NULL. */
+const char* fa_status_string(int status);
+
+/* Detail of the last non-OK return on the calling thread ("" if none). */
+const char* fa_last_error_detail(void);
+
+/*
+ * Kernel timing.  While enabled, every kernel the library launches is
+ * bracketed by a pair of HIP events recorded on the launch stream.
+ * fa_timing_read() waits for the recorded events of one kernel kind, returns
+ * the summed elapsed milliseconds and the launch count, and clears them.
+ * kernel: 0 forward, 1 backward preprocess (D), 2 backward dK/dV,
+ * 3 backward dQ.  Not thread-safe; meant for benchmarks.
+ */
+int fa_timing_enable(int enable);
+int fa_timing_read(int kernel, double* total_ms, int* launches);
+const char* fa_kernel_name(int kernel);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,125 @@
+"""CPU tests of the C ABI: libfa.so loads, exports every function include/fa.h
+declares, and rejects bad arguments on the host before any HIP call (so no
+GPU is needed).  Pointers passed here are never dereferenced: each call is
+built to fail validation."""
+
+import ctypes
+import os
+import re
+
+import pytest
+
+from exact_io_aware_52_amd import _binding, build_lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(_binding.library_path()):
+        build_lib.build()
+    return _binding.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for want in ("fa_forward", "fa_forward_blocksparse", "fa_backward",
+                 "fa_backward_workspace_bytes", "fa_status_string", "fa_last_error_detail"):
+        assert want in names
+
+
+def test_library_exports_every_declared_function(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+FAKE = 0x10000           # 16-byte aligned, never dereferenced
+BAD_ALIGN = 0x10002
+
+
+def fwd(lib, q=FAKE, o=FAKE, lse=FAKE, B=1, H=1, N=64, d=64, scale=0.125, causal=0,
+        key_lens=None, dtype=2):
+    return lib.fa_forward(q, FAKE, FAKE, o, lse, B, H, N, d, scale, causal, key_lens, dtype, None)
+
+
+def detail(lib):
+    return lib.fa_last_error_detail().decode()
+
+
+def test_forward_validation(lib):
+    assert fwd(lib, q=None) == _binding.FA_ERR_INVALID_ARG
+    assert "q is NULL" in detail(lib)
+    assert fwd(lib, q=BAD_ALIGN) == _binding.FA_ERR_INVALID_ARG
+    assert "aligned" in detail(lib)
+    assert fwd(lib, lse=FAKE + 2) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, d=96) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd(lib, d=32) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd(lib, B=-1) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, N=-5) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, dtype=7) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, scale=-1.0) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd(lib, scale=float("nan")) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, scale=float("inf")) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, key_lens=FAKE + 1, q=None) == _binding.FA_ERR_INVALID_ARG
+    assert fwd(lib, B=1 << 20, H=1 << 10, N=1 << 20) == _binding.FA_ERR_INVALID_ARG
+
+
+def test_empty_problems_are_noops(lib):
+    # Nothing to compute: OK without touching any pointer.
+    assert fwd(lib, q=None, o=None, lse=None, N=0) == _binding.FA_OK
+    assert fwd(lib, q=None, o=None, lse=None, B=0) == _binding.FA_OK
+    assert lib.fa_backward(None, None, None, None, None, None, None, None, None, 1, 0, 10, 64,
+                           0.1, 0, None, None, 128, 2, None, 0, None) == _binding.FA_OK
+    assert lib.fa_backward_workspace_bytes(0, 4, 10, 64) == 0
+
+
+def test_blocksparse_validation(lib):
+    f = lib.fa_forward_blocksparse
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 64, 0.1, 0, None, None, 128, 2, None) \
+        == _binding.FA_ERR_INVALID_ARG
+    assert "block_mask" in detail(lib)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 64, 0.1, 0, None, FAKE, 64, 2, None) \
+        == _binding.FA_ERR_UNSUPPORTED
+
+
+def bwd(lib, ws=FAKE, ws_bytes=1 << 30, dq=FAKE, bm=None, bs=128, d=64, N=100):
+    return lib.fa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, 2, 3, N, d, 0.1, 1,
+                           None, bm, bs, 1, ws, ws_bytes, None)
+
+
+def test_backward_validation(lib):
+    need = lib.fa_backward_workspace_bytes(2, 3, 100, 64)
+    assert need >= 2 * 3 * 100 * 4 and need % 256 == 0
+    assert bwd(lib, ws=None) == _binding.FA_ERR_WORKSPACE
+    assert bwd(lib, ws_bytes=need - 1) == _binding.FA_ERR_WORKSPACE
+    assert "needed" in detail(lib)
+    assert bwd(lib, ws=FAKE + 8) == _binding.FA_ERR_INVALID_ARG
+    assert bwd(lib, dq=None) == _binding.FA_ERR_INVALID_ARG
+    assert bwd(lib, dq=BAD_ALIGN) == _binding.FA_ERR_INVALID_ARG
+    assert bwd(lib, bm=FAKE, bs=256) == _binding.FA_ERR_UNSUPPORTED
+    assert bwd(lib, d=80) == _binding.FA_ERR_UNSUPPORTED
+
+
+def test_status_strings_and_timing(lib):
+    assert lib.fa_status_string(0) == b"FA_OK"
+    assert lib.fa_status_string(3) == b"FA_ERR_WORKSPACE"
+    assert lib.fa_status_string(99) == b"FA_ERR_UNKNOWN"
+    assert lib.fa_kernel_name(0) == b"fa_fwd_kernel"
+    ms, n = ctypes.c_double(), ctypes.c_int()
+    assert lib.fa_timing_read(2, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert n.value == 0 and ms.value == 0.0
+    assert lib.fa_timing_read(9, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    q = torch.zeros(1, 1, 8, 64)
+    with pytest.raises(Exception):
+        _binding.fa_forward(q, q, q)          # no silent CPU fallback
