@@ -142,7 +142,11 @@ __global__ __launch_bounds__(256) void fa_bwd_preprocess_kernel(BwdParams p, lon
 template <typename T, int D>
 struct DkDvCfg {
   typedef raw_t<T> raw;
+  // 64 query rows per step.  At d = 128 the persistent per-wave state (K, V
+  // operands and the dK, dV accumulators: 192 VGPRs) only fits one wave per
+  // SIMD, so one work-group per CU may use 140 KB of double-buffered LDS.
   static constexpr int BQ = (sizeof(raw) == 4 && D == 128) ? 32 : 64;
+  static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
   static constexpr int RS = D + 16 / (int)sizeof(raw);  // row-major stride (+16 B)
   static constexpr int TS = BQ + 4;                      // transposed stride
   static constexpr int Q_ELEMS = BQ * RS;
@@ -153,7 +157,8 @@ struct DkDvCfg {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    DkDvCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
@@ -351,7 +356,9 @@ __global__ __launch_bounds__(256) void fa_bwd_dkdv_kernel(BwdParams p) {
 template <typename T, int D>
 struct DqCfg {
   typedef raw_t<T> raw;
-  static constexpr int BC = (sizeof(raw) == 4 && D == 128) ? 32 : 64;
+  // 64 keys per step at d = 64; 32 at d = 128 so that two work-groups
+  // (double-buffered stages) fit in one CU's LDS.
+  static constexpr int BC = D == 128 ? 32 : 64;
   static constexpr int RS = D + 16 / (int)sizeof(raw);
   static constexpr int TS = BC + 4;
   static constexpr int K_ELEMS = BC * RS;
@@ -360,7 +367,8 @@ struct DqCfg {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(
+    BwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;

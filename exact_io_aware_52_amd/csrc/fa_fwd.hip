@@ -64,7 +64,10 @@ struct FwdSmem {
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_fwd_kernel(FwdParams p) {
+// Two waves per SIMD: one wave's softmax can run while the other's matrix
+// products do.
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(
+    FwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
