@@ -91,13 +91,19 @@ int check_tensor(const void* p, const char* name, size_t align) {
   return FA_OK;
 }
 
-int check_block(const uint8_t* block_mask, int block_size, bool required) {
+// Kernels cache one row of the block mask in LDS: at most 1024 blocks.
+constexpr int kMaxMaskBlocks = 1024;
+
+int check_block(const uint8_t* block_mask, int block_size, int N, bool required) {
   if (!block_mask) {
     if (required) return fail(FA_ERR_INVALID_ARG, "block_mask is NULL");
     return FA_OK;
   }
   if (block_size != 128)
     return fail(FA_ERR_UNSUPPORTED, "block_size=%d (supported: 128)", block_size);
+  if ((N + 127) / 128 > kMaxMaskBlocks)
+    return fail(FA_ERR_UNSUPPORTED, "block mask for N=%d exceeds %d blocks per row", N,
+                kMaxMaskBlocks);
   return FA_OK;
 }
 
@@ -109,7 +115,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
   if (st != FA_OK) return st;
-  if ((st = check_block(block_mask, block_size, sparse)) != FA_OK) return st;
+  if ((st = check_block(block_mask, block_size, N, sparse)) != FA_OK) return st;
   if (empty) return FA_OK;
   if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
       (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||
@@ -158,7 +164,7 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
   if (st != FA_OK) return st;
-  if ((st = check_block(block_mask, block_size, false)) != FA_OK) return st;
+  if ((st = check_block(block_mask, block_size, N, false)) != FA_OK) return st;
   if (empty) return FA_OK;
   if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
       (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||

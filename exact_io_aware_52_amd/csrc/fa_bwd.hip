@@ -41,7 +41,8 @@ template <> __device__ __forceinline__ float to_f32<float>(uint32_t r) { return 
 // ----------------------------------------------------------------------------
 // Stager for an R x D tile read as 4 x 4 element blocks: one global pass feeds
 // a row-major copy and/or a transposed copy in LDS.  Rows at or past `limit`
-// are filled with zeros.
+// are read from row limit-1 (a valid address; no predicated loads): every use
+// of such a row is masked by the caller.
 template <typename T, int R, int D>
 struct Stager {
   typedef raw_t<T> raw;
@@ -57,13 +58,8 @@ struct Stager {
       const int a = c / (D / 4), bc = c % (D / 4);
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int row = row0 + 4 * a + e;
-        if (row < limit) {
-          reg[i][e] = *reinterpret_cast<const raw4*>(g + (size_t)row * D + 4 * bc);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) reg[i][e][t] = 0;
-        }
+        const int row = min(row0 + 4 * a + e, limit - 1);
+        reg[i][e] = *reinterpret_cast<const raw4*>(g + (size_t)row * D + 4 * bc);
       }
     }
   }

@@ -118,6 +118,129 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// ---------------------------------------------------------------- LDS staging
+// Byte address of a __shared__ object within LDS.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// Direct HBM -> LDS copy: lane i's 16 bytes at g land at LDS byte lds + 16 i.
+// Written as inline asm so that the compiler does not order every later LDS
+// read behind it; callers wait for completion with wait_vmcnt and a barrier.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "s"(lds)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Wait until at most N of this wave's vector-memory operations are in flight.
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Row-major tiles in LDS are stored as 16-byte chunks, with the chunk index of
+// row r XORed by swizzle(r) so that the reads below hit distinct banks (there
+// is no room for row padding: a DMA wave writes 1 KB contiguously).
+//   K-style reads (ds_read_b128, lanes on 32 consecutive rows, same chunk):
+//     8 chunks per row: (r >> 1) & 7;   16+ chunks per row: r & 15.
+//   Transposed reads (ds_read_b64_tr_b16, 8 rows x 4 chunks per wave):
+//     8 chunks per row: ((r >> 1) & 1) << 2;   16 chunks per row: (r & 3) << 2.
+template <int CPR> __device__ __forceinline__ int swz_rows(int r) {
+  return CPR >= 16 ? (r & 15) : ((r >> 1) & 7);
+}
+template <int CPR> __device__ __forceinline__ int swz_tr(int r) {
+  return CPR >= 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+}
+
+// Copies rows row0 .. row0+ROWS-1 (D elements each, row-major in HBM; rows
+// past N-1 repeat row N-1) into an LDS tile at byte address `lds` with the
+// given chunk swizzle.  The tile is split over the work-group's 4 waves; each
+// wave issues ROWS*D*sizeof(raw)/4096 DMA instructions.
+template <typename raw, int ROWS, int D, bool TR>
+__device__ __forceinline__ void dma_tile(const raw* __restrict__ g, int row0, int N, uint32_t lds,
+                                         int wave, int lane) {
+  constexpr int CPR = D * (int)sizeof(raw) / 16;  // chunks per row
+  constexpr int VEC = 16 / (int)sizeof(raw);
+  constexpr int NI = ROWS * CPR / 256;           // instructions per wave
+  static_assert(ROWS * CPR % 256 == 0, "tile must split into 1 KB per-wave pieces");
+#pragma unroll
+  for (int i = 0; i < NI; ++i) {
+    const int blk = i * 4 + wave;        // 1 KB block of the tile
+    const int pos = blk * 64 + lane;     // chunk position within the tile
+    const int r = pos / CPR, cs = pos % CPR;
+    const int c = cs ^ (TR ? swz_tr<CPR>(r) : swz_rows<CPR>(r));
+    const int row = min(row0 + r, N - 1);
+    dma16(g + (size_t)row * D + c * VEC, lds + blk * 1024);
+  }
+}
+
+// Eight contiguous elements of row `row` starting at element `col` (a multiple
+// of 8 / 4 for 16- / 32-bit types) from a swizzled row-major tile.
+template <typename T, int D>
+__device__ __forceinline__ frag_t<T> load_frag_swz(const raw_t<T>* tile, int row, int col) {
+  constexpr int CPR = D * (int)sizeof(raw_t<T>) / 16;
+  constexpr int VEC = 16 / (int)sizeof(raw_t<T>);
+  const raw_t<T>* rp = tile + row * D;
+  if constexpr (VEC == 8) {
+    return load_frag<T>(rp + (((col / VEC) ^ swz_rows<CPR>(row)) * VEC));
+  } else {
+    typedef raw_t<T> raw4v __attribute__((ext_vector_type(4)));
+    const raw4v lo = *reinterpret_cast<const raw4v*>(rp + (((col / VEC) ^ swz_rows<CPR>(row)) * VEC));
+    const raw4v hi = *reinterpret_cast<const raw4v*>(rp + ((((col / VEC) + 1) ^ swz_rows<CPR>(row)) * VEC));
+    raw8_t<T> r8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r8[i] = lo[i]; r8[4 + i] = hi[i]; }
+    return __builtin_bit_cast(frag_t<T>, r8);
+  }
+}
+
+// Acc-ordered A operand of a product whose contraction runs over the ROWS of a
+// row-major tile (e.g. V^T P^T: rows = keys): lane (c, h) receives elements
+// (k0 + pi(h, s), col0 + c), pi the acc-ordered slot map.  16-bit types use
+// two transposed LDS reads (ds_read_b64_tr_b16: within each 16-lane group,
+// lane j takes element j % 4 of the 8-byte rows addressed by lanes
+// j / 4 + 4t, t = 0..3); the tile must use the swz_tr swizzle.  fp32 reads
+// the eight elements one by one (swz_rows swizzle).
+template <typename T, int D>
+__device__ __forceinline__ frag_t<T> load_frag_tr(const raw_t<T>* tile, int k0, int col0,
+                                                  int lane) {
+  typedef raw_t<T> raw;
+  constexpr int CPR = D * (int)sizeof(raw) / 16;
+  if constexpr (sizeof(raw) == 2) {
+    typedef short s16x4 __attribute__((ext_vector_type(4)));
+    typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+    const int g = lane >> 4, s = lane & 15;
+    const int r0 = k0 + 4 * (g >> 1) + (s >> 2);
+    const int col = col0 + 16 * (g & 1) + 4 * (s & 3);  // 4 elements = half a chunk
+    auto addr = [&](int r) {
+      const int chunk = (col >> 3) ^ swz_tr<CPR>(r);
+      return (lds_s16x4*)(const __attribute__((address_space(3))) raw*)(tile + r * D + chunk * 8 +
+                                                                          (col & 7));
+    };
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(r0));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(addr(r0 + 8));
+    raw8_t<T> r8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { r8[i] = (raw)lo[i]; r8[4 + i] = (raw)hi[i]; }
+    return __builtin_bit_cast(frag_t<T>, r8);
+  } else {
+    const int c = lane & 31, h = lane >> 5;
+    const int col = col0 + c;
+    raw8_t<T> r8;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int r = k0 + (u < 4 ? 4 * h + u : 8 + 4 * h + (u - 4));
+      r8[u] = tile[r * D + (((col / 4) ^ swz_rows<CPR>(r)) * 4) + (col & 3)];
+    }
+    return __builtin_bit_cast(frag_t<T>, r8);
+  }
+}
+
 // Work-group id -> (tile, head) for a grid of ntiles * BH work-groups.
 // Work-groups are dispatched round-robin over the 8 XCDs (id % 8); when BH is a
 // multiple of 8 every tile of one head is kept on one XCD so that its K/V (or

@@ -1,31 +1,43 @@
 // Tiled exact attention, forward pass, for gfx950.
 //
 // FlashAttention forward (review page "Method"; slides steps 01-04; visual
-// guide, "online softmax"): each work-group owns one tile of BR = 128 query
-// rows of one (b, h) head and streams the key/value tiles that tile needs
-// through LDS.  Scores never leave the compute unit; only O and the per-row
+// guide, "online softmax"): each work-group owns one tile of 128 query rows
+// of one (b, h) head and streams the key/value tiles that tile needs through
+// LDS.  Scores never leave the compute unit; only O and the per-row
 // logsumexp are written.  The pages' pseudocode runs key/value blocks in the
 // outer loop and carries per-query-block state through memory; here the
 // query tile is the outer (grid) dimension so that its state (running max m,
 // denominator l, fp32 accumulator) stays in registers for the whole sweep.
 // Both orders give the same result in exact arithmetic.
 //
-// Work split: 4 waves, wave w owns queries i0 + 32w .. i0 + 32w + 31.  Each
-// step a wave forms the transposed score tile S^T (keys x queries) for a
-// BC = 64-key tile: A = K tile rows from LDS, B = the wave's Q rows, held in
-// registers for the whole kernel.  With keys as accumulator rows, each lane
-// owns one query column, so the row max and row sum of the softmax are an
-// in-register reduction plus one exchange with the lane 32 apart, and the
-// exponentiated tile is already the B operand of O^T += V^T P^T (V^T is
-// written to LDS transposed when the tile is staged).
+// Work split: 4 waves, wave w owns queries i0 + 32w .. i0 + 32w + 31.  For a
+// tile of BC keys a wave forms the transposed score tile S^T (keys x
+// queries): A = K rows from LDS, B = the wave's Q rows, held in registers for
+// the whole kernel.  With keys as accumulator rows each lane owns one query
+// column, so the row max and row sum are in-register reductions plus one
+// exchange with the lane 32 apart, and the exponentiated tile is already the
+// B operand of O^T += V^T P^T (V^T is written to LDS transposed when staged).
 //
-// Pipeline: K/V tile j+1 is fetched from HBM into registers while tile j is
-// being multiplied; it is written to the other half of a double buffer in LDS
-// after the step, and one barrier per step separates the two.
+// Staging: K and V tiles go from HBM straight into a 4-slot LDS ring by
+// direct-to-LDS loads (no staging registers, no vector instructions); a tile
+// is requested two steps before its keys are first used.  K is read as
+// row-major matrix operands; V^T, the A operand of O^T += V^T P^T, is read
+// from the row-major V tile with the transposing LDS read.
 //
-// Masks are decided per tile: tiles beyond the causal diagonal, past the key
-// length or with a zero block-mask entry are skipped (never loaded); only the
-// tiles that straddle a boundary apply an element mask.
+// Software pipeline: K runs one tile ahead of V.  In step i a wave issues
+// the matrix products of the next tile's scores while it exponentiates the
+// current tile and accumulates P V for it, so one wave always has
+// independent matrix-core and vector work in flight.  One barrier per step.
+//
+// Online softmax with lazy rescaling: the running max m only moves (and the
+// accumulator and denominator are rescaled) when a new tile's max exceeds it
+// by more than 2^8 in exp2 units; otherwise probabilities are taken relative
+// to the stale max (at most 256, exactly representable scale).  The result is
+// the same exact softmax.
+//
+// Masks are decided per tile: tiles past the causal diagonal, past the key
+// length or with a zero block-mask entry are skipped (never loaded); only
+// tiles that straddle a boundary apply an element mask, on a slower path.
 
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -35,8 +47,8 @@ namespace {
 
 constexpr int kFwdWaves = 4;
 constexpr int kFwdBR = 32 * kFwdWaves;  // query rows per work-group
-constexpr int kFwdBC = 64;              // keys per staged K/V tile
 constexpr int kMaskBlock = 128;         // block-mask granularity (keys and queries)
+constexpr float kLazy = 8.0f;           // rescale when the max grows by > 2^8
 
 struct FwdParams {
   const void* q;
@@ -52,33 +64,70 @@ struct FwdParams {
   int causal;
 };
 
-template <typename T, int D>
-struct FwdSmem {
-  typedef raw_t<T> raw;
-  static constexpr int VEC = 16 / sizeof(raw);       // elements per 16-byte chunk
-  static constexpr int KS = D + VEC;                 // K row stride (+16 B against bank conflicts)
-  static constexpr int VTS = kFwdBC + 4;              // V^T row stride (+4 elements)
-  static constexpr int K_ELEMS = kFwdBC * KS;
-  static constexpr int V_ELEMS = D * VTS;
-  static constexpr int STAGE = K_ELEMS + V_ELEMS;
-};
+constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 131072)
 
 template <typename T, int D>
-// Two waves per SIMD: one wave's softmax can run while the other's matrix
-// products do.
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_fwd_kernel(
-    FwdParams p) {
+struct FwdCfg {
+  typedef raw_t<T> raw;
+  static constexpr int BC = D == 128 ? 32 : 64;                // keys per step
+  static constexpr int NKB = BC / 32;                           // 32-key blocks per step
+  static constexpr int NS = 4;                                  // LDS ring slots
+  static constexpr int TILE_BYTES = BC * D * (int)sizeof(raw);  // one K or V tile
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
+  static constexpr int LPT = 2 * TILE_BYTES / 4096;             // DMA instructions per wave per tile
+  // Two waves per SIMD for 16-bit inputs; the fp32 instances (accuracy, not
+  // speed) take the whole register file.
+  static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
+};
+
+// Sum of the eight probabilities of a B-operand fragment, added to acc.  For
+// 16-bit types the sum is taken over the rounded values the P V product uses.
+__device__ __forceinline__ float frag_sum(const frag_t<__bf16>& f, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {(__bf16)1.f, (__bf16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bf16x2 pr = {f[2 * i], f[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2_f32_bf16(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const frag_t<_Float16>& f, float acc) {
+  typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+  const f16x2 one = {(_Float16)1.f, (_Float16)1.f};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f16x2 pr = {f[2 * i], f[2 * i + 1]};
+    acc = __builtin_amdgcn_fdot2(pr, one, acc, false);
+  }
+  return acc;
+}
+__device__ __forceinline__ float frag_sum(const frag_t<float>& f, float acc) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc += f[i];
+  return acc;
+}
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    FwdCfg<T, D>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef FwdSmem<T, D> L;
-  constexpr int BC = kFwdBC;
-  constexpr int VEC = L::VEC;
-  constexpr int KCH = BC * D / VEC / 256;  // 16-byte K chunks per thread
-  constexpr int VBL = BC * D / 16 / 256;   // 4x4 V blocks per thread
-  static_assert(KCH >= 1 && VBL >= 1, "tile too small for 256 threads");
+  typedef FwdCfg<T, D> L;
+  constexpr int BC = L::BC;
+  constexpr int NKB = L::NKB;
 
-  __shared__ __attribute__((aligned(16))) raw smem[2 * L::STAGE];
+  constexpr int LPT = L::LPT;
+  constexpr bool TRV = sizeof(raw) == 2;  // V^T through transposing LDS reads
+
+  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ uint8_t mask_row[kMaxMaskBlocks];
+  const uint32_t ring_lds = lds_addr(ring);
+  auto ktile = [&](int s) { return reinterpret_cast<const raw*>(ring + s * L::SLOT_BYTES); };
+  auto vtile = [&](int s) {
+    return reinterpret_cast<const raw*>(ring + s * L::SLOT_BYTES + L::TILE_BYTES);
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -92,17 +141,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   const int N = p.N;
   const int i0 = qt * kFwdBR;
   const int qw0 = i0 + 32 * w;  // first query of this wave
+  const int myq = qw0 + col;
 
   int kend = N;
   if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
   int kv_end = kend;
   if (p.causal) kv_end = min(kv_end, i0 + kFwdBR);
   const int nkt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
-  const uint8_t* bm = p.block_mask ? p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk : nullptr;
-  auto kept = [&](int j) { return bm == nullptr || bm[(j * BC) / kMaskBlock] != 0; };
+  const bool sparse = p.block_mask != nullptr;
+  if (sparse) {
+    const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
+    for (int i = tid; i < p.nblk; i += 256) mask_row[i] = bm[i];
+  }
   auto next_kept = [&](int j) {
-    while (j < nkt && !kept(j)) ++j;
+    while (j < nkt && sparse && mask_row[(j * BC) / kMaskBlock] == 0) ++j;
     return j;
+  };
+  // Tile t holds keys t*BC .. t*BC+BC-1.  A wave skips tiles wholly past its
+  // causal diagonal and element-masks tiles that straddle a boundary.
+  auto active = [&](int t) { return !p.causal || t * BC <= qw0 + 31; };
+  auto masked = [&](int t) {
+    return (p.causal && t * BC + BC - 1 > qw0) || (t * BC + BC > kend);
   };
 
   const size_t head = (size_t)bh * N * D;
@@ -112,167 +171,171 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
 
   // The wave's Q rows as B operands (contiguous slot map over d).
   frag_t<T> qf[D / 16];
-  {
-    const int qrow = qw0 + col;
 #pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-      qf[kc] = qrow < N ? load_frag<T>(Qg + (size_t)qrow * D + kc * 16 + hh * 8) : zero_frag<T>();
-  }
+  for (int kc = 0; kc < D / 16; ++kc)
+    qf[kc] = myq < N ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
+  __syncthreads();  // mask_row visible
 
-  // Staging registers for one K/V tile.
-  uint4 kreg[KCH];
-  raw4 vreg[VBL][4];
-  auto fetch = [&](int j) {
-    const int kt0 = j * BC;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / VEC), cv = c % (D / VEC);
-      kreg[i] = kt0 + row < N
-                    ? *reinterpret_cast<const uint4*>(Kg + (size_t)(kt0 + row) * D + cv * VEC)
-                    : make_uint4(0, 0, 0, 0);
-    }
-#pragma unroll
-    for (int i = 0; i < VBL; ++i) {
-      const int c = tid + 256 * i;
-      const int a = c / (D / 4), bc = c % (D / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = kt0 + 4 * a + e;
-        if (row < N) {
-          vreg[i][e] = *reinterpret_cast<const raw4*>(Vg + (size_t)row * D + 4 * bc);
-        } else {
-#pragma unroll
-          for (int t = 0; t < 4; ++t) vreg[i][e][t] = 0;
-        }
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-    raw* Ks = smem + buf * L::STAGE;
-    raw* Vt = Ks + L::K_ELEMS;
-#pragma unroll
-    for (int i = 0; i < KCH; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c / (D / VEC), cv = c % (D / VEC);
-      *reinterpret_cast<uint4*>(Ks + row * L::KS + cv * VEC) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < VBL; ++i) {
-      const int c = tid + 256 * i;
-      const int a = c / (D / 4), bc = c % (D / 4);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        raw4 col4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) col4[e] = vreg[i][e][t];
-        *reinterpret_cast<raw4*>(Vt + (4 * bc + t) * L::VTS + 4 * a) = col4;
-      }
-    }
+  // K and V of tile t into ring slot s (LPT DMA instructions per wave).
+  auto issue = [&](int t, int s) {
+    const uint32_t base = ring_lds + s * L::SLOT_BYTES;
+    dma_tile<raw, BC, D, false>(Kg, t * BC, N, base, w, lane);
+    dma_tile<raw, BC, D, TRV>(Vg, t * BC, N, base + L::TILE_BYTES, w, lane);
   };
 
+  // ---- per-wave math
+  const float c = p.c;
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-  float m_run = kNegInf;  // running max of raw scores q.k for this lane's query
-  float l_run = 0.f;      // this lane's half of the running denominator
-  const float c = p.c;
-  const int myq = qw0 + col;
+  float m_run = kNegInf;  // running (possibly stale) max of raw scores, this lane's query
+  float l_run = 0.f;      // this lane's half of the denominator, relative to m_run
 
-  int j = next_kept(0);
-  if (j < nkt) {
-    fetch(j);
-    stash(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (j < nkt) {
-    const int jn = next_kept(j + 1);
-    if (jn < nkt) fetch(jn);
-    const int kt0 = j * BC;
-    const raw* Ks = smem + buf * L::STAGE;
-    const raw* Vt = Ks + L::K_ELEMS;
-
-    if (!p.causal || kt0 <= qw0 + 31) {
-      // S^T = K_j Q^T for this wave's 32 queries.
-      f32x16 sacc[BC / 32];
+  // S^T for one tile: rows = keys of the tile, columns = this wave's queries.
+  auto scores = [&](const raw* Ks, f32x16 (&s)[NKB]) {
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        sacc[kb] = zero16();
+    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const frag_t<T> a = load_frag<T>(Ks + (kb * 32 + col) * L::KS + kc * 16 + hh * 8);
-          sacc[kb] = Tr::mma(a, qf[kc], sacc[kb]);
-        }
+    for (int kc = 0; kc < D / 16; ++kc)
+#pragma unroll
+      for (int kb = 0; kb < NKB; ++kb) {
+        const frag_t<T> a = load_frag_swz<T, D>(Ks, kb * 32 + col, kc * 16 + hh * 8);
+        s[kb] = Tr::mma(a, qf[kc], s[kb]);
       }
-      const bool masked = (p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend);
-      if (masked) {
+  };
+  auto apply_mask = [&](int t, f32x16 (&s)[NKB]) {
 #pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int key = kt0 + kb * 32 + acc_row(r, hh);
-            if (key >= kend || (p.causal && key > myq)) sacc[kb][r] = kNegInf;
-          }
+      for (int r = 0; r < 16; ++r) {
+        const int key = t * BC + kb * 32 + acc_row(r, hh);
+        if (key >= kend || (p.causal && key > myq)) s[kb][r] = kNegInf;
       }
-      float mx = kNegInf;
+  };
+  auto tile_max = [&](const f32x16 (&s)[NKB]) {
+    float mx = kNegInf;
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-      mx = pair_max(mx);
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == kNegInf ? 0.f : m_new;
-      const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_use) * c);
-      const float mc = m_use * c;
-      float rs = 0.f;
-      if (masked) {
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float s = sacc[kb][r];
-            const float e = s == kNegInf ? 0.f : fast_exp2(fmaf(s, c, -mc));
-            sacc[kb][r] = e;
-            rs += e;
-          }
-      } else {
-#pragma unroll
-        for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = fast_exp2(fmaf(sacc[kb][r], c, -mc));
-            sacc[kb][r] = e;
-            rs += e;
-          }
-      }
-      l_run = fmaf(l_run, alpha, rs);
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
+    return pair_max(mx);
+  };
+  // Move the running max if this tile's max outruns it (wave-uniform branch).
+  auto maybe_rescale = [&](float m_tile) {
+    const bool need = m_tile > m_run && (m_run == kNegInf || (m_tile - m_run) * c > kLazy);
+    if (__builtin_amdgcn_ballot_w64(need) != 0) {
+      const float m_new = fmaxf(m_run, m_tile);
+      const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
       m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-
-      // O^T += V_j^T P^T.
-      frag_t<T> pf[BC / 16];
+    }
+  };
+  // P = exp2(c*s - c*m) rounded to T, as B operands; accumulates the row sum.
+  auto softmax = [&](const f32x16 (&s)[NKB], frag_t<T> (&pf)[2 * NKB], bool has_mask) {
+    const float mc = m_run == kNegInf ? 0.f : m_run * c;
+    float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        pf[2 * kb] = acc_to_frag<T>(sacc[kb], 0);
-        pf[2 * kb + 1] = acc_to_frag<T>(sacc[kb], 1);
-      }
+    for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+      for (int t = 0; t < 2; ++t) {
+        frag_t<T> f;
 #pragma unroll
-        for (int kc = 0; kc < BC / 16; ++kc) {
-          const frag_t<T> a = load_frag_acc_order<T>(Vt + (db * 32 + col) * L::VTS + kc * 16, hh);
-          oacc[db] = Tr::mma(a, pf[kc], oacc[db]);
+        for (int u = 0; u < 8; ++u) {
+          const float x = s[kb][8 * t + u];
+          float e = fast_exp2(fmaf(x, c, -mc));
+          if (has_mask) e = x == kNegInf ? 0.f : e;
+          f[u] = (T)e;
         }
+        pf[2 * kb + t] = f;
+        rs = frag_sum(f, rs);
+      }
+    l_run += rs;
+  };
+  auto pv = [&](const raw* Vs, const frag_t<T> (&pf)[2 * NKB]) {
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc)
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const frag_t<T> a = load_frag_tr<T, D>(Vs, kc * 16, db * 32, lane);
+        oacc[db] = Tr::mma(a, pf[kc], oacc[db]);
+      }
+  };
+
+  // Kept tiles of this work-group, in order; tl[k] is the tile of step i + k.
+  int tl[4];
+  tl[0] = next_kept(0);
+  tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
+  tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
+  tl[3] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+  if (tl[0] < nkt) {
+    issue(tl[0], 0);
+    if (tl[1] < nkt) issue(tl[1], 1);
+    if (tl[2] < nkt) issue(tl[2], 2);
+    // wait for tile 0 (later tiles may stay in flight)
+    if (tl[2] < nkt) wait_vmcnt<2 * LPT>();
+    else if (tl[1] < nkt) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+
+    f32x16 sa[NKB], sb[NKB];
+    float m_tile_a = kNegInf, m_tile_b = kNegInf;
+    if (active(tl[0])) {
+      scores(ktile(0), sa);
+      if (masked(tl[0])) apply_mask(tl[0], sa);
+      m_tile_a = tile_max(sa);
     }
 
-    if (jn < nkt) stash(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    j = jn;
+    // Step i: tile tl[0] (scores in scur, max m_cur) is exponentiated and
+    // multiplied into O; tile tl[1]'s scores go to snext.
+    int step = 0;
+    auto body = [&](f32x16 (&scur)[NKB], f32x16 (&snext)[NKB], float m_cur, float& m_next) {
+      const int t_cur = tl[0], t_nxt = tl[1];
+      if (t_nxt < nkt) {
+        // tile tl[1] must have landed; tl[2] may still be in flight
+        if (tl[2] < nkt) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+      }
+      __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
+      if (tl[3] < nkt) issue(tl[3], (step + 3) & 3);
+      const raw* Kn = ktile((step + 1) & 3);
+      const raw* Vc = vtile(step & 3);
+      const bool act_cur = active(t_cur);
+      const bool act_nxt = t_nxt < nkt && active(t_nxt);
+      if (act_cur) maybe_rescale(m_cur);
+      frag_t<T> pf[2 * NKB];
+      if (act_cur && act_nxt && !masked(t_cur) && !masked(t_nxt)) {
+        // interior: straight-line, next tile's products overlap this softmax
+        scores(Kn, snext);
+        softmax(scur, pf, false);
+        pv(Vc, pf);
+        m_next = tile_max(snext);
+      } else {
+        if (act_nxt) {
+          scores(Kn, snext);
+          if (masked(t_nxt)) apply_mask(t_nxt, snext);
+          m_next = tile_max(snext);
+        }
+        if (act_cur) {
+          softmax(scur, pf, masked(t_cur));
+          pv(Vc, pf);
+        }
+      }
+      tl[0] = tl[1];
+      tl[1] = tl[2];
+      tl[2] = tl[3];
+      tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+      ++step;
+    };
+    while (true) {
+      body(sa, sb, m_tile_a, m_tile_b);
+      if (tl[0] >= nkt) break;
+      body(sb, sa, m_tile_b, m_tile_a);
+      if (tl[0] >= nkt) break;
+    }
   }
 
   // Epilogue: O = acc / l, LSE = scale * m + ln(l).
@@ -286,9 +349,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
       for (int g = 0; g < 4; ++g) {
         raw4 out;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const T val = (T)(oacc[db][4 * g + t] * inv);
-          out[t] = __builtin_bit_cast(raw, val);
+        for (int u = 0; u < 4; ++u) {
+          const T val = (T)(oacc[db][4 * g + u] * inv);
+          out[u] = __builtin_bit_cast(raw, val);
         }
         *reinterpret_cast<raw4*>(Og + db * 32 + 8 * g + 4 * hh) = out;
       }

@@ -33,7 +33,8 @@
  *   block_mask uint8[nb][nb] on the device, nb = ceil(N / block_size), one
  *              mask shared by every (b, h); entry (I, J) != 0 keeps the keys
  *              of block J for the queries of block I (visual guide,
- *              block-sparse paragraph).  block_size must be 128.
+ *              block-sparse paragraph).  block_size must be 128 and
+ *              nb <= 1024 (N <= 131072) when a block mask is given.
  *   Masks combine by logical AND.  A query row with no visible key gets
  *   O = 0 and LSE = -inf and contributes nothing to any gradient.
  *   Empty problems (B, H or N equal to 0) return FA_OK and launch nothing.

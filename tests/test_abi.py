@@ -87,6 +87,10 @@ def test_blocksparse_validation(lib):
     assert "block_mask" in detail(lib)
     assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 64, 0.1, 0, None, FAKE, 64, 2, None) \
         == _binding.FA_ERR_UNSUPPORTED
+    # one mask row is cached on chip: at most 1024 blocks (N <= 131072)
+    assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 131073, 64, 0.1, 0, None, FAKE, 128, 2, None) \
+        == _binding.FA_ERR_UNSUPPORTED
+    assert "1024" in detail(lib)
 
 
 def bwd(lib, ws=FAKE, ws_bytes=1 << 30, dq=FAKE, bm=None, bs=128, d=64, N=100):
