@@ -152,7 +152,7 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
-  return round_up((size_t)B * H * N * sizeof(float), 256);
+  return round_up(2 * (size_t)B * H * N * sizeof(float), 256);
 }
 
 int fa_backward(const void* q, const void* k, const void* v, const void* o, const void* dout,

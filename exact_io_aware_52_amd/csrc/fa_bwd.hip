@@ -7,19 +7,24 @@
 //   dQ = scale dS K.
 //
 // Three launches on the caller's stream:
-//   1. fa_bwd_preprocess_kernel: D for every row (reads O and dO once).
+//   1. fa_bwd_preprocess_kernel: D and LSE * log2(e) for every row, into the
+//      caller's workspace (reads O and dO once).
 //   2. fa_bwd_dkdv_kernel: one work-group per 128 keys of a head; its four
 //      waves keep K, V (as matrix operands) and the dK, dV accumulators in
 //      registers and sweep the query tiles that see those keys.  The score
 //      tile is formed with queries as accumulator rows, so P and dS are the B
 //      operands of dV^T += dO^T P and dK^T += Q^T dS straight from registers;
-//      Q and dO are staged in LDS both row-major and transposed.
+//      dO^T and Q^T come from the row-major tiles by transposing LDS reads.
 //   3. fa_bwd_dq_kernel: one work-group per 128 queries; the same
 //      recomputation with keys as accumulator rows (as in the forward) feeds
-//      dQ^T += K^T dS^T, with K staged row-major and transposed.
+//      dQ^T += K^T dS^T, K^T again by transposing reads.
 // Splitting dQ into its own pass recomputes S and dP once more (6 d flops per
 // pair on top of the 8 d of the dK/dV pass) but needs no atomics, keeps every
 // accumulator in registers and makes the result deterministic.
+//
+// Streaming (both passes): the tiles of the streamed operand go from HBM
+// straight into a 4-slot LDS ring by direct-to-LDS loads, requested two steps
+// before use; one barrier per step.
 
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -28,6 +33,7 @@ namespace fa {
 namespace {
 
 constexpr int kMaskBlock = 128;
+constexpr int kMaxMaskBlocks = 1024;   // block-mask row cached in LDS (N <= 131072)
 
 template <typename T> __device__ __forceinline__ float to_f32(raw_t<T> r);
 template <> __device__ __forceinline__ float to_f32<__bf16>(uint16_t r) {
@@ -37,56 +43,6 @@ template <> __device__ __forceinline__ float to_f32<_Float16>(uint16_t r) {
   return (float)__builtin_bit_cast(_Float16, r);
 }
 template <> __device__ __forceinline__ float to_f32<float>(uint32_t r) { return __uint_as_float(r); }
-
-// ----------------------------------------------------------------------------
-// Stager for an R x D tile read as 4 x 4 element blocks: one global pass feeds
-// a row-major copy and/or a transposed copy in LDS.  Rows at or past `limit`
-// are read from row limit-1 (a valid address; no predicated loads): every use
-// of such a row is masked by the caller.
-template <typename T, int R, int D>
-struct Stager {
-  typedef raw_t<T> raw;
-  typedef raw4_t<T> raw4;
-  static constexpr int NB = R * D / 16 / 256;
-  static_assert(NB >= 1 && (R * D / 16) % 256 == 0, "tile does not split over 256 threads");
-  raw4 reg[NB][4];
-
-  __device__ __forceinline__ void fetch(const raw* __restrict__ g, int row0, int limit, int tid) {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int c = tid + 256 * i;
-      const int a = c / (D / 4), bc = c % (D / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int row = min(row0 + 4 * a + e, limit - 1);
-        reg[i][e] = *reinterpret_cast<const raw4*>(g + (size_t)row * D + 4 * bc);
-      }
-    }
-  }
-  __device__ __forceinline__ void store_rows(raw* s, int stride, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int c = tid + 256 * i;
-      const int a = c / (D / 4), bc = c % (D / 4);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) *reinterpret_cast<raw4*>(s + (4 * a + e) * stride + 4 * bc) = reg[i][e];
-    }
-  }
-  __device__ __forceinline__ void store_transposed(raw* s, int stride, int tid) const {
-#pragma unroll
-    for (int i = 0; i < NB; ++i) {
-      const int c = tid + 256 * i;
-      const int a = c / (D / 4), bc = c % (D / 4);
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        raw4 col4;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) col4[e] = reg[i][e][t];
-        *reinterpret_cast<raw4*>(s + (4 * bc + t) * stride + 4 * a) = col4;
-      }
-    }
-  }
-};
 
 struct BwdParams {
   const void* q;
@@ -98,7 +54,8 @@ struct BwdParams {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;
+  float* lse2;   // workspace: LSE * log2(e), +inf for rows without a visible key
+  float* dvec;   // workspace: D = rowsum(dO * O)
   const int32_t* key_lens;
   const uint8_t* block_mask;
   int H, N, BH, nblk;
@@ -108,7 +65,7 @@ struct BwdParams {
 };
 
 // ----------------------------------------------------------------------------
-// 1. D_i = sum_k dO_ik O_ik, float32, one row per group of TPR threads.
+// 1. D_i = sum_k dO_ik O_ik and LSE_i * log2(e), one row per group of TPR threads.
 template <typename T, int D>
 __global__ __launch_bounds__(256) void fa_bwd_preprocess_kernel(BwdParams p, long long rows) {
   typedef raw_t<T> raw;
@@ -130,7 +87,13 @@ __global__ __launch_bounds__(256) void fa_bwd_preprocess_kernel(BwdParams p, lon
   }
 #pragma unroll
   for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && sub == 0) p.dvec[row] = acc;
+  if (row < rows && sub == 0) {
+    p.dvec[row] = acc;
+    const float l = p.lse[row];
+    // Rows without any visible key get +inf, so that every probability
+    // recomputed for them is exp2(-inf) = 0.
+    p.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -138,18 +101,15 @@ __global__ __launch_bounds__(256) void fa_bwd_preprocess_kernel(BwdParams p, lon
 template <typename T, int D>
 struct DkDvCfg {
   typedef raw_t<T> raw;
-  // 64 query rows per step.  At d = 128 the persistent per-wave state (K, V
-  // operands and the dK, dV accumulators: 192 VGPRs) only fits one wave per
-  // SIMD, so one work-group per CU may use 140 KB of double-buffered LDS.
   static constexpr int BQ = (sizeof(raw) == 4 && D == 128) ? 32 : 64;
+  static constexpr int NS = 4;
+  static constexpr int TILE_BYTES = BQ * D * (int)sizeof(raw);   // one of Q, dO
+  static constexpr int ROWV_BYTES = 64 * 4;                      // LSE2 or D words (one DMA)
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES + 2 * ROWV_BYTES;
+  static constexpr int LPT = 2 * TILE_BYTES / 4096;              // 16-byte DMAs per wave per tile
+  // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
+  // accumulators: 192 VGPRs) only fits one wave per SIMD.
   static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
-  static constexpr int RS = D + 16 / (int)sizeof(raw);  // row-major stride (+16 B)
-  static constexpr int TS = BQ + 4;                      // transposed stride
-  static constexpr int Q_ELEMS = BQ * RS;
-  static constexpr int QT_ELEMS = D * TS;
-  // per stage: Q, dO (row-major), Q^T, dO^T, then 2*BQ floats (LSE*log2e, D)
-  static constexpr int STAGE_RAW = 2 * Q_ELEMS + 2 * QT_ELEMS;
-  static constexpr int STAGE_BYTES = STAGE_RAW * sizeof(raw) + 2 * BQ * 4;
 };
 
 template <typename T, int D>
@@ -161,8 +121,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   typedef DkDvCfg<T, D> L;
   constexpr int BQ = L::BQ;
   constexpr int BK = 128;
+  constexpr int LPT = L::LPT;
 
-  __shared__ __attribute__((aligned(16))) char smem_bytes[2 * L::STAGE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ uint8_t mask_col[kMaxMaskBlocks];
+  const uint32_t ring_lds = lds_addr(ring);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -187,8 +150,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + head;
   const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + head;
   const raw* __restrict__ dOg = reinterpret_cast<const raw*>(p.dout) + head;
-  const float* __restrict__ lse = p.lse + (size_t)bh * N;
-  const float* __restrict__ dvec = p.dvec + (size_t)bh * N;
+  const float* __restrict__ lse2g = p.lse2 + (size_t)bh * N;
+  const float* __restrict__ dvecg = p.dvec + (size_t)bh * N;
+
+  // Query tiles that see keys [j0, j0 + BK); the block-mask column of this
+  // key block is cached in LDS.
+  const int nqt = (N + BQ - 1) / BQ;
+  const int t_begin = p.causal ? j0 / BQ : 0;
+  const int t_end = j0 < kend ? nqt : t_begin;  // no visible key in this tile: nothing to do
+  const bool sparse = p.block_mask != nullptr;
+  if (sparse) {
+    for (int i = tid; i < p.nblk; i += 256)
+      mask_col[i] = p.block_mask[(size_t)i * p.nblk + j0 / kMaskBlock];
+  }
 
   f32x16 dk_acc[D / 32], dv_acc[D / 32];
 #pragma unroll
@@ -196,134 +170,128 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     dk_acc[db] = zero16();
     dv_acc[db] = zero16();
   }
+  // K and V of this wave's keys as B operands (contiguous slot map over d).
+  frag_t<T> kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    const bool ok = myk < N;
+    kf[kc] = ok ? load_frag<T>(Kg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+    vf[kc] = ok ? load_frag<T>(Vg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+  }
+  __syncthreads();  // mask_col visible
 
-  // Query-tile range that sees keys [j0, j0 + BK).
-  const int nqt = (N + BQ - 1) / BQ;
-  int t_begin = p.causal ? j0 / BQ : 0;
-  int t_end = j0 < kend ? nqt : t_begin;  // no visible key in this tile: nothing to do
-  const uint8_t* bm_col = p.block_mask ? p.block_mask + j0 / kMaskBlock : nullptr;
-  auto kept = [&](int t) {
-    return bm_col == nullptr || bm_col[(size_t)((t * BQ) / kMaskBlock) * p.nblk] != 0;
-  };
   auto next_kept = [&](int t) {
-    while (t < t_end && !kept(t)) ++t;
+    if (!sparse) return t;
+    while (t < t_end && mask_col[(t * BQ) / kMaskBlock] == 0) ++t;
     return t;
   };
 
-  if (t_begin < t_end) {
-    // K and V of this wave's keys as B operands (contiguous slot map over d).
-    frag_t<T> kf[D / 16], vf[D / 16];
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      const bool ok = myk < N;
-      kf[kc] = ok ? load_frag<T>(Kg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
-      vf[kc] = ok ? load_frag<T>(Vg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+  DmaPlan<raw, BQ, D, kBoth> plan;
+  plan.init(w, lane);
+  // Q, dO rows of tile t, plus (waves 0 and 1) its LSE2 and D words.
+  auto issue = [&](int t, int s) {
+    const uint32_t base = ring_lds + s * L::SLOT_BYTES;
+    const int qi0 = t * BQ;
+    plan.copy(Qg, qi0, N, base, lane);
+    plan.copy(dOg, qi0, N, base + L::TILE_BYTES, lane);
+    if (w < 2) {
+      const uint32_t voff = (uint32_t)min(qi0 + lane, N - 1) * 4u;
+      dma4s(voff, w == 0 ? (const void*)lse2g : (const void*)dvecg,
+            base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
     }
-
-    Stager<T, BQ, D> sq, sdo;
-    float lse2_r = 0.f, dvec_r = 0.f;
-    auto fetch = [&](int t) {
-      const int i0 = t * BQ;
-      sq.fetch(Qg, i0, N, tid);
-      sdo.fetch(dOg, i0, N, tid);
-      if (tid < BQ) {
-        const int i = i0 + tid;
-        const float l = i < N ? lse[i] : kNegInf;
-        // Rows without any visible key (LSE = -inf) and rows past N get
-        // +inf here, so that their recomputed probabilities are exactly 0.
-        lse2_r = l == kNegInf ? __builtin_inff() : l * kLog2e;
-        dvec_r = i < N ? dvec[i] : 0.f;
-      }
-    };
-    auto stash = [&](int buf) {
-      raw* base = reinterpret_cast<raw*>(smem_bytes + buf * L::STAGE_BYTES);
-      sq.store_rows(base, L::RS, tid);
-      sdo.store_rows(base + L::Q_ELEMS, L::RS, tid);
-      sq.store_transposed(base + 2 * L::Q_ELEMS, L::TS, tid);
-      sdo.store_transposed(base + 2 * L::Q_ELEMS + L::QT_ELEMS, L::TS, tid);
-      float* f = reinterpret_cast<float*>(base + L::STAGE_RAW);
-      if (tid < BQ) {
-        f[tid] = lse2_r;
-        f[BQ + tid] = dvec_r;
-      }
-    };
-
-    const float c = p.c;
-    int t = next_kept(t_begin);
-    if (t < t_end) {
-      fetch(t);
-      stash(0);
+  };
+  // wait until at most `tiles` whole tiles of this wave's DMAs are in flight
+  auto wait_tiles = [&](int tiles) {
+    if (w < 2) {
+      if (tiles == 2) wait_vmcnt<2 * (LPT + 1)>();
+      else if (tiles == 1) wait_vmcnt<LPT + 1>();
+      else wait_vmcnt<0>();
+    } else {
+      if (tiles == 2) wait_vmcnt<2 * LPT>();
+      else if (tiles == 1) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
     }
-    __syncthreads();
-    int buf = 0;
-    while (t < t_end) {
-      const int tn = next_kept(t + 1);
-      if (tn < t_end) fetch(tn);
-      const int qi0 = t * BQ;
-      const raw* Qs = reinterpret_cast<const raw*>(smem_bytes + buf * L::STAGE_BYTES);
-      const raw* dOs = Qs + L::Q_ELEMS;
-      const raw* QTs = Qs + 2 * L::Q_ELEMS;
-      const raw* dOTs = QTs + L::QT_ELEMS;
-      const float* lse2s = reinterpret_cast<const float*>(Qs + L::STAGE_RAW);
-      const float* dvs = lse2s + BQ;
+  };
 
-      if (!p.causal || kw0 <= qi0 + BQ - 1) {
-        // S (queries x keys) and dP, with queries as accumulator rows.
-        f32x16 sacc[BQ / 32], pacc[BQ / 32];
+  const float c = p.c;
+  auto step_math = [&](const char* slot, int qi0) {
+    const raw* Qs = reinterpret_cast<const raw*>(slot);
+    const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
+    const float* dvs = lse2s + 64;
+    // S (queries x keys) and dP, with queries as accumulator rows.
+    f32x16 sacc[BQ / 32], pacc[BQ / 32];
 #pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb) {
-          sacc[qb] = zero16();
-          pacc[qb] = zero16();
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      sacc[qb] = zero16();
+      pacc[qb] = zero16();
 #pragma unroll
-          for (int kc = 0; kc < D / 16; ++kc) {
-            const frag_t<T> aq = load_frag<T>(Qs + (qb * 32 + col) * L::RS + kc * 16 + hh * 8);
-            sacc[qb] = Tr::mma(aq, kf[kc], sacc[qb]);
-            const frag_t<T> ad = load_frag<T>(dOs + (qb * 32 + col) * L::RS + kc * 16 + hh * 8);
-            pacc[qb] = Tr::mma(ad, vf[kc], pacc[qb]);
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
+        sacc[qb] = Tr::mma(aq, kf[kc], sacc[qb]);
+        const frag_t<T> ad = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, kc * 16 + hh * 8);
+        pacc[qb] = Tr::mma(ad, vf[kc], pacc[qb]);
+      }
+    }
+    const bool masked = (p.causal && kw0 + 31 > qi0) || (kw0 + 32 > kend) || (qi0 + BQ > N);
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dvs + r0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g + u;
+          float pr = fast_exp2(fmaf(sacc[qb][r], c, -lv[u]));
+          if (masked) {
+            const int qi = qi0 + r0 + u;
+            if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
           }
-        }
-        const bool masked =
-            (p.causal && kw0 + 31 > qi0) || (kw0 + 32 > kend) || (qi0 + BQ > N);
-#pragma unroll
-        for (int qb = 0; qb < BQ / 32; ++qb)
-#pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
-            const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
-            const float4 d4 = *reinterpret_cast<const float4*>(dvs + r0);
-            const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-            const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
-#pragma unroll
-            for (int u = 0; u < 4; ++u) {
-              const int r = 4 * g + u;
-              float pr = fast_exp2(fmaf(sacc[qb][r], c, -lv[u]));
-              if (masked) {
-                const int qi = qi0 + r0 + u;
-                if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
-              }
-              sacc[qb][r] = pr;                        // P
-              pacc[qb][r] = pr * (pacc[qb][r] - dv[u]);  // dS = P (dP - D)
-            }
-          }
-        // dV^T += dO^T P,  dK^T += Q^T dS  (k = queries, acc-ordered slots).
-#pragma unroll
-        for (int qc = 0; qc < BQ / 16; ++qc) {
-          const frag_t<T> pf = acc_to_frag<T>(sacc[qc / 2], qc % 2);
-          const frag_t<T> sf = acc_to_frag<T>(pacc[qc / 2], qc % 2);
-#pragma unroll
-          for (int db = 0; db < D / 32; ++db) {
-            const frag_t<T> ado = load_frag_acc_order<T>(dOTs + (db * 32 + col) * L::TS + qc * 16, hh);
-            dv_acc[db] = Tr::mma(ado, pf, dv_acc[db]);
-            const frag_t<T> aq = load_frag_acc_order<T>(QTs + (db * 32 + col) * L::TS + qc * 16, hh);
-            dk_acc[db] = Tr::mma(aq, sf, dk_acc[db]);
-          }
+          sacc[qb][r] = pr;                          // P
+          pacc[qb][r] = pr * (pacc[qb][r] - dv[u]);  // dS = P (dP - D)
         }
       }
+    // dV^T += dO^T P,  dK^T += Q^T dS  (k = queries, acc-ordered slots).
+#pragma unroll
+    for (int qc = 0; qc < BQ / 16; ++qc) {
+      const frag_t<T> pf = acc_to_frag<T>(sacc[qc / 2], qc % 2);
+      const frag_t<T> sf = acc_to_frag<T>(pacc[qc / 2], qc % 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const frag_t<T> ado = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
+        dv_acc[db] = Tr::mma(ado, pf, dv_acc[db]);
+        const frag_t<T> aq = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
+        dk_acc[db] = Tr::mma(aq, sf, dk_acc[db]);
+      }
+    }
+  };
 
-      if (tn < t_end) stash(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-      t = tn;
+  // Kept query tiles in order; tl[k] is the tile of step i + k.
+  int tl[3];
+  tl[0] = t_begin < t_end ? next_kept(t_begin) : t_end;
+  tl[1] = tl[0] < t_end ? next_kept(tl[0] + 1) : t_end;
+  tl[2] = tl[1] < t_end ? next_kept(tl[1] + 1) : t_end;
+  if (tl[0] < t_end) {
+    issue(tl[0], 0);
+    if (tl[1] < t_end) issue(tl[1], 1);
+    if (tl[2] < t_end) issue(tl[2], 2);
+    int step = 0;
+    while (true) {
+      // tile tl[0] must have landed (tl[1], and at step 0 tl[2], may stay in flight)
+      wait_tiles((tl[1] < t_end) + (step == 0 && tl[2] < t_end));
+      __syncthreads();  // every wave is done with step i-1
+      if (step > 0 && tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+      const int qi0 = tl[0] * BQ;
+      if (!p.causal || kw0 <= qi0 + BQ - 1) step_math(ring + (step & 3) * L::SLOT_BYTES, qi0);
+      tl[0] = tl[1];
+      tl[1] = tl[2];
+      tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+      ++step;
+      if (tl[0] >= t_end) break;
     }
   }
 
@@ -352,27 +320,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 template <typename T, int D>
 struct DqCfg {
   typedef raw_t<T> raw;
-  // 64 keys per step at d = 64; 32 at d = 128 so that two work-groups
-  // (double-buffered stages) fit in one CU's LDS.
+  // 64 keys per step at d = 64; 32 at d = 128 (two work-groups per CU).
   static constexpr int BC = D == 128 ? 32 : 64;
-  static constexpr int RS = D + 16 / (int)sizeof(raw);
-  static constexpr int TS = BC + 4;
-  static constexpr int K_ELEMS = BC * RS;
-  static constexpr int KT_ELEMS = D * TS;
-  static constexpr int STAGE = 2 * K_ELEMS + KT_ELEMS;  // K, V row-major; K^T
+  static constexpr int NS = 4;
+  static constexpr int TILE_BYTES = BC * D * (int)sizeof(raw);   // one of K, V
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
+  static constexpr int LPT = 2 * TILE_BYTES / 4096;
+  static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
 };
 
 template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void fa_bwd_dq_kernel(
-    BwdParams p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    DqCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
   typedef DqCfg<T, D> L;
   constexpr int BC = L::BC;
   constexpr int BR = 128;
+  constexpr int LPT = L::LPT;
 
-  __shared__ __attribute__((aligned(16))) raw smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ uint8_t mask_row[kMaxMaskBlocks];
+  const uint32_t ring_lds = lds_addr(ring);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -394,12 +364,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   int kv_end = kend;
   if (p.causal) kv_end = min(kv_end, i0 + BR);
   const int nkt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
-  const uint8_t* bm = p.block_mask ? p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk : nullptr;
-  auto kept = [&](int j) { return bm == nullptr || bm[(j * BC) / kMaskBlock] != 0; };
-  auto next_kept = [&](int j) {
-    while (j < nkt && !kept(j)) ++j;
-    return j;
-  };
+  const bool sparse = p.block_mask != nullptr;
+  if (sparse) {
+    const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
+    for (int i = tid; i < p.nblk; i += 256) mask_row[i] = bm[i];
+  }
 
   const size_t head = (size_t)bh * N * D;
   const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
@@ -416,85 +385,98 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void f
   }
   float lse2 = __builtin_inff(), dval = 0.f;
   if (myq < N) {
-    const float l = p.lse[(size_t)bh * N + myq];
-    lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
+    lse2 = p.lse2[(size_t)bh * N + myq];
     dval = p.dvec[(size_t)bh * N + myq];
   }
+  __syncthreads();  // mask_row visible
+
+  auto next_kept = [&](int j) {
+    if (!sparse) return j;
+    while (j < nkt && mask_row[(j * BC) / kMaskBlock] == 0) ++j;
+    return j;
+  };
 
   f32x16 dq_acc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq_acc[db] = zero16();
 
-  Stager<T, BC, D> sk, sv;
-  auto fetch = [&](int j) {
-    sk.fetch(Kg, j * BC, N, tid);
-    sv.fetch(Vg, j * BC, N, tid);
+  DmaPlan<raw, BC, D, kBoth> kplan;
+  DmaPlan<raw, BC, D, kRows> vplan;
+  kplan.init(w, lane);
+  vplan.init(w, lane);
+  auto issue = [&](int t, int s) {
+    const uint32_t base = ring_lds + s * L::SLOT_BYTES;
+    kplan.copy(Kg, t * BC, N, base, lane);
+    vplan.copy(Vg, t * BC, N, base + L::TILE_BYTES, lane);
   };
-  auto stash = [&](int buf) {
-    raw* Ks = smem + buf * L::STAGE;
-    sk.store_rows(Ks, L::RS, tid);
-    sv.store_rows(Ks + L::K_ELEMS, L::RS, tid);
-    sk.store_transposed(Ks + 2 * L::K_ELEMS, L::TS, tid);
+  auto wait_tiles = [&](int tiles) {
+    if (tiles == 2) wait_vmcnt<2 * LPT>();
+    else if (tiles == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
   };
 
   const float c = p.c;
-  int j = next_kept(0);
-  if (j < nkt) {
-    fetch(j);
-    stash(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (j < nkt) {
-    const int jn = next_kept(j + 1);
-    if (jn < nkt) fetch(jn);
-    const int kt0 = j * BC;
-    const raw* Ks = smem + buf * L::STAGE;
-    const raw* Vs = Ks + L::K_ELEMS;
-    const raw* KTs = Ks + 2 * L::K_ELEMS;
-
-    if (!p.causal || kt0 <= qw0 + 31) {
-      f32x16 sacc[BC / 32], pacc[BC / 32];
+  auto step_math = [&](const char* slot, int kt0) {
+    const raw* Ks = reinterpret_cast<const raw*>(slot);
+    const raw* Vs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    f32x16 sacc[BC / 32], pacc[BC / 32];
 #pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb) {
-        sacc[kb] = zero16();
-        pacc[kb] = zero16();
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      sacc[kb] = zero16();
+      pacc[kb] = zero16();
 #pragma unroll
-        for (int kc = 0; kc < D / 16; ++kc) {
-          const frag_t<T> ak = load_frag<T>(Ks + (kb * 32 + col) * L::RS + kc * 16 + hh * 8);
-          sacc[kb] = Tr::mma(ak, qf[kc], sacc[kb]);
-          const frag_t<T> av = load_frag<T>(Vs + (kb * 32 + col) * L::RS + kc * 16 + hh * 8);
-          pacc[kb] = Tr::mma(av, df[kc], pacc[kb]);
-        }
-      }
-      const bool masked = (p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend);
-#pragma unroll
-      for (int kb = 0; kb < BC / 32; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float pr = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
-          if (masked) {
-            const int key = kt0 + kb * 32 + acc_row(r, hh);
-            if (key >= kend || (p.causal && key > myq)) pr = 0.f;
-          }
-          pacc[kb][r] = pr * (pacc[kb][r] - dval);  // dS^T
-        }
-      // dQ^T += K^T dS^T  (k = keys, acc-ordered slots).
-#pragma unroll
-      for (int kc = 0; kc < BC / 16; ++kc) {
-        const frag_t<T> sf = acc_to_frag<T>(pacc[kc / 2], kc % 2);
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const frag_t<T> a = load_frag_acc_order<T>(KTs + (db * 32 + col) * L::TS + kc * 16, hh);
-          dq_acc[db] = Tr::mma(a, sf, dq_acc[db]);
-        }
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const frag_t<T> ak = load_frag_swz<T, D, kBoth>(Ks, kb * 32 + col, kc * 16 + hh * 8);
+        sacc[kb] = Tr::mma(ak, qf[kc], sacc[kb]);
+        const frag_t<T> av = load_frag_swz<T, D, kRows>(Vs, kb * 32 + col, kc * 16 + hh * 8);
+        pacc[kb] = Tr::mma(av, df[kc], pacc[kb]);
       }
     }
+    const bool masked = (p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend);
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
+        if (masked) {
+          const int key = kt0 + kb * 32 + acc_row(r, hh);
+          if (key >= kend || (p.causal && key > myq)) pr = 0.f;
+        }
+        pacc[kb][r] = pr * (pacc[kb][r] - dval);  // dS^T
+      }
+    // dQ^T += K^T dS^T  (k = keys, acc-ordered slots).
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc) {
+      const frag_t<T> sf = acc_to_frag<T>(pacc[kc / 2], kc % 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const frag_t<T> a = load_frag_tr<T, D, kBoth>(Ks, kc * 16, db * 32, lane);
+        dq_acc[db] = Tr::mma(a, sf, dq_acc[db]);
+      }
+    }
+  };
 
-    if (jn < nkt) stash(buf ^ 1);
-    __syncthreads();
-    buf ^= 1;
-    j = jn;
+  int tl[3];
+  tl[0] = next_kept(0);
+  tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
+  tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
+  if (tl[0] < nkt) {
+    issue(tl[0], 0);
+    if (tl[1] < nkt) issue(tl[1], 1);
+    if (tl[2] < nkt) issue(tl[2], 2);
+    int step = 0;
+    while (true) {
+      wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));
+      __syncthreads();  // every wave is done with step i-1
+      if (step > 0 && tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+      const int kt0 = tl[0] * BC;
+      if (!p.causal || kt0 <= qw0 + 31) step_math(ring + (step & 3) * L::SLOT_BYTES, kt0);
+      tl[0] = tl[1];
+      tl[1] = tl[2];
+      tl[2] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+      ++step;
+      if (tl[0] >= nkt) break;
+    }
   }
 
   if (myq < N) {
@@ -516,7 +498,10 @@ template <typename T, int D>
 hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   BwdParams p;
   p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.dout = t.dout; p.lse = t.lse;
-  p.dq = t.dq; p.dk = t.dk; p.dv = t.dv; p.dvec = t.dvec;
+  p.dq = t.dq; p.dk = t.dk; p.dv = t.dv;
+  const size_t rows_total = (size_t)pb.B * pb.H * pb.N;
+  p.dvec = t.workspace;
+  p.lse2 = t.workspace + rows_total;
   p.key_lens = pb.key_lens;
   p.block_mask = pb.block_mask;
   p.H = pb.H;
@@ -527,7 +512,7 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
 
-  const long long rows = (long long)p.BH * pb.N;
+  const long long rows = (long long)rows_total;
   constexpr int TPR = D * (int)sizeof(raw_t<T>) / 16;
   const unsigned pre_grid = (unsigned)((rows + (256 / TPR) - 1) / (256 / TPR));
   timing_begin(kBwdPre, pb.stream);

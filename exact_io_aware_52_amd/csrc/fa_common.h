@@ -135,6 +135,15 @@ __device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
                : "v"(g), "s"(lds)
                : "memory", "m0");
 }
+
+// Same copy with a wave-uniform base address in SGPRs and a per-lane 32-bit
+// byte offset: no per-lane address arithmetic.
+__device__ __forceinline__ void dma16s(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
+}
 #pragma clang diagnostic pop
 
 // Wait until at most N of this wave's vector-memory operations are in flight.
@@ -143,25 +152,40 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Row-major tiles in LDS are stored as 16-byte chunks, with the chunk index of
-// row r XORed by swizzle(r) so that the reads below hit distinct banks (there
-// is no room for row padding: a DMA wave writes 1 KB contiguously).
-//   K-style reads (ds_read_b128, lanes on 32 consecutive rows, same chunk):
-//     8 chunks per row: (r >> 1) & 7;   16+ chunks per row: r & 15.
-//   Transposed reads (ds_read_b64_tr_b16, 8 rows x 4 chunks per wave):
-//     8 chunks per row: ((r >> 1) & 1) << 2;   16 chunks per row: (r & 3) << 2.
-template <int CPR> __device__ __forceinline__ int swz_rows(int r) {
-  return CPR >= 16 ? (r & 15) : ((r >> 1) & 7);
+// 4-byte variant (lane i's word lands at LDS byte lds + 4 i).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma4s(uint32_t voff, const void* sbase, uint32_t lds) {
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dword %0, %1"
+               :
+               : "v"(voff), "s"(sbase), "s"(lds)
+               : "memory", "m0");
 }
-template <int CPR> __device__ __forceinline__ int swz_tr(int r) {
-  return CPR >= 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+#pragma clang diagnostic pop
+
+// Row-major tiles in LDS are stored as 16-byte chunks, with the chunk index of
+// row r XORed by a swizzle of r so that reads hit distinct banks (there is no
+// room for row padding: a DMA wave writes 1 KB contiguously).  Model: one LDS
+// cycle serves 256 B = 16 chunk-wide bank groups, group = (r*CPR + chunk) % 16.
+//   kRows  row reads (ds_read_b128, 16 lanes on 16 consecutive rows, one chunk
+//          each): conflict-free;
+//   kTr    transposed reads (ds_read_b64_tr_b16, 8 rows x 4 chunks per wave):
+//          each group hit twice, the minimum;
+//   kBoth  both of the above at once (tiles read both ways).
+enum SwzKind { kRows = 0, kTr = 1, kBoth = 2 };
+template <int CPR, int KIND> __device__ __forceinline__ int swz(int r) {
+  if constexpr (KIND == kRows) return CPR >= 16 ? (r & 15) : ((r >> 1) & 7);
+  if constexpr (KIND == kTr) return CPR >= 16 ? ((r & 3) << 2) : (((r >> 1) & 1) << 2);
+  if constexpr (CPR == 8) return (((r >> 1) & 1) << 2) | ((r >> 2) & 3);
+  if constexpr (CPR == 16) return ((r & 3) << 2) | ((r >> 2) & 3);
+  return r & 15;  // 32 chunks per row (fp32, d = 128): row reads only
 }
 
 // Copies rows row0 .. row0+ROWS-1 (D elements each, row-major in HBM; rows
 // past N-1 repeat row N-1) into an LDS tile at byte address `lds` with the
 // given chunk swizzle.  The tile is split over the work-group's 4 waves; each
 // wave issues ROWS*D*sizeof(raw)/4096 DMA instructions.
-template <typename raw, int ROWS, int D, bool TR>
+template <typename raw, int ROWS, int D, int KIND>
 __device__ __forceinline__ void dma_tile(const raw* __restrict__ g, int row0, int N, uint32_t lds,
                                          int wave, int lane) {
   constexpr int CPR = D * (int)sizeof(raw) / 16;  // chunks per row
@@ -173,25 +197,59 @@ __device__ __forceinline__ void dma_tile(const raw* __restrict__ g, int row0, in
     const int blk = i * 4 + wave;        // 1 KB block of the tile
     const int pos = blk * 64 + lane;     // chunk position within the tile
     const int r = pos / CPR, cs = pos % CPR;
-    const int c = cs ^ (TR ? swz_tr<CPR>(r) : swz_rows<CPR>(r));
+    const int c = cs ^ swz<CPR, KIND>(r);
     const int row = min(row0 + r, N - 1);
     dma16(g + (size_t)row * D + c * VEC, lds + blk * 1024);
   }
 }
 
+// The same tile copy for tiles whose ROWS rows all exist: this lane's byte
+// offsets within the tile are computed once, each copy only supplies the
+// tile's (wave-uniform) first-row address.
+template <typename raw, int ROWS, int D, int KIND>
+struct DmaPlan {
+  static constexpr int CPR = D * (int)sizeof(raw) / 16;
+  static constexpr int VEC = 16 / (int)sizeof(raw);
+  static constexpr int NI = ROWS * CPR / 256;
+  static_assert(ROWS * CPR % 256 == 0, "tile must split into 1 KB per-wave pieces");
+  uint32_t off[NI];
+  int wave;
+  __device__ __forceinline__ void init(int wave_, int lane) {
+    wave = wave_;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int pos = (i * 4 + wave) * 64 + lane;
+      const int r = pos / CPR, cs = pos % CPR;
+      const int c = cs ^ swz<CPR, KIND>(r);
+      off[i] = (uint32_t)((r * D + c * VEC) * (int)sizeof(raw));
+    }
+  }
+  __device__ __forceinline__ void issue(const raw* first_row, uint32_t lds) const {
+#pragma unroll
+    for (int i = 0; i < NI; ++i) dma16s(off[i], first_row, lds + (i * 4 + wave) * 1024);
+  }
+  // rows row0 .. row0+ROWS-1 of g, or the clamped copy if the tile is ragged
+  __device__ __forceinline__ void copy(const raw* g, int row0, int N, uint32_t lds,
+                                       int lane) const {
+    if (row0 + ROWS <= N) issue(g + (size_t)row0 * D, lds);
+    else dma_tile<raw, ROWS, D, KIND>(g, row0, N, lds, wave, lane);
+  }
+};
+
 // Eight contiguous elements of row `row` starting at element `col` (a multiple
-// of 8 / 4 for 16- / 32-bit types) from a swizzled row-major tile.
-template <typename T, int D>
+// of 8) from a swizzled row-major tile: the contiguous-slot operand.
+template <typename T, int D, int KIND>
 __device__ __forceinline__ frag_t<T> load_frag_swz(const raw_t<T>* tile, int row, int col) {
   constexpr int CPR = D * (int)sizeof(raw_t<T>) / 16;
   constexpr int VEC = 16 / (int)sizeof(raw_t<T>);
   const raw_t<T>* rp = tile + row * D;
+  const int sw = swz<CPR, KIND>(row);
   if constexpr (VEC == 8) {
-    return load_frag<T>(rp + (((col / VEC) ^ swz_rows<CPR>(row)) * VEC));
+    return load_frag<T>(rp + (((col / VEC) ^ sw) * VEC));
   } else {
     typedef raw_t<T> raw4v __attribute__((ext_vector_type(4)));
-    const raw4v lo = *reinterpret_cast<const raw4v*>(rp + (((col / VEC) ^ swz_rows<CPR>(row)) * VEC));
-    const raw4v hi = *reinterpret_cast<const raw4v*>(rp + ((((col / VEC) + 1) ^ swz_rows<CPR>(row)) * VEC));
+    const raw4v lo = *reinterpret_cast<const raw4v*>(rp + (((col / VEC) ^ sw) * VEC));
+    const raw4v hi = *reinterpret_cast<const raw4v*>(rp + ((((col / VEC) + 1) ^ sw) * VEC));
     raw8_t<T> r8;
 #pragma unroll
     for (int i = 0; i < 4; ++i) { r8[i] = lo[i]; r8[4 + i] = hi[i]; }
@@ -204,9 +262,8 @@ __device__ __forceinline__ frag_t<T> load_frag_swz(const raw_t<T>* tile, int row
 // (k0 + pi(h, s), col0 + c), pi the acc-ordered slot map.  16-bit types use
 // two transposed LDS reads (ds_read_b64_tr_b16: within each 16-lane group,
 // lane j takes element j % 4 of the 8-byte rows addressed by lanes
-// j / 4 + 4t, t = 0..3); the tile must use the swz_tr swizzle.  fp32 reads
-// the eight elements one by one (swz_rows swizzle).
-template <typename T, int D>
+// j / 4 + 4t, t = 0..3).  fp32 reads the eight elements one by one.
+template <typename T, int D, int KIND>
 __device__ __forceinline__ frag_t<T> load_frag_tr(const raw_t<T>* tile, int k0, int col0,
                                                   int lane) {
   typedef raw_t<T> raw;
@@ -218,7 +275,7 @@ __device__ __forceinline__ frag_t<T> load_frag_tr(const raw_t<T>* tile, int k0, 
     const int r0 = k0 + 4 * (g >> 1) + (s >> 2);
     const int col = col0 + 16 * (g & 1) + 4 * (s & 3);  // 4 elements = half a chunk
     auto addr = [&](int r) {
-      const int chunk = (col >> 3) ^ swz_tr<CPR>(r);
+      const int chunk = (col >> 3) ^ swz<CPR, KIND>(r);
       return (lds_s16x4*)(const __attribute__((address_space(3))) raw*)(tile + r * D + chunk * 8 +
                                                                           (col & 7));
     };
@@ -235,7 +292,7 @@ __device__ __forceinline__ frag_t<T> load_frag_tr(const raw_t<T>* tile, int k0, 
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int r = k0 + (u < 4 ? 4 * h + u : 8 + 4 * h + (u - 4));
-      r8[u] = tile[r * D + (((col / 4) ^ swz_rows<CPR>(r)) * 4) + (col & 3)];
+      r8[u] = tile[r * D + (((col / 4) ^ swz<CPR, KIND>(r)) * 4) + (col & 3)];
     }
     return __builtin_bit_cast(frag_t<T>, r8);
   }

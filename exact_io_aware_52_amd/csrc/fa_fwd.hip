@@ -78,6 +78,10 @@ struct FwdCfg {
   // Two waves per SIMD for 16-bit inputs; the fp32 instances (accuracy, not
   // speed) take the whole register file.
   static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
+  // Software pipelining (next tile's scores during this tile's softmax) pays
+  // at d = 64, where exponentials rival the matrix products; at d = 128 the
+  // products dominate and the second score buffer would not fit 256 VGPRs.
+  static constexpr bool PIPE = D == 64;
 };
 
 // Sum of the eight probabilities of a B-operand fragment, added to acc.  For
@@ -119,7 +123,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   constexpr int NKB = L::NKB;
 
   constexpr int LPT = L::LPT;
-  constexpr bool TRV = sizeof(raw) == 2;  // V^T through transposing LDS reads
+  constexpr int VSWZ = sizeof(raw) == 2 ? kTr : kRows;  // V^T via transposing reads
 
   __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
   __shared__ uint8_t mask_row[kMaxMaskBlocks];
@@ -154,7 +158,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     for (int i = tid; i < p.nblk; i += 256) mask_row[i] = bm[i];
   }
   auto next_kept = [&](int j) {
-    while (j < nkt && sparse && mask_row[(j * BC) / kMaskBlock] == 0) ++j;
+    if (!sparse) return j;
+    while (j < nkt && mask_row[(j * BC) / kMaskBlock] == 0) ++j;
     return j;
   };
   // Tile t holds keys t*BC .. t*BC+BC-1.  A wave skips tiles wholly past its
@@ -176,11 +181,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     qf[kc] = myq < N ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
   __syncthreads();  // mask_row visible
 
-  // K and V of tile t into ring slot s (LPT DMA instructions per wave).
+  // K and V of tile t into ring slot s (LPT DMA instructions per wave).  Only
+  // the ragged last tile computes clamped per-lane addresses.
+  DmaPlan<raw, BC, D, kRows> kplan;
+  DmaPlan<raw, BC, D, VSWZ> vplan;
+  kplan.init(w, lane);
+  vplan.init(w, lane);
   auto issue = [&](int t, int s) {
     const uint32_t base = ring_lds + s * L::SLOT_BYTES;
-    dma_tile<raw, BC, D, false>(Kg, t * BC, N, base, w, lane);
-    dma_tile<raw, BC, D, TRV>(Vg, t * BC, N, base + L::TILE_BYTES, w, lane);
+    kplan.copy(Kg, t * BC, N, base, lane);
+    vplan.copy(Vg, t * BC, N, base + L::TILE_BYTES, lane);
   };
 
   // ---- per-wave math
@@ -199,7 +209,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     for (int kc = 0; kc < D / 16; ++kc)
 #pragma unroll
       for (int kb = 0; kb < NKB; ++kb) {
-        const frag_t<T> a = load_frag_swz<T, D>(Ks, kb * 32 + col, kc * 16 + hh * 8);
+        const frag_t<T> a = load_frag_swz<T, D, kRows>(Ks, kb * 32 + col, kc * 16 + hh * 8);
         s[kb] = Tr::mma(a, qf[kc], s[kb]);
       }
   };
@@ -260,7 +270,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     for (int kc = 0; kc < BC / 16; ++kc)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const frag_t<T> a = load_frag_tr<T, D>(Vs, kc * 16, db * 32, lane);
+        const frag_t<T> a = load_frag_tr<T, D, VSWZ>(Vs, kc * 16, db * 32, lane);
         oacc[db] = Tr::mma(a, pf[kc], oacc[db]);
       }
   };
@@ -330,11 +340,42 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
       ++step;
     };
-    while (true) {
-      body(sa, sb, m_tile_a, m_tile_b);
-      if (tl[0] >= nkt) break;
-      body(sb, sa, m_tile_b, m_tile_a);
-      if (tl[0] >= nkt) break;
+    if constexpr (L::PIPE) {
+      while (true) {
+        body(sa, sb, m_tile_a, m_tile_b);
+        if (tl[0] >= nkt) break;
+        body(sb, sa, m_tile_b, m_tile_a);
+        if (tl[0] >= nkt) break;
+      }
+    } else {
+      // Step i: scores, softmax and P V of tile tl[0] from ring slot i % 4.
+      while (true) {
+        const int t_cur = tl[0];
+        frag_t<T> pf[2 * NKB];
+        if (step > 0) {
+          // tile tl[0] must have landed; tl[1] may still be in flight
+          if (tl[1] < nkt) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+          __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
+          if (tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+          if (active(t_cur)) {
+            scores(ktile(step & 3), sa);
+            if (masked(t_cur)) apply_mask(t_cur, sa);
+            m_tile_a = tile_max(sa);
+          }
+        }
+        if (active(t_cur)) {
+          maybe_rescale(m_tile_a);
+          softmax(sa, pf, masked(t_cur));
+          pv(vtile(step & 3), pf);
+        }
+        tl[0] = tl[1];
+        tl[1] = tl[2];
+        tl[2] = tl[3];
+        tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+        ++step;
+        if (tl[0] >= nkt) break;
+      }
     }
   }
 

@@ -38,7 +38,8 @@ struct BwdTensors {
   void* dq;
   void* dk;
   void* dv;
-  float* dvec;  // D = rowsum(dO * O), float32 [B, H, N], in the caller's workspace
+  float* workspace;  // caller's workspace: D = rowsum(dO * O), then LSE * log2(e),
+                    // each float32 [B, H, N]
 };
 
 // Event bracketing of launches (active only while timing is enabled).

@@ -100,8 +100,8 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
  * block_size is ignored then.  Overwrites dq, dk, dv (dtype).
  * workspace: device memory of at least fa_backward_workspace_bytes(B,H,N,d)
  * bytes, 16-byte aligned, owned by the caller, contents need not be
- * initialised; it holds D as float32 [B,H,N].  Calls that share a workspace
- * must be ordered on one stream.
+ * initialised; it holds D = rowsum(dout * o) and LSE * log2(e), each float32
+ * [B,H,N].  Calls that share a workspace must be ordered on one stream.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,

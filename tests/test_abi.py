@@ -100,7 +100,7 @@ def bwd(lib, ws=FAKE, ws_bytes=1 << 30, dq=FAKE, bm=None, bs=128, d=64, N=100):
 
 def test_backward_validation(lib):
     need = lib.fa_backward_workspace_bytes(2, 3, 100, 64)
-    assert need >= 2 * 3 * 100 * 4 and need % 256 == 0
+    assert need >= 2 * 2 * 3 * 100 * 4 and need % 256 == 0
     assert bwd(lib, ws=None) == _binding.FA_ERR_WORKSPACE
     assert bwd(lib, ws_bytes=need - 1) == _binding.FA_ERR_WORKSPACE
     assert "needed" in detail(lib)
