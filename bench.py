@@ -39,9 +39,9 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.h"],
-    "bwd_pre": ["fa_bwd.hip", "fa_common.h"],
-    "bwd_dkdv": ["fa_bwd.hip", "fa_common.h"],
-    "bwd_dq": ["fa_bwd.hip", "fa_common.h"],
+    "bwd_pre": ["fa_bwd_impl.h", "fa_common.h"],
+    "bwd_dkdv": ["fa_bwd_impl.h", "fa_common.h"],
+    "bwd_dq": ["fa_bwd_impl.h", "fa_common.h"],
 }
 
 

@@ -19,7 +19,10 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip"]
+SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip"]
+# Sources compiled without the VGPR-form matrix-core option: with it, LLVM's
+# "Rewrite AGPR-Copy-MFMA" pass crashes on the fp32 backward instances.
+NO_VGPR_FORM = {"fa_bwd_f32.hip"}
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.
@@ -42,7 +45,11 @@ def hipcc():
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [hipcc()] + COMMON + ["-c", os.path.join(CSRC, src), "-o", obj]
+    flags = list(COMMON)
+    if src in NO_VGPR_FORM:
+        i = flags.index("-amdgpu-mfma-vgpr-form=1")
+        del flags[i - 1:i + 1]
+    cmd = [hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops' is not a recognized feature"
     err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)

@@ -1,0 +1,543 @@
+// Tiled exact attention, backward pass, for gfx950 (kernel templates; the
+// instances live in fa_bwd.hip (16-bit) and fa_bwd_f32.hip (fp32)).
+//
+// The backward recomputes each probability tile on chip from the saved
+// logsumexp instead of reading an N x N matrix (review page, "Method" and
+// claim C7).  With P = exp(S - LSE) and D = rowsum(dO * O):
+//   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dK = scale dS^T Q,
+//   dQ = scale dS K.
+//
+// Three launches on the caller's stream:
+//   1. fa_bwd_preprocess_kernel: D and LSE * log2(e) for every row, into the
+//      caller's workspace (reads O and dO once).
+//   2. fa_bwd_dkdv_kernel: one work-group per 128 keys of a head; its four
+//      waves keep K, V (as matrix operands) and the dK, dV accumulators in
+//      registers and sweep the query tiles that see those keys.  The score
+//      tile is formed with queries as accumulator rows, so P and dS are the B
+//      operands of dV^T += dO^T P and dK^T += Q^T dS straight from registers;
+//      dO^T and Q^T come from the row-major tiles by transposing LDS reads.
+//   3. fa_bwd_dq_kernel: one work-group per 128 queries; the same
+//      recomputation with keys as accumulator rows (as in the forward) feeds
+//      dQ^T += K^T dS^T, K^T again by transposing reads.
+// Splitting dQ into its own pass recomputes S and dP once more (6 d flops per
+// pair on top of the 8 d of the dK/dV pass) but needs no atomics, keeps every
+// accumulator in registers and makes the result deterministic.
+//
+// Streaming (both passes): the tiles of the streamed operand go from HBM
+// straight into a 4-slot LDS ring by direct-to-LDS loads, requested two steps
+// before use; one barrier per step.
+
+#pragma once
+
+#include "fa_common.h"
+#include "fa_internal.h"
+
+namespace fa {
+namespace {
+
+constexpr int kMaskBlock = 128;
+constexpr int kMaxMaskBlocks = 1024;   // block-mask row cached in LDS (N <= 131072)
+
+template <typename T> __device__ __forceinline__ float to_f32(raw_t<T> r);
+template <> __device__ __forceinline__ float to_f32<__bf16>(uint16_t r) {
+  return __uint_as_float((uint32_t)r << 16);
+}
+template <> __device__ __forceinline__ float to_f32<_Float16>(uint16_t r) {
+  return (float)__builtin_bit_cast(_Float16, r);
+}
+template <> __device__ __forceinline__ float to_f32<float>(uint32_t r) { return __uint_as_float(r); }
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const void* dout;
+  const float* lse;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* lse2;   // workspace: LSE * log2(e), +inf for rows without a visible key
+  float* dvec;   // workspace: D = rowsum(dO * O)
+  const int32_t* key_lens;
+  const uint8_t* block_mask;
+  int H, N, BH, nblk;
+  float scale;
+  float c;  // scale * log2(e)
+  int causal;
+};
+
+// ----------------------------------------------------------------------------
+// 1. D_i = sum_k dO_ik O_ik and LSE_i * log2(e), one row per group of TPR threads.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_bwd_preprocess_kernel(BwdParams p, long long rows) {
+  typedef raw_t<T> raw;
+  constexpr int VEC = 16 / sizeof(raw);
+  constexpr int TPR = D / VEC;  // threads per row
+  const int tid = threadIdx.x;
+  const long long row = (long long)blockIdx.x * (256 / TPR) + tid / TPR;
+  const int sub = tid % TPR;
+  float acc = 0.f;
+  if (row < rows) {
+    const raw* O = reinterpret_cast<const raw*>(p.o) + row * D + sub * VEC;
+    const raw* dO = reinterpret_cast<const raw*>(p.dout) + row * D + sub * VEC;
+    const uint4 a = *reinterpret_cast<const uint4*>(O);
+    const uint4 b = *reinterpret_cast<const uint4*>(dO);
+    const raw* ar = reinterpret_cast<const raw*>(&a);
+    const raw* br = reinterpret_cast<const raw*>(&b);
+#pragma unroll
+    for (int i = 0; i < VEC; ++i) acc = fmaf(to_f32<T>(ar[i]), to_f32<T>(br[i]), acc);
+  }
+#pragma unroll
+  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
+  if (row < rows && sub == 0) {
+    p.dvec[row] = acc;
+    const float l = p.lse[row];
+    // Rows without any visible key get +inf, so that every probability
+    // recomputed for them is exp2(-inf) = 0.
+    p.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 2. dK, dV.  Work-group: 4 waves x 32 keys; query tiles of BQ rows.
+template <typename T, int D>
+struct DkDvCfg {
+  typedef raw_t<T> raw;
+  static constexpr int BQ = (sizeof(raw) == 4 && D == 128) ? 32 : 64;
+  static constexpr int NS = 4;
+  static constexpr int TILE_BYTES = BQ * D * (int)sizeof(raw);   // one of Q, dO
+  static constexpr int ROWV_BYTES = 64 * 4;                      // LSE2 or D words (one DMA)
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES + 2 * ROWV_BYTES;
+  static constexpr int LPT = 2 * TILE_BYTES / 4096;              // 16-byte DMAs per wave per tile
+  // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
+  // accumulators: 192 VGPRs) only fits one wave per SIMD.
+  static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    DkDvCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
+  typedef raw_t<T> raw;
+  typedef raw4_t<T> raw4;
+  typedef Traits<T> Tr;
+  typedef DkDvCfg<T, D> L;
+  constexpr int BQ = L::BQ;
+  constexpr int BK = 128;
+  constexpr int LPT = L::LPT;
+
+  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ uint8_t mask_col[kMaxMaskBlocks];
+  const uint32_t ring_lds = lds_addr(ring);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hh = lane >> 5;
+  const int N = p.N;
+  const int nkt = (N + BK - 1) / BK;
+
+  int kt, bh;
+  map_tile(blockIdx.x, nkt, p.BH, false, kt, bh);
+  const int b = bh / p.H;
+  const int j0 = kt * BK;
+  const int kw0 = j0 + 32 * w;  // first key of this wave
+  const int myk = kw0 + col;
+
+  int kend = N;
+  if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
+
+  const size_t head = (size_t)bh * N * D;
+  const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
+  const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + head;
+  const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + head;
+  const raw* __restrict__ dOg = reinterpret_cast<const raw*>(p.dout) + head;
+  const float* __restrict__ lse2g = p.lse2 + (size_t)bh * N;
+  const float* __restrict__ dvecg = p.dvec + (size_t)bh * N;
+
+  // Query tiles that see keys [j0, j0 + BK); the block-mask column of this
+  // key block is cached in LDS.
+  const int nqt = (N + BQ - 1) / BQ;
+  const int t_begin = p.causal ? j0 / BQ : 0;
+  const int t_end = j0 < kend ? nqt : t_begin;  // no visible key in this tile: nothing to do
+  const bool sparse = p.block_mask != nullptr;
+  if (sparse) {
+    for (int i = tid; i < p.nblk; i += 256)
+      mask_col[i] = p.block_mask[(size_t)i * p.nblk + j0 / kMaskBlock];
+  }
+
+  f32x16 dk_acc[D / 32], dv_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) {
+    dk_acc[db] = zero16();
+    dv_acc[db] = zero16();
+  }
+  // K and V of this wave's keys as B operands (contiguous slot map over d).
+  frag_t<T> kf[D / 16], vf[D / 16];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    const bool ok = myk < N;
+    kf[kc] = ok ? load_frag<T>(Kg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+    vf[kc] = ok ? load_frag<T>(Vg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+  }
+  __syncthreads();  // mask_col visible
+
+  auto next_kept = [&](int t) {
+    if (!sparse) return t;
+    while (t < t_end && mask_col[(t * BQ) / kMaskBlock] == 0) ++t;
+    return t;
+  };
+
+  DmaPlan<raw, BQ, D, kBoth> plan;
+  plan.init(w, lane);
+  // Q, dO rows of tile t, plus (waves 0 and 1) its LSE2 and D words.
+  auto issue = [&](int t, int s) {
+    const uint32_t base = ring_lds + s * L::SLOT_BYTES;
+    const int qi0 = t * BQ;
+    plan.copy(Qg, qi0, N, base, lane);
+    plan.copy(dOg, qi0, N, base + L::TILE_BYTES, lane);
+    if (w < 2) {
+      const uint32_t voff = (uint32_t)min(qi0 + lane, N - 1) * 4u;
+      dma4s(voff, w == 0 ? (const void*)lse2g : (const void*)dvecg,
+            base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
+    }
+  };
+  // wait until at most `tiles` whole tiles of this wave's DMAs are in flight
+  auto wait_tiles = [&](int tiles) {
+    if (w < 2) {
+      if (tiles == 2) wait_vmcnt<2 * (LPT + 1)>();
+      else if (tiles == 1) wait_vmcnt<LPT + 1>();
+      else wait_vmcnt<0>();
+    } else {
+      if (tiles == 2) wait_vmcnt<2 * LPT>();
+      else if (tiles == 1) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
+    }
+  };
+
+  const float c = p.c;
+  auto step_math = [&](const char* slot, int qi0) {
+    const raw* Qs = reinterpret_cast<const raw*>(slot);
+    const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
+    const float* dvs = lse2s + 64;
+    // S (queries x keys) and dP, with queries as accumulator rows.
+    f32x16 sacc[BQ / 32], pacc[BQ / 32];
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb) {
+      sacc[qb] = zero16();
+      pacc[qb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
+        sacc[qb] = Tr::mma(aq, kf[kc], sacc[qb]);
+        const frag_t<T> ad = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, kc * 16 + hh * 8);
+        pacc[qb] = Tr::mma(ad, vf[kc], pacc[qb]);
+      }
+    }
+    const bool masked = (p.causal && kw0 + 31 > qi0) || (kw0 + 32 > kend) || (qi0 + BQ > N);
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
+        const float4 d4 = *reinterpret_cast<const float4*>(dvs + r0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g + u;
+          float pr = fast_exp2(fmaf(sacc[qb][r], c, -lv[u]));
+          if (masked) {
+            const int qi = qi0 + r0 + u;
+            if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
+          }
+          sacc[qb][r] = pr;                          // P
+          pacc[qb][r] = pr * (pacc[qb][r] - dv[u]);  // dS = P (dP - D)
+        }
+      }
+    // dV^T += dO^T P,  dK^T += Q^T dS  (k = queries, acc-ordered slots).
+#pragma unroll
+    for (int qc = 0; qc < BQ / 16; ++qc) {
+      const frag_t<T> pf = acc_to_frag<T>(sacc[qc / 2], qc % 2);
+      const frag_t<T> sf = acc_to_frag<T>(pacc[qc / 2], qc % 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const frag_t<T> ado = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
+        dv_acc[db] = Tr::mma(ado, pf, dv_acc[db]);
+        const frag_t<T> aq = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
+        dk_acc[db] = Tr::mma(aq, sf, dk_acc[db]);
+      }
+    }
+  };
+
+  // Kept query tiles in order; tl[k] is the tile of step i + k.
+  int tl[3];
+  tl[0] = t_begin < t_end ? next_kept(t_begin) : t_end;
+  tl[1] = tl[0] < t_end ? next_kept(tl[0] + 1) : t_end;
+  tl[2] = tl[1] < t_end ? next_kept(tl[1] + 1) : t_end;
+  if (tl[0] < t_end) {
+    issue(tl[0], 0);
+    if (tl[1] < t_end) issue(tl[1], 1);
+    if (tl[2] < t_end) issue(tl[2], 2);
+    int step = 0;
+    while (true) {
+      // tile tl[0] must have landed (tl[1], and at step 0 tl[2], may stay in flight)
+      wait_tiles((tl[1] < t_end) + (step == 0 && tl[2] < t_end));
+      __syncthreads();  // every wave is done with step i-1
+      if (step > 0 && tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+      const int qi0 = tl[0] * BQ;
+      if (!p.causal || kw0 <= qi0 + BQ - 1) step_math(ring + (step & 3) * L::SLOT_BYTES, qi0);
+      tl[0] = tl[1];
+      tl[1] = tl[2];
+      tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+      ++step;
+      if (tl[0] >= t_end) break;
+    }
+  }
+
+  // Store dK = scale * (dK^T)^T and dV; lane owns key `myk`, rows d of its half.
+  if (myk < N) {
+    raw* dKg = reinterpret_cast<raw*>(p.dk) + head + (size_t)myk * D;
+    raw* dVg = reinterpret_cast<raw*>(p.dv) + head + (size_t)myk * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        raw4 ok, ov;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          ok[u] = __builtin_bit_cast(raw, (T)(dk_acc[db][4 * g + u] * p.scale));
+          ov[u] = __builtin_bit_cast(raw, (T)dv_acc[db][4 * g + u]);
+        }
+        *reinterpret_cast<raw4*>(dKg + db * 32 + 8 * g + 4 * hh) = ok;
+        *reinterpret_cast<raw4*>(dVg + db * 32 + 8 * g + 4 * hh) = ov;
+      }
+  }
+}
+
+// ----------------------------------------------------------------------------
+// 3. dQ.  Work-group: 4 waves x 32 queries; key tiles of BC rows.
+template <typename T, int D>
+struct DqCfg {
+  typedef raw_t<T> raw;
+  // 64 keys per step at d = 64; 32 at d = 128 (two work-groups per CU).
+  static constexpr int BC = D == 128 ? 32 : 64;
+  static constexpr int NS = 4;
+  static constexpr int TILE_BYTES = BC * D * (int)sizeof(raw);   // one of K, V
+  static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
+  static constexpr int LPT = 2 * TILE_BYTES / 4096;
+  static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    DqCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
+  typedef raw_t<T> raw;
+  typedef raw4_t<T> raw4;
+  typedef Traits<T> Tr;
+  typedef DqCfg<T, D> L;
+  constexpr int BC = L::BC;
+  constexpr int BR = 128;
+  constexpr int LPT = L::LPT;
+
+  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ uint8_t mask_row[kMaxMaskBlocks];
+  const uint32_t ring_lds = lds_addr(ring);
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int col = lane & 31;
+  const int hh = lane >> 5;
+  const int N = p.N;
+  const int nq = (N + BR - 1) / BR;
+
+  int qt, bh;
+  map_tile(blockIdx.x, nq, p.BH, p.causal != 0, qt, bh);
+  const int b = bh / p.H;
+  const int i0 = qt * BR;
+  const int qw0 = i0 + 32 * w;
+  const int myq = qw0 + col;
+
+  int kend = N;
+  if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
+  int kv_end = kend;
+  if (p.causal) kv_end = min(kv_end, i0 + BR);
+  const int nkt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  const bool sparse = p.block_mask != nullptr;
+  if (sparse) {
+    const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
+    for (int i = tid; i < p.nblk; i += 256) mask_row[i] = bm[i];
+  }
+
+  const size_t head = (size_t)bh * N * D;
+  const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
+  const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + head;
+  const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + head;
+  const raw* __restrict__ dOg = reinterpret_cast<const raw*>(p.dout) + head;
+
+  frag_t<T> qf[D / 16], df[D / 16];
+#pragma unroll
+  for (int kc = 0; kc < D / 16; ++kc) {
+    const bool ok = myq < N;
+    qf[kc] = ok ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
+    df[kc] = ok ? load_frag<T>(dOg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
+  }
+  float lse2 = __builtin_inff(), dval = 0.f;
+  if (myq < N) {
+    lse2 = p.lse2[(size_t)bh * N + myq];
+    dval = p.dvec[(size_t)bh * N + myq];
+  }
+  __syncthreads();  // mask_row visible
+
+  auto next_kept = [&](int j) {
+    if (!sparse) return j;
+    while (j < nkt && mask_row[(j * BC) / kMaskBlock] == 0) ++j;
+    return j;
+  };
+
+  f32x16 dq_acc[D / 32];
+#pragma unroll
+  for (int db = 0; db < D / 32; ++db) dq_acc[db] = zero16();
+
+  DmaPlan<raw, BC, D, kBoth> kplan;
+  DmaPlan<raw, BC, D, kRows> vplan;
+  kplan.init(w, lane);
+  vplan.init(w, lane);
+  auto issue = [&](int t, int s) {
+    const uint32_t base = ring_lds + s * L::SLOT_BYTES;
+    kplan.copy(Kg, t * BC, N, base, lane);
+    vplan.copy(Vg, t * BC, N, base + L::TILE_BYTES, lane);
+  };
+  auto wait_tiles = [&](int tiles) {
+    if (tiles == 2) wait_vmcnt<2 * LPT>();
+    else if (tiles == 1) wait_vmcnt<LPT>();
+    else wait_vmcnt<0>();
+  };
+
+  const float c = p.c;
+  auto step_math = [&](const char* slot, int kt0) {
+    const raw* Ks = reinterpret_cast<const raw*>(slot);
+    const raw* Vs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    f32x16 sacc[BC / 32], pacc[BC / 32];
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb) {
+      sacc[kb] = zero16();
+      pacc[kb] = zero16();
+#pragma unroll
+      for (int kc = 0; kc < D / 16; ++kc) {
+        const frag_t<T> ak = load_frag_swz<T, D, kBoth>(Ks, kb * 32 + col, kc * 16 + hh * 8);
+        sacc[kb] = Tr::mma(ak, qf[kc], sacc[kb]);
+        const frag_t<T> av = load_frag_swz<T, D, kRows>(Vs, kb * 32 + col, kc * 16 + hh * 8);
+        pacc[kb] = Tr::mma(av, df[kc], pacc[kb]);
+      }
+    }
+    const bool masked = (p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend);
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float pr = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
+        if (masked) {
+          const int key = kt0 + kb * 32 + acc_row(r, hh);
+          if (key >= kend || (p.causal && key > myq)) pr = 0.f;
+        }
+        pacc[kb][r] = pr * (pacc[kb][r] - dval);  // dS^T
+      }
+    // dQ^T += K^T dS^T  (k = keys, acc-ordered slots).
+#pragma unroll
+    for (int kc = 0; kc < BC / 16; ++kc) {
+      const frag_t<T> sf = acc_to_frag<T>(pacc[kc / 2], kc % 2);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const frag_t<T> a = load_frag_tr<T, D, kBoth>(Ks, kc * 16, db * 32, lane);
+        dq_acc[db] = Tr::mma(a, sf, dq_acc[db]);
+      }
+    }
+  };
+
+  int tl[3];
+  tl[0] = next_kept(0);
+  tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
+  tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
+  if (tl[0] < nkt) {
+    issue(tl[0], 0);
+    if (tl[1] < nkt) issue(tl[1], 1);
+    if (tl[2] < nkt) issue(tl[2], 2);
+    int step = 0;
+    while (true) {
+      wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));
+      __syncthreads();  // every wave is done with step i-1
+      if (step > 0 && tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+      const int kt0 = tl[0] * BC;
+      if (!p.causal || kt0 <= qw0 + 31) step_math(ring + (step & 3) * L::SLOT_BYTES, kt0);
+      tl[0] = tl[1];
+      tl[1] = tl[2];
+      tl[2] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+      ++step;
+      if (tl[0] >= nkt) break;
+    }
+  }
+
+  if (myq < N) {
+    raw* dQg = reinterpret_cast<raw*>(p.dq) + head + (size_t)myq * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        raw4 out;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          out[u] = __builtin_bit_cast(raw, (T)(dq_acc[db][4 * g + u] * p.scale));
+        *reinterpret_cast<raw4*>(dQg + db * 32 + 8 * g + 4 * hh) = out;
+      }
+  }
+}
+
+template <typename T, int D>
+hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
+  BwdParams p;
+  p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.dout = t.dout; p.lse = t.lse;
+  p.dq = t.dq; p.dk = t.dk; p.dv = t.dv;
+  const size_t rows_total = (size_t)pb.B * pb.H * pb.N;
+  p.dvec = t.workspace;
+  p.lse2 = t.workspace + rows_total;
+  p.key_lens = pb.key_lens;
+  p.block_mask = pb.block_mask;
+  p.H = pb.H;
+  p.N = pb.N;
+  p.BH = pb.B * pb.H;
+  p.nblk = (pb.N + kMaskBlock - 1) / kMaskBlock;
+  p.scale = pb.scale;
+  p.c = pb.scale * kLog2e;
+  p.causal = pb.causal;
+
+  const long long rows = (long long)rows_total;
+  constexpr int TPR = D * (int)sizeof(raw_t<T>) / 16;
+  const unsigned pre_grid = (unsigned)((rows + (256 / TPR) - 1) / (256 / TPR));
+  timing_begin(kBwdPre, pb.stream);
+  hipLaunchKernelGGL((fa_bwd_preprocess_kernel<T, D>), dim3(pre_grid), dim3(256), 0, pb.stream, p,
+                     rows);
+  hipError_t e = hipGetLastError();
+  timing_end(kBwdPre, pb.stream);
+  if (e != hipSuccess) return e;
+
+  const unsigned tiles128 = (unsigned)((pb.N + 127) / 128);
+  timing_begin(kBwdDkDv, pb.stream);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
+  e = hipGetLastError();
+  timing_end(kBwdDkDv, pb.stream);
+  if (e != hipSuccess) return e;
+
+  timing_begin(kBwdDq, pb.stream);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
+  e = hipGetLastError();
+  timing_end(kBwdDq, pb.stream);
+  return e;
+}
+
+}  // namespace
+}  // namespace fa
