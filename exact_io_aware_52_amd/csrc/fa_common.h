@@ -183,18 +183,18 @@ template <int CPR, int KIND> __device__ __forceinline__ int swz(int r) {
 
 // Copies rows row0 .. row0+ROWS-1 (D elements each, row-major in HBM; rows
 // past N-1 repeat row N-1) into an LDS tile at byte address `lds` with the
-// given chunk swizzle.  The tile is split over the work-group's 4 waves; each
-// wave issues ROWS*D*sizeof(raw)/4096 DMA instructions.
-template <typename raw, int ROWS, int D, int KIND>
+// given chunk swizzle.  The tile is split over the work-group's NW waves; each
+// wave issues ROWS*D*sizeof(raw)/(1024*NW) DMA instructions.
+template <typename raw, int ROWS, int D, int KIND, int NW = 4>
 __device__ __forceinline__ void dma_tile(const raw* __restrict__ g, int row0, int N, uint32_t lds,
                                          int wave, int lane) {
   constexpr int CPR = D * (int)sizeof(raw) / 16;  // chunks per row
   constexpr int VEC = 16 / (int)sizeof(raw);
-  constexpr int NI = ROWS * CPR / 256;           // instructions per wave
-  static_assert(ROWS * CPR % 256 == 0, "tile must split into 1 KB per-wave pieces");
+  constexpr int NI = ROWS * CPR / (64 * NW);      // instructions per wave
+  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into 1 KB per-wave pieces");
 #pragma unroll
   for (int i = 0; i < NI; ++i) {
-    const int blk = i * 4 + wave;        // 1 KB block of the tile
+    const int blk = i * NW + wave;       // 1 KB block of the tile
     const int pos = blk * 64 + lane;     // chunk position within the tile
     const int r = pos / CPR, cs = pos % CPR;
     const int c = cs ^ swz<CPR, KIND>(r);
@@ -206,19 +206,19 @@ __device__ __forceinline__ void dma_tile(const raw* __restrict__ g, int row0, in
 // The same tile copy for tiles whose ROWS rows all exist: this lane's byte
 // offsets within the tile are computed once, each copy only supplies the
 // tile's (wave-uniform) first-row address.
-template <typename raw, int ROWS, int D, int KIND>
+template <typename raw, int ROWS, int D, int KIND, int NW = 4>
 struct DmaPlan {
   static constexpr int CPR = D * (int)sizeof(raw) / 16;
   static constexpr int VEC = 16 / (int)sizeof(raw);
-  static constexpr int NI = ROWS * CPR / 256;
-  static_assert(ROWS * CPR % 256 == 0, "tile must split into 1 KB per-wave pieces");
+  static constexpr int NI = ROWS * CPR / (64 * NW);
+  static_assert(ROWS * CPR % (64 * NW) == 0, "tile must split into 1 KB per-wave pieces");
   uint32_t off[NI];
   int wave;
   __device__ __forceinline__ void init(int wave_, int lane) {
     wave = wave_;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const int pos = (i * 4 + wave) * 64 + lane;
+      const int pos = (i * NW + wave) * 64 + lane;
       const int r = pos / CPR, cs = pos % CPR;
       const int c = cs ^ swz<CPR, KIND>(r);
       off[i] = (uint32_t)((r * D + c * VEC) * (int)sizeof(raw));
@@ -226,13 +226,13 @@ struct DmaPlan {
   }
   __device__ __forceinline__ void issue(const raw* first_row, uint32_t lds) const {
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16s(off[i], first_row, lds + (i * 4 + wave) * 1024);
+    for (int i = 0; i < NI; ++i) dma16s(off[i], first_row, lds + (i * NW + wave) * 1024);
   }
   // rows row0 .. row0+ROWS-1 of g, or the clamped copy if the tile is ragged
   __device__ __forceinline__ void copy(const raw* g, int row0, int N, uint32_t lds,
                                        int lane) const {
     if (row0 + ROWS <= N) issue(g + (size_t)row0 * D, lds);
-    else dma_tile<raw, ROWS, D, KIND>(g, row0, N, lds, wave, lane);
+    else dma_tile<raw, ROWS, D, KIND, NW>(g, row0, N, lds, wave, lane);
   }
 };
 

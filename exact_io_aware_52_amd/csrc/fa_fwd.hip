@@ -10,34 +10,46 @@
 // denominator l, fp32 accumulator) stays in registers for the whole sweep.
 // Both orders give the same result in exact arithmetic.
 //
-// Work split: 4 waves, wave w owns queries i0 + 32w .. i0 + 32w + 31.  For a
-// tile of BC keys a wave forms the transposed score tile S^T (keys x
+// Work split: 4 waves, wave w owns queries i0 + 32w .. i0 + 32w + 31.  For
+// each sub-tile of 32 keys a wave forms the transposed score tile S^T (keys x
 // queries): A = K rows from LDS, B = the wave's Q rows, held in registers for
 // the whole kernel.  With keys as accumulator rows each lane owns one query
-// column, so the row max and row sum are in-register reductions plus one
-// exchange with the lane 32 apart, and the exponentiated tile is already the
-// B operand of O^T += V^T P^T (V^T is written to LDS transposed when staged).
+// column, so row reductions are in-register plus one exchange with the lane
+// 32 apart, and the exponentiated tile is already the B operand of
+// O^T += V^T P^T.
 //
-// Staging: K and V tiles go from HBM straight into a 4-slot LDS ring by
-// direct-to-LDS loads (no staging registers, no vector instructions); a tile
-// is requested two steps before its keys are first used.  K is read as
-// row-major matrix operands; V^T, the A operand of O^T += V^T P^T, is read
-// from the row-major V tile with the transposing LDS read.
+// Staging: K and V tiles (64 keys at d = 64 for 16-bit types, else 32) go
+// from HBM straight into a 4-slot LDS ring by direct-to-LDS loads (no staging
+// registers, no vector instructions); a tile is requested two steps before
+// its keys are first used.  K is read as row-major matrix operands; V^T, the
+// A operand of O^T += V^T P^T, is read from the row-major V tile with the
+// transposing LDS read.  One barrier per ring tile.
 //
-// Software pipeline: K runs one tile ahead of V.  In step i a wave issues
-// the matrix products of the next tile's scores while it exponentiates the
-// current tile and accumulates P V for it, so one wave always has
-// independent matrix-core and vector work in flight.  One barrier per step.
+// Software pipeline (all instances but 16-bit d = 128, whose second score
+// buffer would not fit 256 VGPRs): K runs one sub-tile ahead of V.  A wave
+// issues the products of the next sub-tile's scores while it exponentiates
+// the current one and accumulates its P V, so it always has independent
+// matrix-core and vector work in flight.  Dense interior tiles (visible in
+// full to every wave, whole tiles ahead) run in a loop with no per-tile
+// decisions.
 //
-// Online softmax with lazy rescaling: the running max m only moves (and the
-// accumulator and denominator are rescaled) when a new tile's max exceeds it
-// by more than 2^8 in exp2 units; otherwise probabilities are taken relative
-// to the stale max (at most 256, exactly representable scale).  The result is
-// the same exact softmax.
+// Online softmax with a lazy reference: Q is multiplied by scale * log2(e)
+// once, when loaded, so scores come out of the matrix core in exp2 units, and
+// the C operand of each sub-tile's first product holds -ra, the row's
+// reference point; the products therefore deliver s - ra and each
+// probability is one exp2.  A sub-tile is accepted as is when every lane's
+// sum of its probabilities is at most 2^8 (which bounds each one); only
+// otherwise, or before a row's first visible key, is the sub-tile max taken
+// and the reference moved, with the accumulator and denominator rescaled.
+// The result is the same exact softmax: the reference cancels in O = acc / l.
+// (fp16 with scale * log2(e) > 1 keeps Q as given, where the product could
+// overflow fp16, and scales each score instead.)
 //
-// Masks are decided per tile: tiles past the causal diagonal, past the key
-// length or with a zero block-mask entry are skipped (never loaded); only
-// tiles that straddle a boundary apply an element mask, on a slower path.
+// Masks are decided per sub-tile: tiles past the causal diagonal, past the
+// key length or with a zero block-mask entry are skipped (never loaded); only
+// sub-tiles that straddle a boundary apply an element mask.
+
+#include <type_traits>
 
 #include "fa_common.h"
 #include "fa_internal.h"
@@ -48,7 +60,6 @@ namespace {
 constexpr int kFwdWaves = 4;
 constexpr int kFwdBR = 32 * kFwdWaves;  // query rows per work-group
 constexpr int kMaskBlock = 128;         // block-mask granularity (keys and queries)
-constexpr float kLazy = 8.0f;           // rescale when the max grows by > 2^8
 
 struct FwdParams {
   const void* q;
@@ -69,19 +80,20 @@ constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 13
 template <typename T, int D>
 struct FwdCfg {
   typedef raw_t<T> raw;
-  static constexpr int BC = D == 128 ? 32 : 64;                // keys per step
-  static constexpr int NKB = BC / 32;                           // 32-key blocks per step
+  // BT keys per ring slot (one DMA tile, one barrier); the math runs on
+  // 32-key sub-tiles, NSUB per slot.
+  static constexpr int BT = (D == 64 && sizeof(raw) == 2) ? 64 : 32;
+  static constexpr int NSUB = BT / 32;
   static constexpr int NS = 4;                                  // LDS ring slots
-  static constexpr int TILE_BYTES = BC * D * (int)sizeof(raw);  // one K or V tile
+  static constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);  // one K or V tile
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
   static constexpr int LPT = 2 * TILE_BYTES / 4096;             // DMA instructions per wave per tile
   // Two waves per SIMD for 16-bit inputs; the fp32 instances (accuracy, not
   // speed) take the whole register file.
   static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
-  // Software pipelining (next tile's scores during this tile's softmax) pays
-  // at d = 64, where exponentials rival the matrix products; at d = 128 the
-  // products dominate and the second score buffer would not fit 256 VGPRs.
-  static constexpr bool PIPE = D == 64;
+  // Software pipelining across sub-tiles needs a second score buffer, which
+  // the 16-bit d = 128 instance cannot hold within 256 VGPRs.
+  static constexpr bool PIPE = !(sizeof(raw) == 2 && D == 128);
 };
 
 // Sum of the eight probabilities of a B-operand fragment, added to acc.  For
@@ -112,15 +124,25 @@ __device__ __forceinline__ float frag_sum(const frag_t<float>& f, float acc) {
   return acc;
 }
 
-template <typename T, int D>
+// Q rows pre-multiplied by c = scale * log2(e) and rounded back to T, so that
+// the matrix core delivers scores already in exp2 units.  Used unless T is
+// fp16 and c > 1 (where c * q could overflow fp16).
+template <typename T>
+__device__ __forceinline__ frag_t<T> times_c(frag_t<T> f, float c) {
+#pragma unroll
+  for (int u = 0; u < 8; ++u) f[u] = (T)((float)f[u] * c);
+  return f;
+}
+
+template <typename T, int D, bool PS>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     FwdCfg<T, D>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
   typedef FwdCfg<T, D> L;
-  constexpr int BC = L::BC;
-  constexpr int NKB = L::NKB;
+  constexpr int BT = L::BT;
+  constexpr int NSUB = L::NSUB;
 
   constexpr int LPT = L::LPT;
   constexpr int VSWZ = sizeof(raw) == 2 ? kTr : kRows;  // V^T via transposing reads
@@ -151,7 +173,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
   int kv_end = kend;
   if (p.causal) kv_end = min(kv_end, i0 + kFwdBR);
-  const int nkt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  const int nkt = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
@@ -159,120 +181,160 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   }
   auto next_kept = [&](int j) {
     if (!sparse) return j;
-    while (j < nkt && mask_row[(j * BC) / kMaskBlock] == 0) ++j;
+    while (j < nkt && mask_row[(j * BT) / kMaskBlock] == 0) ++j;
     return j;
   };
-  // Tile t holds keys t*BC .. t*BC+BC-1.  A wave skips tiles wholly past its
-  // causal diagonal and element-masks tiles that straddle a boundary.
-  auto active = [&](int t) { return !p.causal || t * BC <= qw0 + 31; };
-  auto masked = [&](int t) {
-    return (p.causal && t * BC + BC - 1 > qw0) || (t * BC + BC > kend);
-  };
-
   const size_t head = (size_t)bh * N * D;
   const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
   const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + head;
   const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + head;
+  const float c = p.c;
 
   // The wave's Q rows as B operands (contiguous slot map over d).
   frag_t<T> qf[D / 16];
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc)
+  for (int kc = 0; kc < D / 16; ++kc) {
     qf[kc] = myq < N ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
+    if constexpr (PS) qf[kc] = times_c<T>(qf[kc], c);
+  }
   __syncthreads();  // mask_row visible
 
   // K and V of tile t into ring slot s (LPT DMA instructions per wave).  Only
   // the ragged last tile computes clamped per-lane addresses.
-  DmaPlan<raw, BC, D, kRows> kplan;
-  DmaPlan<raw, BC, D, VSWZ> vplan;
+  DmaPlan<raw, BT, D, kRows> kplan;
+  DmaPlan<raw, BT, D, VSWZ> vplan;
   kplan.init(w, lane);
   vplan.init(w, lane);
   auto issue = [&](int t, int s) {
     const uint32_t base = ring_lds + s * L::SLOT_BYTES;
-    kplan.copy(Kg, t * BC, N, base, lane);
-    vplan.copy(Vg, t * BC, N, base + L::TILE_BYTES, lane);
+    kplan.copy(Kg, t * BT, N, base, lane);
+    vplan.copy(Vg, t * BT, N, base + L::TILE_BYTES, lane);
   };
 
   // ---- per-wave math
-  const float c = p.c;
+  // Scores live in "accumulator units": c*s (exp2 units) when Q is
+  // pre-scaled, raw s otherwise; to_e2 maps them to exp2 units.
+  auto to_e2 = [&](float x) { return PS ? x : x * c; };
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-  float m_run = kNegInf;  // running (possibly stale) max of raw scores, this lane's query
-  float l_run = 0.f;      // this lane's half of the denominator, relative to m_run
+  // Reference point of this lane's query row, in accumulator units:
+  // probabilities are p = exp2(to_e2(s - ra)).  ra is the row max as of its
+  // last move and moves only when a sub-tile's probabilities would exceed 2^8.
+  float ra = 0.f;
+  float l_run = 0.f;      // this lane's half of the denominator, relative to ra
+  bool ref = false;       // ra is a row max (pair-uniform); before that, O = l = 0
+  bool all_ref = false;   // wave-uniform: ref holds on every lane
+  f32x16 cinit = zero16();  // -ra in every element: C operand of a tile's first product
 
-  // S^T for one tile: rows = keys of the tile, columns = this wave's queries.
-  auto scores = [&](const raw* Ks, f32x16 (&s)[NKB]) {
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb) s[kb] = zero16();
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-#pragma unroll
-      for (int kb = 0; kb < NKB; ++kb) {
-        const frag_t<T> a = load_frag_swz<T, D, kRows>(Ks, kb * 32 + col, kc * 16 + hh * 8);
-        s[kb] = Tr::mma(a, qf[kc], s[kb]);
-      }
+  // Sub-tile (t, h): keys t*BT + 32h .. +31.  A wave skips sub-tiles wholly
+  // past its causal diagonal and element-masks those that straddle a boundary.
+  auto active = [&](int t, int h) { return !p.causal || t * BT + 32 * h <= qw0 + 31; };
+  auto masked = [&](int t, int h) {
+    const int k0 = t * BT + 32 * h;
+    return (p.causal && k0 + 31 > qw0) || (k0 + 32 > kend);
   };
-  auto apply_mask = [&](int t, f32x16 (&s)[NKB]) {
+  // S^T of one sub-tile minus the reference: rows = keys, columns = queries.
+  auto scores = [&](const raw* Ks, int h, f32x16& s) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = t * BC + kb * 32 + acc_row(r, hh);
-        if (key >= kend || (p.causal && key > myq)) s[kb][r] = kNegInf;
-      }
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const frag_t<T> a = load_frag_swz<T, D, kRows>(Ks, 32 * h + col, kc * 16 + hh * 8);
+      s = Tr::mma(a, qf[kc], kc == 0 ? cinit : s);
+    }
   };
-  auto tile_max = [&](const f32x16 (&s)[NKB]) {
-    float mx = kNegInf;
+  auto apply_mask = [&](int t, int h, f32x16& s) {
 #pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[kb][r]);
-    return pair_max(mx);
+    for (int r = 0; r < 16; ++r) {
+      const int key = t * BT + 32 * h + acc_row(r, hh);
+      if (key >= kend || (p.causal && key > myq)) s[r] = kNegInf;
+    }
   };
-  // Move the running max if this tile's max outruns it (wave-uniform branch).
-  auto maybe_rescale = [&](float m_tile) {
-    const bool need = m_tile > m_run && (m_run == kNegInf || (m_tile - m_run) * c > kLazy);
-    if (__builtin_amdgcn_ballot_w64(need) != 0) {
-      const float m_new = fmaxf(m_run, m_tile);
-      const float alpha = m_run == kNegInf ? 0.f : fast_exp2((m_run - m_new) * c);
-      m_run = m_new;
+  // P = exp2(s - ra - shift) rounded to T, as B operands; returns this lane's
+  // sum of the rounded values (masked keys hold -inf and give 0).
+  auto expo = [&](const f32x16& s, frag_t<T> (&pf)[2], float shift) {
+    float rs = 0.f;
+#pragma unroll
+    for (int h2 = 0; h2 < 2; ++h2) {
+      frag_t<T> f;
+#pragma unroll
+      for (int u = 0; u < 8; ++u) f[u] = (T)fast_exp2(to_e2(s[8 * h2 + u] - shift));
+      pf[h2] = f;
+      rs = frag_sum(f, rs);
+    }
+    return rs;
+  };
+  // Accept the sub-tile if every lane's probabilities are at most 2^8 (their
+  // sum bounds each one) and the row has a reference; otherwise (wave-uniform
+  // branch, rare) move the reference of the rows whose sub-tile max exceeds
+  // it, rescale their accumulator and denominator and redo the exponentials.
+  // snext, the next sub-tile's scores if already formed, shifts with the
+  // reference.
+  auto settle = [&](const f32x16& s, frag_t<T> (&pf)[2], float rs, f32x16& snext) {
+    if (!all_ref || __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0) {
+      float mx = kNegInf;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
+      mx = pair_max(mx);
+      const bool move = mx != kNegInf && (!ref || mx > 0.f);
+      const float shift = move ? mx : 0.f;
+      const float alpha = move && ref ? fast_exp2(-to_e2(mx)) : 1.f;
+      ra += shift;
+      ref = ref || move;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) snext[r] -= shift;
+      rs = expo(s, pf, shift);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) cinit[r] = -ra;
+      all_ref = __builtin_amdgcn_ballot_w64(!ref) == 0;
     }
-  };
-  // P = exp2(c*s - c*m) rounded to T, as B operands; accumulates the row sum.
-  auto softmax = [&](const f32x16 (&s)[NKB], frag_t<T> (&pf)[2 * NKB], bool has_mask) {
-    const float mc = m_run == kNegInf ? 0.f : m_run * c;
-    float rs = 0.f;
-#pragma unroll
-    for (int kb = 0; kb < NKB; ++kb)
-#pragma unroll
-      for (int t = 0; t < 2; ++t) {
-        frag_t<T> f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float x = s[kb][8 * t + u];
-          float e = fast_exp2(fmaf(x, c, -mc));
-          if (has_mask) e = x == kNegInf ? 0.f : e;
-          f[u] = (T)e;
-        }
-        pf[2 * kb + t] = f;
-        rs = frag_sum(f, rs);
-      }
     l_run += rs;
   };
-  auto pv = [&](const raw* Vs, const frag_t<T> (&pf)[2 * NKB]) {
+  auto pv = [&](const raw* Vs, int h, const frag_t<T> (&pf)[2]) {
 #pragma unroll
-    for (int kc = 0; kc < BC / 16; ++kc)
+    for (int kc = 0; kc < 2; ++kc)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
-        const frag_t<T> a = load_frag_tr<T, D, VSWZ>(Vs, kc * 16, db * 32, lane);
+        const frag_t<T> a = load_frag_tr<T, D, VSWZ>(Vs, 32 * h + kc * 16, db * 32, lane);
         oacc[db] = Tr::mma(a, pf[kc], oacc[db]);
       }
+  };
+  // Sub-step with both sub-tiles visible in full: the next one's products
+  // overlap this one's exponentials.
+  auto interior = [&](f32x16& scur, f32x16& snext, int hc, const raw* Vc, int hn,
+                      const raw* Kn) {
+    frag_t<T> pf[2];
+    scores(Kn, hn, snext);
+    const float rs = expo(scur, pf, 0.f);
+    settle(scur, pf, rs, snext);
+    pv(Vc, hc, pf);
+  };
+  // One sub-step: exponentiate sub-tile (tc, hc), whose scores are in scur,
+  // and add its P V, while the products of the next sub-tile (tn, hn), if
+  // any, form in snext: one wave always has independent matrix-core and
+  // vector work in flight.
+  auto substep = [&](f32x16& scur, f32x16& snext, int tc, int hc, const raw* Vc, int tn, int hn,
+                     const raw* Kn, bool has_next) {
+    const bool act_c = active(tc, hc);
+    const bool act_n = has_next && active(tn, hn);
+    if (act_c && act_n && !masked(tn, hn)) {
+      interior(scur, snext, hc, Vc, hn, Kn);
+    } else {
+      if (act_n) {
+        scores(Kn, hn, snext);
+        apply_mask(tn, hn, snext);
+      }
+      if (act_c) {
+        frag_t<T> pf[2];
+        const float rs = expo(scur, pf, 0.f);
+        settle(scur, pf, rs, snext);
+        pv(Vc, hc, pf);
+      }
+    }
   };
 
   // Kept tiles of this work-group, in order; tl[k] is the tile of step i + k.
@@ -281,7 +343,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
   tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
   tl[3] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
-  if (tl[0] < nkt) {
+  if (tl[0] < nkt && L::PIPE) {
     issue(tl[0], 0);
     if (tl[1] < nkt) issue(tl[1], 1);
     if (tl[2] < nkt) issue(tl[2], 2);
@@ -291,48 +353,60 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     else wait_vmcnt<0>();
     __syncthreads();
 
-    f32x16 sa[NKB], sb[NKB];
-    float m_tile_a = kNegInf, m_tile_b = kNegInf;
-    if (active(tl[0])) {
-      scores(ktile(0), sa);
-      if (masked(tl[0])) apply_mask(tl[0], sa);
-      m_tile_a = tile_max(sa);
+    f32x16 sa, sb;
+    if (active(tl[0], 0)) {
+      scores(ktile(0), 0, sa);
+      if (masked(tl[0], 0)) apply_mask(tl[0], 0, sa);
     }
 
-    // Step i: tile tl[0] (scores in scur, max m_cur) is exponentiated and
-    // multiplied into O; tile tl[1]'s scores go to snext.
+    // Step i works on the tile in ring slot i % 4: on entry its first
+    // sub-tile's scores are formed; on exit, those of the next tile.
     int step = 0;
-    auto body = [&](f32x16 (&scur)[NKB], f32x16 (&snext)[NKB], float m_cur, float& m_next) {
-      const int t_cur = tl[0], t_nxt = tl[1];
-      if (t_nxt < nkt) {
+    if constexpr (NSUB == 2) {
+      // Interior steps of a dense problem: tiles i and i+1 are visible in
+      // full to every wave (below the key length and, if causal, at or below
+      // wave 0's first query) and tile i+3 is whole, so a step needs no
+      // per-tile decision: one wait, one barrier, the DMA, the math.
+      if (!sparse) {
+        int lim = min(min(nkt, N / BT) - 4, kend / BT - 2);
+        if (p.causal) lim = min(lim, (i0 + 1) / BT - 2);
+        const int n_int = max(0, lim + 1);
+        for (; step < n_int; ++step) {
+          wait_vmcnt<LPT>();  // tile i+1 landed; tile i+2 may be in flight
+          __syncthreads();    // slot (i+3)%4 is free
+          const uint32_t nb = ring_lds + ((step + 3) & 3) * L::SLOT_BYTES;
+          kplan.issue(Kg + (size_t)(step + 3) * BT * D, nb);
+          vplan.issue(Vg + (size_t)(step + 3) * BT * D, nb + L::TILE_BYTES);
+          const raw* Kc = ktile(step & 3);
+          const raw* Vc = vtile(step & 3);
+          interior(sa, sb, 0, Vc, 1, Kc);
+          interior(sb, sa, 1, Vc, 0, ktile((step + 1) & 3));
+        }
+        if (n_int > 0) {
+          tl[0] = min(n_int, nkt);
+          tl[1] = min(n_int + 1, nkt);
+          tl[2] = min(n_int + 2, nkt);
+          tl[3] = min(n_int + 3, nkt);
+        }
+      }
+    }
+    auto body = [&](f32x16& s0, f32x16& s1) {
+      if (tl[1] < nkt) {
         // tile tl[1] must have landed; tl[2] may still be in flight
         if (tl[2] < nkt) wait_vmcnt<LPT>();
         else wait_vmcnt<0>();
       }
       __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
       if (tl[3] < nkt) issue(tl[3], (step + 3) & 3);
+      const raw* Kc = ktile(step & 3);
       const raw* Kn = ktile((step + 1) & 3);
       const raw* Vc = vtile(step & 3);
-      const bool act_cur = active(t_cur);
-      const bool act_nxt = t_nxt < nkt && active(t_nxt);
-      if (act_cur) maybe_rescale(m_cur);
-      frag_t<T> pf[2 * NKB];
-      if (act_cur && act_nxt && !masked(t_cur) && !masked(t_nxt)) {
-        // interior: straight-line, next tile's products overlap this softmax
-        scores(Kn, snext);
-        softmax(scur, pf, false);
-        pv(Vc, pf);
-        m_next = tile_max(snext);
+      const bool more = tl[1] < nkt;
+      if constexpr (NSUB == 2) {
+        substep(s0, s1, tl[0], 0, Vc, tl[0], 1, Kc, true);
+        substep(s1, s0, tl[0], 1, Vc, tl[1], 0, Kn, more);
       } else {
-        if (act_nxt) {
-          scores(Kn, snext);
-          if (masked(t_nxt)) apply_mask(t_nxt, snext);
-          m_next = tile_max(snext);
-        }
-        if (act_cur) {
-          softmax(scur, pf, masked(t_cur));
-          pv(Vc, pf);
-        }
+        substep(s0, s1, tl[0], 0, Vc, tl[1], 0, Kn, more);
       }
       tl[0] = tl[1];
       tl[1] = tl[2];
@@ -340,46 +414,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
       ++step;
     };
-    if constexpr (L::PIPE) {
-      while (true) {
-        body(sa, sb, m_tile_a, m_tile_b);
-        if (tl[0] >= nkt) break;
-        body(sb, sa, m_tile_b, m_tile_a);
-        if (tl[0] >= nkt) break;
-      }
-    } else {
-      // Step i: scores, softmax and P V of tile tl[0] from ring slot i % 4.
-      while (true) {
-        const int t_cur = tl[0];
-        frag_t<T> pf[2 * NKB];
-        if (step > 0) {
-          // tile tl[0] must have landed; tl[1] may still be in flight
-          if (tl[1] < nkt) wait_vmcnt<LPT>();
-          else wait_vmcnt<0>();
-          __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
-          if (tl[2] < nkt) issue(tl[2], (step + 2) & 3);
-          if (active(t_cur)) {
-            scores(ktile(step & 3), sa);
-            if (masked(t_cur)) apply_mask(t_cur, sa);
-            m_tile_a = tile_max(sa);
-          }
+    while (true) {
+      body(sa, sb);
+      if (tl[0] >= nkt) break;
+      body(NSUB == 2 ? sa : sb, NSUB == 2 ? sb : sa);
+      if (tl[0] >= nkt) break;
+    }
+  } else if (tl[0] < nkt) {
+    // Without the pipeline: step i forms, exponentiates and multiplies into
+    // O the scores of the tile in ring slot i % 4, two tiles in flight.
+    issue(tl[0], 0);
+    if (tl[1] < nkt) issue(tl[1], 1);
+    for (int step = 0;; ++step) {
+      if (tl[1] < nkt) wait_vmcnt<LPT>();  // tl[0] landed; tl[1] may be in flight
+      else wait_vmcnt<0>();
+      __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
+      if (tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+      const raw* Kc = ktile(step & 3);
+      const raw* Vc = vtile(step & 3);
+#pragma unroll
+      for (int h = 0; h < NSUB; ++h) {
+        if (active(tl[0], h)) {
+          f32x16 s, unused;
+          frag_t<T> pf[2];
+          scores(Kc, h, s);
+          if (masked(tl[0], h)) apply_mask(tl[0], h, s);
+          const float rs = expo(s, pf, 0.f);
+          settle(s, pf, rs, unused);
+          pv(Vc, h, pf);
         }
-        if (active(t_cur)) {
-          maybe_rescale(m_tile_a);
-          softmax(sa, pf, masked(t_cur));
-          pv(vtile(step & 3), pf);
-        }
-        tl[0] = tl[1];
-        tl[1] = tl[2];
-        tl[2] = tl[3];
-        tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
-        ++step;
-        if (tl[0] >= nkt) break;
       }
+      tl[0] = tl[1];
+      tl[1] = tl[2];
+      tl[2] = tl[3];
+      tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+      if (tl[0] >= nkt) break;
     }
   }
 
-  // Epilogue: O = acc / l, LSE = scale * m + ln(l).
+  // Epilogue: O = acc / l, LSE = ln(2^ra l) (ra in exp2 units), or
+  // scale ra + ln(l) when ra is a raw score.
   const float l_tot = pair_sum(l_run);
   if (myq < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -396,8 +470,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         }
         *reinterpret_cast<raw4*>(Og + db * 32 + 8 * g + 4 * hh) = out;
       }
-    if (hh == 0)
-      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : kNegInf;
+    if (hh == 0) {
+      const float base = PS ? ra * kLn2 : ra * p.scale;
+      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? base + __logf(l_tot) : kNegInf;
+    }
   }
 }
 
@@ -416,8 +492,13 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
+  // fp16 keeps raw scores when c * q could overflow it
+  const bool prescale = !(sizeof(T) == 2 && !std::is_same<T, __bf16>::value && p.c > 1.f);
   timing_begin(kFwd, pb.stream);
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D>), dim3(grid), dim3(256), 0, pb.stream, p);
+  if (prescale)
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, true>), dim3(grid), dim3(256), 0, pb.stream, p);
+  else
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, false>), dim3(grid), dim3(256), 0, pb.stream, p);
   hipError_t e = hipGetLastError();
   timing_end(kFwd, pb.stream);
   return e;
