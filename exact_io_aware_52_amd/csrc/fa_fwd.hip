@@ -49,8 +49,6 @@
 // key length or with a zero block-mask entry are skipped (never loaded); only
 // sub-tiles that straddle a boundary apply an element mask.
 
-#include <type_traits>
-
 #include "fa_common.h"
 #include "fa_internal.h"
 
@@ -124,17 +122,7 @@ __device__ __forceinline__ float frag_sum(const frag_t<float>& f, float acc) {
   return acc;
 }
 
-// Q rows pre-multiplied by c = scale * log2(e) and rounded back to T, so that
-// the matrix core delivers scores already in exp2 units.  Used unless T is
-// fp16 and c > 1 (where c * q could overflow fp16).
-template <typename T>
-__device__ __forceinline__ frag_t<T> times_c(frag_t<T> f, float c) {
-#pragma unroll
-  for (int u = 0; u < 8; ++u) f[u] = (T)((float)f[u] * c);
-  return f;
-}
-
-template <typename T, int D, bool PS>
+template <typename T, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     FwdCfg<T, D>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
   typedef raw_t<T> raw;
@@ -195,7 +183,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int kc = 0; kc < D / 16; ++kc) {
     qf[kc] = myq < N ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
-    if constexpr (PS) qf[kc] = times_c<T>(qf[kc], c);
   }
   __syncthreads();  // mask_row visible
 
@@ -212,20 +199,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   };
 
   // ---- per-wave math
-  // Scores live in "accumulator units": c*s (exp2 units) when Q is
-  // pre-scaled, raw s otherwise; to_e2 maps them to exp2 units.
-  auto to_e2 = [&](float x) { return PS ? x : x * c; };
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-  // Reference point of this lane's query row, in accumulator units:
-  // probabilities are p = exp2(to_e2(s - ra)).  ra is the row max as of its
-  // last move and moves only when a sub-tile's probabilities would exceed 2^8.
+  // Reference point of this lane's query row in exp2 units: probabilities are
+  // p = exp2(c s - ra).  ra is the row max (times c) as of its last move and
+  // moves only when a sub-tile's probabilities would exceed 2^8.
   float ra = 0.f;
   float l_run = 0.f;      // this lane's half of the denominator, relative to ra
   bool ref = false;       // ra is a row max (pair-uniform); before that, O = l = 0
   bool all_ref = false;   // wave-uniform: ref holds on every lane
-  f32x16 cinit = zero16();  // -ra in every element: C operand of a tile's first product
 
   // Sub-tile (t, h): keys t*BT + 32h .. +31.  A wave skips sub-tiles wholly
   // past its causal diagonal and element-masks those that straddle a boundary.
@@ -234,12 +217,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     const int k0 = t * BT + 32 * h;
     return (p.causal && k0 + 31 > qw0) || (k0 + 32 > kend);
   };
-  // S^T of one sub-tile minus the reference: rows = keys, columns = queries.
+  // S^T of one sub-tile: rows = keys, columns = queries.
   auto scores = [&](const raw* Ks, int h, f32x16& s) {
 #pragma unroll
     for (int kc = 0; kc < D / 16; ++kc) {
       const frag_t<T> a = load_frag_swz<T, D, kRows>(Ks, 32 * h + col, kc * 16 + hh * 8);
-      s = Tr::mma(a, qf[kc], kc == 0 ? cinit : s);
+      s = Tr::mma(a, qf[kc], kc == 0 ? zero16() : s);
     }
   };
   auto apply_mask = [&](int t, int h, f32x16& s) {
@@ -249,15 +232,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       if (key >= kend || (p.causal && key > myq)) s[r] = kNegInf;
     }
   };
-  // P = exp2(s - ra - shift) rounded to T, as B operands; returns this lane's
-  // sum of the rounded values (masked keys hold -inf and give 0).
-  auto expo = [&](const f32x16& s, frag_t<T> (&pf)[2], float shift) {
+  // P = exp2(c s - ra) rounded to T, as B operands; returns this lane's sum
+  // of the rounded values.  Masked keys hold -inf and give 0 (selected
+  // explicitly: with scale 0, c s would be NaN).
+  auto expo = [&](const f32x16& s, frag_t<T> (&pf)[2], bool has_mask) {
     float rs = 0.f;
 #pragma unroll
     for (int h2 = 0; h2 < 2; ++h2) {
       frag_t<T> f;
 #pragma unroll
-      for (int u = 0; u < 8; ++u) f[u] = (T)fast_exp2(to_e2(s[8 * h2 + u] - shift));
+      for (int u = 0; u < 8; ++u) {
+        const float x = s[8 * h2 + u];
+        float e = fast_exp2(fmaf(x, c, -ra));
+        if (has_mask) e = x == kNegInf ? 0.f : e;
+        f[u] = (T)e;
+      }
       pf[h2] = f;
       rs = frag_sum(f, rs);
     }
@@ -267,29 +256,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   // sum bounds each one) and the row has a reference; otherwise (wave-uniform
   // branch, rare) move the reference of the rows whose sub-tile max exceeds
   // it, rescale their accumulator and denominator and redo the exponentials.
-  // snext, the next sub-tile's scores if already formed, shifts with the
-  // reference.
-  auto settle = [&](const f32x16& s, frag_t<T> (&pf)[2], float rs, f32x16& snext) {
+  auto settle = [&](const f32x16& s, frag_t<T> (&pf)[2], float rs, bool has_mask) {
     if (!all_ref || __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0) {
       float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
       mx = pair_max(mx);
-      const bool move = mx != kNegInf && (!ref || mx > 0.f);
-      const float shift = move ? mx : 0.f;
-      const float alpha = move && ref ? fast_exp2(-to_e2(mx)) : 1.f;
-      ra += shift;
+      const float m2 = mx == kNegInf ? kNegInf : mx * c;
+      const bool move = m2 != kNegInf && (!ref || m2 > ra);
+      const float alpha = move && ref ? fast_exp2(ra - m2) : 1.f;
+      ra = move ? m2 : ra;
       ref = ref || move;
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db)
 #pragma unroll
         for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) snext[r] -= shift;
-      rs = expo(s, pf, shift);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) cinit[r] = -ra;
+      rs = expo(s, pf, has_mask);
       all_ref = __builtin_amdgcn_ballot_w64(!ref) == 0;
     }
     l_run += rs;
@@ -309,8 +292,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
                       const raw* Kn) {
     frag_t<T> pf[2];
     scores(Kn, hn, snext);
-    const float rs = expo(scur, pf, 0.f);
-    settle(scur, pf, rs, snext);
+    const float rs = expo(scur, pf, false);
+    settle(scur, pf, rs, false);
     pv(Vc, hc, pf);
   };
   // One sub-step: exponentiate sub-tile (tc, hc), whose scores are in scur,
@@ -321,7 +304,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
                      const raw* Kn, bool has_next) {
     const bool act_c = active(tc, hc);
     const bool act_n = has_next && active(tn, hn);
-    if (act_c && act_n && !masked(tn, hn)) {
+    if (act_c && act_n && !masked(tc, hc) && !masked(tn, hn)) {
       interior(scur, snext, hc, Vc, hn, Kn);
     } else {
       if (act_n) {
@@ -330,8 +313,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       }
       if (act_c) {
         frag_t<T> pf[2];
-        const float rs = expo(scur, pf, 0.f);
-        settle(scur, pf, rs, snext);
+        const bool mc = masked(tc, hc);
+        const float rs = expo(scur, pf, mc);
+        settle(scur, pf, rs, mc);
         pv(Vc, hc, pf);
       }
     }
@@ -435,12 +419,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int h = 0; h < NSUB; ++h) {
         if (active(tl[0], h)) {
-          f32x16 s, unused;
+          f32x16 s;
           frag_t<T> pf[2];
           scores(Kc, h, s);
-          if (masked(tl[0], h)) apply_mask(tl[0], h, s);
-          const float rs = expo(s, pf, 0.f);
-          settle(s, pf, rs, unused);
+          const bool mc = masked(tl[0], h);
+          if (mc) apply_mask(tl[0], h, s);
+          const float rs = expo(s, pf, mc);
+          settle(s, pf, rs, mc);
           pv(Vc, h, pf);
         }
       }
@@ -452,8 +437,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  // Epilogue: O = acc / l, LSE = ln(2^ra l) (ra in exp2 units), or
-  // scale ra + ln(l) when ra is a raw score.
+  // Epilogue: O = acc / l, LSE = ln(2^ra l) = ra ln(2) + ln(l).
   const float l_tot = pair_sum(l_run);
   if (myq < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -471,8 +455,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         *reinterpret_cast<raw4*>(Og + db * 32 + 8 * g + 4 * hh) = out;
       }
     if (hh == 0) {
-      const float base = PS ? ra * kLn2 : ra * p.scale;
-      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? base + __logf(l_tot) : kNegInf;
+      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
     }
   }
 }
@@ -492,13 +475,8 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
-  // fp16 keeps raw scores when c * q could overflow it
-  const bool prescale = !(sizeof(T) == 2 && !std::is_same<T, __bf16>::value && p.c > 1.f);
   timing_begin(kFwd, pb.stream);
-  if (prescale)
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, true>), dim3(grid), dim3(256), 0, pb.stream, p);
-  else
-    hipLaunchKernelGGL((fa_fwd_kernel<T, D, false>), dim3(grid), dim3(256), 0, pb.stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<T, D>), dim3(grid), dim3(256), 0, pb.stream, p);
   hipError_t e = hipGetLastError();
   timing_end(kFwd, pb.stream);
   return e;

@@ -155,6 +155,17 @@ def test_block_mask_with_empty_rows():
     compare(gpu, run_oracle(prob), TOL["fp16"], label="empty mask rows")
 
 
+@pytest.mark.parametrize("dtype,d,causal", [("fp16", 64, True), ("fp16", 128, False),
+                                             ("bf16", 64, False), ("bf16", 128, True)])
+def test_large_scale(dtype, d, causal):
+    # scale * log2(e) > 1: fp16 keeps Q unscaled and scales each score (the
+    # pre-scaled product could overflow fp16); bf16 still pre-scales.  Scores
+    # have standard deviation sqrt(d), so rows are close to one-hot.
+    prob = inputs.make_problem(1, 2, 300, d, dtype, seed=83 + d, causal=causal, scale=1.0)
+    compare(run_gpu(prob), run_oracle(prob), TOL[dtype], label=f"scale 1 {dtype} d{d}",
+            magnitude_scaled=True)
+
+
 def test_scale_zero_is_uniform_attention():
     prob = inputs.make_problem(1, 2, 200, 64, "fp32", seed=79, causal=True, scale=0.0)
     compare(run_gpu(prob), run_oracle(prob), TOL["fp32"], label="scale 0")
