@@ -33,17 +33,16 @@
 // full to every wave, whole tiles ahead) run in a loop with no per-tile
 // decisions.
 //
-// Online softmax with a lazy reference: Q is multiplied by scale * log2(e)
-// once, when loaded, so scores come out of the matrix core in exp2 units, and
-// the C operand of each sub-tile's first product holds -ra, the row's
-// reference point; the products therefore deliver s - ra and each
-// probability is one exp2.  A sub-tile is accepted as is when every lane's
-// sum of its probabilities is at most 2^8 (which bounds each one); only
-// otherwise, or before a row's first visible key, is the sub-tile max taken
-// and the reference moved, with the accumulator and denominator rescaled.
-// The result is the same exact softmax: the reference cancels in O = acc / l.
-// (fp16 with scale * log2(e) > 1 keeps Q as given, where the product could
-// overflow fp16, and scales each score instead.)
+// Online softmax with a lazy reference: each probability is
+// exp2(fma(s, c, -ra)), s the fp32 score, c = scale * log2(e) and ra the
+// row's reference point in exp2 units.  A sub-tile is accepted as is when
+// every lane's sum of its probabilities is at most 2^8 (which bounds each
+// one), so no per-tile max is taken; only otherwise, or before a row's first
+// visible key, is the sub-tile max formed and the reference moved, with the
+// accumulator and denominator rescaled.  The result is the same exact
+// softmax: the reference cancels in O = acc / l.  (Pre-multiplying Q by c
+// would save the multiply but round c q to the input type, an error that
+// grows with the size of the scores.)
 //
 // Masks are decided per sub-tile: tiles past the causal diagonal, past the
 // key length or with a zero block-mask entry are skipped (never loaded); only
