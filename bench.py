@@ -39,7 +39,6 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.h"],
-    "bwd_pre": ["fa_bwd_impl.h", "fa_common.h"],
     "bwd_dkdv": ["fa_bwd_impl.h", "fa_common.h"],
     "bwd_dq": ["fa_bwd_impl.h", "fa_common.h"],
 }
@@ -150,7 +149,7 @@ def main():
         print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30}))
         return
 
-    for k in ("fwd", "bwd_pre", "bwd_dkdv", "bwd_dq"):
+    for k in ("fwd", "bwd_dkdv", "bwd_dq"):
         KERNEL_NAMES[k] = fa_kernel_name(k)
 
     prob = make_workload(args)

@@ -14,7 +14,7 @@ import torch
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KERNEL_KINDS = {"fwd": 0, "bwd_pre": 1, "bwd_dkdv": 2, "bwd_dq": 3}
+KERNEL_KINDS = {"fwd": 0, "bwd_dkdv": 1, "bwd_dq": 2}
 
 _LIB = None
 

@@ -225,7 +225,6 @@ int fa_timing_read(int kernel, double* total_ms, int* launches) {
 const char* fa_kernel_name(int kernel) {
   switch (kernel) {
     case fa::kFwd: return "fa_fwd_kernel";
-    case fa::kBwdPre: return "fa_bwd_preprocess_kernel";
     case fa::kBwdDkDv: return "fa_bwd_dkdv_kernel";
     case fa::kBwdDq: return "fa_bwd_dq_kernel";
   }

@@ -7,18 +7,19 @@
 //   dV = P^T dO,  dP = dO V^T,  dS = P * (dP - D),  dK = scale dS^T Q,
 //   dQ = scale dS K.
 //
-// Three launches on the caller's stream:
-//   1. fa_bwd_preprocess_kernel: D and LSE * log2(e) for every row, into the
-//      caller's workspace (reads O and dO once).
+// Two launches on the caller's stream:
+//   1. fa_bwd_dq_kernel: one work-group per 128 queries; scores recomputed
+//      with keys as accumulator rows (as in the forward) feed
+//      dQ^T += K^T dS^T, K^T by transposing LDS reads.  Each lane holds its
+//      query's Q and dO rows; it also reads the O row, forms
+//      D = rowsum(dO * O) and writes -D and LSE * log2(e) to the caller's
+//      workspace for the second pass.
 //   2. fa_bwd_dkdv_kernel: one work-group per 128 keys of a head; its four
 //      waves keep K, V (as matrix operands) and the dK, dV accumulators in
 //      registers and sweep the query tiles that see those keys.  The score
 //      tile is formed with queries as accumulator rows, so P and dS are the B
 //      operands of dV^T += dO^T P and dK^T += Q^T dS straight from registers;
 //      dO^T and Q^T come from the row-major tiles by transposing LDS reads.
-//   3. fa_bwd_dq_kernel: one work-group per 128 queries; the same
-//      recomputation with keys as accumulator rows (as in the forward) feeds
-//      dQ^T += K^T dS^T, K^T again by transposing reads.
 // Splitting dQ into its own pass recomputes S and dP once more (6 d flops per
 // pair on top of the 8 d of the dK/dV pass) but needs no atomics, keeps every
 // accumulator in registers and makes the result deterministic.
@@ -58,7 +59,7 @@ struct BwdParams {
   void* dk;
   void* dv;
   float* lse2;   // workspace: LSE * log2(e), +inf for rows without a visible key
-  float* dvec;   // workspace: D = rowsum(dO * O)
+  float* dvec;   // workspace: -D = -rowsum(dO * O)
   const int32_t* key_lens;
   const uint8_t* block_mask;
   int H, N, BH, nblk;
@@ -68,39 +69,7 @@ struct BwdParams {
 };
 
 // ----------------------------------------------------------------------------
-// 1. D_i = sum_k dO_ik O_ik and LSE_i * log2(e), one row per group of TPR threads.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void fa_bwd_preprocess_kernel(BwdParams p, long long rows) {
-  typedef raw_t<T> raw;
-  constexpr int VEC = 16 / sizeof(raw);
-  constexpr int TPR = D / VEC;  // threads per row
-  const int tid = threadIdx.x;
-  const long long row = (long long)blockIdx.x * (256 / TPR) + tid / TPR;
-  const int sub = tid % TPR;
-  float acc = 0.f;
-  if (row < rows) {
-    const raw* O = reinterpret_cast<const raw*>(p.o) + row * D + sub * VEC;
-    const raw* dO = reinterpret_cast<const raw*>(p.dout) + row * D + sub * VEC;
-    const uint4 a = *reinterpret_cast<const uint4*>(O);
-    const uint4 b = *reinterpret_cast<const uint4*>(dO);
-    const raw* ar = reinterpret_cast<const raw*>(&a);
-    const raw* br = reinterpret_cast<const raw*>(&b);
-#pragma unroll
-    for (int i = 0; i < VEC; ++i) acc = fmaf(to_f32<T>(ar[i]), to_f32<T>(br[i]), acc);
-  }
-#pragma unroll
-  for (int off = TPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, TPR);
-  if (row < rows && sub == 0) {
-    p.dvec[row] = acc;
-    const float l = p.lse[row];
-    // Rows without any visible key get +inf, so that every probability
-    // recomputed for them is exp2(-inf) = 0.
-    p.lse2[row] = l == kNegInf ? __builtin_inff() : l * kLog2e;
-  }
-}
-
-// ----------------------------------------------------------------------------
-// 2. dK, dV.  Work-group: 4 waves x 32 keys; query tiles of BQ rows.
+// dK, dV.  Work-group: 4 waves x 32 keys; query tiles of BQ rows.
 template <typename T, int D>
 struct DkDvCfg {
   typedef raw_t<T> raw;
@@ -113,6 +82,9 @@ struct DkDvCfg {
   // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
   // accumulators: 192 VGPRs) only fits one wave per SIMD.
   static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
+  // Defer each tile's dV, dK products by one step (needs the registers of
+  // one wave per SIMD).
+  static constexpr bool DEFER = WAVES_PER_SIMD == 1;
 };
 
 template <typename T, int D>
@@ -217,35 +189,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   };
 
   const float c = p.c;
-  auto step_math = [&](const char* slot, int qi0) {
+  typedef f32x16 qblk[BQ / 32];
+  // S (queries x keys) and dP = dO V^T of the query tile in `slot`, with
+  // queries as accumulator rows.
+  auto sdp = [&](const char* slot, qblk& sacc, qblk& pacc) {
     const raw* Qs = reinterpret_cast<const raw*>(slot);
     const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
-    const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
-    const float* dvs = lse2s + 64;
-    // S (queries x keys) and dP, with queries as accumulator rows.
-    f32x16 sacc[BQ / 32], pacc[BQ / 32];
+    const float* dns = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES) + 64;
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb) {
-      sacc[qb] = zero16();
-      pacc[qb] = zero16();
+      // -D of the accumulator rows (queries qb*32 + 8g + 4hh + u)
+      f32x16 dneg;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const float4 d4 = *reinterpret_cast<const float4*>(dns + qb * 32 + 8 * g + 4 * hh);
+        dneg[4 * g] = d4.x;
+        dneg[4 * g + 1] = d4.y;
+        dneg[4 * g + 2] = d4.z;
+        dneg[4 * g + 3] = d4.w;
+      }
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
-        sacc[qb] = Tr::mma(aq, kf[kc], sacc[qb]);
+        sacc[qb] = Tr::mma(aq, kf[kc], kc == 0 ? zero16() : sacc[qb]);
         const frag_t<T> ad = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, kc * 16 + hh * 8);
-        pacc[qb] = Tr::mma(ad, vf[kc], pacc[qb]);
+        pacc[qb] = Tr::mma(ad, vf[kc], kc == 0 ? dneg : pacc[qb]);  // dP - D
       }
     }
-    const bool masked = (p.causal && kw0 + 31 > qi0) || (kw0 + 32 > kend) || (qi0 + BQ > N);
+  };
+  // In place: P = exp2(c S - LSE2) into sacc, dS = P (dP - D) into pacc.
+  auto soft = [&](const char* slot, int qi0, bool masked, qblk& sacc, qblk& pacc) {
+    const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
 #pragma unroll
     for (int qb = 0; qb < BQ / 32; ++qb)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
         const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
-        const float4 d4 = *reinterpret_cast<const float4*>(dvs + r0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * g + u;
@@ -255,25 +236,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
             if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
           }
           sacc[qb][r] = pr;                          // P
-          pacc[qb][r] = pr * (pacc[qb][r] - dv[u]);  // dS = P (dP - D)
+          pacc[qb][r] = pr * pacc[qb][r];            // dS = P (dP - D)
         }
       }
-    // dV^T += dO^T P,  dK^T += Q^T dS  (k = queries, acc-ordered slots).
+  };
+  // P and dS of a tile as B operands over the query dimension.
+  typedef frag_t<T> qfrag[BQ / 16];
+  auto to_frags = [&](const qblk& sacc, const qblk& pacc, qfrag& pf, qfrag& sf) {
 #pragma unroll
     for (int qc = 0; qc < BQ / 16; ++qc) {
-      const frag_t<T> pf = acc_to_frag<T>(sacc[qc / 2], qc % 2);
-      const frag_t<T> sf = acc_to_frag<T>(pacc[qc / 2], qc % 2);
+      pf[qc] = acc_to_frag<T>(sacc[qc / 2], qc % 2);
+      sf[qc] = acc_to_frag<T>(pacc[qc / 2], qc % 2);
+    }
+  };
+  // dV^T += dO^T P,  dK^T += Q^T dS  (k = queries, acc-ordered slots).
+  auto grads = [&](const char* slot, const qfrag& pf, const qfrag& sf) {
+    const raw* Qs = reinterpret_cast<const raw*>(slot);
+    const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+#pragma unroll
+    for (int qc = 0; qc < BQ / 16; ++qc)
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) {
         const frag_t<T> ado = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
-        dv_acc[db] = Tr::mma(ado, pf, dv_acc[db]);
+        dv_acc[db] = Tr::mma(ado, pf[qc], dv_acc[db]);
         const frag_t<T> aq = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
-        dk_acc[db] = Tr::mma(aq, sf, dk_acc[db]);
+        dk_acc[db] = Tr::mma(aq, sf[qc], dk_acc[db]);
       }
-    }
+  };
+  auto slot_of = [&](int s) { return ring + (s & 3) * L::SLOT_BYTES; };
+  // Query tile t reaches this wave's keys (under a causal mask the first
+  // tiles may not; once a tile does, every later one does).
+  auto active = [&](int t) { return !p.causal || kw0 <= t * BQ + BQ - 1; };
+  auto masked = [&](int t) {
+    const int qi0 = t * BQ;
+    return (p.causal && kw0 + 31 > qi0) || (kw0 + 32 > kend) || (qi0 + BQ > N);
   };
 
-  // Kept query tiles in order; tl[k] is the tile of step i + k.
+  // Kept query tiles in order; tl[k] is the tile of step i + k.  Step i
+  // forms S and dP of tile i, then runs the dV, dK products of tile i-1
+  // (deferred by one step, still in ring slot i-1) alongside the softmax of
+  // tile i, so the matrix core has work while the exponentials run.
   int tl[3];
   tl[0] = t_begin < t_end ? next_kept(t_begin) : t_end;
   tl[1] = tl[0] < t_end ? next_kept(tl[0] + 1) : t_end;
@@ -281,21 +283,78 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (tl[0] < t_end) {
     issue(tl[0], 0);
     if (tl[1] < t_end) issue(tl[1], 1);
-    if (tl[2] < t_end) issue(tl[2], 2);
+    // Dense interior: every wave's keys see tile t in full, and tiles t+1,
+    // t+2 are whole.
+    int lo = t_end, hi = -1;
+    if (!sparse && j0 + BK <= kend) {
+      lo = p.causal ? (j0 + BK - 1 + BQ - 1) / BQ : t_begin;
+      hi = min(N / BQ - 3, t_end - 3);
+    }
+    qfrag pf, sf;  // deferred P, dS of the previous tile (zero: nothing yet)
+#pragma unroll
+    for (int qc = 0; qc < BQ / 16; ++qc) {
+      pf[qc] = zero_frag<T>();
+      sf[qc] = zero_frag<T>();
+    }
+    int prev = -1;  // step of the deferred tile
     int step = 0;
     while (true) {
-      // tile tl[0] must have landed (tl[1], and at step 0 tl[2], may stay in flight)
-      wait_tiles((tl[1] < t_end) + (step == 0 && tl[2] < t_end));
-      __syncthreads();  // every wave is done with step i-1
-      if (step > 0 && tl[2] < t_end) issue(tl[2], (step + 2) & 3);
-      const int qi0 = tl[0] * BQ;
-      if (!p.causal || kw0 <= qi0 + BQ - 1) step_math(ring + (step & 3) * L::SLOT_BYTES, qi0);
-      tl[0] = tl[1];
-      tl[1] = tl[2];
-      tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+      const int t = tl[0];
+      // With nothing deferred the zero fragments are multiplied with the
+      // current (finite) slot, adding nothing.
+      const char* pslot = slot_of(prev >= 0 ? prev : step);
+      (void)pslot;
+      if (t >= lo && t <= hi) {
+        wait_tiles(1);    // tile t landed; t+1 may be in flight
+        __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
+        const uint32_t base = ring_lds + ((step + 2) & 3) * L::SLOT_BYTES;
+        const int qn = (t + 2) * BQ;
+        plan.issue(Qg + (size_t)qn * D, base);
+        plan.issue(dOg + (size_t)qn * D, base + L::TILE_BYTES);
+        if (w < 2)
+          dma4s((uint32_t)(qn + lane) * 4u, w == 0 ? (const void*)lse2g : (const void*)dvecg,
+                base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
+        qblk sacc, pacc;
+        sdp(slot_of(step), sacc, pacc);
+        if constexpr (L::DEFER) {
+          grads(pslot, pf, sf);
+          soft(slot_of(step), t * BQ, false, sacc, pacc);
+          to_frags(sacc, pacc, pf, sf);
+          prev = step;
+        } else {
+          soft(slot_of(step), t * BQ, false, sacc, pacc);
+          to_frags(sacc, pacc, pf, sf);
+          grads(slot_of(step), pf, sf);
+        }
+        tl[0] = t + 1;
+        tl[1] = t + 2;
+        tl[2] = min(t + 3, t_end);
+      } else {
+        wait_tiles(tl[1] < t_end ? 1 : 0);  // tile t landed; tl[1] may be in flight
+        __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
+        if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+        if (active(t)) {
+          qblk sacc, pacc;
+          sdp(slot_of(step), sacc, pacc);
+          if constexpr (L::DEFER) {
+            grads(pslot, pf, sf);
+            soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
+            to_frags(sacc, pacc, pf, sf);
+            prev = step;
+          } else {
+            soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
+            to_frags(sacc, pacc, pf, sf);
+            grads(slot_of(step), pf, sf);
+          }
+        }
+        tl[0] = tl[1];
+        tl[1] = tl[2];
+        tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+      }
       ++step;
       if (tl[0] >= t_end) break;
     }
+    if (prev >= 0) grads(slot_of(prev), pf, sf);  // the last tile
   }
 
   // Store dK = scale * (dK^T)^T and dV; lane owns key `myk`, rows d of its half.
@@ -319,7 +378,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 }
 
 // ----------------------------------------------------------------------------
-// 3. dQ.  Work-group: 4 waves x 32 queries; key tiles of BC rows.
+// dQ (and D).  Work-group: 4 waves x 32 queries; key tiles of BC rows.
 template <typename T, int D>
 struct DqCfg {
   typedef raw_t<T> raw;
@@ -386,11 +445,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     qf[kc] = ok ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
     df[kc] = ok ? load_frag<T>(dOg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
   }
-  float lse2 = __builtin_inff(), dval = 0.f;
+  // D = rowsum(dO * O) of this lane's query (each lane holds half of d) and
+  // LSE * log2(e); both also go to the workspace for the dK/dV pass, which
+  // runs after this one.  Rows without a visible key get LSE2 = +inf, so that
+  // every probability recomputed for them is exp2(-inf) = 0.
+  float part = 0.f, lse2 = __builtin_inff();
   if (myq < N) {
-    lse2 = p.lse2[(size_t)bh * N + myq];
-    dval = p.dvec[(size_t)bh * N + myq];
+    const raw* Og = reinterpret_cast<const raw*>(p.o) + head + (size_t)myq * D;
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const frag_t<T> of = load_frag<T>(Og + kc * 16 + hh * 8);
+#pragma unroll
+      for (int u = 0; u < 8; ++u) part = fmaf((float)of[u], (float)df[kc][u], part);
+    }
+    const float l = p.lse[(size_t)bh * N + myq];
+    lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
+  const float dneg = -pair_sum(part);  // -D
+  if (myq < N && hh == 0) {
+    p.dvec[(size_t)bh * N + myq] = dneg;
+    p.lse2[(size_t)bh * N + myq] = lse2;
+  }
+  f32x16 dinit;  // C operand starting each dP^T product: it delivers dP^T - D
+#pragma unroll
+  for (int r = 0; r < 16; ++r) dinit[r] = dneg;
   __syncthreads();  // mask_row visible
 
   auto next_kept = [&](int j) {
@@ -425,14 +503,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     f32x16 sacc[BC / 32], pacc[BC / 32];
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb) {
-      sacc[kb] = zero16();
-      pacc[kb] = zero16();
 #pragma unroll
       for (int kc = 0; kc < D / 16; ++kc) {
         const frag_t<T> ak = load_frag_swz<T, D, kBoth>(Ks, kb * 32 + col, kc * 16 + hh * 8);
-        sacc[kb] = Tr::mma(ak, qf[kc], sacc[kb]);
+        sacc[kb] = Tr::mma(ak, qf[kc], kc == 0 ? zero16() : sacc[kb]);
         const frag_t<T> av = load_frag_swz<T, D, kRows>(Vs, kb * 32 + col, kc * 16 + hh * 8);
-        pacc[kb] = Tr::mma(av, df[kc], pacc[kb]);
+        pacc[kb] = Tr::mma(av, df[kc], kc == 0 ? dinit : pacc[kb]);
       }
     }
     const bool masked = (p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend);
@@ -445,7 +521,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
           const int key = kt0 + kb * 32 + acc_row(r, hh);
           if (key >= kend || (p.causal && key > myq)) pr = 0.f;
         }
-        pacc[kb][r] = pr * (pacc[kb][r] - dval);  // dS^T
+        pacc[kb][r] = pr * pacc[kb][r];  // dS^T = P^T (dP^T - D)
       }
     // dQ^T += K^T dS^T  (k = keys, acc-ordered slots).
 #pragma unroll
@@ -515,27 +591,17 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
 
-  const long long rows = (long long)rows_total;
-  constexpr int TPR = D * (int)sizeof(raw_t<T>) / 16;
-  const unsigned pre_grid = (unsigned)((rows + (256 / TPR) - 1) / (256 / TPR));
-  timing_begin(kBwdPre, pb.stream);
-  hipLaunchKernelGGL((fa_bwd_preprocess_kernel<T, D>), dim3(pre_grid), dim3(256), 0, pb.stream, p,
-                     rows);
+  const unsigned tiles128 = (unsigned)((pb.N + 127) / 128);
+  timing_begin(kBwdDq, pb.stream);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
   hipError_t e = hipGetLastError();
-  timing_end(kBwdPre, pb.stream);
+  timing_end(kBwdDq, pb.stream);
   if (e != hipSuccess) return e;
 
-  const unsigned tiles128 = (unsigned)((pb.N + 127) / 128);
   timing_begin(kBwdDkDv, pb.stream);
   hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
   e = hipGetLastError();
   timing_end(kBwdDkDv, pb.stream);
-  if (e != hipSuccess) return e;
-
-  timing_begin(kBwdDq, pb.stream);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
-  e = hipGetLastError();
-  timing_end(kBwdDq, pb.stream);
   return e;
 }
 

@@ -77,20 +77,25 @@ constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 13
 template <typename T, int D>
 struct FwdCfg {
   typedef raw_t<T> raw;
+  static constexpr bool B16 = sizeof(raw) == 2;
   // BT keys per ring slot (one DMA tile, one barrier); the math runs on
   // 32-key sub-tiles, NSUB per slot.
-  static constexpr int BT = (D == 64 && sizeof(raw) == 2) ? 64 : 32;
+  static constexpr int BT = (B16 && D == 64) ? 64 : 32;
   static constexpr int NSUB = BT / 32;
-  static constexpr int NS = 4;                                  // LDS ring slots
+  // Software pipelining across sub-tiles (a second score buffer); the 16-bit
+  // instances instead keep more waves resident, which interleave matrix and
+  // vector work across waves and hide the LDS latency.
+  static constexpr bool PIPE = !B16;
+  // Resident waves per SIMD (VGPR budget 512 / WAVES_PER_SIMD) and LDS ring
+  // slots: at d = 64, 3 waves (<= 168 VGPRs) and a 3-slot ring (49 KB, three
+  // work-groups per CU); at d = 128 the VGPRs allow 2.  The fp32 instances
+  // (accuracy, not speed) take the whole register file.
+  static constexpr int WAVES_PER_SIMD = B16 ? (D == 64 ? 3 : 2) : 1;
+  static constexpr int NS = B16 ? (D == 64 ? 3 : 4) : 4;
   static constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);  // one K or V tile
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
   static constexpr int LPT = 2 * TILE_BYTES / 4096;             // DMA instructions per wave per tile
-  // Two waves per SIMD for 16-bit inputs; the fp32 instances (accuracy, not
-  // speed) take the whole register file.
-  static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
-  // Software pipelining across sub-tiles needs a second score buffer, which
-  // the 16-bit d = 128 instance cannot hold within 256 VGPRs.
-  static constexpr bool PIPE = !(sizeof(raw) == 2 && D == 128);
+  static_assert(!PIPE || NS == 4, "the pipelined loop uses a 4-slot ring");
 };
 
 // Sum of the eight probabilities of a B-operand fragment, added to acc.  For
@@ -256,7 +261,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   // branch, rare) move the reference of the rows whose sub-tile max exceeds
   // it, rescale their accumulator and denominator and redo the exponentials.
   auto settle = [&](const f32x16& s, frag_t<T> (&pf)[2], float rs, bool has_mask) {
-    if (!all_ref || __builtin_amdgcn_ballot_w64(!(rs <= 256.f)) != 0) {
+    // (The ballot is taken unconditionally so that the exponentials above
+    // stay on the straight-line path.)
+    const uint64_t over = __builtin_amdgcn_ballot_w64(!(rs <= 256.f));
+    if (over != 0 || !all_ref) {
       float mx = kNegInf;
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[r]);
@@ -405,33 +413,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     }
   } else if (tl[0] < nkt) {
     // Without the pipeline: step i forms, exponentiates and multiplies into
-    // O the scores of the tile in ring slot i % 4, two tiles in flight.
-    issue(tl[0], 0);
-    if (tl[1] < nkt) issue(tl[1], 1);
-    for (int step = 0;; ++step) {
-      if (tl[1] < nkt) wait_vmcnt<LPT>();  // tl[0] landed; tl[1] may be in flight
-      else wait_vmcnt<0>();
-      __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
-      if (tl[2] < nkt) issue(tl[2], (step + 2) & 3);
-      const raw* Kc = ktile(step & 3);
-      const raw* Vc = vtile(step & 3);
+    // O the scores of tile i, from ring slot i % NS, with the next NS - 1
+    // tiles requested ahead (several work-groups per CU hide the latency).
+    constexpr int NS = L::NS, PD = NS - 1;
+    static_assert(PD >= 1 && PD <= 3, "ring of 2 to 4 slots");
 #pragma unroll
-      for (int h = 0; h < NSUB; ++h) {
-        if (active(tl[0], h)) {
-          f32x16 s;
+    for (int k = 0; k < PD; ++k)
+      if (tl[k] < nkt) issue(tl[k], k);
+    int cur = 0, nxt = PD;  // ring slots of tile i and of tile i + PD
+    // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
+    int lo = nkt, hi = -1;
+    if (!sparse) {
+      lo = 0;
+      hi = min(min(nkt, N / BT) - 1 - PD, kend / BT - 1);
+      if (p.causal) hi = min(hi, (i0 + 1) / BT - 1);
+    }
+    for (int step = 0;; ++step) {
+      const int t = tl[0];
+      const raw* Kc = ktile(cur);
+      const raw* Vc = vtile(cur);
+      if (t >= lo && t <= hi) {
+        wait_vmcnt<(PD - 1) * LPT>();  // tile t landed; t+1 .. t+PD-1 may be in flight
+        __syncthreads();               // every wave is done with step i-1: slot nxt is free
+        const uint32_t nb = ring_lds + nxt * L::SLOT_BYTES;
+        kplan.issue(Kg + (size_t)(t + PD) * BT * D, nb);
+        vplan.issue(Vg + (size_t)(t + PD) * BT * D, nb + L::TILE_BYTES);
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) {
+          f32x16 sc;
           frag_t<T> pf[2];
-          scores(Kc, h, s);
-          const bool mc = masked(tl[0], h);
-          if (mc) apply_mask(tl[0], h, s);
-          const float rs = expo(s, pf, mc);
-          settle(s, pf, rs, mc);
+          scores(Kc, h, sc);
+          const float rs = expo(sc, pf, false);
+          settle(sc, pf, rs, false);
           pv(Vc, h, pf);
         }
+#pragma unroll
+        for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
+        tl[PD] = min(t + PD + 1, nkt);
+      } else {
+        int inflight = 0;  // later tiles requested so far
+#pragma unroll
+        for (int k = 1; k < PD; ++k) inflight += tl[k] < nkt;
+        if (inflight >= 2) wait_vmcnt<2 * LPT>();
+        else if (inflight == 1) wait_vmcnt<LPT>();
+        else wait_vmcnt<0>();
+        __syncthreads();  // every wave is done with step i-1: slot nxt is free
+        if (tl[PD] < nkt) issue(tl[PD], nxt);
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) {
+          if (active(t, h)) {
+            f32x16 sc;
+            frag_t<T> pf[2];
+            scores(Kc, h, sc);
+            const bool mc = masked(t, h);
+            if (mc) apply_mask(t, h, sc);
+            const float rs = expo(sc, pf, mc);
+            settle(sc, pf, rs, mc);
+            pv(Vc, h, pf);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
+        tl[PD] = tl[PD] < nkt ? next_kept(tl[PD] + 1) : nkt;
       }
-      tl[0] = tl[1];
-      tl[1] = tl[2];
-      tl[2] = tl[3];
-      tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+      cur = cur + 1 == NS ? 0 : cur + 1;
+      nxt = nxt + 1 == NS ? 0 : nxt + 1;
       if (tl[0] >= nkt) break;
     }
   }

@@ -8,7 +8,7 @@
 
 namespace fa {
 
-enum KernelKind { kFwd = 0, kBwdPre = 1, kBwdDkDv = 2, kBwdDq = 3, kNumKernelKinds = 4 };
+enum KernelKind { kFwd = 0, kBwdDkDv = 1, kBwdDq = 2, kNumKernelKinds = 3 };
 
 struct Problem {
   int B, H, N, d;
@@ -38,7 +38,7 @@ struct BwdTensors {
   void* dq;
   void* dk;
   void* dv;
-  float* workspace;  // caller's workspace: D = rowsum(dO * O), then LSE * log2(e),
+  float* workspace;  // caller's workspace: -D = -rowsum(dO * O), then LSE * log2(e),
                     // each float32 [B, H, N]
 };
 

@@ -100,8 +100,9 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
  * block_size is ignored then.  Overwrites dq, dk, dv (dtype).
  * workspace: device memory of at least fa_backward_workspace_bytes(B,H,N,d)
  * bytes, 16-byte aligned, owned by the caller, contents need not be
- * initialised; it holds D = rowsum(dout * o) and LSE * log2(e), each float32
- * [B,H,N].  Calls that share a workspace must be ordered on one stream.
+ * initialised; the dQ pass fills it with -D = -rowsum(dout * o) and
+ * LSE * log2(e), each float32 [B,H,N], which the dK/dV pass that follows
+ * reads.  Calls that share a workspace must be ordered on one stream.
  */
 int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -124,8 +125,9 @@ const char* fa_last_error_detail(void);
  * bracketed by a pair of HIP events recorded on the launch stream.
  * fa_timing_read() waits for the recorded events of one kernel kind, returns
  * the summed elapsed milliseconds and the launch count, and clears them.
- * kernel: 0 forward, 1 backward preprocess (D), 2 backward dK/dV,
- * 3 backward dQ.  Not thread-safe; meant for benchmarks.
+ * kernel: 0 forward, 1 backward dK/dV, 2 backward dQ (which also forms D
+ * and LSE * log2(e) for the dK/dV pass).  Not thread-safe; meant for
+ * benchmarks.
  */
 int fa_timing_enable(int enable);
 int fa_timing_read(int kernel, double* total_ms, int* launches);

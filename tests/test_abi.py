@@ -118,6 +118,7 @@ def test_status_strings_and_timing(lib):
     assert lib.fa_kernel_name(0) == b"fa_fwd_kernel"
     ms, n = ctypes.c_double(), ctypes.c_int()
     assert lib.fa_timing_read(2, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert lib.fa_timing_read(3, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
     assert n.value == 0 and ms.value == 0.0
     assert lib.fa_timing_read(9, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
 
