@@ -60,7 +60,9 @@ def compulsory_bytes(prob, which):
     heads = prob.B * prob.H
     n, d = prob.N, prob.d
     fwd = heads * (4 * n * d * s + 4 * n)
-    bwd = heads * (8 * n * d * s + 12 * n)
+    # backward: read Q, K, V, O, dO, write dQ, dK, dV; LSE read, -D and
+    # LSE*log2(e) written by the dQ pass and read back by the dK/dV pass
+    bwd = heads * (8 * n * d * s + 20 * n)
     return {"fwd": fwd, "bwd": bwd, "fwd+bwd": fwd + bwd}[which]
 
 
