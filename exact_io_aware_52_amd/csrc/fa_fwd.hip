@@ -353,34 +353,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     // Step i works on the tile in ring slot i % 4: on entry its first
     // sub-tile's scores are formed; on exit, those of the next tile.
     int step = 0;
-    if constexpr (NSUB == 2) {
-      // Interior steps of a dense problem: tiles i and i+1 are visible in
-      // full to every wave (below the key length and, if causal, at or below
-      // wave 0's first query) and tile i+3 is whole, so a step needs no
-      // per-tile decision: one wait, one barrier, the DMA, the math.
-      if (!sparse) {
-        int lim = min(min(nkt, N / BT) - 4, kend / BT - 2);
-        if (p.causal) lim = min(lim, (i0 + 1) / BT - 2);
-        const int n_int = max(0, lim + 1);
-        for (; step < n_int; ++step) {
-          wait_vmcnt<LPT>();  // tile i+1 landed; tile i+2 may be in flight
-          __syncthreads();    // slot (i+3)%4 is free
-          const uint32_t nb = ring_lds + ((step + 3) & 3) * L::SLOT_BYTES;
-          kplan.issue(Kg + (size_t)(step + 3) * BT * D, nb);
-          vplan.issue(Vg + (size_t)(step + 3) * BT * D, nb + L::TILE_BYTES);
-          const raw* Kc = ktile(step & 3);
-          const raw* Vc = vtile(step & 3);
-          interior(sa, sb, 0, Vc, 1, Kc);
-          interior(sb, sa, 1, Vc, 0, ktile((step + 1) & 3));
-        }
-        if (n_int > 0) {
-          tl[0] = min(n_int, nkt);
-          tl[1] = min(n_int + 1, nkt);
-          tl[2] = min(n_int + 2, nkt);
-          tl[3] = min(n_int + 3, nkt);
-        }
-      }
-    }
     auto body = [&](f32x16& s0, f32x16& s1) {
       if (tl[1] < nkt) {
         // tile tl[1] must have landed; tl[2] may still be in flight
