@@ -416,6 +416,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
           frag_t<T> pf[2];
           scores(Kc, h, sc);
           const float rs = expo(sc, pf, false);
+          if (h > 0) {
+            // This block also holds the P V products of sub-tile h-1 (after
+            // its settle branch): score reads and products first, then each
+            // P V product beside a share of the exponentials.
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * D / 32, 0);
+#pragma unroll
+            for (int i = 0; i < 2 * D / 32; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * D / 32), 0);
+            }
+          }
           settle(sc, pf, rs, false);
           pv(Vc, h, pf);
         }
