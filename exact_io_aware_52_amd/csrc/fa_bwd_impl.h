@@ -82,9 +82,10 @@ struct DkDvCfg {
   // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
   // accumulators: 192 VGPRs) only fits one wave per SIMD.
   static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
-  // Defer each tile's dV, dK products by one step (needs the registers of
-  // one wave per SIMD).
-  static constexpr bool DEFER = WAVES_PER_SIMD == 1;
+  // Read each group of matrix operands one group ahead of its products
+  // (explicit, fenced with scheduling barriers): with one wave per SIMD no
+  // other wave hides the LDS latency, and the registers are there.
+  static constexpr bool PREFETCH = WAVES_PER_SIMD == 1;
 };
 
 template <typename T, int D>
@@ -196,9 +197,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     const raw* Qs = reinterpret_cast<const raw*>(slot);
     const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
     const float* dns = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES) + 64;
-#pragma unroll
-    for (int qb = 0; qb < BQ / 32; ++qb) {
-      // -D of the accumulator rows (queries qb*32 + 8g + 4hh + u)
+    // -D of the accumulator rows of block qb (queries qb*32 + 8g + 4hh + u)
+    auto dneg_of = [&](int qb) {
       f32x16 dneg;
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
@@ -208,12 +208,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         dneg[4 * g + 2] = d4.z;
         dneg[4 * g + 3] = d4.w;
       }
+      return dneg;
+    };
+    if constexpr (L::PREFETCH) {
+      // groups of GK k-steps of one query block, read one group ahead
+      constexpr int GK = 4, NG = D / 16 / GK;
+      frag_t<T> fq[2][GK], fd[2][GK];
+      auto ld = [&](int g, int b) {
+        const int qb = g / NG, k0 = (g % NG) * GK;
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
-        sacc[qb] = Tr::mma(aq, kf[kc], kc == 0 ? zero16() : sacc[qb]);
-        const frag_t<T> ad = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, kc * 16 + hh * 8);
-        pacc[qb] = Tr::mma(ad, vf[kc], kc == 0 ? dneg : pacc[qb]);  // dP - D
+        for (int j = 0; j < GK; ++j) {
+          fq[b][j] = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, (k0 + j) * 16 + hh * 8);
+          fd[b][j] = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, (k0 + j) * 16 + hh * 8);
+        }
+      };
+      ld(0, 0);
+      f32x16 dneg;
+#pragma unroll
+      for (int g = 0; g < BQ / 32 * NG; ++g) {
+        const int qb = g / NG, k0 = (g % NG) * GK;
+        if (k0 == 0) dneg = dneg_of(qb);
+        if (g + 1 < BQ / 32 * NG) ld(g + 1, (g + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < GK; ++j) {
+          const int kc = k0 + j;
+          sacc[qb] = Tr::mma(fq[g & 1][j], kf[kc], kc == 0 ? zero16() : sacc[qb]);
+          pacc[qb] = Tr::mma(fd[g & 1][j], vf[kc], kc == 0 ? dneg : pacc[qb]);  // dP - D
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb) {
+        const f32x16 dneg = dneg_of(qb);
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
+          sacc[qb] = Tr::mma(aq, kf[kc], kc == 0 ? zero16() : sacc[qb]);
+          const frag_t<T> ad = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, kc * 16 + hh * 8);
+          pacc[qb] = Tr::mma(ad, vf[kc], kc == 0 ? dneg : pacc[qb]);  // dP - D
+        }
       }
     }
   };
@@ -253,15 +288,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   auto grads = [&](const char* slot, const qfrag& pf, const qfrag& sf) {
     const raw* Qs = reinterpret_cast<const raw*>(slot);
     const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    if constexpr (L::PREFETCH) {
+      frag_t<T> ga[2][D / 32], gq[2][D / 32];
+      auto ld = [&](int qc, int b) {
 #pragma unroll
-    for (int qc = 0; qc < BQ / 16; ++qc)
+        for (int db = 0; db < D / 32; ++db) {
+          ga[b][db] = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
+          gq[b][db] = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
+        }
+      };
+      ld(0, 0);
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const frag_t<T> ado = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
-        dv_acc[db] = Tr::mma(ado, pf[qc], dv_acc[db]);
-        const frag_t<T> aq = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
-        dk_acc[db] = Tr::mma(aq, sf[qc], dk_acc[db]);
+      for (int qc = 0; qc < BQ / 16; ++qc) {
+        if (qc + 1 < BQ / 16) ld(qc + 1, (qc + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          dv_acc[db] = Tr::mma(ga[qc & 1][db], pf[qc], dv_acc[db]);
+          dk_acc[db] = Tr::mma(gq[qc & 1][db], sf[qc], dk_acc[db]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
       }
+    } else {
+#pragma unroll
+      for (int qc = 0; qc < BQ / 16; ++qc)
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) {
+          const frag_t<T> ado = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
+          dv_acc[db] = Tr::mma(ado, pf[qc], dv_acc[db]);
+          const frag_t<T> aq = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
+          dk_acc[db] = Tr::mma(aq, sf[qc], dk_acc[db]);
+        }
+    }
   };
   auto slot_of = [&](int s) { return ring + (s & 3) * L::SLOT_BYTES; };
   // Query tile t reaches this wave's keys (under a causal mask the first
@@ -273,9 +331,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   };
 
   // Kept query tiles in order; tl[k] is the tile of step i + k.  Step i
-  // forms S and dP of tile i, then runs the dV, dK products of tile i-1
-  // (deferred by one step, still in ring slot i-1) alongside the softmax of
-  // tile i, so the matrix core has work while the exponentials run.
+  // forms S and dP of tile i, its softmax, then the dV, dK products.
   int tl[3];
   tl[0] = t_begin < t_end ? next_kept(t_begin) : t_end;
   tl[1] = tl[0] < t_end ? next_kept(tl[0] + 1) : t_end;
@@ -290,20 +346,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       lo = p.causal ? (j0 + BK - 1 + BQ - 1) / BQ : t_begin;
       hi = min(N / BQ - 3, t_end - 3);
     }
-    qfrag pf, sf;  // deferred P, dS of the previous tile (zero: nothing yet)
-#pragma unroll
-    for (int qc = 0; qc < BQ / 16; ++qc) {
-      pf[qc] = zero_frag<T>();
-      sf[qc] = zero_frag<T>();
-    }
-    int prev = -1;  // step of the deferred tile
     int step = 0;
     while (true) {
       const int t = tl[0];
-      // With nothing deferred the zero fragments are multiplied with the
-      // current (finite) slot, adding nothing.
-      const char* pslot = slot_of(prev >= 0 ? prev : step);
-      (void)pslot;
       if (t >= lo && t <= hi) {
         wait_tiles(1);    // tile t landed; t+1 may be in flight
         __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
@@ -315,17 +360,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
           dma4s((uint32_t)(qn + lane) * 4u, w == 0 ? (const void*)lse2g : (const void*)dvecg,
                 base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
         qblk sacc, pacc;
+        qfrag pf, sf;
         sdp(slot_of(step), sacc, pacc);
-        if constexpr (L::DEFER) {
-          grads(pslot, pf, sf);
-          soft(slot_of(step), t * BQ, false, sacc, pacc);
-          to_frags(sacc, pacc, pf, sf);
-          prev = step;
-        } else {
-          soft(slot_of(step), t * BQ, false, sacc, pacc);
-          to_frags(sacc, pacc, pf, sf);
-          grads(slot_of(step), pf, sf);
-        }
+        soft(slot_of(step), t * BQ, false, sacc, pacc);
+        to_frags(sacc, pacc, pf, sf);
+        grads(slot_of(step), pf, sf);
         tl[0] = t + 1;
         tl[1] = t + 2;
         tl[2] = min(t + 3, t_end);
@@ -335,17 +374,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
         if (active(t)) {
           qblk sacc, pacc;
+          qfrag pf, sf;
           sdp(slot_of(step), sacc, pacc);
-          if constexpr (L::DEFER) {
-            grads(pslot, pf, sf);
-            soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
-            to_frags(sacc, pacc, pf, sf);
-            prev = step;
-          } else {
-            soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
-            to_frags(sacc, pacc, pf, sf);
-            grads(slot_of(step), pf, sf);
-          }
+          soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
+          to_frags(sacc, pacc, pf, sf);
+          grads(slot_of(step), pf, sf);
         }
         tl[0] = tl[1];
         tl[1] = tl[2];
@@ -354,7 +387,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       ++step;
       if (tl[0] >= t_end) break;
     }
-    if (prev >= 0) grads(slot_of(prev), pf, sf);  // the last tile
   }
 
   // Store dK = scale * (dK^T)^T and dV; lane owns key `myk`, rows d of its half.
