@@ -18,20 +18,21 @@
 // 32 apart, and the exponentiated tile is already the B operand of
 // O^T += V^T P^T.
 //
-// Staging: K and V tiles (64 keys at d = 64 for 16-bit types, else 32) go
-// from HBM straight into a 4-slot LDS ring by direct-to-LDS loads (no staging
-// registers, no vector instructions); a tile is requested two steps before
-// its keys are first used.  K is read as row-major matrix operands; V^T, the
-// A operand of O^T += V^T P^T, is read from the row-major V tile with the
-// transposing LDS read.  One barrier per ring tile.
+// Staging: K and V tiles (64 keys for 16-bit types, 32 for fp32) go
+// from HBM straight into an LDS ring of NS slots by direct-to-LDS loads (no
+// staging registers, no vector instructions); a tile is requested NS - 1
+// steps before its keys are used.  K is read as row-major matrix operands;
+// V^T, the A operand of O^T += V^T P^T, is read from the row-major V tile
+// with the transposing LDS read.  One barrier per ring tile.
 //
-// Software pipeline (all instances but 16-bit d = 128, whose second score
-// buffer would not fit 256 VGPRs): K runs one sub-tile ahead of V.  A wave
-// issues the products of the next sub-tile's scores while it exponentiates
-// the current one and accumulates its P V, so it always has independent
-// matrix-core and vector work in flight.  Dense interior tiles (visible in
-// full to every wave, whole tiles ahead) run in a loop with no per-tile
-// decisions.
+// 16-bit instances keep several waves per SIMD resident (3 at d = 64, 2 at
+// d = 128), which interleave matrix and vector work across waves; within a
+// wave, the block of a tile's second sub-tile is ordered so that the first
+// sub-tile's P V products run beside the second one's exponentials.  The
+// fp32 instances (one wave per SIMD) use a software pipeline instead: K runs
+// one sub-tile ahead of V, the next sub-tile's score products issuing while
+// the current one is exponentiated.  Dense interior tiles (visible in full
+// to every wave, whole tiles ahead) run a loop with no per-tile decisions.
 //
 // Online softmax with a lazy reference: each probability is
 // exp2(fma(s, c, -ra)), s the fp32 score, c = scale * log2(e) and ra the
@@ -80,7 +81,7 @@ struct FwdCfg {
   static constexpr bool B16 = sizeof(raw) == 2;
   // BT keys per ring slot (one DMA tile, one barrier); the math runs on
   // 32-key sub-tiles, NSUB per slot.
-  static constexpr int BT = (B16 && D == 64) ? 64 : 32;
+  static constexpr int BT = B16 ? 64 : 32;
   static constexpr int NSUB = BT / 32;
   // Software pipelining across sub-tiles (a second score buffer); the 16-bit
   // instances instead keep more waves resident, which interleave matrix and
@@ -88,10 +89,11 @@ struct FwdCfg {
   static constexpr bool PIPE = !B16;
   // Resident waves per SIMD (VGPR budget 512 / WAVES_PER_SIMD) and LDS ring
   // slots: at d = 64, 3 waves (<= 168 VGPRs) and a 3-slot ring (49 KB, three
-  // work-groups per CU); at d = 128 the VGPRs allow 2.  The fp32 instances
-  // (accuracy, not speed) take the whole register file.
+  // work-groups per CU); at d = 128 the VGPRs allow 2 waves, and a 2-slot
+  // ring of 64-key tiles (64 KB) fits two work-groups per CU.  The fp32
+  // instances (accuracy, not speed) take the whole register file.
   static constexpr int WAVES_PER_SIMD = B16 ? (D == 64 ? 3 : 2) : 1;
-  static constexpr int NS = B16 ? (D == 64 ? 3 : 4) : 4;
+  static constexpr int NS = B16 ? (D == 64 ? 3 : 2) : 4;
   static constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);  // one K or V tile
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
   static constexpr int LPT = 2 * TILE_BYTES / 4096;             // DMA instructions per wave per tile
