@@ -78,6 +78,8 @@ KERNEL_NAMES = {}
 def make_workload(args):
     if args.config == "long_causal":
         return inputs.workload("long_causal", args.n, args.d)
+    if args.config == "block_sparse_long":
+        return inputs.workload("block_sparse_long", args.n)
     return inputs.workload(args.config)
 
 
@@ -120,7 +122,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gpt2_small",
                     choices=["tiny", "gpt2_small", "bert_large_padded", "long_causal",
-                             "block_sparse"])
+                             "block_sparse", "block_sparse_long"])
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--d", type=int, default=64)
     ap.add_argument("--cpu-budget", type=float, default=12.0,

@@ -64,7 +64,8 @@ class Problem:
 
 
 def make_problem(B, H, N, d, dtype, seed, causal=False, scale=None,
-                 key_len_range=None, block_keep_p=None, block_size=128, name=""):
+                 key_len_range=None, block_keep_p=None, block_size=128, name="",
+                 block_band=None, block_global=0):
     if dtype not in DTYPES:
         raise ValueError(f"unknown dtype {dtype!r}")
     rng = np.random.default_rng(seed)
@@ -78,11 +79,22 @@ def make_problem(B, H, N, d, dtype, seed, causal=False, scale=None,
         lo, hi = key_len_range
         key_lens = np.random.default_rng(seed + 1_000_003).integers(
             lo, hi + 1, B).astype(np.int32)
+    # Block mask: i.i.d. blocks kept with probability block_keep_p, the diagonal
+    # always; optionally a band of block_band blocks on each side of the
+    # diagonal and block_global "global" blocks (the first block rows and
+    # columns kept in full).
     block_mask = None
-    if block_keep_p is not None:
+    if block_keep_p is not None or block_band is not None:
         nb = -(-N // block_size)
-        bm = np.random.default_rng(seed + 2_000_003).random((nb, nb)) < block_keep_p
+        p = 0.0 if block_keep_p is None else block_keep_p
+        bm = np.random.default_rng(seed + 2_000_003).random((nb, nb)) < p
         np.fill_diagonal(bm, True)
+        if block_band:
+            ib, jb = np.indices((nb, nb))
+            bm |= np.abs(ib - jb) <= block_band
+        if block_global:
+            bm[:block_global, :] = True
+            bm[:, :block_global] = True
         block_mask = bm.astype(np.uint8)
     return Problem(B, H, N, d, dtype, bool(causal), np.float32(scale), q, k, v, do,
                    key_lens, block_mask, block_size, seed, name)
@@ -91,6 +103,10 @@ def make_problem(B, H, N, d, dtype, seed, causal=False, scale=None,
 # The five workloads.  Shapes follow GPT-2-small, BERT-large, long-context
 # (Long Range Arena / Path-X lengths) and long-context block-sparse attention.
 LONG_POINTS = [(n, d) for n in (2048, 4096, 8192, 16384) for d in (64, 128)]
+# Longer-context block-sparse attention with a structured pattern: a local
+# band (one block on each side of the diagonal), one global block row and
+# column, and i.i.d. blocks with probability 1/32.
+SPARSE_LONG_N = (32768, 65536)
 
 
 def config(name, n=None, d=None):
@@ -111,6 +127,11 @@ def config(name, n=None, d=None):
     if name == "block_sparse":
         return dict(B=1, H=8, N=16384, d=64, dtype="bf16", seed=5, causal=False,
                     scale=1 / 8, block_keep_p=1 / 8, block_size=128, name=name)
+    if name == "block_sparse_long":
+        idx = SPARSE_LONG_N.index(n)
+        return dict(B=1, H=8, N=n, d=64, dtype="bf16", seed=6 + 10 * idx, causal=False,
+                    scale=1 / 8, block_keep_p=1 / 32, block_band=1, block_global=1,
+                    block_size=128, name=f"block_sparse_long_N{n}")
     raise KeyError(name)
 
 

@@ -2,7 +2,7 @@
 product path never imports it (see attention.py's header)."""
 
 from .attention import (visibility, head_forward, head_backward, head_probabilities,
-                        forward, backward)
+                        head_rows, forward, backward)
 
 __all__ = ["visibility", "head_forward", "head_backward", "head_probabilities",
-           "forward", "backward"]
+           "head_rows", "forward", "backward"]

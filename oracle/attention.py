@@ -43,15 +43,16 @@ upcast; ``scale`` is the float32 value handed to the GPU, upcast.
 import numpy as np
 
 
-def visibility(n, causal=False, key_len=None, block_mask=None, block_size=128):
+def visibility(n, causal=False, key_len=None, block_mask=None, block_size=128, rows=None):
     """Boolean [n, n] matrix: entry (i, j) is True iff query i may attend key j.
 
     Combines the three masks of the method (causal, key padding, block mask)
-    by logical AND, as read above.
+    by logical AND, as read above.  With ``rows`` (query indices), only those
+    rows: [len(rows), n].
     """
-    i = np.arange(n)[:, None]
+    i = (np.arange(n) if rows is None else np.asarray(rows))[:, None]
     j = np.arange(n)[None, :]
-    vis = np.ones((n, n), dtype=bool)
+    vis = np.ones((i.shape[0], n), dtype=bool)
     if causal:
         vis &= j <= i
     if key_len is not None:
@@ -138,6 +139,24 @@ def head_backward(q, k, v, do, scale, causal=False, key_len=None, block_mask=Non
         dq[r0:r1] = scale * (ds @ k)            # dQ = scale * dS K
         dk += scale * (ds.T @ q[r0:r1])         # dK = scale * dS^T Q
     return dq, dk, dv
+
+
+def head_rows(q, k, v, do, scale, rows, causal=False, key_len=None, block_mask=None,
+              block_size=128):
+    """O, LSE and dQ of the given query rows of one head, from the same
+    definitions (each row's softmax over all its visible keys; D, dP, dS and
+    dQ = scale * dS K row by row).  Costs O(N d) per row, for checking
+    sampled rows of problems too large for a whole head.
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    rows = np.asarray(rows)
+    scale = float(scale)
+    vis = visibility(q.shape[0], causal, key_len, block_mask, block_size, rows=rows)
+    o_r, lse_r, p_r = _head_forward(q[rows], k, v, scale, vis)
+    d_r = np.sum(do[rows] * o_r, axis=1)        # D = rowsum(dO * O)
+    dp_r = do[rows] @ v.T                       # dP = dO V^T
+    ds_r = p_r * (dp_r - d_r[:, None])          # dS = P * (dP - D)
+    return o_r, lse_r, scale * (ds_r @ k)       # dQ = scale * dS K
 
 
 def _heads(x):

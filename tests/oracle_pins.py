@@ -264,5 +264,25 @@ def check_row_chunking(orc, n=37, d=6):
             np.testing.assert_allclose(b, a, atol=1e-13)
 
 
+def check_rows(orc, n=41, d=6):
+    # O, LSE, dQ of sampled rows equal the same rows of the whole-head oracle
+    # (itself pinned above), for every mask kind, unsorted and repeated rows,
+    # and rows that see no key.
+    q, k, v, do = (_rand((n, d), 700 + t) for t in range(4))
+    bm = np.array([[1, 0, 1], [0, 1, 0], [1, 1, 1]], np.uint8)
+    rows = np.array([40, 0, 7, 7, 23, 16, 31])
+    for kw in (dict(), dict(causal=True), dict(key_len=9), dict(key_len=0),
+               dict(block_mask=bm, block_size=16), dict(causal=True, key_len=30, block_mask=bm,
+                                                        block_size=16)):
+        o, lse = orc.head_forward(q, k, v, 0.45, **kw)
+        dq, _, _ = orc.head_backward(q, k, v, do, 0.45, **kw)
+        ro, rl, rdq = orc.head_rows(q, k, v, do, 0.45, rows, **kw)
+        np.testing.assert_allclose(ro, o[rows], atol=1e-14)
+        np.testing.assert_array_equal(np.isneginf(rl), np.isneginf(lse[rows]))
+        fin = ~np.isneginf(rl)
+        np.testing.assert_allclose(rl[fin], lse[rows][fin], atol=1e-14)
+        np.testing.assert_allclose(rdq, dq[rows], atol=1e-13)
+
+
 ALL_PINS = [check_golden, check_finite_differences, check_torch_reference,
-            check_invariants, check_special_cases, check_row_chunking]
+            check_invariants, check_special_cases, check_row_chunking, check_rows]

@@ -221,3 +221,43 @@ def test_config_block_sparse():
     heads = [(0, 3)]
     compare(run_gpu(prob), run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads,
             "block_sparse")
+
+
+@pytest.mark.parametrize("n", inputs.SPARSE_LONG_N)
+def test_config_block_sparse_long(n):
+    # Structured block mask (band, global row and column, i.i.d. 1/32) at 32K
+    # and 64K keys.  At 32K one whole head is compared.  At both sizes: O,
+    # LSE and dQ on sampled rows of two heads (the oracle's row function), and
+    # on every head the two identities the closed-form gradient satisfies,
+    # sum_j dV_j = sum_i dO_i and sum_j dK_j = 0, within the spread that
+    # rounding the stored values (and P, O) to bf16 leaves in such sums.
+    prob = inputs.workload("block_sparse_long", n)
+    gpu = run_gpu(prob)
+    if n <= 32768:
+        heads = [(0, 5)]
+        compare(gpu, run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads,
+                f"block_sparse_long N={n}")
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, n // 2, n // 2 + 1, n - 129, n - 128,
+                                      n - 1], rng.integers(0, n, 22)]))
+    for b, h in [(0, 2), (0, 7)]:
+        o, lse, dq = oracle.head_rows(*(x[b, h].astype(np.float64) for x in (prob.q, prob.k, prob.v, prob.do)),
+                                      float(prob.scale), rows, block_mask=prob.block_mask,
+                                      block_size=prob.block_size)
+        ref = {"o": o, "lse": lse, "dq": dq}
+        got = {k: gpu[k][b, h][rows] for k in ref}
+        compare(got, ref, TOL["bf16"], label=f"block_sparse_long N={n} rows of head ({b},{h})")
+    u = 2.0 ** -8      # bf16 unit roundoff
+    for b in range(prob.B):
+        for h in range(prob.H):
+            dv, dk, do = gpu["dv"][b, h], gpu["dk"][b, h], prob.do[b, h].astype(np.float64)
+            q, o = prob.q[b, h].astype(np.float64), gpu["o"][b, h]
+            dev_v = np.abs(dv.sum(axis=0) - do.sum(axis=0))
+            bound_v = 6 * u * (np.sqrt((dv ** 2).sum(axis=0)) + np.sqrt((do ** 2).sum(axis=0)))
+            assert np.all(dev_v <= bound_v), (b, h, "sum dV", dev_v.max(), bound_v.min())
+            # sum_j dS_ij = D_i(exact O) - D_i(bf16 O): spread |dO_i| |O_i| u per row
+            spread = float(prob.scale) * np.sqrt(((np.abs(q) * (np.abs(do) * np.abs(o)).sum(axis=1, keepdims=True) * u) ** 2).sum(axis=0))
+            dev_k = np.abs(dk.sum(axis=0))
+            bound_k = 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0)))
+            assert np.all(dev_k <= bound_k), (b, h, "sum dK", dev_k.max(), bound_k.min())
+    log(f"[parity] block_sparse_long N={n}: dK, dV sums within bounds on all heads")

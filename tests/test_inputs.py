@@ -50,6 +50,19 @@ def test_block_mask_recipe():
     assert 0.11 < density < 0.16          # expected (128 + 127*16) / 128^2 = 13.2 %
 
 
+def test_structured_block_mask_recipe():
+    # band of one block each side, first block row and column, i.i.d. 1/32
+    p = inputs.make_problem(1, 1, 128 * 64, 1, "bf16", seed=6, block_keep_p=1 / 32,
+                            block_band=1, block_global=1)
+    bm = p.block_mask.astype(bool)
+    ib, jb = np.indices(bm.shape)
+    assert bm[np.abs(ib - jb) <= 1].all() and bm[0].all() and bm[:, 0].all()
+    rest = ~((np.abs(ib - jb) <= 1) | (ib == 0) | (jb == 0))
+    assert 0.015 < bm[rest].mean() < 0.05            # i.i.d. part at p = 1/32
+    cfg = inputs.config("block_sparse_long", 65536)
+    assert cfg["N"] == 65536 and cfg["block_band"] == 1 and cfg["block_global"] == 1
+
+
 @pytest.mark.parametrize("kw", [
     dict(causal=False), dict(causal=True), dict(key_len=37), dict(causal=True, key_len=50),
     dict(block="rand"), dict(causal=True, block="rand", key_len=70),

@@ -33,6 +33,10 @@ MUTATIONS = {
     "lse_without_max": ("m + np.log(l_safe)", "np.log(l_safe)"),
     "D_from_dO_only": ("d_row = (do[r0:r1] * o).sum(axis=1)", "d_row = do[r0:r1].sum(axis=1)"),
     "softmax_over_queries": ("p = ex / l_safe[:, None]", "p = ex / ex.sum(axis=0)[None, :]"),
+    "rows_drop_D_term": ("ds_r = p_r * (dp_r - d_r[:, None])", "ds_r = p_r * dp_r"),
+    "rows_dQ_wrong_operand": ("scale * (ds_r @ k)", "scale * (ds_r @ q)"),
+    "rows_mask_ignores_rows": ("i = (np.arange(n) if rows is None else np.asarray(rows))[:, None]",
+                               "i = np.arange(n)[:len(rows) if rows is not None else n, None]"),
 }
 
 
