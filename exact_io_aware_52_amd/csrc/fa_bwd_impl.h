@@ -83,9 +83,12 @@ struct DkDvCfg {
   // accumulators: 192 VGPRs) only fits one wave per SIMD.
   static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
   // Read each group of matrix operands one group ahead of its products
-  // (explicit, fenced with scheduling barriers): with one wave per SIMD no
-  // other wave hides the LDS latency, and the registers are there.
-  static constexpr bool PREFETCH = WAVES_PER_SIMD == 1;
+  // (explicit, fenced with scheduling barriers): the compiler otherwise reads
+  // each operand just before its product.  Groups of GK k-steps: 4 at
+  // d = 128 (one wave per SIMD, registers to spare), 2 at d = 64 (two waves
+  // per SIMD, 256 VGPRs).
+  static constexpr bool PREFETCH = true;
+  static constexpr int GK = D == 64 ? 2 : 4;
 };
 
 template <typename T, int D>
@@ -212,7 +215,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     };
     if constexpr (L::PREFETCH) {
       // groups of GK k-steps of one query block, read one group ahead
-      constexpr int GK = 4, NG = D / 16 / GK;
+      constexpr int GK = L::GK, NG = D / 16 / GK;
       frag_t<T> fq[2][GK], fd[2][GK];
       auto ld = [&](int g, int b) {
         const int qb = g / NG, k0 = (g % NG) * GK;
