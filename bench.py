@@ -28,7 +28,8 @@ sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
                                    fa_forward, fa_forward_blocksparse, fa_kernel_name,
-                                   fa_timing_enable, fa_timing_read, inputs)
+                                   fa_set_forward_block_rows, fa_timing_enable, fa_timing_read,
+                                   inputs)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
@@ -125,6 +126,8 @@ def main():
                              "block_sparse", "block_sparse_long"])
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--d", type=int, default=64)
+    ap.add_argument("--fwd-block-rows", type=int, default=128, choices=[64, 128, 256],
+                    help="query rows per forward work-group (tile height)")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of host work for the oracle baseline (0 disables)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -154,6 +157,7 @@ def main():
     for k in ("fwd", "bwd_dkdv", "bwd_dq"):
         KERNEL_NAMES[k] = fa_kernel_name(k)
 
+    fa_set_forward_block_rows(args.fwd_block_rows)
     prob = make_workload(args)
     dt = TORCH_DT[prob.dtype]
     q, k, v, do = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v, prob.do))
@@ -239,7 +243,8 @@ def main():
         "config": {"workload": prob.name, "B": prob.B, "H": prob.H, "N": prob.N, "d": prob.d,
                    "causal": prob.causal,
                    "key_padding": prob.key_lens is not None,
-                   "block_sparse": prob.block_mask is not None, "parallelism": "none"},
+                   "block_sparse": prob.block_mask is not None,
+                   "fwd_block_rows": args.fwd_block_rows, "parallelism": "none"},
         "fwd_ms": round(ms_fwd, 4),
         "fwd_tflops": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12, 2),
         "frac_of_peak_fwd_bwd": round(value / PEAK_TFLOPS[prob.dtype], 4),

@@ -53,8 +53,11 @@ def load_library():
     lib.fa_timing_read.argtypes = [I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
     lib.fa_kernel_name.argtypes = [I]
     lib.fa_kernel_name.restype = ctypes.c_char_p
+    lib.fa_set_forward_block_rows.argtypes = [I]
+    lib.fa_get_forward_block_rows.argtypes = []
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_backward,
-               lib.fa_timing_enable, lib.fa_timing_read):
+               lib.fa_timing_enable, lib.fa_timing_read, lib.fa_set_forward_block_rows,
+               lib.fa_get_forward_block_rows):
         fn.restype = I
     _LIB = lib
     return lib
@@ -190,6 +193,15 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
                          workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("fa_backward", st)
     return dq, dk, dv
+
+
+def fa_set_forward_block_rows(rows):
+    """Query rows per forward work-group: 64, 128 (default) or 256."""
+    _check("fa_set_forward_block_rows", load_library().fa_set_forward_block_rows(int(rows)))
+
+
+def fa_get_forward_block_rows():
+    return int(load_library().fa_get_forward_block_rows())
 
 
 def fa_timing_enable(enable=True):

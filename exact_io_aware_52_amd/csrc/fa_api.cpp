@@ -37,6 +37,7 @@ struct KindTimes {
   size_t used = 0;              // pairs recorded since the last read
 };
 bool g_timing = false;
+int g_fwd_rows = 128;  // fa_set_forward_block_rows
 KindTimes g_times[fa::kNumKernelKinds];
 
 }  // namespace
@@ -77,10 +78,11 @@ int check_common(int B, int H, int N, int d, float scale, fa_dtype dtype, bool* 
   if (!std::isfinite(scale)) return fail(FA_ERR_INVALID_ARG, "scale is not finite");
   if (scale < 0.f) return fail(FA_ERR_UNSUPPORTED, "negative scale %g", (double)scale);
   if (*empty) return FA_OK;
-  // One work-group per 128 query rows (forward) or 128 keys (backward) per head.
-  const long long tiles = ((long long)N + 127) / 128;
+  // One work-group per 64, 128 or 256 query rows (forward) or 128 keys
+  // (backward) per head; the bound is taken for the smallest tile.
+  const long long tiles = ((long long)N + 63) / 64;
   if ((long long)B * H * tiles > 0x7fffffffLL)
-    return fail(FA_ERR_INVALID_ARG, "problem too large: B*H*ceil(N/128) exceeds 2^31-1");
+    return fail(FA_ERR_INVALID_ARG, "problem too large: B*H*ceil(N/64) exceeds 2^31-1");
   if ((long long)N * d > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "N*d exceeds 2^31-1");
   return FA_OK;
 }
@@ -116,13 +118,17 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   int st = check_common(B, H, N, d, scale, dtype, &empty);
   if (st != FA_OK) return st;
   if ((st = check_block(block_mask, block_size, N, sparse)) != FA_OK) return st;
+  const int rows = g_fwd_rows;
+  if (block_mask && rows > 128)
+    return fail(FA_ERR_UNSUPPORTED, "block-sparse forward with %d query rows per tile (at most 128)",
+                rows);
   if (empty) return FA_OK;
   if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
       (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||
       (st = check_tensor(lse, "lse", 4)))
     return st;
   if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
-  fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
+  fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream, rows};
   fa::FwdTensors t{q, k, v, o, lse};
   hipError_t e = fa::launch_forward(p, t);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
@@ -149,6 +155,15 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
                       block_size, true, dtype, stream);
 }
+
+int fa_set_forward_block_rows(int rows) {
+  if (rows != 64 && rows != 128 && rows != 256)
+    return fail(FA_ERR_UNSUPPORTED, "forward block rows %d (supported: 64, 128, 256)", rows);
+  g_fwd_rows = rows;
+  return FA_OK;
+}
+
+int fa_get_forward_block_rows(void) { return g_fwd_rows; }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;

@@ -1,8 +1,9 @@
 // Tiled exact attention, forward pass, for gfx950.
 //
 // FlashAttention forward (review page "Method"; slides steps 01-04; visual
-// guide, "online softmax"): each work-group owns one tile of 128 query rows
-// of one (b, h) head and streams the key/value tiles that tile needs through
+// guide, "online softmax"): each work-group owns one tile of 32 NW query
+// rows of one (b, h) head (NW = 4 waves, 128 rows, by default; 64 and 256
+// rows on request) and streams the key/value tiles that tile needs through
 // LDS.  Scores never leave the compute unit; only O and the per-row
 // logsumexp are written.  The pages' pseudocode runs key/value blocks in the
 // outer loop and carries per-query-block state through memory; here the
@@ -10,7 +11,7 @@
 // denominator l, fp32 accumulator) stays in registers for the whole sweep.
 // Both orders give the same result in exact arithmetic.
 //
-// Work split: 4 waves, wave w owns queries i0 + 32w .. i0 + 32w + 31.  For
+// Work split: NW waves, wave w owns queries i0 + 32w .. i0 + 32w + 31.  For
 // each sub-tile of 32 keys a wave forms the transposed score tile S^T (keys x
 // queries): A = K rows from LDS, B = the wave's Q rows, held in registers for
 // the whole kernel.  With keys as accumulator rows each lane owns one query
@@ -55,8 +56,6 @@
 namespace fa {
 namespace {
 
-constexpr int kFwdWaves = 4;
-constexpr int kFwdBR = 32 * kFwdWaves;  // query rows per work-group
 constexpr int kMaskBlock = 128;         // block-mask granularity (keys and queries)
 
 struct FwdParams {
@@ -75,9 +74,11 @@ struct FwdParams {
 
 constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 131072)
 
-template <typename T, int D>
+// NW waves per work-group, 32 query rows each (BR = 32 NW rows per tile).
+template <typename T, int D, int NW>
 struct FwdCfg {
   typedef raw_t<T> raw;
+  static constexpr int BR = 32 * NW;
   static constexpr bool B16 = sizeof(raw) == 2;
   // BT keys per ring slot (one DMA tile, one barrier); the math runs on
   // 32-key sub-tiles, NSUB per slot.
@@ -90,13 +91,17 @@ struct FwdCfg {
   // Resident waves per SIMD (VGPR budget 512 / WAVES_PER_SIMD) and LDS ring
   // slots: at d = 64, 3 waves (<= 168 VGPRs) and a 3-slot ring (49 KB, three
   // work-groups per CU); at d = 128 the VGPRs allow 2 waves, and a 2-slot
-  // ring of 64-key tiles (64 KB) fits two work-groups per CU.  The fp32
-  // instances (accuracy, not speed) take the whole register file.
+  // ring of 64-key tiles (64 KB) fits two work-groups per CU.  The ring does
+  // not depend on NW, so LDS caps the work-groups per CU whatever their
+  // height: 64-row tiles (NW = 2) hold half the default's waves per CU (6 at
+  // d = 64, 4 at d = 128), and 256-row tiles (NW = 8) one work-group, 8
+  // waves, since two of them would need more VGPRs than a SIMD holds.  The
+  // fp32 instances (accuracy, not speed) take the whole register file.
   static constexpr int WAVES_PER_SIMD = B16 ? (D == 64 ? 3 : 2) : 1;
   static constexpr int NS = B16 ? (D == 64 ? 3 : 2) : 4;
   static constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);  // one K or V tile
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
-  static constexpr int LPT = 2 * TILE_BYTES / 4096;             // DMA instructions per wave per tile
+  static constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);      // DMA instructions per wave per tile
   static_assert(!PIPE || NS == 4, "the pipelined loop uses a 4-slot ring");
 };
 
@@ -128,13 +133,14 @@ __device__ __forceinline__ float frag_sum(const frag_t<float>& f, float acc) {
   return acc;
 }
 
-template <typename T, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    FwdCfg<T, D>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
+    FwdCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef FwdCfg<T, D> L;
+  typedef FwdCfg<T, D, NW> L;
+  constexpr int BR = L::BR;
   constexpr int BT = L::BT;
   constexpr int NSUB = L::NSUB;
 
@@ -159,19 +165,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, qt, bh);
   const int b = bh / p.H;
   const int N = p.N;
-  const int i0 = qt * kFwdBR;
+  const int i0 = qt * BR;
   const int qw0 = i0 + 32 * w;  // first query of this wave
   const int myq = qw0 + col;
 
   int kend = N;
   if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
   int kv_end = kend;
-  if (p.causal) kv_end = min(kv_end, i0 + kFwdBR);
+  if (p.causal) kv_end = min(kv_end, i0 + BR);
   const int nkt = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
-    for (int i = tid; i < p.nblk; i += 256) mask_row[i] = bm[i];
+    for (int i = tid; i < p.nblk; i += 64 * NW) mask_row[i] = bm[i];
   }
   auto next_kept = [&](int j) {
     if (!sparse) return j;
@@ -194,8 +200,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
   // K and V of tile t into ring slot s (LPT DMA instructions per wave).  Only
   // the ragged last tile computes clamped per-lane addresses.
-  DmaPlan<raw, BT, D, kRows> kplan;
-  DmaPlan<raw, BT, D, VSWZ> vplan;
+  DmaPlan<raw, BT, D, kRows, NW> kplan;
+  DmaPlan<raw, BT, D, VSWZ, NW> vplan;
   kplan.init(w, lane);
   vplan.init(w, lane);
   auto issue = [&](int t, int s) {
@@ -492,8 +498,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, int NW>
 hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
+  constexpr int BR = FwdCfg<T, D, NW>::BR;
   FwdParams p;
   p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.lse = t.lse;
   p.key_lens = pb.key_lens;
@@ -501,29 +508,39 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.H = pb.H;
   p.N = pb.N;
   p.BH = pb.B * pb.H;
-  p.nq = (pb.N + kFwdBR - 1) / kFwdBR;
+  p.nq = (pb.N + BR - 1) / BR;
   p.nblk = (pb.N + kMaskBlock - 1) / kMaskBlock;
   p.scale = pb.scale;
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
   timing_begin(kFwd, pb.stream);
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D>), dim3(grid), dim3(256), 0, pb.stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid), dim3(64 * NW), 0, pb.stream, p);
   hipError_t e = hipGetLastError();
   timing_end(kFwd, pb.stream);
   return e;
+}
+
+// Query rows per tile (work-group): 128 by default; 64 and 256 on request.
+template <typename T, int D>
+hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
+  switch (pb.fwd_rows) {
+    case 64: return launch_fwd_t<T, D, 2>(pb, t);
+    case 256: return launch_fwd_t<T, D, 8>(pb, t);
+    default: return launch_fwd_t<T, D, 4>(pb, t);
+  }
 }
 
 }  // namespace
 
 hipError_t launch_forward(const Problem& p, const FwdTensors& t) {
   switch (p.dtype * 1000 + p.d) {
-    case 0 * 1000 + 64: return launch_fwd_t<float, 64>(p, t);
-    case 0 * 1000 + 128: return launch_fwd_t<float, 128>(p, t);
-    case 1 * 1000 + 64: return launch_fwd_t<_Float16, 64>(p, t);
-    case 1 * 1000 + 128: return launch_fwd_t<_Float16, 128>(p, t);
-    case 2 * 1000 + 64: return launch_fwd_t<__bf16, 64>(p, t);
-    case 2 * 1000 + 128: return launch_fwd_t<__bf16, 128>(p, t);
+    case 0 * 1000 + 64: return launch_fwd_rows<float, 64>(p, t);
+    case 0 * 1000 + 128: return launch_fwd_rows<float, 128>(p, t);
+    case 1 * 1000 + 64: return launch_fwd_rows<_Float16, 64>(p, t);
+    case 1 * 1000 + 128: return launch_fwd_rows<_Float16, 128>(p, t);
+    case 2 * 1000 + 64: return launch_fwd_rows<__bf16, 64>(p, t);
+    case 2 * 1000 + 128: return launch_fwd_rows<__bf16, 128>(p, t);
   }
   return hipErrorInvalidValue;
 }

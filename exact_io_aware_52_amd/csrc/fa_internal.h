@@ -18,6 +18,7 @@ struct Problem {
   const uint8_t* block_mask;  // device, may be null
   int dtype;                  // fa_dtype
   hipStream_t stream;
+  int fwd_rows = 128;         // forward: query rows per work-group (64, 128, 256)
 };
 
 struct FwdTensors {

@@ -111,6 +111,21 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 fa_dtype dtype, void* workspace, size_t workspace_bytes,
                 hipStream_t stream);
 
+/*
+ * Query rows per forward work-group, the tile height B_r of the tiled IO
+ * analysis (review page, claims C2 and C3: tiling reduces HBM reads and
+ * writes, with an IO cost that depends on the on-chip memory size; K and V
+ * are read once per query tile, so that traffic falls as B_r grows): 64,
+ * 128 (default) or 256.  A
+ * tuning and measurement setting; results agree to rounding for every value.
+ * The block-sparse forward supports 64 and 128 (a 128-token mask block
+ * holds a whole tile) and returns FA_ERR_UNSUPPORTED for 256.  Process-wide,
+ * read at each forward call, not synchronised between threads.  Returns
+ * FA_OK, or FA_ERR_UNSUPPORTED for any other value (the setting is kept).
+ */
+int fa_set_forward_block_rows(int rows);
+int fa_get_forward_block_rows(void);
+
 /* Workspace bytes fa_backward needs for these sizes (0 for an empty problem). */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 

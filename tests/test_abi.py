@@ -123,6 +123,25 @@ def test_status_strings_and_timing(lib):
     assert lib.fa_timing_read(9, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
 
 
+def test_forward_block_rows_setting(lib):
+    assert lib.fa_get_forward_block_rows() == 128
+    for bad in (0, 32, 96, 512, -128):
+        assert lib.fa_set_forward_block_rows(bad) == _binding.FA_ERR_UNSUPPORTED
+        assert lib.fa_get_forward_block_rows() == 128
+    try:
+        for rows in (64, 256, 128):
+            assert lib.fa_set_forward_block_rows(rows) == _binding.FA_OK
+            assert lib.fa_get_forward_block_rows() == rows
+        # 256-row tiles span two 128-token mask blocks: not for the block-sparse forward
+        assert lib.fa_set_forward_block_rows(256) == _binding.FA_OK
+        f = lib.fa_forward_blocksparse
+        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 64, 0.1, 0, None, FAKE, 128, 2, None) \
+            == _binding.FA_ERR_UNSUPPORTED
+        assert "256" in detail(lib)
+    finally:
+        lib.fa_set_forward_block_rows(128)
+
+
 def test_binding_refuses_cpu_tensors():
     import torch
     q = torch.zeros(1, 1, 8, 64)

@@ -15,7 +15,8 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_52_amd import fa_backward, fa_forward, fa_forward_blocksparse, inputs
+from exact_io_aware_52_amd import (fa_backward, fa_forward, fa_forward_blocksparse,
+                                   fa_set_forward_block_rows, inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -164,6 +165,34 @@ def test_large_scale(dtype, d, causal):
     prob = inputs.make_problem(1, 2, 300, d, dtype, seed=83 + d, causal=causal, scale=1.0)
     compare(run_gpu(prob), run_oracle(prob), TOL[dtype], label=f"scale 1 {dtype} d{d}",
             magnitude_scaled=True)
+
+
+ROW_CASES = [
+    # rows, B, H, N, d, dtype, causal, key_len_range, block_keep_p
+    (64, 1, 2, 300, 64, "bf16", True, None, None),
+    (64, 2, 1, 257, 128, "fp16", False, (1, 257), None),
+    (64, 1, 2, 384, 64, "bf16", False, None, 0.5),
+    (64, 1, 1, 200, 64, "fp32", True, None, None),
+    (256, 1, 2, 600, 64, "bf16", True, None, None),
+    (256, 2, 1, 520, 128, "bf16", False, (100, 520), None),
+    (256, 1, 1, 300, 128, "fp32", True, None, None),
+]
+
+
+@pytest.mark.parametrize("case", ROW_CASES, ids=lambda c: "rows{}_N{}d{}_{}".format(c[0], c[3], c[4], c[5]))
+def test_forward_block_rows(case):
+    # query tiles of 64 and 256 rows (the tile-height setting) give the same
+    # results as the oracle
+    rows, B, H, N, d, dtype, causal, klr, bkp = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=97 + rows + N, causal=causal,
+                               key_len_range=klr, block_keep_p=bkp)
+    fa_set_forward_block_rows(rows)
+    try:
+        gpu = run_gpu(prob)
+    finally:
+        fa_set_forward_block_rows(128)
+    compare(gpu, run_oracle(prob), TOL[dtype], label=f"{rows} rows {case[1:]}",
+            magnitude_scaled=klr is not None and klr[0] < 4)
 
 
 def test_scale_zero_is_uniform_attention():
