@@ -34,7 +34,10 @@ Readings where the pages are silent (each is also listed in the design notes):
   (b, h); entry (I, J) nonzero keeps every (i, j) with i // bs == I and
   j // bs == J; masks combine by logical AND;
 * a query row that sees no key at all has O = 0, LSE = -inf and contributes
-  nothing to any gradient.
+  nothing to any gradient;
+* with nq queries against nk cached keys (inference, ``forward_kv``), the
+  queries are the newest nq positions of a sequence of L = key_lens[b] filled
+  cache entries, and causal is aligned bottom-right: j <= i + L - nq.
 
 Everything is float64.  Inputs are the dtype-rounded values the GPU receives,
 upcast; ``scale`` is the float32 value handed to the GPU, upcast.
@@ -157,6 +160,50 @@ def head_rows(q, k, v, do, scale, rows, causal=False, key_len=None, block_mask=N
     dp_r = do[rows] @ v.T                       # dP = dO V^T
     ds_r = p_r * (dp_r - d_r[:, None])          # dS = P * (dP - D)
     return o_r, lse_r, scale * (ds_r @ k)       # dQ = scale * dS K
+
+
+def visibility_kv(nq, nk, causal=False, key_len=None):
+    """Boolean [nq, nk]: query i of nq new queries may attend key j of nk.
+
+    Inference reading (the pages say only that the kernel came to serve
+    inference; the alignment is this module's reading): the key/value tensors
+    hold a cache of which the first L = key_len (clamped to [0, nk]; nk when
+    None) positions are filled, and the nq queries are the newest nq positions
+    of that sequence, so query i sits at position i + L - nq.  Causal then
+    means key j is visible iff j <= i + L - nq (aligned bottom-right); keys
+    j >= L are never visible.  With nq = nk = L this is the top-left causal
+    mask of ``visibility``.
+    """
+    L = nk if key_len is None else min(max(int(key_len), 0), nk)
+    i = np.arange(nq)[:, None]
+    j = np.arange(nk)[None, :]
+    vis = np.broadcast_to(j < L, (nq, nk)).copy()
+    if causal:
+        vis &= j <= i + (L - nq)
+    return vis
+
+
+def head_forward_kv(q, k, v, scale, causal=False, key_len=None):
+    """Forward of nq queries (q: [nq, d]) against nk keys and values (k, v:
+    [nk, d]) with the visibility of ``visibility_kv``.  Returns (O, LSE);
+    rows that see no key have O = 0 and LSE = -inf."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    vis = visibility_kv(q.shape[0], k.shape[0], causal, key_len)
+    o, lse, _ = _head_forward(q, k, v, float(scale), vis)
+    return o, lse
+
+
+def forward_kv(q, k, v, scale, causal=False, key_lens=None, heads=None):
+    """Batched ``head_forward_kv``: q [B, H, nq, d], k and v [B, H, nk, d].
+    Returns (O [B, H, nq, d], LSE [B, H, nq]); ``heads`` as in ``forward``."""
+    B, H, nq, _ = _heads(q)
+    o = np.full((B, H, nq, v.shape[-1]), np.nan)
+    lse = np.full((B, H, nq), np.nan)
+    todo = heads if heads is not None else [(b, h) for b in range(B) for h in range(H)]
+    for b, h in todo:
+        kl = None if key_lens is None else int(key_lens[b])
+        o[b, h], lse[b, h] = head_forward_kv(q[b, h], k[b, h], v[b, h], scale, causal, kl)
+    return o, lse
 
 
 def _heads(x):

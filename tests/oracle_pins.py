@@ -284,5 +284,71 @@ def check_rows(orc, n=41, d=6):
         np.testing.assert_allclose(rdq, dq[rows], atol=1e-13)
 
 
+def check_kv_torch_lower_right(orc, B=2, H=2, d=8):
+    # Bottom-right causal against torch's own lower-right causal bias (an
+    # independent library definition of the alignment).  The cache fill L is
+    # applied here by handing torch only the first L keys.
+    from torch.nn.attention.bias import causal_lower_right
+    import warnings
+    for ci, (nq, nk, lens) in enumerate([(5, 13, None), (1, 40, [40, 17]), (9, 9, None),
+                                          (7, 30, [12, 30]), (16, 20, [20, 19])]):
+        q = _rand((B, H, nq, d), 800 + ci)
+        k, v = (_rand((B, H, nk, d), 810 + 2 * ci + t) for t in range(2))
+        for causal in (False, True):
+            o, lse = orc.forward_kv(q, k, v, 0.35, causal=causal, key_lens=lens)
+            for b in range(B):
+                L = nk if lens is None else lens[b]
+                tq, tk, tv = (torch.tensor(x[b]) for x in (q, k[:, :, :L], v[:, :, :L]))
+                with warnings.catch_warnings():
+                    warnings.simplefilter("ignore")
+                    mask = causal_lower_right(nq, L) if causal else None
+                    to = torch.nn.functional.scaled_dot_product_attention(
+                        tq, tk, tv, attn_mask=mask, scale=0.35)
+                msg = f"kv case {ci} causal {causal} batch {b}"
+                np.testing.assert_allclose(o[b], to.numpy(), atol=1e-12, err_msg=msg)
+                # logsumexp from torch's own softmax normaliser over the same keys
+                s = 0.35 * (tq @ tk.transpose(-1, -2))
+                if causal:
+                    keep = mask._materialize(torch.device("cpu"))
+                    s = s.masked_fill(~keep, -math.inf)
+                np.testing.assert_allclose(lse[b], torch.logsumexp(s, dim=-1).numpy(),
+                                           atol=1e-12, err_msg=msg)
+
+
+def check_kv_decode(orc, n=29, d=6):
+    # Decoding the newest positions against a cache equals the same rows of
+    # full causal self-attention over the filled part (the forward oracle is
+    # pinned above); a cache larger than its fill changes nothing.
+    x = [_rand((n, d), 900 + t) for t in range(3)]
+    o_full, lse_full = orc.head_forward(x[0], x[1], x[2], 0.5, causal=True)
+    for nq in (1, 3, n):
+        pad = np.full((11, d), 7.0)          # unfilled cache entries (never visible)
+        k = np.concatenate([x[1], pad])
+        v = np.concatenate([x[2], pad])
+        o, lse = orc.head_forward_kv(x[0][n - nq:], k, v, 0.5, causal=True, key_len=n)
+        np.testing.assert_allclose(o, o_full[n - nq:], atol=1e-14)
+        np.testing.assert_allclose(lse, lse_full[n - nq:], atol=1e-14)
+    # one query with causal sees every filled key: the non-causal result
+    o1, l1 = orc.head_forward_kv(x[0][:1], x[1], x[2], 0.5, causal=True, key_len=17)
+    o2, l2 = orc.head_forward(np.concatenate([x[0][:1], np.zeros((n - 1, d))]), x[1], x[2], 0.5,
+                              key_len=17)
+    np.testing.assert_allclose(o1[0], o2[0], atol=1e-14)
+    np.testing.assert_allclose(l1[0], l2[0], atol=1e-14)
+    # more queries than filled keys: the first nq - L rows see nothing
+    q8 = np.concatenate([_rand((5, d), 950), x[0][:3]])   # rows 5..7 are positions 0..2
+    o, lse = orc.head_forward_kv(q8, x[1], x[2], 0.5, causal=True, key_len=3)
+    assert np.all(o[:5] == 0) and np.all(np.isneginf(lse[:5]))
+    np.testing.assert_allclose(o[5:], o_full[:3], atol=1e-14)
+    # an empty cache: every row sees nothing
+    o, lse = orc.head_forward_kv(x[0][:4], x[1], x[2], 0.5, causal=False, key_len=0)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+    # fills outside [0, nk] are clamped: nk + 5 acts as a full cache, -3 as an empty one
+    o, lse = orc.head_forward_kv(x[0][n - 4:], x[1], x[2], 0.5, causal=True, key_len=n + 5)
+    np.testing.assert_allclose(o, o_full[n - 4:], atol=1e-14)
+    o, lse = orc.head_forward_kv(x[0][:4], x[1], x[2], 0.5, causal=True, key_len=-3)
+    assert np.all(o == 0) and np.all(np.isneginf(lse))
+
+
 ALL_PINS = [check_golden, check_finite_differences, check_torch_reference,
-            check_invariants, check_special_cases, check_row_chunking, check_rows]
+            check_invariants, check_special_cases, check_row_chunking, check_rows,
+            check_kv_torch_lower_right, check_kv_decode]

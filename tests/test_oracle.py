@@ -26,7 +26,7 @@ MUTATIONS = {
     "dV_untransposed": ("dv += p.T @ do[r0:r1]", "dv += p @ do[r0:r1]"),
     "dP_wrong_operand": ("dp = do[r0:r1] @ v.T", "dp = do[r0:r1] @ k.T"),
     "scores_without_scale": ("s = scale * (q @ k.T)", "s = (q @ k.T)"),
-    "causal_strict": ("vis &= j <= i", "vis &= j < i"),
+    "causal_strict": ("vis &= j <= i\n", "vis &= j < i\n"),
     "padding_off_by_one": ("vis &= j < int(key_len)", "vis &= j <= int(key_len)"),
     "block_mask_transposed": ("bm[i // block_size, j // block_size]",
                               "bm[j // block_size, i // block_size]"),
@@ -37,6 +37,13 @@ MUTATIONS = {
     "rows_dQ_wrong_operand": ("scale * (ds_r @ k)", "scale * (ds_r @ q)"),
     "rows_mask_ignores_rows": ("i = (np.arange(n) if rows is None else np.asarray(rows))[:, None]",
                                "i = np.arange(n)[:len(rows) if rows is not None else n, None]"),
+    "kv_causal_top_left": ("vis &= j <= i + (L - nq)", "vis &= j <= i"),
+    "kv_causal_strict": ("vis &= j <= i + (L - nq)", "vis &= j < i + (L - nq)"),
+    "kv_shift_from_capacity": ("vis &= j <= i + (L - nq)", "vis &= j <= i + (nk - nq)"),
+    "kv_fill_ignored": ("vis = np.broadcast_to(j < L, (nq, nk)).copy()",
+                        "vis = np.ones((nq, nk), dtype=bool)"),
+    "kv_fill_unclamped": ("L = nk if key_len is None else min(max(int(key_len), 0), nk)",
+                          "L = nk if key_len is None else int(key_len)"),
 }
 
 
