@@ -7,7 +7,10 @@ GPT-2-small-shaped causal self-attention (B=8, H=12, N=1024, d=64, bf16).
     python bench.py [--steps K] [--warmup W] [--config NAME [--n N --d D]]
 
 Prints one JSON line.  ``value`` is algorithmic forward+backward TFLOP/s
-(14 * d flops per kept query-key pair) of the whole job.  ``roofline``
+(14 * d flops per kept query-key pair) of the whole job.  The inference
+workloads (``--config kv_decode`` / ``kv_chunk``: new queries against a
+key/value cache, fa_forward_kv) have no backward: there a step is one
+inference forward and ``value`` its algorithmic TFLOP/s (4 * d per pair).  ``roofline``
 describes the kernel that takes most of the step, timed with the library's
 per-launch HIP events over a second pass of the same K steps; ``cpu_baseline``
 times the fp64 oracle on the host on a bounded sample of the same workload.
@@ -27,7 +30,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
-                                   fa_forward, fa_forward_blocksparse, fa_kernel_name,
+                                   fa_forward, fa_forward_blocksparse, fa_forward_kv,
+                                   fa_forward_kv_workspace_bytes, fa_kernel_name,
                                    fa_set_forward_block_rows, fa_timing_enable, fa_timing_read,
                                    inputs)
 
@@ -40,6 +44,7 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
 KERNEL_SOURCES = {
     "fwd": ["fa_fwd.hip", "fa_common.h"],
+    "fwd_combine": ["fa_fwd.hip", "fa_common.h"],
     "bwd_dkdv": ["fa_bwd_impl.h", "fa_common.h"],
     "bwd_dq": ["fa_bwd_impl.h", "fa_common.h"],
 }
@@ -116,6 +121,128 @@ def cpu_baseline(prob, budget_s):
                       f"the same workload), fp64 forward+backward, {dt:.1f} s"}
 
 
+def kv_splits(prob):
+    """Key-range splits the library plans for this inference problem (read
+    back from its workspace size: splits x rows x (d + 1) fp32 values)."""
+    need = fa_forward_kv_workspace_bytes(prob.B, prob.H, prob.Nq, prob.Nk, prob.d,
+                                         TORCH_DT[prob.dtype])
+    return max(1, need // (prob.B * prob.H * prob.Nq * (prob.d + 1) * 4))
+
+
+def cpu_baseline_kv(prob, budget_s):
+    """The fp64 oracle's inference forward, one head at a time, for about
+    ``budget_s`` seconds; TFLOP/s at 4 * d flops per kept pair."""
+    import oracle   # test infrastructure; used only for this reported baseline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:   # pragma: no cover
+        threads = os.cpu_count()
+    heads = [(b, h) for b in range(prob.B) for h in range(prob.H)]
+    done, pairs = 0, 0
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        b, h = heads[done % len(heads)]
+        kl = None if prob.key_lens is None else int(prob.key_lens[b])
+        oracle.head_forward_kv(*(x[b, h].astype(np.float64) for x in (prob.q, prob.k, prob.v)),
+                               float(prob.scale), causal=prob.causal, key_len=kl)
+        L = accounting.kv_fill(prob, b)
+        i = np.arange(prob.Nq)
+        pairs += int((np.clip(i + L - prob.Nq + 1, 0, L) if prob.causal
+                      else np.full(prob.Nq, L)).sum())
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": 4 * prob.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} heads ({done / len(heads):.2f} passes over the {len(heads)} heads of "
+                      f"the same workload), fp64 inference forward, {dt:.1f} s"}
+
+
+def bench_kv(args, dev):
+    """One step = one fa_forward_kv call (new queries against a key/value
+    cache); no backward.  The roofline names the bound with the longer time
+    at peak for the forward kernel's work: HBM bytes or matrix flops."""
+    KERNEL_NAMES["fwd_combine"] = fa_kernel_name("fwd_combine")
+    prob = inputs.kv_workload(args.config)
+    dt = TORCH_DT[prob.dtype]
+    q, k, v = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v))
+    kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).to(dev)
+    o = torch.empty_like(q)
+    lse = torch.empty(prob.B, prob.H, prob.Nq, dtype=torch.float32, device=dev)
+    need = fa_forward_kv_workspace_bytes(prob.B, prob.H, prob.Nq, prob.Nk, prob.d, dt)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    scale = float(prob.scale)
+
+    def step():
+        fa_forward_kv(q, k, v, scale=scale, causal=prob.causal, key_lens=kl, o=o, lse=lse,
+                      workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+
+    fa_timing_enable(True)
+    for kind in ("fwd", "fwd_combine"):
+        fa_timing_read(kind)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    fa_timing_enable(False)
+    kernels = {}
+    for kind in ("fwd", "fwd_combine"):
+        total, n = fa_timing_read(kind)
+        kernels[kind] = {"name": KERNEL_NAMES[kind], "avg_us": 1e3 * total / max(n, 1),
+                         "launches": n}
+
+    pairs = accounting.kv_kept_pairs(prob)
+    flops = 4 * prob.d * pairs
+    splits = kv_splits(prob)
+    nbytes = accounting.kv_forward_bytes(prob, splits)
+    t_fwd = kernels["fwd"]["avg_us"] * 1e-6
+    peak = PEAK_TFLOPS[prob.dtype]
+    if nbytes / (PEAK_HBM_GBS * 1e9) > flops / (peak * 1e12):
+        achieved = nbytes / t_fwd / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
+                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
+    else:
+        achieved = flops / t_fwd / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
+    roof["traffic"] = read_traffic(KERNEL_NAMES["fwd"], prob.name)
+    roof["kernel"] = KERNEL_NAMES["fwd"]
+    roof["kernel_avg_us"] = round(kernels["fwd"]["avg_us"], 2)
+    roof["algorithmic_bytes"] = nbytes
+    result = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob.dtype,
+        "data": "synthetic",
+        "config": {"workload": prob.name, "pass": "inference forward (no backward)",
+                   "B": prob.B, "H": prob.H, "Nq": prob.Nq, "Nk": prob.Nk, "d": prob.d,
+                   "causal": prob.causal, "cache_fill": "key_lens" if prob.key_lens is not None
+                   else "full", "key_splits": splits, "parallelism": "none"},
+        "hbm_GBps_step": round(nbytes / (ms_step * 1e-3) / 1e9, 1),
+        "kernels_us": {v["name"]: round(v["avg_us"], 2) for v in kernels.values()},
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline_kv(prob, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -123,7 +250,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gpt2_small",
                     choices=["tiny", "gpt2_small", "bert_large_padded", "long_causal",
-                             "block_sparse", "block_sparse_long"])
+                             "block_sparse", "block_sparse_long", "kv_decode", "kv_chunk"])
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--d", type=int, default=64)
     ap.add_argument("--fwd-block-rows", type=int, default=128, choices=[64, 128, 256],
@@ -156,6 +283,10 @@ def main():
 
     for k in ("fwd", "bwd_dkdv", "bwd_dq"):
         KERNEL_NAMES[k] = fa_kernel_name(k)
+
+    if args.config.startswith("kv_"):
+        bench_kv(args, dev)
+        return
 
     fa_set_forward_block_rows(args.fwd_block_rows)
     prob = make_workload(args)

@@ -5,11 +5,13 @@ declared in ``include/fa.h``); this package only marshals torch tensors
 (device memory and the current stream) into those calls.
 
     from exact_io_aware_52_amd import fa_forward, fa_backward, fa_forward_blocksparse
+    from exact_io_aware_52_amd import fa_forward_kv     # inference: Nq queries, Nk cache
 """
 
 from ._binding import (  # noqa: F401
     FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP,
     FaError, library_path, load_library, fa_forward, fa_forward_blocksparse, fa_backward,
     fa_backward_workspace_bytes, fa_timing_enable, fa_timing_read, fa_kernel_name,
-    fa_set_forward_block_rows, fa_get_forward_block_rows, KERNEL_KINDS,
+    fa_set_forward_block_rows, fa_get_forward_block_rows, fa_forward_kv,
+    fa_forward_kv_workspace_bytes, KERNEL_KINDS,
 )

@@ -14,7 +14,7 @@ import torch
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KERNEL_KINDS = {"fwd": 0, "bwd_dkdv": 1, "bwd_dq": 2}
+KERNEL_KINDS = {"fwd": 0, "bwd_dkdv": 1, "bwd_dq": 2, "fwd_combine": 3}
 
 _LIB = None
 
@@ -55,9 +55,12 @@ def load_library():
     lib.fa_kernel_name.restype = ctypes.c_char_p
     lib.fa_set_forward_block_rows.argtypes = [I]
     lib.fa_get_forward_block_rows.argtypes = []
+    lib.fa_forward_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, Z, P]
+    lib.fa_forward_kv_workspace_bytes.argtypes = [I, I, I, I, I, I]
+    lib.fa_forward_kv_workspace_bytes.restype = Z
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_backward,
                lib.fa_timing_enable, lib.fa_timing_read, lib.fa_set_forward_block_rows,
-               lib.fa_get_forward_block_rows):
+               lib.fa_get_forward_block_rows, lib.fa_forward_kv):
         fn.restype = I
     _LIB = lib
     return lib
@@ -162,6 +165,48 @@ def fa_forward_blocksparse(q, k, v, block_mask, block_size=128, scale=None, caus
         raise ValueError("block_mask is required")
     return _forward("fa_forward_blocksparse", q, k, v, scale, causal, key_lens, block_mask,
                     block_size, o, lse)
+
+
+def fa_forward_kv_workspace_bytes(B, H, Nq, Nk, d, dtype):
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_forward_kv_workspace_bytes(B, H, Nq, Nk, d, code))
+
+
+def fa_forward_kv(q, k, v, scale=None, causal=False, key_lens=None, o=None, lse=None,
+                  workspace=None):
+    """Inference forward: q [B,H,Nq,d] against a cache k, v [B,H,Nk,d] whose
+    first key_lens[b] entries are filled; causal aligned bottom-right.
+    Returns (O [B,H,Nq,d], LSE [B,H,Nq] float32)."""
+    lib = load_library()
+    if q.dim() != 4 or k.dim() != 4:
+        raise ValueError("q must be [B, H, Nq, d] and k, v [B, H, Nk, d]")
+    B, H, Nq, d = q.shape
+    Nk = k.shape[2]
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (B, H, Nk, d) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be [B, H, Nk, d] with q's dtype and device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device (the library has no CPU path)")
+    o = torch.empty_like(q) if o is None else _like("o", o, q)
+    lse = (torch.empty((B, H, Nq), dtype=torch.float32, device=q.device) if lse is None
+           else _like("lse", lse, q, (B, H, Nq), torch.float32))
+    need = fa_forward_kv_workspace_bytes(B, H, Nq, Nk, d, q.dtype)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    kl = _lens(key_lens, B, q.device)
+    st = lib.fa_forward_kv(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, Nq, Nk, d,
+                           _scale(scale, d), int(bool(causal)), _ptr(kl),
+                           _DTYPE_CODE[q.dtype], _ptr(workspace),
+                           workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("fa_forward_kv", st)
+    return o, lse
 
 
 def fa_backward_workspace_bytes(B, H, N, d):

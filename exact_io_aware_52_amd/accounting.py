@@ -85,3 +85,41 @@ def tiled_forward_bytes(prob, block_rows):
     frac = kept_pairs(prob) / dense if dense else 0.0
     tiles = -(-n // block_rows)
     return compulsory_bytes(prob, "fwd") + prob.B * prob.H * tiles * 2 * frac * n * d * s
+
+
+# ----------------------------------------------------------------------------- inference
+
+def kv_fill(prob, b):
+    """Visible cache entries of batch b of a KvProblem (key_lens clamped)."""
+    if prob.key_lens is None:
+        return prob.Nk
+    return max(0, min(int(prob.key_lens[b]), prob.Nk))
+
+
+def kv_kept_pairs(prob):
+    """Visible (query, key) pairs of a KvProblem: row i of batch b sees
+    min(L, i + L - Nq + 1) keys under the bottom-right causal mask (none when
+    that is negative) and all L otherwise."""
+    total = 0
+    i = np.arange(prob.Nq, dtype=np.int64)
+    for b in range(prob.B):
+        L = kv_fill(prob, b)
+        per = np.clip(i + L - prob.Nq + 1, 0, L) if prob.causal else np.full(prob.Nq, L)
+        total += prob.H * int(per.sum())
+    return total
+
+
+def kv_forward_bytes(prob, splits):
+    """Algorithmic HBM bytes of the inference forward kernel: Q and the
+    visible part of the K and V cache read once (further query tiles re-read
+    the cache from L2), and either O and the fp32 LSE written or, with the
+    key range split, the fp32 partial O and LSE of every split."""
+    s = ELEM_BYTES[prob.dtype]
+    heads = prob.B * prob.H
+    q = heads * prob.Nq * prob.d * s
+    kv = 2 * prob.H * prob.d * s * sum(kv_fill(prob, b) for b in range(prob.B))
+    if splits > 1:
+        out = splits * heads * prob.Nq * (prob.d + 1) * 4
+    else:
+        out = heads * prob.Nq * (prob.d * s + 4)
+    return q + kv + out

@@ -7,6 +7,7 @@
 
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -137,6 +138,48 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
 
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
+// Inference forward plan: query rows per work-group and key-range splits.
+// Few queries against a long cache leave too few work-groups to fill the
+// chip (and to keep enough key/value reads in flight), so the key range is
+// split until the work-groups fill one round of the slots the chip holds at
+// once (256 CUs times the work-groups whose K/V ring fits one CU's 160 KB of
+// LDS: 3 for 16-bit d = 64, 2 for 16-bit d = 128 and fp32 d = 64, 1 for
+// fp32 d = 128), each split keeping at least 256 keys; a second pass merges
+// the split results.  Measured on the inference workloads: one round beats
+// two or four (partial results cost traffic) and no split (idle CUs).
+struct KvPlan {
+  int rows;    // 32 (one wave; 16-bit types), 64 or 128
+  int splits;  // 1: no workspace, O and LSE written directly
+  int chunk;   // keys per split, a multiple of 64
+};
+
+KvPlan kv_plan(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
+  KvPlan pl;
+  pl.rows = (Nq <= 32 && dtype != FA_F32) ? 32 : (Nq <= 64 ? 64 : 128);
+  pl.splits = 1;
+  pl.chunk = 0;
+  const int per_cu = dtype == FA_F32 ? (d == 64 ? 2 : 1) : (d == 64 ? 3 : 2);
+  const long long slots = 256LL * per_cu;
+  const long long groups = (long long)B * H * ((Nq + pl.rows - 1) / pl.rows);
+  const long long ktiles = ((long long)Nk + 63) / 64;
+  if (groups <= 0 || ktiles <= 0 || groups >= slots) return pl;
+  long long s = (slots + groups - 1) / groups;
+  s = std::min<long long>(s, std::max<long long>(ktiles / 4, 1));
+  s = std::min<long long>(s, 64);
+  if (s <= 1) return pl;
+  const long long per = (ktiles + s - 1) / s;  // key tiles per split
+  pl.chunk = (int)(per * 64);
+  pl.splits = (int)((ktiles + per - 1) / per);
+  if (pl.splits <= 1) pl.splits = 1, pl.chunk = 0;
+  return pl;
+}
+
+size_t kv_workspace(int B, int H, int Nq, int d, const KvPlan& pl) {
+  if (pl.splits <= 1) return 0;
+  const size_t rows = (size_t)pl.splits * B * H * Nq;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
 }  // namespace
 
 extern "C" {
@@ -154,6 +197,51 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
                            fa_dtype dtype, hipStream_t stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
                       block_size, true, dtype, stream);
+}
+
+size_t fa_forward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {
+  if (B <= 0 || H <= 0 || Nq <= 0 || Nk <= 0 || d <= 0) return 0;
+  return kv_workspace(B, H, Nq, d, kv_plan(B, H, Nq, Nk, d, dtype));
+}
+
+int fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int Nq, int Nk, int d, float scale, int causal, const int32_t* key_lens,
+                  fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_detail[0] = 0;
+  if (Nk < 0) return fail(FA_ERR_INVALID_ARG, "negative size Nk=%d", Nk);
+  bool empty = false;
+  int st = check_common(B, H, Nq, d, scale, dtype, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  if ((long long)Nk * d > 0x7fffffffLL) return fail(FA_ERR_INVALID_ARG, "Nk*d exceeds 2^31-1");
+  if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(o, "o", 16)) ||
+      (st = check_tensor(lse, "lse", 4)))
+    return st;
+  if (Nk > 0 && ((st = check_tensor(k, "k", 16)) || (st = check_tensor(v, "v", 16)))) return st;
+  if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
+  const KvPlan pl = kv_plan(B, H, Nq, Nk, d, dtype);
+  const size_t need = kv_workspace(B, H, Nq, d, pl);
+  if (need > 0) {
+    if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  }
+  fa::Problem p{B, H, Nq, d, scale, causal ? 1 : 0, key_lens, nullptr, (int)dtype, stream, pl.rows};
+  p.nk = Nk;
+  p.causal_br = 1;
+  p.splits = pl.splits;
+  p.chunk = pl.chunk;
+  if (pl.splits > 1) {
+    const size_t rows = (size_t)pl.splits * B * H * Nq;
+    p.opart = static_cast<float*>(workspace);
+    p.lpart = reinterpret_cast<float*>(static_cast<char*>(workspace) +
+                                       round_up(rows * d * sizeof(float), 256));
+  }
+  fa::FwdTensors t{q, k, v, o, lse};
+  hipError_t e = fa::launch_forward(p, t);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return FA_OK;
 }
 
 int fa_set_forward_block_rows(int rows) {
@@ -242,6 +330,7 @@ const char* fa_kernel_name(int kernel) {
     case fa::kFwd: return "fa_fwd_kernel";
     case fa::kBwdDkDv: return "fa_bwd_dkdv_kernel";
     case fa::kBwdDq: return "fa_bwd_dq_kernel";
+    case fa::kFwdCombine: return "fa_fwd_combine_kernel";
   }
   return "unknown";
 }

@@ -66,10 +66,21 @@ struct FwdParams {
   float* lse;
   const int32_t* key_lens;
   const uint8_t* block_mask;
-  int H, N, BH, nq, nblk;
+  int H, N, BH, nq, nblk;  // N: query rows per head; nq: query tiles per head
+  int nk;                  // key (and value) rows per head: N for self-attention
   float scale;
   float c;  // scale * log2(e): exponents are taken base 2
   int causal;
+  // Causal alignment: 0 = top-left (query i sees keys j <= i); 1 = bottom-right
+  // to the visible key count L (query i sees keys j <= i + L - N).
+  int causal_br;
+  // Key range split over gridDim.y work-groups per query tile: split s covers
+  // keys [s * chunk, (s + 1) * chunk) (chunk a multiple of the key tile) and
+  // writes its normalised partial O (fp32) and LSE to opart / lpart at
+  // [s][bh][row]; with one split (opart null) O and LSE are written directly.
+  int chunk;
+  float* opart;
+  float* lpart;
 };
 
 constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 131072)
@@ -164,16 +175,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   int qt, bh;
   map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, qt, bh);
   const int b = bh / p.H;
-  const int N = p.N;
+  const int N = p.N;    // query rows
+  const int NK = p.nk;  // key rows
   const int i0 = qt * BR;
   const int qw0 = i0 + 32 * w;  // first query of this wave
   const int myq = qw0 + col;
 
-  int kend = N;
-  if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
-  int kv_end = kend;
-  if (p.causal) kv_end = min(kv_end, i0 + BR);
-  const int nkt = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;
+  int kend = NK;
+  if (p.key_lens) kend = min(max(p.key_lens[b], 0), NK);
+  // Query i sees keys j <= i + shift under the causal mask.
+  const int shift = p.causal_br ? kend - N : 0;
+  // This work-group's key range: [kbeg, kv_end), whole key tiles from kbeg.
+  const int kbeg = blockIdx.y * p.chunk;
+  int kv_end = min(kend, kbeg + p.chunk);
+  if (p.causal) kv_end = min(kv_end, i0 + BR + shift);
+  const int t0 = kbeg / BT;  // first key tile of the range
+  const int nkt = kv_end > kbeg ? (kv_end + BT - 1) / BT : t0;
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
@@ -184,10 +201,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     while (j < nkt && mask_row[(j * BT) / kMaskBlock] == 0) ++j;
     return j;
   };
-  const size_t head = (size_t)bh * N * D;
+  const size_t head = (size_t)bh * N * D;     // Q and O rows of this head
+  const size_t khead = (size_t)bh * NK * D;   // K and V rows
   const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
-  const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + head;
-  const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + head;
+  const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + khead;
+  const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + khead;
   const float c = p.c;
 
   // The wave's Q rows as B operands (contiguous slot map over d).
@@ -206,8 +224,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   vplan.init(w, lane);
   auto issue = [&](int t, int s) {
     const uint32_t base = ring_lds + s * L::SLOT_BYTES;
-    kplan.copy(Kg, t * BT, N, base, lane);
-    vplan.copy(Vg, t * BT, N, base + L::TILE_BYTES, lane);
+    kplan.copy(Kg, t * BT, NK, base, lane);
+    vplan.copy(Vg, t * BT, NK, base + L::TILE_BYTES, lane);
   };
 
   // ---- per-wave math
@@ -224,10 +242,10 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 
   // Sub-tile (t, h): keys t*BT + 32h .. +31.  A wave skips sub-tiles wholly
   // past its causal diagonal and element-masks those that straddle a boundary.
-  auto active = [&](int t, int h) { return !p.causal || t * BT + 32 * h <= qw0 + 31; };
+  auto active = [&](int t, int h) { return !p.causal || t * BT + 32 * h <= qw0 + 31 + shift; };
   auto masked = [&](int t, int h) {
     const int k0 = t * BT + 32 * h;
-    return (p.causal && k0 + 31 > qw0) || (k0 + 32 > kend);
+    return (p.causal && k0 + 31 > qw0 + shift) || (k0 + 32 > kend);
   };
   // S^T of one sub-tile: rows = keys, columns = queries.
   auto scores = [&](const raw* Ks, int h, f32x16& s) {
@@ -241,7 +259,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int key = t * BT + 32 * h + acc_row(r, hh);
-      if (key >= kend || (p.causal && key > myq)) s[r] = kNegInf;
+      if (key >= kend || (p.causal && key > myq + shift)) s[r] = kNegInf;
     }
   };
   // P = exp2(c s - ra) rounded to T, as B operands; returns this lane's sum
@@ -338,58 +356,60 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 
   // Kept tiles of this work-group, in order; tl[k] is the tile of step i + k.
   int tl[4];
-  tl[0] = next_kept(0);
+  tl[0] = next_kept(t0);
   tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
   tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
   tl[3] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
-  if (tl[0] < nkt && L::PIPE) {
-    issue(tl[0], 0);
-    if (tl[1] < nkt) issue(tl[1], 1);
-    if (tl[2] < nkt) issue(tl[2], 2);
-    // wait for tile 0 (later tiles may stay in flight)
-    if (tl[2] < nkt) wait_vmcnt<2 * LPT>();
-    else if (tl[1] < nkt) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-    __syncthreads();
+  if constexpr (L::PIPE) {
+    if (tl[0] < nkt) {
+      issue(tl[0], 0);
+      if (tl[1] < nkt) issue(tl[1], 1);
+      if (tl[2] < nkt) issue(tl[2], 2);
+      // wait for tile 0 (later tiles may stay in flight)
+      if (tl[2] < nkt) wait_vmcnt<2 * LPT>();
+      else if (tl[1] < nkt) wait_vmcnt<LPT>();
+      else wait_vmcnt<0>();
+      __syncthreads();
 
-    f32x16 sa, sb;
-    if (active(tl[0], 0)) {
-      scores(ktile(0), 0, sa);
-      if (masked(tl[0], 0)) apply_mask(tl[0], 0, sa);
-    }
+      f32x16 sa, sb;
+      if (active(tl[0], 0)) {
+        scores(ktile(0), 0, sa);
+        if (masked(tl[0], 0)) apply_mask(tl[0], 0, sa);
+      }
 
-    // Step i works on the tile in ring slot i % 4: on entry its first
-    // sub-tile's scores are formed; on exit, those of the next tile.
-    int step = 0;
-    auto body = [&](f32x16& s0, f32x16& s1) {
-      if (tl[1] < nkt) {
-        // tile tl[1] must have landed; tl[2] may still be in flight
-        if (tl[2] < nkt) wait_vmcnt<LPT>();
-        else wait_vmcnt<0>();
+      // Step i works on the tile in ring slot i % 4: on entry its first
+      // sub-tile's scores are formed; on exit, those of the next tile.
+      int step = 0;
+      auto body = [&](f32x16& s0, f32x16& s1) {
+        if (tl[1] < nkt) {
+          // tile tl[1] must have landed; tl[2] may still be in flight
+          if (tl[2] < nkt) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+        }
+        __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
+        if (tl[3] < nkt) issue(tl[3], (step + 3) & 3);
+        const raw* Kc = ktile(step & 3);
+        const raw* Kn = ktile((step + 1) & 3);
+        const raw* Vc = vtile(step & 3);
+        const bool more = tl[1] < nkt;
+        if constexpr (NSUB == 2) {
+          substep(s0, s1, tl[0], 0, Vc, tl[0], 1, Kc, true);
+          substep(s1, s0, tl[0], 1, Vc, tl[1], 0, Kn, more);
+        } else {
+          substep(s0, s1, tl[0], 0, Vc, tl[1], 0, Kn, more);
+        }
+        tl[0] = tl[1];
+        tl[1] = tl[2];
+        tl[2] = tl[3];
+        tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+        ++step;
+      };
+      while (true) {
+        body(sa, sb);
+        if (tl[0] >= nkt) break;
+        body(NSUB == 2 ? sa : sb, NSUB == 2 ? sb : sa);
+        if (tl[0] >= nkt) break;
       }
-      __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
-      if (tl[3] < nkt) issue(tl[3], (step + 3) & 3);
-      const raw* Kc = ktile(step & 3);
-      const raw* Kn = ktile((step + 1) & 3);
-      const raw* Vc = vtile(step & 3);
-      const bool more = tl[1] < nkt;
-      if constexpr (NSUB == 2) {
-        substep(s0, s1, tl[0], 0, Vc, tl[0], 1, Kc, true);
-        substep(s1, s0, tl[0], 1, Vc, tl[1], 0, Kn, more);
-      } else {
-        substep(s0, s1, tl[0], 0, Vc, tl[1], 0, Kn, more);
-      }
-      tl[0] = tl[1];
-      tl[1] = tl[2];
-      tl[2] = tl[3];
-      tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
-      ++step;
-    };
-    while (true) {
-      body(sa, sb);
-      if (tl[0] >= nkt) break;
-      body(NSUB == 2 ? sa : sb, NSUB == 2 ? sb : sa);
-      if (tl[0] >= nkt) break;
     }
   } else if (tl[0] < nkt) {
     // Without the pipeline: step i forms, exponentiates and multiplies into
@@ -404,11 +424,12 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
     int lo = nkt, hi = -1;
     if (!sparse) {
-      lo = 0;
-      hi = min(min(nkt, N / BT) - 1 - PD, kend / BT - 1);
-      if (p.causal) hi = min(hi, (i0 + 1) / BT - 1);
+      lo = t0;
+      hi = min(min(nkt, NK / BT) - 1 - PD, kend / BT - 1);
+      // whole tile visible to query i0: (t + 1) BT - 1 <= i0 + shift
+      if (p.causal) hi = min(hi, i0 + shift + 1 >= 0 ? (i0 + shift + 1) / BT - 1 : -1);
     }
-    for (int step = 0;; ++step) {
+    for (;;) {
       const int t = tl[0];
       const raw* Kc = ktile(cur);
       const raw* Vc = vtile(cur);
@@ -444,12 +465,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
         tl[PD] = min(t + PD + 1, nkt);
       } else {
-        int inflight = 0;  // later tiles requested so far
+        int inflight = 0;  // later tiles requested so far (at most PD - 1)
 #pragma unroll
         for (int k = 1; k < PD; ++k) inflight += tl[k] < nkt;
-        if (inflight >= 2) wait_vmcnt<2 * LPT>();
-        else if (inflight == 1) wait_vmcnt<LPT>();
-        else wait_vmcnt<0>();
+        if constexpr (PD >= 3) {
+          if (inflight >= 2) wait_vmcnt<2 * LPT>();
+          else if (inflight == 1) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+        } else if constexpr (PD == 2) {
+          if (inflight == 1) wait_vmcnt<LPT>();
+          else wait_vmcnt<0>();
+        } else {
+          wait_vmcnt<0>();
+        }
         __syncthreads();  // every wave is done with step i-1: slot nxt is free
         if (tl[PD] < nkt) issue(tl[PD], nxt);
 #pragma unroll
@@ -477,7 +505,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 
   // Epilogue: O = acc / l, LSE = ln(2^ra l) = ra ln(2) + ln(l).
   const float l_tot = pair_sum(l_run);
-  if (myq < N) {
+  if (p.opart && myq < N) {
+    // One split of the key range: fp32 partial results for the combine pass.
+    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    const size_t prow = ((size_t)blockIdx.y * p.BH + bh) * N + myq;
+    float* Op = p.opart + prow * D;
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 out;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) out[u] = oacc[db][4 * g + u] * inv;
+        *reinterpret_cast<f32x4*>(Op + db * 32 + 8 * g + 4 * hh) = out;
+      }
+    if (hh == 0) p.lpart[prow] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
+  } else if (myq < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
     raw* Og = reinterpret_cast<raw*>(p.o) + head + (size_t)myq * D;
 #pragma unroll
@@ -498,6 +541,70 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
+// Merge of the key-range splits of one query row (the online-softmax merge of
+// per-block states, applied across work-groups): with split results (O_s,
+// LSE_s), LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.  A row
+// that no split saw keys for gets O = 0, LSE = -inf.  D / 4 threads per row,
+// four output elements each.
+struct CombineParams {
+  const float* opart;
+  const float* lpart;
+  void* o;
+  float* lse;
+  int rows;    // B * H * N
+  int splits;
+};
+
+template <typename T, int D>
+__global__ __launch_bounds__(256) void fa_fwd_combine_kernel(CombineParams p) {
+  typedef raw_t<T> raw;
+  constexpr int TPR = D / 4;
+  constexpr int RPB = 256 / TPR;
+  const int row = blockIdx.x * RPB + (int)threadIdx.x / TPR;
+  if (row >= p.rows) return;
+  const int c4 = ((int)threadIdx.x % TPR) * 4;
+  float m = kNegInf;
+  for (int s = 0; s < p.splits; ++s) m = fmaxf(m, p.lpart[(size_t)s * p.rows + row]);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  float sum = 0.f;
+  if (m != kNegInf) {
+    for (int s = 0; s < p.splits; ++s) {
+      const float ls = p.lpart[(size_t)s * p.rows + row];
+      if (ls == kNegInf) continue;
+      const float wgt = expf(ls - m);
+      const f32x4 os = *reinterpret_cast<const f32x4*>(p.opart + ((size_t)s * p.rows + row) * D + c4);
+      sum += wgt;
+      acc += wgt * os;
+    }
+  }
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  raw* Og = reinterpret_cast<raw*>(p.o) + (size_t)row * D + c4;
+#pragma unroll
+  for (int u = 0; u < 4; ++u) {
+    const T val = (T)(acc[u] * inv);
+    Og[u] = __builtin_bit_cast(raw, val);
+  }
+  if (c4 == 0) p.lse[row] = sum > 0.f ? m + logf(sum) : kNegInf;
+}
+
+template <typename T, int D>
+hipError_t launch_fwd_combine(const Problem& pb, const FwdTensors& t, int splits) {
+  constexpr int RPB = 256 / (D / 4);
+  CombineParams c;
+  c.opart = pb.opart;
+  c.lpart = pb.lpart;
+  c.o = t.o;
+  c.lse = t.lse;
+  c.rows = pb.B * pb.H * pb.N;
+  c.splits = splits;
+  const unsigned grid = (unsigned)((c.rows + RPB - 1) / RPB);
+  timing_begin(kFwdCombine, pb.stream);
+  hipLaunchKernelGGL((fa_fwd_combine_kernel<T, D>), dim3(grid), dim3(256), 0, pb.stream, c);
+  hipError_t e = hipGetLastError();
+  timing_end(kFwdCombine, pb.stream);
+  return e;
+}
+
 template <typename T, int D, int NW>
 hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   constexpr int BR = FwdCfg<T, D, NW>::BR;
@@ -507,24 +614,36 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.block_mask = pb.block_mask;
   p.H = pb.H;
   p.N = pb.N;
+  p.nk = pb.nk < 0 ? pb.N : pb.nk;
   p.BH = pb.B * pb.H;
   p.nq = (pb.N + BR - 1) / BR;
   p.nblk = (pb.N + kMaskBlock - 1) / kMaskBlock;
   p.scale = pb.scale;
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
+  p.causal_br = pb.causal_br;
+  const int splits = pb.splits > 1 ? pb.splits : 1;
+  p.chunk = splits > 1 ? pb.chunk : max(p.nk, 1);
+  p.opart = splits > 1 ? pb.opart : nullptr;
+  p.lpart = splits > 1 ? pb.lpart : nullptr;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
   timing_begin(kFwd, pb.stream);
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid), dim3(64 * NW), 0, pb.stream, p);
+  hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid, splits), dim3(64 * NW), 0, pb.stream,
+                     p);
   hipError_t e = hipGetLastError();
   timing_end(kFwd, pb.stream);
-  return e;
+  if (e != hipSuccess || splits == 1) return e;
+  return launch_fwd_combine<T, D>(pb, t, splits);
 }
 
-// Query rows per tile (work-group): 128 by default; 64 and 256 on request.
+// Query rows per tile (work-group): 128 by default; 64 and 256 on request;
+// 32 (one wave, 16-bit types) for inference with few queries.
 template <typename T, int D>
 hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
   switch (pb.fwd_rows) {
+    case 32:
+      if constexpr (sizeof(T) == 2) return launch_fwd_t<T, D, 1>(pb, t);
+      else return launch_fwd_t<T, D, 2>(pb, t);
     case 64: return launch_fwd_t<T, D, 2>(pb, t);
     case 256: return launch_fwd_t<T, D, 8>(pb, t);
     default: return launch_fwd_t<T, D, 4>(pb, t);

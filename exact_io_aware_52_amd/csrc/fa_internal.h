@@ -8,7 +8,7 @@
 
 namespace fa {
 
-enum KernelKind { kFwd = 0, kBwdDkDv = 1, kBwdDq = 2, kNumKernelKinds = 3 };
+enum KernelKind { kFwd = 0, kBwdDkDv = 1, kBwdDq = 2, kFwdCombine = 3, kNumKernelKinds = 4 };
 
 struct Problem {
   int B, H, N, d;
@@ -18,7 +18,14 @@ struct Problem {
   const uint8_t* block_mask;  // device, may be null
   int dtype;                  // fa_dtype
   hipStream_t stream;
-  int fwd_rows = 128;         // forward: query rows per work-group (64, 128, 256)
+  int fwd_rows = 128;         // forward: query rows per work-group (32, 64, 128, 256)
+  // Forward of N queries against nk keys (inference): nk < 0 means nk = N.
+  int nk = -1;
+  int causal_br = 0;          // causal aligned bottom-right to the visible key count
+  int splits = 1;             // key-range splits per query tile
+  int chunk = 0;              // keys per split (a multiple of 64)
+  float* opart = nullptr;     // [splits][B*H][N][d] fp32 partial O (splits > 1)
+  float* lpart = nullptr;     // [splits][B*H][N] fp32 partial LSE
 };
 
 struct FwdTensors {

@@ -16,6 +16,12 @@ shapes here):
   ``default_rng(seed + 1_000_003).integers(lo, hi + 1, B)`` (inclusive range);
 * the block mask comes from ``default_rng(seed + 2_000_003).random((nb, nb))
   < p`` with the diagonal forced to 1, nb = ceil(N / block_size).
+
+Inference problems (``make_kv_problem``: Nq new queries against a key/value
+cache of Nk entries) draw Q [B, H, Nq, d], then K and V [B, H, Nk, d], the
+same way; the cache fill per batch comes from
+``default_rng(seed + 1_000_003).integers(lo, hi + 1, B)``.  Cache entries past
+the fill hold ordinary draws, which the method must never see.
 """
 
 from dataclasses import dataclass, field
@@ -98,6 +104,60 @@ def make_problem(B, H, N, d, dtype, seed, causal=False, scale=None,
         block_mask = bm.astype(np.uint8)
     return Problem(B, H, N, d, dtype, bool(causal), np.float32(scale), q, k, v, do,
                    key_lens, block_mask, block_size, seed, name)
+
+
+@dataclass
+class KvProblem:
+    """Nq new queries against a key/value cache of Nk entries, of which the
+    first key_lens[b] are filled (all Nk when key_lens is None)."""
+    B: int
+    H: int
+    Nq: int
+    Nk: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: np.float32
+    q: np.ndarray           # [B, H, Nq, d]
+    k: np.ndarray           # [B, H, Nk, d]
+    v: np.ndarray
+    key_lens: Optional[np.ndarray] = None
+    seed: int = 0
+    name: str = ""
+
+
+def make_kv_problem(B, H, Nq, Nk, d, dtype, seed, causal=True, scale=None, fill_range=None,
+                    name=""):
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    rng = np.random.default_rng(seed)
+    q = round_to_dtype(rng.standard_normal((B, H, Nq, d), dtype=np.float32), dtype)
+    k, v = (round_to_dtype(rng.standard_normal((B, H, Nk, d), dtype=np.float32), dtype)
+            for _ in range(2))
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    key_lens = None
+    if fill_range is not None:
+        lo, hi = fill_range
+        key_lens = np.random.default_rng(seed + 1_000_003).integers(
+            lo, hi + 1, B).astype(np.int32)
+    return KvProblem(B, H, Nq, Nk, d, dtype, bool(causal), np.float32(scale), q, k, v,
+                     key_lens, seed, name)
+
+
+# Inference workloads: one decode step of a batch of sequences against their
+# caches (one new query each, fills between half and all of the capacity), and
+# a chunk of 512 new queries appended to caches of the same kind.
+KV_CONFIGS = {
+    "kv_decode": dict(B=16, H=16, Nq=1, Nk=8192, d=128, dtype="bf16", seed=7, causal=True,
+                      fill_range=(4096, 8192)),
+    "kv_chunk": dict(B=4, H=16, Nq=512, Nk=8192, d=128, dtype="bf16", seed=8, causal=True,
+                     fill_range=(4096, 8192)),
+}
+
+
+def kv_workload(name):
+    return make_kv_problem(name=name, **KV_CONFIGS[name])
 
 
 # The five workloads.  Shapes follow GPT-2-small, BERT-large, long-context

@@ -90,6 +90,35 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
                            fa_dtype dtype, hipStream_t stream);
 
 /*
+ * Inference forward: Nq new queries against a key/value cache of Nk entries
+ * (review page, "Caveats": the kernel later became central to inference
+ * stacks; "Agent Infrastructure Takeaways": for long contexts, memory
+ * traffic and key/value residency dominate the cost).  The pages give no
+ * detail; the reading here: q, o [B,H,Nq,d]; k, v [B,H,Nk,d]; lse [B,H,Nq]
+ * float32.  key_lens (int32[B] on device, or NULL for all Nk) gives the
+ * filled part of each batch's cache, L_b = key_lens[b] clamped to [0, Nk];
+ * keys j >= L_b are never visible.  The queries are the newest Nq positions
+ * of that sequence, so with causal set query i sees key j iff
+ * j <= i + L_b - Nq (aligned bottom-right; with Nq = Nk = L_b this is
+ * fa_forward's causal mask).  A row that sees no key gets O = 0 and
+ * LSE = -inf.  Nk may be 0 (every row sees no key).
+ * With few queries (decode) the key range is split over several
+ * work-groups, whose float32 partial results a second pass merges; they go
+ * to workspace, caller-owned device memory of at least
+ * fa_forward_kv_workspace_bytes(B,H,Nq,Nk,d,dtype) bytes, 16-byte aligned,
+ * need not be initialised.  workspace may be NULL when that size is 0.
+ * Calls that share a workspace must be ordered on one stream.  The tile
+ * height is chosen from Nq (fa_set_forward_block_rows does not apply).
+ */
+int fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int Nq, int Nk, int d, float scale, int causal,
+                  const int32_t* key_lens, fa_dtype dtype, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes fa_forward_kv needs for these sizes (0: none needed). */
+size_t fa_forward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
+
+/*
  * Backward pass (review page, "Method" and claim C7: recompute the attention
  * tiles on chip from the saved normalisation values).  Gradient of
  * L = sum(dout * o): with P = exp(S - LSE), D = rowsum(dout * o),
@@ -141,8 +170,8 @@ const char* fa_last_error_detail(void);
  * fa_timing_read() waits for the recorded events of one kernel kind, returns
  * the summed elapsed milliseconds and the launch count, and clears them.
  * kernel: 0 forward, 1 backward dK/dV, 2 backward dQ (which also forms D
- * and LSE * log2(e) for the dK/dV pass).  Not thread-safe; meant for
- * benchmarks.
+ * and LSE * log2(e) for the dK/dV pass), 3 the merge of split forward
+ * results (fa_forward_kv).  Not thread-safe; meant for benchmarks.
  */
 int fa_timing_enable(int enable);
 int fa_timing_read(int kernel, double* total_ms, int* launches);

@@ -118,9 +118,42 @@ def test_status_strings_and_timing(lib):
     assert lib.fa_kernel_name(0) == b"fa_fwd_kernel"
     ms, n = ctypes.c_double(), ctypes.c_int()
     assert lib.fa_timing_read(2, ctypes.byref(ms), ctypes.byref(n)) == 0
-    assert lib.fa_timing_read(3, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
+    assert lib.fa_timing_read(3, ctypes.byref(ms), ctypes.byref(n)) == 0
+    assert lib.fa_kernel_name(3) == b"fa_fwd_combine_kernel"
+    assert lib.fa_timing_read(4, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
     assert n.value == 0 and ms.value == 0.0
     assert lib.fa_timing_read(9, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
+
+
+def kv(lib, q=FAKE, k=FAKE, B=2, H=3, Nq=1, Nk=1000, d=64, dtype=2, ws=FAKE, ws_bytes=1 << 30,
+       key_lens=None):
+    return lib.fa_forward_kv(q, k, FAKE, FAKE, FAKE, B, H, Nq, Nk, d, 0.1, 1, key_lens, dtype,
+                             ws, ws_bytes, None)
+
+
+def test_forward_kv_validation(lib):
+    W = lib.fa_forward_kv_workspace_bytes
+    # decode against a long cache splits the key range: it needs a workspace
+    need = W(2, 3, 1, 1000, 64, 2)
+    assert need > 0 and need % 256 == 0
+    assert W(2, 3, 1, 1000, 64, 2) == need                      # deterministic plan
+    # enough query tiles already fill the chip: no split, no workspace
+    assert W(8, 16, 1024, 1024, 64, 2) == 0
+    assert W(1, 1, 1, 100, 64, 2) == 0                         # too few keys to split
+    assert W(0, 3, 1, 1000, 64, 2) == 0 and W(2, 3, 1, 0, 64, 2) == 0
+    assert kv(lib, Nk=-1) == _binding.FA_ERR_INVALID_ARG
+    assert kv(lib, d=96) == _binding.FA_ERR_UNSUPPORTED
+    assert kv(lib, dtype=7) == _binding.FA_ERR_INVALID_ARG
+    assert kv(lib, q=None) == _binding.FA_ERR_INVALID_ARG
+    assert kv(lib, k=None) == _binding.FA_ERR_INVALID_ARG
+    assert kv(lib, ws=None) == _binding.FA_ERR_WORKSPACE
+    assert "workspace" in detail(lib)
+    assert kv(lib, ws_bytes=need - 1) == _binding.FA_ERR_WORKSPACE
+    assert kv(lib, ws=BAD_ALIGN) == _binding.FA_ERR_INVALID_ARG
+    assert kv(lib, key_lens=0x10001) == _binding.FA_ERR_INVALID_ARG
+    # empty problems return before touching any pointer
+    assert kv(lib, q=None, Nq=0) == _binding.FA_OK
+    assert kv(lib, q=None, B=0) == _binding.FA_OK
 
 
 def test_forward_block_rows_setting(lib):
