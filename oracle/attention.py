@@ -37,7 +37,10 @@ Readings where the pages are silent (each is also listed in the design notes):
   nothing to any gradient;
 * with nq queries against nk cached keys (inference, ``forward_kv``), the
   queries are the newest nq positions of a sequence of L = key_lens[b] filled
-  cache entries, and causal is aligned bottom-right: j <= i + L - nq.
+  cache entries, and causal is aligned bottom-right: j <= i + L - nq;
+* packed variable-length batches (``forward_varlen``) lay sequences back to
+  back per head, [H, T, d], delimited by prefix sums cu[0..B]; each sequence
+  is the problem above with its own query and key counts.
 
 Everything is float64.  Inputs are the dtype-rounded values the GPU receives,
 upcast; ``scale`` is the float32 value handed to the GPU, upcast.
@@ -203,6 +206,28 @@ def forward_kv(q, k, v, scale, causal=False, key_lens=None, heads=None):
     for b, h in todo:
         kl = None if key_lens is None else int(key_lens[b])
         o[b, h], lse[b, h] = head_forward_kv(q[b, h], k[b, h], v[b, h], scale, causal, kl)
+    return o, lse
+
+
+def forward_varlen(q, k, v, cu_q, cu_k, scale, causal=False):
+    """Packed variable-length forward.  q: [H, Tq, d] and k, v: [H, Tk, d]
+    hold B sequences back to back; sequence b owns query rows
+    cu_q[b] .. cu_q[b+1] - 1 and key rows cu_k[b] .. cu_k[b+1] - 1 of every
+    head.  Each sequence attends only to its own keys, with the visibility
+    of ``visibility_kv`` (nq = its query count, nk = L = its key count, so
+    causal is aligned bottom-right; with equal counts it is top-left).
+    Returns (O [H, Tq, d], LSE [H, Tq]).  Rows outside every sequence are
+    left as NaN."""
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    H, Tq, _ = q.shape
+    o = np.full((H, Tq, v.shape[-1]), np.nan)
+    lse = np.full((H, Tq), np.nan)
+    for b in range(len(cu_q) - 1):
+        q0, q1 = int(cu_q[b]), int(cu_q[b + 1])
+        k0, k1 = int(cu_k[b]), int(cu_k[b + 1])
+        for h in range(H):
+            o[h, q0:q1], lse[h, q0:q1] = head_forward_kv(q[h, q0:q1], k[h, k0:k1], v[h, k0:k1],
+                                                         scale, causal)
     return o, lse
 
 

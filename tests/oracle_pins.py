@@ -349,6 +349,50 @@ def check_kv_decode(orc, n=29, d=6):
     assert np.all(o == 0) and np.all(np.isneginf(lse))
 
 
+def check_varlen(orc, H=3, d=5):
+    # Packed sequences against torch, one sequence at a time: the slices are
+    # taken here from the prefix sums, and torch's lower-right causal bias
+    # (or none) gives each sequence's attention.
+    from torch.nn.attention.bias import causal_lower_right
+    import warnings
+    lq = [4, 0, 9, 1, 6]
+    lk = [7, 3, 9, 0, 2]
+    cq = np.concatenate([[0], np.cumsum(lq)])
+    ck = np.concatenate([[0], np.cumsum(lk)])
+    q = _rand((H, cq[-1], d), 960)
+    k, v = (_rand((H, ck[-1], d), 961 + t) for t in range(2))
+    for causal in (False, True):
+        o, lse = orc.forward_varlen(q, k, v, cq, ck, 0.45, causal=causal)
+        for b in range(len(lq)):
+            rows = slice(cq[b], cq[b + 1])
+            if lq[b] == 0:
+                continue
+            if lk[b] == 0:          # no keys at all: O = 0, LSE = -inf
+                assert np.all(o[:, rows] == 0) and np.all(np.isneginf(lse[:, rows]))
+                continue
+            tq = torch.tensor(q[:, rows])
+            tk, tv = (torch.tensor(x[:, ck[b]:ck[b + 1]]) for x in (k, v))
+            with warnings.catch_warnings():
+                warnings.simplefilter("ignore")
+                mask = causal_lower_right(lq[b], lk[b]) if causal else None
+                to = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask,
+                                                                      scale=0.45)
+            ref = to.numpy()
+            seen = ~np.isnan(ref).any(axis=-1)          # torch gives NaN for rows with no key
+            np.testing.assert_allclose(o[:, rows][seen], ref[seen], atol=1e-12,
+                                       err_msg=f"varlen seq {b} causal {causal}")
+            assert np.all(o[:, rows][~seen] == 0) and np.all(np.isneginf(lse[:, rows][~seen]))
+    # equal lengths: the packed problem is the batched one, head-major
+    B, n = 3, 6
+    qb, kb, vb = (_rand((B, H, n, d), 970 + t) for t in range(3))
+    pack = lambda x: np.ascontiguousarray(x.transpose(1, 0, 2, 3).reshape(H, B * n, d))
+    cu = np.arange(B + 1) * n
+    o, lse = orc.forward_varlen(pack(qb), pack(kb), pack(vb), cu, cu, 0.3, causal=True)
+    ob, lb = orc.forward(qb, kb, vb, 0.3, causal=True)
+    np.testing.assert_allclose(o, pack(ob), atol=1e-14)
+    np.testing.assert_allclose(lse, lb.transpose(1, 0, 2).reshape(H, B * n), atol=1e-14)
+
+
 ALL_PINS = [check_golden, check_finite_differences, check_torch_reference,
             check_invariants, check_special_cases, check_row_chunking, check_rows,
-            check_kv_torch_lower_right, check_kv_decode]
+            check_kv_torch_lower_right, check_kv_decode, check_varlen]

@@ -44,6 +44,11 @@ MUTATIONS = {
                         "vis = np.ones((nq, nk), dtype=bool)"),
     "kv_fill_unclamped": ("L = nk if key_len is None else min(max(int(key_len), 0), nk)",
                           "L = nk if key_len is None else int(key_len)"),
+    "varlen_keys_from_query_offsets": ("k0, k1 = int(cu_k[b]), int(cu_k[b + 1])",
+                                       "k0, k1 = int(cu_q[b]), int(cu_q[b + 1])"),
+    "varlen_end_off_by_one": ("q0, q1 = int(cu_q[b]), int(cu_q[b + 1])",
+                              "q0, q1 = int(cu_q[b]), int(cu_q[b + 1]) - 1"),
+    "varlen_keys_of_next_sequence": ("k[h, k0:k1], v[h, k0:k1]", "k[h, k0:k1], v[h, k1:k1 + k1 - k0]"),
 }
 
 
