@@ -9,7 +9,8 @@ GPT-2-small-shaped causal self-attention (B=8, H=12, N=1024, d=64, bf16).
 Prints one JSON line.  ``value`` is algorithmic forward+backward TFLOP/s
 (14 * d flops per kept query-key pair) of the whole job.  The inference
 workloads (``--config kv_decode`` / ``kv_chunk``: new queries against a
-key/value cache, fa_forward_kv) have no backward: there a step is one
+key/value cache, fa_forward_kv; ``varlen_prefill``: packed sequences of
+several lengths, fa_forward_varlen) have no backward: there a step is one
 inference forward and ``value`` its algorithmic TFLOP/s (4 * d per pair).  ``roofline``
 describes the kernel that takes most of the step, timed with the library's
 per-launch HIP events over a second pass of the same K steps; ``cpu_baseline``
@@ -31,7 +32,8 @@ sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
                                    fa_forward, fa_forward_blocksparse, fa_forward_kv,
-                                   fa_forward_kv_workspace_bytes, fa_kernel_name,
+                                   fa_forward_kv_workspace_bytes, fa_forward_varlen,
+                                   fa_kernel_name,
                                    fa_set_forward_block_rows, fa_timing_enable, fa_timing_read,
                                    inputs)
 
@@ -243,6 +245,100 @@ def bench_kv(args, dev):
     print(json.dumps(result), flush=True)
 
 
+def bench_varlen(args, dev):
+    """One step = one fa_forward_varlen call over a packed batch of causal
+    sequences; roofline against the matrix peak (4 * d flops per kept pair)."""
+    prob = inputs.varlen_workload(args.config)
+    dt = TORCH_DT[prob.dtype]
+    q, k, v = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v))
+    cq, ck = (torch.from_numpy(c).to(dev) for c in (prob.cu_q, prob.cu_k))
+    o = torch.empty_like(q)
+    lse = torch.empty(prob.H, q.shape[1], dtype=torch.float32, device=dev)
+    mq = int(prob.lens_q.max())
+    scale = float(prob.scale)
+
+    def step():
+        fa_forward_varlen(q, k, v, cq, ck, mq, scale=scale, causal=prob.causal, o=o, lse=lse)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
+    fa_timing_enable(True)
+    fa_timing_read("fwd")
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    fa_timing_enable(False)
+    total, n = fa_timing_read("fwd")
+    avg_us = 1e3 * total / max(n, 1)
+    pairs = accounting.varlen_kept_pairs(prob)
+    flops = 4 * prob.d * pairs
+    peak = PEAK_TFLOPS[prob.dtype]
+    achieved = flops / (avg_us * 1e-6) / 1e12
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": read_traffic(KERNEL_NAMES["fwd"], prob.name),
+            "kernel": KERNEL_NAMES["fwd"], "kernel_avg_us": round(avg_us, 2)}
+    result = {
+        "metric": "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": prob.dtype,
+        "data": "synthetic",
+        "config": {"workload": prob.name, "pass": "packed variable-length forward (no backward)",
+                   "H": prob.H, "sequences": prob.B, "total_tokens": int(prob.cu_q[-1]),
+                   "max_seqlen": mq, "d": prob.d, "causal": prob.causal, "parallelism": "none"},
+        "kernels_us": {KERNEL_NAMES["fwd"]: round(avg_us, 2)},
+        "roofline": roof,
+    }
+    if args.cpu_budget > 0:
+        result["cpu_baseline"] = cpu_baseline_varlen(prob, args.cpu_budget)
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline_varlen(prob, budget_s):
+    """The fp64 oracle on (sequence, head) pairs of the same packed batch
+    for about ``budget_s`` seconds; TFLOP/s at 4 * d flops per kept pair."""
+    import oracle   # test infrastructure; used only for this reported baseline
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max((p.get("num_threads", 1) for p in threadpool_info()), default=1)
+    except Exception:   # pragma: no cover
+        threads = os.cpu_count()
+    items = [(b, h) for b in range(prob.B) for h in range(prob.H)]
+    done, pairs = 0, 0
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        b, h = items[done % len(items)]
+        q0, q1, k0, k1 = (int(x) for x in (prob.cu_q[b], prob.cu_q[b + 1], prob.cu_k[b],
+                                          prob.cu_k[b + 1]))
+        oracle.head_forward_kv(prob.q[h, q0:q1].astype(np.float64),
+                               prob.k[h, k0:k1].astype(np.float64),
+                               prob.v[h, k0:k1].astype(np.float64), float(prob.scale),
+                               causal=prob.causal)
+        nq, L = q1 - q0, k1 - k0
+        i = np.arange(nq)
+        pairs += int((np.clip(i + L - nq + 1, 0, L) if prob.causal else np.full(nq, L)).sum())
+        done += 1
+    dt = time.perf_counter() - t0
+    return {"value": 4 * prob.d * pairs / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{done} (sequence, head) pairs of the {len(items)} in the same packed batch, "
+                      f"fp64 forward, {dt:.1f} s"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -250,7 +346,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--config", default="gpt2_small",
                     choices=["tiny", "gpt2_small", "bert_large_padded", "long_causal",
-                             "block_sparse", "block_sparse_long", "kv_decode", "kv_chunk"])
+                             "block_sparse", "block_sparse_long", "kv_decode", "kv_chunk",
+                             "varlen_prefill"])
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--d", type=int, default=64)
     ap.add_argument("--fwd-block-rows", type=int, default=128, choices=[64, 128, 256],
@@ -286,6 +383,9 @@ def main():
 
     if args.config.startswith("kv_"):
         bench_kv(args, dev)
+        return
+    if args.config.startswith("varlen_"):
+        bench_varlen(args, dev)
         return
 
     fa_set_forward_block_rows(args.fwd_block_rows)

@@ -58,9 +58,10 @@ def load_library():
     lib.fa_forward_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, Z, P]
     lib.fa_forward_kv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.fa_forward_kv_workspace_bytes.restype = Z
+    lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_backward,
                lib.fa_timing_enable, lib.fa_timing_read, lib.fa_set_forward_block_rows,
-               lib.fa_get_forward_block_rows, lib.fa_forward_kv):
+               lib.fa_get_forward_block_rows, lib.fa_forward_kv, lib.fa_forward_varlen):
         fn.restype = I
     _LIB = lib
     return lib
@@ -206,6 +207,42 @@ def fa_forward_kv(q, k, v, scale=None, causal=False, key_lens=None, o=None, lse=
                            _DTYPE_CODE[q.dtype], _ptr(workspace),
                            workspace.numel() * workspace.element_size(), _stream(q.device))
     _check("fa_forward_kv", st)
+    return o, lse
+
+
+def fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=None,
+                      causal=False, o=None, lse=None):
+    """Packed variable-length forward: q [H, Tq, d], k and v [H, Tk, d];
+    cu_seqlens_q / cu_seqlens_k int32 [B+1] prefix sums (device or host).
+    Returns (O [H, Tq, d], LSE [H, Tq] float32); rows outside every sequence
+    are left as allocated."""
+    lib = load_library()
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [H, Tq, d] and k, v [H, Tk, d]")
+    H, Tq, d = q.shape
+    Tk = k.shape[1]
+    for name, t in (("k", k), ("v", v)):
+        if tuple(t.shape) != (H, Tk, d) or t.dtype != q.dtype or t.device != q.device:
+            raise ValueError(f"{name} must be [H, Tk, d] with q's dtype and device")
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if q.dtype not in _DTYPE_CODE:
+        raise ValueError(f"unsupported dtype {q.dtype}")
+    if q.device.type != "cuda":
+        raise ValueError("tensors must be on a GPU device (the library has no CPU path)")
+    cq = torch.as_tensor(cu_seqlens_q).to(device=q.device, dtype=torch.int32).contiguous()
+    ck = torch.as_tensor(cu_seqlens_k).to(device=q.device, dtype=torch.int32).contiguous()
+    if cq.dim() != 1 or ck.shape != cq.shape or cq.numel() < 1:
+        raise ValueError("cu_seqlens_q and cu_seqlens_k must both be [B+1]")
+    B = cq.numel() - 1
+    o = torch.empty_like(q) if o is None else _like("o", o, q)
+    lse = (torch.empty((H, Tq), dtype=torch.float32, device=q.device) if lse is None
+           else _like("lse", lse, q, (H, Tq), torch.float32))
+    st = lib.fa_forward_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), _ptr(cq), _ptr(ck),
+                               B, H, Tq, Tk, int(max_seqlen_q), d, _scale(scale, d),
+                               int(bool(causal)), _DTYPE_CODE[q.dtype], _stream(q.device))
+    _check("fa_forward_varlen", st)
     return o, lse
 
 

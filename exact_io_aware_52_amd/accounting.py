@@ -123,3 +123,15 @@ def kv_forward_bytes(prob, splits):
     else:
         out = heads * prob.Nq * (prob.d * s + 4)
     return q + kv + out
+
+
+def varlen_kept_pairs(prob):
+    """Visible pairs of a packed variable-length problem: each sequence
+    counted as an inference problem with its own query and key counts."""
+    total = 0
+    for nq, nk in zip(prob.lens_q, prob.lens_k):
+        i = np.arange(int(nq), dtype=np.int64)
+        L = int(nk)
+        per = np.clip(i + L - int(nq) + 1, 0, L) if prob.causal else np.full(int(nq), L)
+        total += prob.H * int(per.sum())
+    return total

@@ -244,6 +244,40 @@ int fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* l
   return FA_OK;
 }
 
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int B, int H,
+                      int Tq, int Tk, int max_seqlen_q, int d, float scale, int causal,
+                      fa_dtype dtype, hipStream_t stream) {
+  g_detail[0] = 0;
+  if (Tq < 0 || Tk < 0 || max_seqlen_q < 0)
+    return fail(FA_ERR_INVALID_ARG, "negative size Tq=%d Tk=%d max_seqlen_q=%d", Tq, Tk,
+                max_seqlen_q);
+  bool empty = false;
+  int st = check_common(B, H, max_seqlen_q, d, scale, dtype, &empty);
+  if (st != FA_OK) return st;
+  if (empty || Tq == 0) return FA_OK;
+  if (max_seqlen_q > Tq)
+    return fail(FA_ERR_INVALID_ARG, "max_seqlen_q=%d exceeds Tq=%d", max_seqlen_q, Tq);
+  if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(o, "o", 16)) ||
+      (st = check_tensor(lse, "lse", 4)) || (st = check_tensor(cu_seqlens_q, "cu_seqlens_q", 4)) ||
+      (st = check_tensor(cu_seqlens_k, "cu_seqlens_k", 4)))
+    return st;
+  if (Tk > 0 && ((st = check_tensor(k, "k", 16)) || (st = check_tensor(v, "v", 16)))) return st;
+  const int rows = (max_seqlen_q <= 32 && dtype != FA_F32) ? 32 : (max_seqlen_q <= 64 ? 64 : 128);
+  fa::Problem p{B, H, max_seqlen_q, d, scale, causal ? 1 : 0, nullptr, nullptr, (int)dtype, stream,
+                rows};
+  p.nk = Tk;
+  p.causal_br = 1;
+  p.cu_q = cu_seqlens_q;
+  p.cu_k = cu_seqlens_k;
+  p.Tq = Tq;
+  p.Tk = Tk;
+  fa::FwdTensors t{q, k, v, o, lse};
+  hipError_t e = fa::launch_forward(p, t);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
+  return FA_OK;
+}
+
 int fa_set_forward_block_rows(int rows) {
   if (rows != 64 && rows != 128 && rows != 256)
     return fail(FA_ERR_UNSUPPORTED, "forward block rows %d (supported: 64, 128, 256)", rows);

@@ -81,6 +81,13 @@ struct FwdParams {
   int chunk;
   float* opart;
   float* lpart;
+  // Packed variable-length batch (cu_q null: the [B, H, N, d] layout):
+  // sequence b owns rows cu_q[b] .. cu_q[b+1]-1 of Q and O ([H, Tq, d]) and
+  // cu_k[b] .. cu_k[b+1]-1 of K and V ([H, Tk, d]); N is then the longest
+  // query count, which sizes the grid.
+  const int32_t* cu_q;
+  const int32_t* cu_k;
+  int Tq, Tk;
 };
 
 constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 131072)
@@ -175,8 +182,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   int qt, bh;
   map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, qt, bh);
   const int b = bh / p.H;
-  const int N = p.N;    // query rows
-  const int NK = p.nk;  // key rows
+  int N = p.N;    // query rows of this head
+  int NK = p.nk;  // key rows
+  size_t head = (size_t)bh * N * D;    // Q and O rows of this head
+  size_t khead = (size_t)bh * NK * D;  // K and V rows
+  size_t lrow = (size_t)bh * N;        // LSE of query row 0
+  if (p.cu_q) {
+    // Packed sequences: offsets clamped into the tensors, whatever cu holds.
+    const int h = bh - b * p.H;
+    const int q0 = min(max(p.cu_q[b], 0), p.Tq), q1 = min(max(p.cu_q[b + 1], q0), p.Tq);
+    const int k0 = min(max(p.cu_k[b], 0), p.Tk), k1 = min(max(p.cu_k[b + 1], k0), p.Tk);
+    N = q1 - q0;
+    NK = k1 - k0;
+    head = ((size_t)h * p.Tq + q0) * D;
+    khead = ((size_t)h * p.Tk + k0) * D;
+    lrow = (size_t)h * p.Tq + q0;
+    if (qt * BR >= N) return;  // past this sequence's queries: the whole work-group, before any barrier
+  }
   const int i0 = qt * BR;
   const int qw0 = i0 + 32 * w;  // first query of this wave
   const int myq = qw0 + col;
@@ -201,8 +223,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     while (j < nkt && mask_row[(j * BT) / kMaskBlock] == 0) ++j;
     return j;
   };
-  const size_t head = (size_t)bh * N * D;     // Q and O rows of this head
-  const size_t khead = (size_t)bh * NK * D;   // K and V rows
   const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
   const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + khead;
   const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + khead;
@@ -536,7 +556,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         *reinterpret_cast<raw4*>(Og + db * 32 + 8 * g + 4 * hh) = out;
       }
     if (hh == 0) {
-      p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
+      p.lse[lrow + myq] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
     }
   }
 }
@@ -626,6 +646,10 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.chunk = splits > 1 ? pb.chunk : max(p.nk, 1);
   p.opart = splits > 1 ? pb.opart : nullptr;
   p.lpart = splits > 1 ? pb.lpart : nullptr;
+  p.cu_q = pb.cu_q;
+  p.cu_k = pb.cu_k;
+  p.Tq = pb.Tq;
+  p.Tk = pb.Tk;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
   timing_begin(kFwd, pb.stream);
   hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid, splits), dim3(64 * NW), 0, pb.stream,

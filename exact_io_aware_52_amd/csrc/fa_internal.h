@@ -26,6 +26,11 @@ struct Problem {
   int chunk = 0;              // keys per split (a multiple of 64)
   float* opart = nullptr;     // [splits][B*H][N][d] fp32 partial O (splits > 1)
   float* lpart = nullptr;     // [splits][B*H][N] fp32 partial LSE
+  // Packed variable-length batch: Q/O [H, Tq, d], K/V [H, Tk, d], sequence b
+  // at rows cu_q[b] .. and cu_k[b] ..; N is the longest query count and nk = Tk.
+  const int32_t* cu_q = nullptr;
+  const int32_t* cu_k = nullptr;
+  int Tq = 0, Tk = 0;
 };
 
 struct FwdTensors {

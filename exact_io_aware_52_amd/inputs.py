@@ -160,6 +160,67 @@ def kv_workload(name):
     return make_kv_problem(name=name, **KV_CONFIGS[name])
 
 
+@dataclass
+class VarlenProblem:
+    """B sequences packed back to back per head: q [H, Tq, d], k and v
+    [H, Tk, d]; sequence b owns rows cu_q[b] .. cu_q[b+1]-1 and
+    cu_k[b] .. cu_k[b+1]-1."""
+    H: int
+    d: int
+    dtype: str
+    causal: bool
+    scale: np.float32
+    lens_q: np.ndarray
+    lens_k: np.ndarray
+    cu_q: np.ndarray        # int32 [B+1]
+    cu_k: np.ndarray
+    q: np.ndarray
+    k: np.ndarray
+    v: np.ndarray
+    seed: int = 0
+    name: str = ""
+
+    @property
+    def B(self):
+        return len(self.lens_q)
+
+
+def make_varlen_problem(H, d, dtype, seed, lens_q=None, lens_k=None, len_range=None, B=None,
+                        causal=True, scale=None, name=""):
+    """Sequence lengths are given, or drawn from
+    default_rng(seed + 1_000_003).integers(lo, hi + 1, B) (keys: the same
+    lengths, self-attention, unless lens_k is given); then Q [H, Tq, d], K and
+    V [H, Tk, d] are drawn from default_rng(seed) in that order."""
+    if dtype not in DTYPES:
+        raise ValueError(f"unknown dtype {dtype!r}")
+    if lens_q is None:
+        lo, hi = len_range
+        lens_q = np.random.default_rng(seed + 1_000_003).integers(lo, hi + 1, B)
+    lens_q = np.asarray(lens_q, dtype=np.int64)
+    lens_k = lens_q.copy() if lens_k is None else np.asarray(lens_k, dtype=np.int64)
+    cu_q = np.concatenate([[0], np.cumsum(lens_q)]).astype(np.int32)
+    cu_k = np.concatenate([[0], np.cumsum(lens_k)]).astype(np.int32)
+    rng = np.random.default_rng(seed)
+    q = round_to_dtype(rng.standard_normal((H, int(cu_q[-1]), d), dtype=np.float32), dtype)
+    k, v = (round_to_dtype(rng.standard_normal((H, int(cu_k[-1]), d), dtype=np.float32), dtype)
+            for _ in range(2))
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    return VarlenProblem(H, d, dtype, bool(causal), np.float32(scale), lens_q, lens_k, cu_q, cu_k,
+                         q, k, v, seed, name)
+
+
+# Packed variable-length prefill: 16 causal sequences of 128 to 4096 tokens.
+VARLEN_CONFIGS = {
+    "varlen_prefill": dict(H=16, d=128, dtype="bf16", seed=9, len_range=(128, 4096), B=16,
+                           causal=True),
+}
+
+
+def varlen_workload(name):
+    return make_varlen_problem(name=name, **VARLEN_CONFIGS[name])
+
+
 # The five workloads.  Shapes follow GPT-2-small, BERT-large, long-context
 # (Long Range Arena / Path-X lengths) and long-context block-sparse attention.
 LONG_POINTS = [(n, d) for n in (2048, 4096, 8192, 16384) for d in (64, 128)]

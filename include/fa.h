@@ -119,6 +119,26 @@ int fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* l
 size_t fa_forward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype dtype);
 
 /*
+ * Packed variable-length forward (same passages as fa_forward_kv): B
+ * sequences of different lengths stored back to back without padding.
+ * q, o: [H, Tq, d]; k, v: [H, Tk, d]; lse: [H, Tq] float32 (head-major, like
+ * the [B,H,N,d] layout with the batch folded into the rows).  cu_seqlens_q
+ * and cu_seqlens_k: int32[B+1] on device, prefix sums starting at 0:
+ * sequence b owns query rows cu_seqlens_q[b] .. cu_seqlens_q[b+1]-1 and key
+ * rows cu_seqlens_k[b] .. cu_seqlens_k[b+1]-1 of every head, and attends to
+ * its own keys only, with fa_forward_kv's visibility (nq, nk = its own
+ * counts; causal aligned bottom-right, top-left when they are equal).
+ * Offsets are clamped into [0, Tq] / [0, Tk] on the device.  max_seqlen_q
+ * must be at least every sequence's query count (it sizes the grid; query
+ * rows of a longer sequence past it, rounded up to the tile, are not
+ * written).  Rows outside every sequence are not written.  No workspace.
+ */
+int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                      const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
+                      int B, int H, int Tq, int Tk, int max_seqlen_q, int d, float scale,
+                      int causal, fa_dtype dtype, hipStream_t stream);
+
+/*
  * Backward pass (review page, "Method" and claim C7: recompute the attention
  * tiles on chip from the saved normalisation values).  Gradient of
  * L = sum(dout * o): with P = exp(S - LSE), D = rowsum(dout * o),

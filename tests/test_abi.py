@@ -156,6 +156,26 @@ def test_forward_kv_validation(lib):
     assert kv(lib, q=None, B=0) == _binding.FA_OK
 
 
+def varlen(lib, q=FAKE, k=FAKE, cq=FAKE, ck=FAKE, B=3, H=2, Tq=100, Tk=100, mq=50, d=64, dtype=2):
+    return lib.fa_forward_varlen(q, k, FAKE, FAKE, FAKE, cq, ck, B, H, Tq, Tk, mq, d, 0.1, 1,
+                                 dtype, None)
+
+
+def test_forward_varlen_validation(lib):
+    assert varlen(lib, Tk=-1) == _binding.FA_ERR_INVALID_ARG
+    assert varlen(lib, mq=-2) == _binding.FA_ERR_INVALID_ARG
+    assert varlen(lib, mq=101) == _binding.FA_ERR_INVALID_ARG
+    assert "max_seqlen_q" in detail(lib)
+    assert varlen(lib, cq=None) == _binding.FA_ERR_INVALID_ARG
+    assert varlen(lib, ck=0x10002) == _binding.FA_ERR_INVALID_ARG
+    assert varlen(lib, k=None) == _binding.FA_ERR_INVALID_ARG
+    assert varlen(lib, d=80) == _binding.FA_ERR_UNSUPPORTED
+    # empty problems return before touching any pointer
+    assert varlen(lib, q=None, cq=None, Tq=0, mq=0) == _binding.FA_OK
+    assert varlen(lib, q=None, cq=None, B=0) == _binding.FA_OK
+    assert varlen(lib, q=None, cq=None, mq=0) == _binding.FA_OK
+
+
 def test_forward_block_rows_setting(lib):
     assert lib.fa_get_forward_block_rows() == 128
     for bad in (0, 32, 96, 512, -128):

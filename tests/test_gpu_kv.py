@@ -109,3 +109,82 @@ def test_kv_config_full(name):
         heads = sorted({(int(rng.integers(prob.B)), int(rng.integers(prob.H))) for _ in range(8)})
     compare(gpu, run_oracle_kv(prob, heads=heads), TOL[prob.dtype], heads=heads,
             label=f"kv {name}")
+
+
+# ----------------------------------------------------------------------------- packed varlen
+
+def run_gpu_varlen(prob, o=None):
+    from exact_io_aware_52_amd import fa_forward_varlen
+    q, k, v = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v))
+    cq, ck = (torch.from_numpy(c).cuda() for c in (prob.cu_q, prob.cu_k))
+    out, lse = fa_forward_varlen(q, k, v, cq, ck, int(prob.lens_q.max(initial=0)),
+                                 scale=float(prob.scale), causal=prob.causal, o=o)
+    torch.cuda.synchronize()
+    return {"o": out.double().cpu().numpy(), "lse": lse.double().cpu().numpy()}
+
+
+def run_oracle_varlen(prob, heads=None):
+    hs = slice(None) if heads is None else list(heads)
+    o, lse = oracle.forward_varlen(*(x[hs].astype(np.float64) for x in (prob.q, prob.k, prob.v)),
+                                   prob.cu_q, prob.cu_k, float(prob.scale), causal=prob.causal)
+    return {"o": o, "lse": lse}
+
+
+VARLEN_CASES = [
+    # H, d, dtype, causal, lens_q, lens_k (None: same as lens_q)
+    (2, 64, "bf16", True, [0, 1, 37, 300, 129, 64], None),
+    (2, 64, "bf16", False, [200, 3, 0, 65], None),
+    (1, 128, "fp16", True, [5, 100, 0, 64, 40], [200, 50, 10, 0, 40]),   # rows without keys
+    (3, 128, "bf16", True, [31, 33, 17], [1000, 20, 17]),                # 64-row tiles
+    (2, 64, "fp32", True, [70, 1, 129], None),
+    (1, 128, "fp32", False, [10, 300], [300, 10]),
+]
+
+
+@pytest.mark.parametrize("case", VARLEN_CASES, ids=lambda c: "H{}d{}_{}_{}_{}seqs".format(
+    c[0], c[1], c[2], "causal" if c[3] else "full", len(c[4])))
+def test_varlen_small(case):
+    H, d, dtype, causal, lq, lk = case
+    prob = inputs.make_varlen_problem(H, d, dtype, seed=500 + sum(lq), lens_q=lq, lens_k=lk,
+                                      causal=causal)
+    log(f"[varlen] {case}")
+    compare(run_gpu_varlen(prob), run_oracle_varlen(prob), TOL[dtype], label=f"varlen {case}")
+
+
+def test_varlen_rows_outside_sequences_untouched():
+    # Tq holds 7 rows past the last sequence: they keep what the caller put there.
+    prob = inputs.make_varlen_problem(2, 64, "bf16", seed=61, lens_q=[50, 130], causal=True)
+    extra = 7
+    prob.q = np.concatenate([prob.q, np.zeros((2, extra, 64), np.float32)], axis=1)
+    sentinel = torch.full((2, prob.q.shape[1], 64), 3.0, dtype=torch.bfloat16, device="cuda")
+    got = run_gpu_varlen(prob, o=sentinel)
+    assert np.all(got["o"][:, -extra:] == 3.0)
+    ref = run_oracle_varlen(prob)
+    ref["o"], ref["lse"] = ref["o"][:, :-extra], ref["lse"][:, :-extra]
+    got["o"], got["lse"] = got["o"][:, :-extra], got["lse"][:, :-extra]
+    compare(got, ref, TOL["bf16"], label="varlen tail")
+
+
+@pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "fp16")])
+def test_varlen_equal_lengths_equal_batched(d, dtype):
+    # Equal lengths: the packed problem is fa_forward's batched one, bit for bit.
+    B, H, n = 3, 2, 200
+    prob = inputs.make_varlen_problem(H, d, dtype, seed=62, lens_q=[n] * B, causal=True)
+    q, k, v = (dev(x, dtype) for x in (prob.q, prob.k, prob.v))
+    unpack = lambda t: t.reshape(H, B, n, d).transpose(0, 1).contiguous()
+    o, lse = fa_forward(unpack(q), unpack(k), unpack(v), scale=float(prob.scale), causal=True)
+    got = run_gpu_varlen(prob)
+    ob = o.transpose(0, 1).reshape(H, B * n, d).double().cpu().numpy()
+    lb = lse.transpose(0, 1).reshape(H, B * n).double().cpu().numpy()
+    assert np.array_equal(got["o"], ob) and np.array_equal(got["lse"], lb)
+
+
+def test_varlen_config_full():
+    # The packed prefill workload at full size, the launch the bench times; the
+    # oracle recomputes three heads over every sequence.
+    prob = inputs.varlen_workload("varlen_prefill")
+    gpu = run_gpu_varlen(prob)
+    heads = [0, 7, 15]
+    ref = run_oracle_varlen(prob, heads=heads)
+    gpu = {n: t[heads] for n, t in gpu.items()}
+    compare(gpu, ref, TOL[prob.dtype], label="varlen_prefill (heads 0, 7, 15)")
