@@ -392,23 +392,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  // Store dK = scale * (dK^T)^T and dV; lane owns key `myk`, rows d of its half.
-  if (myk < N) {
-    raw* dKg = reinterpret_cast<raw*>(p.dk) + head + (size_t)myk * D;
-    raw* dVg = reinterpret_cast<raw*>(p.dv) + head + (size_t)myk * D;
+  // Store dK = scale * dK and dV.  A lane holds four consecutive d of one key
+  // (key `myk`), so storing straight from the accumulators makes every
+  // instruction write 16 bytes into each of 32 rows; lines that leave L2 half
+  // written cost HBM a read and a write each (measured at N = 1K: 1.7x the
+  // dK, dV bytes written and as much again fetched).  Each tensor goes through
+  // LDS instead (the ring is idle by now), one at a time, and is stored as
+  // whole rows: every store instruction writes 64 lanes x 16 bytes of
+  // complete rows.
+  {
+    constexpr int RB = D * (int)sizeof(raw);  // bytes per row
+    constexpr int RS = RB + 16;               // padded LDS row stride
+    constexpr int CPR = RB / 16;              // 16-byte chunks per row
+    constexpr int RPI = 64 / CPR;             // rows per store instruction
+    static_assert(4 * 32 * RS <= L::NS * L::SLOT_BYTES, "staging fits in the ring");
+    char* const stage = ring + w * 32 * RS;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+    for (int t = 0; t < 2; ++t) {
+      __syncthreads();  // no wave reads the ring (or the previous tensor) any more
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        raw4 ok, ov;
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          ok[u] = __builtin_bit_cast(raw, (T)(dk_acc[db][4 * g + u] * p.scale));
-          ov[u] = __builtin_bit_cast(raw, (T)dv_acc[db][4 * g + u]);
+        for (int g = 0; g < 4; ++g) {
+          raw4 r4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            r4[u] = __builtin_bit_cast(raw, t == 0 ? (T)(dk_acc[db][4 * g + u] * p.scale)
+                                                   : (T)dv_acc[db][4 * g + u]);
+          *reinterpret_cast<raw4*>(stage + col * RS + (db * 32 + 8 * g + 4 * hh) * (int)sizeof(raw)) =
+              r4;
         }
-        *reinterpret_cast<raw4*>(dKg + db * 32 + 8 * g + 4 * hh) = ok;
-        *reinterpret_cast<raw4*>(dVg + db * 32 + 8 * g + 4 * hh) = ov;
+      __syncthreads();
+      char* const out = reinterpret_cast<char*>(t == 0 ? p.dk : p.dv) + head * sizeof(raw);
+#pragma unroll
+      for (int r0 = 0; r0 < 32; r0 += RPI) {
+        const int r = r0 + lane / CPR, c = lane % CPR;
+        if (kw0 + r < N)
+          *reinterpret_cast<uint4*>(out + (size_t)(kw0 + r) * RB + c * 16) =
+              *reinterpret_cast<const uint4*>(stage + r * RS + c * 16);
       }
+    }
   }
 }
 
