@@ -63,6 +63,7 @@ struct BwdParams {
   const int32_t* key_lens;
   const uint8_t* block_mask;
   int H, N, BH, nblk;
+  int hgroup;  // heads per XCD dispatched together (map_tile)
   float scale;
   float c;  // scale * log2(e)
   int causal;
@@ -115,7 +116,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const int nkt = (N + BK - 1) / BK;
 
   int kt, bh;
-  map_tile(blockIdx.x, nkt, p.BH, false, kt, bh);
+  map_tile(blockIdx.x, nkt, p.BH, false, p.hgroup, kt, bh);
   const int b = bh / p.H;
   const int j0 = kt * BK;
   const int kw0 = j0 + 32 * w;  // first key of this wave
@@ -473,7 +474,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const int nq = (N + BR - 1) / BR;
 
   int qt, bh;
-  map_tile(blockIdx.x, nq, p.BH, p.causal != 0, qt, bh);
+  map_tile(blockIdx.x, nq, p.BH, p.causal != 0, p.hgroup, qt, bh);
   const int b = bh / p.H;
   const int i0 = qt * BR;
   const int qw0 = i0 + 32 * w;
@@ -645,6 +646,8 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   p.N = pb.N;
   p.BH = pb.B * pb.H;
   p.nblk = (pb.N + kMaskBlock - 1) / kMaskBlock;
+  // each pass streams two [N, d] operands per head (K and V, or Q and dO)
+  p.hgroup = head_group(p.BH, 2LL * pb.N * pb.d * (long long)sizeof(raw_t<T>));
   p.scale = pb.scale;
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;

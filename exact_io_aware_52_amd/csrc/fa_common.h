@@ -302,15 +302,22 @@ __device__ __forceinline__ frag_t<T> load_frag_tr(const raw_t<T>* tile, int k0, 
 // Work-group id -> (tile, head) for a grid of ntiles * BH work-groups.
 // Work-groups are dispatched round-robin over the 8 XCDs (id % 8); when BH is a
 // multiple of 8 every tile of one head is kept on one XCD so that its K/V (or
-// Q/dO) re-reads hit that XCD's L2.  With reverse set, tiles are handed out
-// from the last (heaviest under a causal mask) to the first.
-__device__ __forceinline__ void map_tile(int bid, int ntiles, int BH, bool reverse,
+// Q/dO) re-reads hit that XCD's L2.  Each XCD takes its BH / 8 heads in
+// groups of `group` heads (all of them when group >= BH / 8), and within a
+// group hands out the heads' tiles by tile index: with reverse set from the
+// last (heaviest under a causal mask) to the first.  Groups bound how many
+// heads' streamed operands share the XCD's L2 at a time.
+__device__ __forceinline__ void map_tile(int bid, int ntiles, int BH, bool reverse, int group,
                                          int& tile, int& bh) {
   int ti;
   if ((BH & 7) == 0) {
     const int xcd = bid & 7, slot = bid >> 3, hpx = BH >> 3;
-    ti = slot / hpx;
-    bh = (slot - ti * hpx) * 8 + xcd;
+    const int G = group > 0 && group < hpx ? group : hpx;
+    const int g = slot / (G * ntiles);          // groups before this one are full
+    const int r = slot - g * G * ntiles;
+    const int Gg = min(G, hpx - g * G);         // heads in this group
+    ti = r / Gg;
+    bh = (g * G + (r - ti * Gg)) * 8 + xcd;
   } else {
     ti = bid / BH;
     bh = bid - ti * BH;

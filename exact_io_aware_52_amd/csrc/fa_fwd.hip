@@ -67,6 +67,7 @@ struct FwdParams {
   const int32_t* key_lens;
   const uint8_t* block_mask;
   int H, N, BH, nq, nblk;  // N: query rows per head; nq: query tiles per head
+  int hgroup;              // heads per XCD dispatched together (map_tile)
   int nk;                  // key (and value) rows per head: N for self-attention
   float scale;
   float c;  // scale * log2(e): exponents are taken base 2
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   const int hh = lane >> 5;
 
   int qt, bh;
-  map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, qt, bh);
+  map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, p.hgroup, qt, bh);
   const int b = bh / p.H;
   int N = p.N;    // query rows of this head
   int NK = p.nk;  // key rows
@@ -636,6 +637,9 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.N = pb.N;
   p.nk = pb.nk < 0 ? pb.N : pb.nk;
   p.BH = pb.B * pb.H;
+  // K and V stream through every query tile of a head
+  p.hgroup = head_group(p.BH, 2LL * (pb.cu_q ? (pb.Tk + pb.B - 1) / std::max(pb.B, 1) : p.nk) * D *
+                                  (long long)sizeof(raw_t<T>));
   p.nq = (pb.N + BR - 1) / BR;
   p.nblk = (pb.N + kMaskBlock - 1) / kMaskBlock;
   p.scale = pb.scale;

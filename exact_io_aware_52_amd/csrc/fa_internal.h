@@ -33,6 +33,18 @@ struct Problem {
   int Tq = 0, Tk = 0;
 };
 
+// Heads per XCD dispatched together (map_tile's group).  The XCDs of MI355X
+// each hold 4 MB of L2: when an XCD's BH / 8 heads stream more than that per
+// sweep, their re-reads would miss it, so heads go two at a time (measured:
+// pairs beat groups of 3 or 4 and the ungrouped order there, and lose to the
+// ungrouped order when everything fits).
+inline int head_group(int BH, long long streamed_bytes_per_head) {
+  const int hpx = BH / 8;
+  if (BH % 8 != 0 || hpx <= 2) return hpx;
+  if ((long long)hpx * streamed_bytes_per_head <= (4LL << 20)) return hpx;
+  return 2;
+}
+
 struct FwdTensors {
   const void* q;
   const void* k;
