@@ -188,3 +188,13 @@ def test_varlen_config_full():
     ref = run_oracle_varlen(prob, heads=heads)
     gpu = {n: t[heads] for n, t in gpu.items()}
     compare(gpu, ref, TOL[prob.dtype], label="varlen_prefill (heads 0, 7, 15)")
+
+
+def test_kv_longest_cache_most_splits():
+    # One query against 131072 cache entries: the plan's cap of 64 key-range
+    # splits, merged by the second pass.
+    prob = inputs.make_kv_problem(1, 2, 1, 131072, 128, "bf16", seed=63, fill_range=(100000, 131072))
+    s = splits_of(prob)
+    log(f"[kv] longest cache splits={s}")
+    assert s == 64
+    compare(run_gpu_kv(prob), run_oracle_kv(prob), TOL["bf16"], label="kv 131072")

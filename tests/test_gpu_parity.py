@@ -290,3 +290,38 @@ def test_config_block_sparse_long(n):
             bound_k = 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0)))
             assert np.all(dev_k <= bound_k), (b, h, "sum dK", dev_k.max(), bound_k.min())
     log(f"[parity] block_sparse_long N={n}: dK, dV sums within bounds on all heads")
+
+
+# ----------------------------------------------------------------------------- maximum sizes
+
+def test_max_block_mask_length():
+    # N = 131072: the longest sequence whose block-mask row (1024 blocks) the
+    # kernels cache on chip.  Sampled rows of O, LSE and dQ against the
+    # oracle's row function; dK, dV through their sum identities.
+    n = 131072
+    prob = inputs.make_problem(1, 1, n, 64, "bf16", seed=91, block_keep_p=1 / 128, block_band=1)
+    gpu = run_gpu(prob)
+    rng = np.random.default_rng(12)
+    rows = np.unique(np.concatenate([[0, 127, 128, n // 2, n - 129, n - 128, n - 1],
+                                     rng.integers(0, n, 9)]))
+    o, lse, dq = oracle.head_rows(*(x[0, 0].astype(np.float64) for x in (prob.q, prob.k, prob.v, prob.do)),
+                                  float(prob.scale), rows, block_mask=prob.block_mask,
+                                  block_size=prob.block_size)
+    got = {k: gpu[k][0, 0][rows] for k in ("o", "lse", "dq")}
+    compare(got, {"o": o, "lse": lse, "dq": dq}, TOL["bf16"], label=f"N={n} block mask, sampled rows")
+    u = 2.0 ** -8
+    dv, dk, do = gpu["dv"][0, 0], gpu["dk"][0, 0], prob.do[0, 0].astype(np.float64)
+    dev_v = np.abs(dv.sum(axis=0) - do.sum(axis=0))
+    assert np.all(dev_v <= 6 * u * (np.sqrt((dv ** 2).sum(axis=0)) + np.sqrt((do ** 2).sum(axis=0))))
+    q, ov = prob.q[0, 0].astype(np.float64), gpu["o"][0, 0]
+    spread = float(prob.scale) * np.sqrt(((np.abs(q) * (np.abs(do) * np.abs(ov)).sum(axis=1, keepdims=True) * u) ** 2).sum(axis=0))
+    assert np.all(np.abs(dk.sum(axis=0)) <= 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0))))
+
+
+def test_many_heads():
+    # 4096 (b, h) heads of 130 rows (a ragged second tile): the largest grids of
+    # the five workloads have ~2K work-groups; this launches 8K per pass.
+    prob = inputs.make_problem(64, 64, 130, 64, "bf16", seed=92, causal=True)
+    gpu = run_gpu(prob)
+    heads = [(0, 0), (7, 63), (31, 5), (63, 63), (40, 17)]
+    compare(gpu, run_oracle(prob, heads=heads), TOL["bf16"], heads, label="4096 heads")
