@@ -343,6 +343,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (tl[0] < t_end) {
     issue(tl[0], 0);
     if (tl[1] < t_end) issue(tl[1], 1);
+    // The K and V fragments arrived by ordinary loads issued before these
+    // copies.  Waiting for everything once here tells the compiler they have
+    // landed; otherwise it waits for them (vmcnt(0)) at their first use
+    // inside the loop, on every step, which also stalls on the tile just
+    // requested.
+    wait_vmcnt<0>();
     // Dense interior: every wave's keys see tile t in full, and tiles t+1,
     // t+2 are whole.
     int lo = t_end, hi = -1;
@@ -602,6 +608,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     issue(tl[0], 0);
     if (tl[1] < nkt) issue(tl[1], 1);
     if (tl[2] < nkt) issue(tl[2], 2);
+    // As in the dK/dV pass: the Q and dO fragments came by ordinary loads;
+    // wait for them here, once, rather than inside the loop.
+    wait_vmcnt<0>();
     int step = 0;
     while (true) {
       wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));

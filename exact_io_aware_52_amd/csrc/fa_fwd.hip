@@ -441,6 +441,11 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int k = 0; k < PD; ++k)
       if (tl[k] < nkt) issue(tl[k], k);
+    // The Q fragments arrived by ordinary loads issued before these copies.
+    // Waiting for everything once here tells the compiler they have landed;
+    // otherwise it waits for them (vmcnt(0)) at their first use inside the
+    // loop, on every step, which also stalls on the tiles just requested.
+    wait_vmcnt<0>();
     int cur = 0, nxt = PD;  // ring slots of tile i and of tile i + PD
     // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
     int lo = nkt, hi = -1;
