@@ -20,9 +20,14 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip"]
-# Sources compiled without the VGPR-form matrix-core option: with it, LLVM's
-# "Rewrite AGPR-Copy-MFMA" pass crashes on the fp32 backward instances.
-NO_VGPR_FORM = {"fa_bwd_f32.hip"}
+# Sources compiled without the VGPR-form matrix-core option.  fp32 backward:
+# with it, LLVM's "Rewrite AGPR-Copy-MFMA" pass crashes.  16-bit backward: the
+# d = 128 dK/dV pass (one wave per SIMD, 474 registers) keeps its dK and dV
+# accumulators in AGPRs; in VGPR form the compiler copies them between the
+# two register files around every product (~150 copies per step against 64
+# AGPR reads of the softmax without it; 7% faster without).  The other
+# backward kernels measure the same either way.
+NO_VGPR_FORM = {"fa_bwd_f32.hip", "fa_bwd.hip"}
 ARCH = "gfx950"
 
 # Packed fp32 VALU instructions are switched off for all device code.

@@ -90,6 +90,11 @@ struct DkDvCfg {
   // per SIMD, 256 VGPRs).
   static constexpr bool PREFETCH = true;
   static constexpr int GK = D == 64 ? 2 : 4;
+  // One wave per SIMD (16-bit, d = 128): no other wave overlaps this one's
+  // softmax with matrix work, so the step interleaves them itself (the
+  // softmax of query block 0 beside the score products of block 1, that of
+  // block 1 beside the first gradient products).
+  static constexpr bool ILV = D == 128 && sizeof(raw) == 2;
 };
 
 template <typename T, int D>
@@ -333,6 +338,119 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     const int qi0 = t * BQ;
     return (p.causal && kw0 + 31 > qi0) || (kw0 + 32 > kend) || (qi0 + BQ > N);
   };
+  // The whole step (sdp, soft, to_frags, grads) with the softmax of each
+  // query block placed beside independent matrix products of the same wave:
+  //   score groups of block 1   + softmax of block 0 (halves 0, 1)
+  //   gradient products qc 0, 1 + softmax of block 1 (halves 0, 1)
+  // Half t of a block is its accumulator registers 8t .. 8t+7, which is
+  // exactly the B operand pf / sf[2 qb + t] of the gradient products.
+  auto step_ilv = [&](const char* slot, int qi0, bool msk) {
+    static_assert(!L::ILV || (BQ == 64 && L::PREFETCH), "interleaved step: two 32-query blocks");
+    const raw* Qs = reinterpret_cast<const raw*>(slot);
+    const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
+    const float* dns = lse2s + 64;
+    qblk sacc, pacc;
+    qfrag pf, sf;
+    auto soft_half = [&](int qb, int t) {
+#pragma unroll
+      for (int g = 2 * t; g < 2 * t + 2; ++g) {
+        const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g + u;
+          float pr = fast_exp2(fmaf(sacc[qb][r], c, -lv[u]));
+          if (msk) {
+            const int qi = qi0 + r0 + u;
+            if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
+          }
+          sacc[qb][r] = pr;                // P
+          pacc[qb][r] = pr * pacc[qb][r];  // dS = P (dP - D)
+        }
+      }
+      pf[2 * qb + t] = acc_to_frag<T>(sacc[qb], t);
+      sf[2 * qb + t] = acc_to_frag<T>(pacc[qb], t);
+    };
+    constexpr int GK = L::GK, NG = D / 16 / GK, NGRP = BQ / 32 * NG;
+    // Matrix products of a region (NP of them: 2 GK score products or
+    // 2 D / 32 gradient products), one at a time, each followed by a share
+    // of the region's vector work (a softmax half: about 36 instructions),
+    // with its two LSE reads first.
+    constexpr int NP = 2 * GK;
+    static_assert(!L::ILV || (NG == 2 && NP == 2 * (D / 32)), "one softmax half per region");
+    auto interleave = [&]() {
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < NP; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x002, (36 + NP - 1) / NP, 0);
+      }
+    };
+    frag_t<T> fq[2][GK], fd[2][GK];
+    auto ld = [&](int g, int b) {
+      const int qb = g / NG, k0 = (g % NG) * GK;
+#pragma unroll
+      for (int j = 0; j < GK; ++j) {
+        fq[b][j] = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, (k0 + j) * 16 + hh * 8);
+        fd[b][j] = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, (k0 + j) * 16 + hh * 8);
+      }
+    };
+    frag_t<T> ga[2][D / 32], gq[2][D / 32];
+    auto gld = [&](int qc, int b) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        ga[b][db] = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
+        gq[b][db] = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
+      }
+    };
+    ld(0, 0);
+    f32x16 dneg;
+#pragma unroll
+    for (int g = 0; g < NGRP; ++g) {
+      const int qb = g / NG, k0 = (g % NG) * GK;
+      if (k0 == 0) {
+#pragma unroll
+        for (int g4 = 0; g4 < 4; ++g4) {
+          const float4 d4 = *reinterpret_cast<const float4*>(dns + qb * 32 + 8 * g4 + 4 * hh);
+          dneg[4 * g4] = d4.x;
+          dneg[4 * g4 + 1] = d4.y;
+          dneg[4 * g4 + 2] = d4.z;
+          dneg[4 * g4 + 3] = d4.w;
+        }
+      }
+      if (g + 1 < NGRP) ld(g + 1, (g + 1) & 1);
+      else gld(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 0; j < GK; ++j) {
+        const int kc = k0 + j;
+        sacc[qb] = Tr::mma(fq[g & 1][j], kf[kc], kc == 0 ? zero16() : sacc[qb]);
+        pacc[qb] = Tr::mma(fd[g & 1][j], vf[kc], kc == 0 ? dneg : pacc[qb]);  // dP - D
+      }
+      if (qb == 1) {
+        soft_half(0, g % NG);
+        interleave();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#pragma unroll
+    for (int qc = 0; qc < BQ / 16; ++qc) {
+      if (qc + 1 < BQ / 16) gld(qc + 1, (qc + 1) & 1);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        dv_acc[db] = Tr::mma(ga[qc & 1][db], pf[qc], dv_acc[db]);
+        dk_acc[db] = Tr::mma(gq[qc & 1][db], sf[qc], dk_acc[db]);
+      }
+      if (qc < 2) {
+        soft_half(1, qc);
+        interleave();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
   // Kept query tiles in order; tl[k] is the tile of step i + k.  Step i
   // forms S and dP of tile i, its softmax, then the dV, dK products.
@@ -369,12 +487,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         if (w < 2)
           dma4s((uint32_t)(qn + lane) * 4u, w == 0 ? (const void*)lse2g : (const void*)dvecg,
                 base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
-        qblk sacc, pacc;
-        qfrag pf, sf;
-        sdp(slot_of(step), sacc, pacc);
-        soft(slot_of(step), t * BQ, false, sacc, pacc);
-        to_frags(sacc, pacc, pf, sf);
-        grads(slot_of(step), pf, sf);
+        if constexpr (L::ILV) {
+          step_ilv(slot_of(step), t * BQ, false);
+        } else {
+          qblk sacc, pacc;
+          qfrag pf, sf;
+          sdp(slot_of(step), sacc, pacc);
+          soft(slot_of(step), t * BQ, false, sacc, pacc);
+          to_frags(sacc, pacc, pf, sf);
+          grads(slot_of(step), pf, sf);
+        }
         tl[0] = t + 1;
         tl[1] = t + 2;
         tl[2] = min(t + 3, t_end);
@@ -383,12 +505,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
         if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
         if (active(t)) {
-          qblk sacc, pacc;
-          qfrag pf, sf;
-          sdp(slot_of(step), sacc, pacc);
-          soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
-          to_frags(sacc, pacc, pf, sf);
-          grads(slot_of(step), pf, sf);
+          if constexpr (L::ILV) {
+            step_ilv(slot_of(step), t * BQ, masked(t));
+          } else {
+            qblk sacc, pacc;
+            qfrag pf, sf;
+            sdp(slot_of(step), sacc, pacc);
+            soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
+            to_frags(sacc, pacc, pf, sf);
+            grads(slot_of(step), pf, sf);
+          }
         }
         tl[0] = tl[1];
         tl[1] = tl[2];
