@@ -33,7 +33,7 @@ sys.path.insert(0, ROOT)
 from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
                                    fa_forward, fa_forward_blocksparse, fa_forward_kv,
                                    fa_forward_kv_workspace_bytes, fa_forward_varlen,
-                                   fa_kernel_name,
+                                   fa_forward_block_rows_for, fa_kernel_name,
                                    fa_set_forward_block_rows, fa_timing_enable, fa_timing_read,
                                    inputs)
 
@@ -350,8 +350,8 @@ def main():
                              "varlen_prefill"])
     ap.add_argument("--n", type=int, default=4096)
     ap.add_argument("--d", type=int, default=64)
-    ap.add_argument("--fwd-block-rows", type=int, default=128, choices=[64, 128, 256],
-                    help="query rows per forward work-group (tile height)")
+    ap.add_argument("--fwd-block-rows", type=int, default=0, choices=[0, 64, 128, 256],
+                    help="query rows per forward work-group (tile height); 0 = chosen per problem")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of host work for the oracle baseline (0 disables)")
     ap.add_argument("--copy-calib", action="store_true",
@@ -390,6 +390,8 @@ def main():
 
     fa_set_forward_block_rows(args.fwd_block_rows)
     prob = make_workload(args)
+    fwd_rows = fa_forward_block_rows_for(prob.B, prob.H, prob.N, prob.d, TORCH_DT[prob.dtype],
+                                         prob.block_mask is not None)
     dt = TORCH_DT[prob.dtype]
     q, k, v, do = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).to(dev)
@@ -475,7 +477,7 @@ def main():
                    "causal": prob.causal,
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
-                   "fwd_block_rows": args.fwd_block_rows, "parallelism": "none"},
+                   "fwd_block_rows": fwd_rows, "parallelism": "none"},
         "fwd_ms": round(ms_fwd, 4),
         "fwd_tflops": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12, 2),
         "frac_of_peak_fwd_bwd": round(value / PEAK_TFLOPS[prob.dtype], 4),

@@ -55,13 +55,15 @@ def load_library():
     lib.fa_kernel_name.restype = ctypes.c_char_p
     lib.fa_set_forward_block_rows.argtypes = [I]
     lib.fa_get_forward_block_rows.argtypes = []
+    lib.fa_forward_block_rows_for.argtypes = [I, I, I, I, I, I]
     lib.fa_forward_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, Z, P]
     lib.fa_forward_kv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.fa_forward_kv_workspace_bytes.restype = Z
     lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_backward,
                lib.fa_timing_enable, lib.fa_timing_read, lib.fa_set_forward_block_rows,
-               lib.fa_get_forward_block_rows, lib.fa_forward_kv, lib.fa_forward_varlen):
+               lib.fa_get_forward_block_rows, lib.fa_forward_block_rows_for, lib.fa_forward_kv,
+               lib.fa_forward_varlen):
         fn.restype = I
     _LIB = lib
     return lib
@@ -278,12 +280,20 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
 
 
 def fa_set_forward_block_rows(rows):
-    """Query rows per forward work-group: 64, 128 (default) or 256."""
+    """Query rows per forward work-group: 64, 128, 256, or 0 (default) to
+    choose per call."""
     _check("fa_set_forward_block_rows", load_library().fa_set_forward_block_rows(int(rows)))
 
 
 def fa_get_forward_block_rows():
     return int(load_library().fa_get_forward_block_rows())
+
+
+def fa_forward_block_rows_for(B, H, N, d, dtype, sparse=False):
+    """Query rows per work-group a forward of these sizes would use."""
+    return int(load_library().fa_forward_block_rows_for(int(B), int(H), int(N), int(d),
+                                                        (_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)),
+                                                        int(bool(sparse))))
 
 
 def fa_timing_enable(enable=True):

@@ -165,15 +165,22 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
  * analysis (review page, claims C2 and C3: tiling reduces HBM reads and
  * writes, with an IO cost that depends on the on-chip memory size; K and V
  * are read once per query tile, so that traffic falls as B_r grows): 64,
- * 128 (default) or 256.  A
- * tuning and measurement setting; results agree to rounding for every value.
- * The block-sparse forward supports 64 and 128 (a 128-token mask block
- * holds a whole tile) and returns FA_ERR_UNSUPPORTED for 256.  Process-wide,
- * read at each forward call, not synchronised between threads.  Returns
- * FA_OK, or FA_ERR_UNSUPPORTED for any other value (the setting is kept).
+ * 128 or 256, or 0 (the default) to choose per call: 256 for 16-bit d = 128
+ * dense problems whose 256-row grid holds at least 512 work-groups, else 128.
+ * A tuning and measurement setting; results agree to rounding for every
+ * value.  The block-sparse forward supports 64 and 128 (a 128-token mask
+ * block holds a whole tile; the automatic choice takes 128 there) and returns
+ * FA_ERR_UNSUPPORTED for 256.  Process-wide, read at each forward call, not
+ * synchronised between threads.  Returns FA_OK, or FA_ERR_UNSUPPORTED for any
+ * other value (the setting is kept).  fa_get_forward_block_rows returns the
+ * setting (0 when automatic).
  */
 int fa_set_forward_block_rows(int rows);
 int fa_get_forward_block_rows(void);
+/* Query rows per work-group that fa_forward (sparse = 0) or
+ * fa_forward_blocksparse (sparse != 0) would use for these sizes under the
+ * current setting.  Host only; no validation beyond that of the rule. */
+int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
 
 /* Workspace bytes fa_backward needs for these sizes (0 for an empty problem). */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);

@@ -177,14 +177,16 @@ def test_forward_varlen_validation(lib):
 
 
 def test_forward_block_rows_setting(lib):
-    assert lib.fa_get_forward_block_rows() == 128
-    for bad in (0, 32, 96, 512, -128):
+    assert lib.fa_get_forward_block_rows() == 0   # chosen per problem
+    for bad in (32, 96, 512, -128):
         assert lib.fa_set_forward_block_rows(bad) == _binding.FA_ERR_UNSUPPORTED
-        assert lib.fa_get_forward_block_rows() == 128
+        assert lib.fa_get_forward_block_rows() == 0
     try:
         for rows in (64, 256, 128):
             assert lib.fa_set_forward_block_rows(rows) == _binding.FA_OK
             assert lib.fa_get_forward_block_rows() == rows
+            for sparse in (0, 1):
+                assert lib.fa_forward_block_rows_for(2, 8, 16384, 128, 2, sparse) == rows
         # 256-row tiles span two 128-token mask blocks: not for the block-sparse forward
         assert lib.fa_set_forward_block_rows(256) == _binding.FA_OK
         f = lib.fa_forward_blocksparse
@@ -192,7 +194,22 @@ def test_forward_block_rows_setting(lib):
             == _binding.FA_ERR_UNSUPPORTED
         assert "256" in detail(lib)
     finally:
-        lib.fa_set_forward_block_rows(128)
+        lib.fa_set_forward_block_rows(0)
+
+
+def test_forward_block_rows_automatic(lib):
+    # 256-row tiles only for 16-bit d=128 dense problems with at least 512
+    # work-groups of 256 rows; 128 otherwise
+    rows_for = lib.fa_forward_block_rows_for
+    assert lib.fa_set_forward_block_rows(0) == _binding.FA_OK
+    assert rows_for(2, 8, 16384, 128, 2, 0) == 256     # 1024 work-groups
+    assert rows_for(2, 8, 8192, 128, 1, 0) == 256      # 512
+    assert rows_for(2, 8, 7937, 128, 2, 0) == 256      # 16 x 32 (ragged last tile)
+    assert rows_for(2, 8, 7936, 128, 2, 0) == 128      # 16 x 31 = 496
+    assert rows_for(2, 8, 4096, 128, 2, 0) == 128      # 256
+    assert rows_for(2, 8, 16384, 64, 2, 0) == 128      # d = 64
+    assert rows_for(2, 8, 16384, 128, 0, 0) == 128     # fp32
+    assert rows_for(2, 8, 16384, 128, 2, 1) == 128     # block-sparse
 
 
 def test_binding_refuses_cpu_tensors():

@@ -190,7 +190,7 @@ def test_forward_block_rows(case):
     try:
         gpu = run_gpu(prob)
     finally:
-        fa_set_forward_block_rows(128)
+        fa_set_forward_block_rows(0)
     compare(gpu, run_oracle(prob), TOL[dtype], label=f"{rows} rows {case[1:]}",
             magnitude_scaled=klr is not None and klr[0] < 4)
 
