@@ -702,18 +702,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         pacc[kb] = Tr::mma(av, df[kc], kc == 0 ? dinit : pacc[kb]);
       }
     }
-    const bool masked = (p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend);
+    // P^T in place, then (tiles on a mask boundary only) the element mask in
+    // a loop of its own behind one wave-uniform branch, then dS^T.  A mask
+    // test inside the exponential loop compiles to one branch per element,
+    // on every tile.
 #pragma unroll
     for (int kb = 0; kb < BC / 32; ++kb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        float pr = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
-        if (masked) {
-          const int key = kt0 + kb * 32 + acc_row(r, hh);
-          if (key >= kend || (p.causal && key > myq)) pr = 0.f;
-        }
-        pacc[kb][r] = pr * pacc[kb][r];  // dS^T = P^T (dP^T - D)
-      }
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = fast_exp2(fmaf(sacc[kb][r], c, -lse2));
+    if ((p.causal && kt0 + BC - 1 > qw0) || (kt0 + BC > kend)) {
+      // first key this lane's query does not see
+      const int lim = p.causal ? min(kend, myq + 1) : kend;
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          sacc[kb][r] = kt0 + kb * 32 + acc_row(r, hh) < lim ? sacc[kb][r] : 0.f;
+    }
+#pragma unroll
+    for (int kb = 0; kb < BC / 32; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[kb][r] = sacc[kb][r] * pacc[kb][r];  // dS^T = P^T (dP^T - D)
     // dQ^T += K^T dS^T  (k = keys, acc-ordered slots).
 #pragma unroll
     for (int kc = 0; kc < BC / 16; ++kc) {
