@@ -261,7 +261,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       }
     }
   };
+  // Queries that see this lane's key: qlo <= i < qhi (the element mask).
+  const int qlo = p.causal ? myk : 0;
+  const int qhi = myk < kend ? N : 0;
   // In place: P = exp2(c S - LSE2) into sacc, dS = P (dP - D) into pacc.
+  // On boundary tiles the mask is applied in a loop of its own behind one
+  // wave-uniform branch: a mask test inside the exponential loop compiles to
+  // one branch per element.
   auto soft = [&](const char* slot, int qi0, bool masked, qblk& sacc, qblk& pacc) {
     const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
 #pragma unroll
@@ -272,17 +278,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
         const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const int r = 4 * g + u;
-          float pr = fast_exp2(fmaf(sacc[qb][r], c, -lv[u]));
-          if (masked) {
-            const int qi = qi0 + r0 + u;
-            if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
-          }
-          sacc[qb][r] = pr;                          // P
-          pacc[qb][r] = pr * pacc[qb][r];            // dS = P (dP - D)
-        }
+        for (int u = 0; u < 4; ++u)
+          sacc[qb][4 * g + u] = fast_exp2(fmaf(sacc[qb][4 * g + u], c, -lv[u]));  // P
       }
+    if (masked) {
+#pragma unroll
+      for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int qi = qi0 + qb * 32 + acc_row(r, hh);
+          sacc[qb][r] = (qi >= qlo) & (qi < qhi) ? sacc[qb][r] : 0.f;
+        }
+    }
+#pragma unroll
+    for (int qb = 0; qb < BQ / 32; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) pacc[qb][r] = sacc[qb][r] * pacc[qb][r];  // dS = P (dP - D)
   };
   // P and dS of a tile as B operands over the query dimension.
   typedef frag_t<T> qfrag[BQ / 16];
@@ -362,9 +373,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         for (int u = 0; u < 4; ++u) {
           const int r = 4 * g + u;
           float pr = fast_exp2(fmaf(sacc[qb][r], c, -lv[u]));
-          if (msk) {
+          if (msk) {  // selects only: no branch per element
             const int qi = qi0 + r0 + u;
-            if (myk >= kend || qi >= N || (p.causal && myk > qi)) pr = 0.f;
+            pr = (qi >= qlo) & (qi < qhi) ? pr : 0.f;
           }
           sacc[qb][r] = pr;                // P
           pacc[qb][r] = pr * pacc[qb][r];  // dS = P (dP - D)
