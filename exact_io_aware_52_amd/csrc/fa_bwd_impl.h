@@ -591,6 +591,11 @@ struct DqCfg {
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
   static constexpr int LPT = 2 * TILE_BYTES / 4096;
   static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
+  // Score/dP operand prefetch group (k-steps; 0: read each operand just
+  // before its product).  One k-step ahead at 16-bit d = 128 (dQ 3.6%
+  // faster at N = 16K); at d = 64 groups of 1, 2 and 4 measured 1-2% slower,
+  // and groups of 4 at d = 128 spill (1.8x slower).
+  static constexpr int GK = (sizeof(raw) == 2 && D == 128) ? 1 : 0;
 };
 
 template <typename T, int D>
@@ -703,14 +708,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     const raw* Ks = reinterpret_cast<const raw*>(slot);
     const raw* Vs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
     f32x16 sacc[BC / 32], pacc[BC / 32];
+    if constexpr (L::GK > 0) {
+      // K and V operands read in groups of GK k-steps, one group ahead of
+      // their products (fenced so that the compiler keeps the order).
+      constexpr int GK = L::GK, NKC = D / 16, NGR = BC / 32 * NKC / GK;
+      static_assert((BC / 32 * NKC) % GK == 0, "whole groups");
+      frag_t<T> fk[2][GK], fv[2][GK];
+      auto ld = [&](int g, int b) {
 #pragma unroll
-    for (int kb = 0; kb < BC / 32; ++kb) {
+        for (int j = 0; j < GK; ++j) {
+          const int i = g * GK + j, kb = i / NKC, kc = i % NKC;
+          fk[b][j] = load_frag_swz<T, D, kBoth>(Ks, kb * 32 + col, kc * 16 + hh * 8);
+          fv[b][j] = load_frag_swz<T, D, kRows>(Vs, kb * 32 + col, kc * 16 + hh * 8);
+        }
+      };
+      ld(0, 0);
 #pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc) {
-        const frag_t<T> ak = load_frag_swz<T, D, kBoth>(Ks, kb * 32 + col, kc * 16 + hh * 8);
-        sacc[kb] = Tr::mma(ak, qf[kc], kc == 0 ? zero16() : sacc[kb]);
-        const frag_t<T> av = load_frag_swz<T, D, kRows>(Vs, kb * 32 + col, kc * 16 + hh * 8);
-        pacc[kb] = Tr::mma(av, df[kc], kc == 0 ? dinit : pacc[kb]);
+      for (int g = 0; g < NGR; ++g) {
+        if (g + 1 < NGR) ld(g + 1, (g + 1) & 1);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < GK; ++j) {
+          const int i = g * GK + j, kb = i / NKC, kc = i % NKC;
+          sacc[kb] = Tr::mma(fk[g & 1][j], qf[kc], kc == 0 ? zero16() : sacc[kb]);
+          pacc[kb] = Tr::mma(fv[g & 1][j], df[kc], kc == 0 ? dinit : pacc[kb]);
+        }
+        // (no fence after the last group: the exponentials may start beside it)
+        if (g + 1 < NGR) __builtin_amdgcn_sched_barrier(0);
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < BC / 32; ++kb) {
+#pragma unroll
+        for (int kc = 0; kc < D / 16; ++kc) {
+          const frag_t<T> ak = load_frag_swz<T, D, kBoth>(Ks, kb * 32 + col, kc * 16 + hh * 8);
+          sacc[kb] = Tr::mma(ak, qf[kc], kc == 0 ? zero16() : sacc[kb]);
+          const frag_t<T> av = load_frag_swz<T, D, kRows>(Vs, kb * 32 + col, kc * 16 + hh * 8);
+          pacc[kb] = Tr::mma(av, df[kc], kc == 0 ? dinit : pacc[kb]);
+        }
       }
     }
     // P^T in place, then (tiles on a mask boundary only) the element mask in
