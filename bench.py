@@ -123,6 +123,114 @@ def cpu_baseline(prob, budget_s):
                       f"the same workload), fp64 forward+backward, {dt:.1f} s"}
 
 
+def standard_attention_mask(prob, dev):
+    """Boolean mask, True where a key is hidden (causal and key padding), or
+    None; shaped to broadcast over [B, H, N, N]."""
+    mask = None
+    if prob.causal:
+        mask = torch.ones(prob.N, prob.N, dtype=torch.bool, device=dev).triu_(1)
+    if prob.key_lens is not None:
+        kl = torch.from_numpy(prob.key_lens).to(dev).long()
+        pad = (torch.arange(prob.N, device=dev)[None, :] >= kl[:, None])[:, None, None, :]
+        mask = pad if mask is None else mask | pad
+    return mask
+
+
+def standard_forward(q, k, v, scale, mask):
+    """Standard attention (the Theta(N d + N^2) side of the IO argument): the
+    GEMM writes S = (scale Q) K^T to HBM in the input dtype, a masking pass
+    (masked workloads only) rewrites it, softmax reads S and writes P, and the
+    second GEMM reads P: 8 bytes per score element at 16 bits, plus 4 for the
+    mask.  Library GEMMs and elementwise kernels; every transposed operand
+    (here K^T, N x d) is made contiguous first."""
+    s = torch.matmul(q * scale, k.transpose(-1, -2).contiguous())
+    if mask is not None:
+        s.masked_fill_(mask, float("-inf"))
+    p = torch.softmax(s, dim=-1)
+    return torch.matmul(p, v), p
+
+
+def standard_backward(q, k, v, do, p, scale):
+    """Its backward from the stored P: dV = P^T dO, dP = dO V^T, dS from the
+    fused softmax backward (P o (dP - rowsum(dP o P)), the kernel autograd
+    uses), dQ = scale dS K, dK = scale dS^T Q.  The products with a
+    transposed N x N operand are formed transposed, (dO^T P)^T and
+    (Q^T dS)^T, so that only N x d operands are transposed (made contiguous);
+    dP and dS go through HBM like S and P."""
+    tr = lambda x: x.transpose(-1, -2).contiguous()   # noqa: E731  (N x d operands only)
+    dv = tr(torch.matmul(tr(do), p))
+    dp = torch.matmul(do, tr(v))
+    ds = torch.ops.aten._softmax_backward_data(dp, p, -1, p.dtype)
+    dq = torch.matmul(ds, k).mul_(scale)
+    dk = tr(torch.matmul(tr(q), ds)).mul_(scale)
+    return dq, dk, dv
+
+
+def bench_standard(args, dev):
+    """Standard (materialising) attention on the same workload, timed beside
+    the tiled kernels; --phase selects what one step is, so that counter runs
+    can attribute HBM bytes per step."""
+    prob = make_workload(args)
+    if prob.block_mask is not None:
+        sys.exit("--standard: block-sparse workloads have no standard counterpart here")
+    dt = TORCH_DT[prob.dtype]
+    q, k, v, do = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v, prob.do))
+    mask = standard_attention_mask(prob, dev)
+    scale = float(prob.scale)
+    kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).to(dev)
+
+    def std_step():
+        _, p = standard_forward(q, k, v, scale, mask)
+        if args.phase == "fwdbwd":
+            standard_backward(q, k, v, do, p, scale)
+
+    o = torch.empty_like(q)
+    lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=dev)
+    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
+    ws = torch.empty(fa_backward_workspace_bytes(prob.B, prob.H, prob.N, prob.d),
+                     dtype=torch.uint8, device=dev)
+
+    def flash_step():
+        fa_forward(q, k, v, scale=scale, causal=prob.causal, key_lens=kl, o=o, lse=lse)
+        if args.phase == "fwdbwd":
+            fa_backward(q, k, v, o, do, lse, scale=scale, causal=prob.causal, key_lens=kl,
+                        dq=dq, dk=dk, dv=dv, workspace=ws)
+
+    def timed(fn, n):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / n
+
+    torch.cuda.synchronize()
+    torch.cuda.reset_peak_memory_stats(dev)
+    base_mem = torch.cuda.memory_allocated(dev)
+    for _ in range(args.warmup):
+        std_step()
+    ms_std = timed(std_step, args.steps)
+    peak_extra = torch.cuda.max_memory_allocated(dev) - base_mem
+    ms_flash = None
+    if not args.standard_only:
+        for _ in range(args.warmup):
+            flash_step()
+        ms_flash = timed(flash_step, args.steps)
+    pairs = accounting.kept_pairs(prob)
+    flops = (4 if args.phase == "fwd" else 14) * prob.d * pairs
+    print(json.dumps({
+        "metric": f"standard (materialising) attention beside the tiled kernels, {args.phase}",
+        "workload": prob.name, "phase": args.phase, "dtype": prob.dtype,
+        "steps": args.steps, "warmup": args.warmup,
+        "standard_ms": round(ms_std, 4),
+        "standard_tflops": round(flops / (ms_std * 1e-3) / 1e12, 2),
+        "standard_extra_device_bytes": int(peak_extra),
+        "tiled_ms": None if ms_flash is None else round(ms_flash, 4),
+        "speedup": None if ms_flash is None else round(ms_std / ms_flash, 2),
+        "standard_model_bytes_fwd": accounting.standard_attention_bytes(prob),
+    }), flush=True)
+
+
 def kv_splits(prob):
     """Key-range splits the library plans for this inference problem (read
     back from its workspace size: splits x rows x (d + 1) fp32 values)."""
@@ -354,6 +462,13 @@ def main():
                     help="query rows per forward work-group (tile height); 0 = chosen per problem")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of host work for the oracle baseline (0 disables)")
+    ap.add_argument("--standard", action="store_true",
+                    help="time standard (materialising) attention on the workload beside the "
+                         "tiled kernels")
+    ap.add_argument("--phase", default="fwdbwd", choices=["fwd", "fwdbwd"],
+                    help="with --standard: what one step is")
+    ap.add_argument("--standard-only", action="store_true",
+                    help="with --standard: run only the standard attention (counter runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -381,6 +496,9 @@ def main():
     for k in ("fwd", "bwd_dkdv", "bwd_dq"):
         KERNEL_NAMES[k] = fa_kernel_name(k)
 
+    if args.standard:
+        bench_standard(args, dev)
+        return
     if args.config.startswith("kv_"):
         bench_kv(args, dev)
         return
