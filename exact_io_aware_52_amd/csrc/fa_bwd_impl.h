@@ -622,7 +622,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const int nq = (N + BR - 1) / BR;
 
   int qt, bh;
-  map_tile(blockIdx.x, nq, p.BH, p.causal != 0, p.hgroup, qt, bh);
+  map_tile(blockIdx.x, nq, p.BH, p.causal != 0, p.hgroup, qt, bh, p.causal != 0);
   const int b = bh / p.H;
   const int i0 = qt * BR;
   const int qw0 = i0 + 32 * w;
