@@ -21,6 +21,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -53,10 +54,16 @@ KERNEL_SOURCES = {
 
 
 def source_hash(kind):
+    """Hash of the code (comments and whitespace removed) of the sources a
+    kernel is built from: a counter summary stays valid across comment-only
+    edits and is dropped when the code changes."""
     h = hashlib.sha256()
     for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "exact_io_aware_52_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "exact_io_aware_52_amd", "csrc", f), encoding="utf-8") as fh:
+            text = fh.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
     return h.hexdigest()[:16]
 
 

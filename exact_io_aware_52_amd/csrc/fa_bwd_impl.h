@@ -27,6 +27,12 @@
 // Streaming (both passes): the tiles of the streamed operand go from HBM
 // straight into a 4-slot LDS ring by direct-to-LDS loads, requested two steps
 // before use; one barrier per step.
+//
+// Masks: tiles that straddle a causal, padding or sequence boundary apply the
+// element mask after the exponentials, in a loop of their own behind one
+// wave-uniform branch (or as selects in the interleaved step); a run-time
+// mask flag tested inside the exponential loop compiles to one branch per
+// element.
 
 #pragma once
 

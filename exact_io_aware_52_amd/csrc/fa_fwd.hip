@@ -2,8 +2,9 @@
 //
 // FlashAttention forward (review page "Method"; slides steps 01-04; visual
 // guide, "online softmax"): each work-group owns one tile of 32 NW query
-// rows of one (b, h) head (NW = 4 waves, 128 rows, by default; 64 and 256
-// rows on request) and streams the key/value tiles that tile needs through
+// rows of one (b, h) head (NW = 4 waves, 128 rows; 256 rows by default for
+// large 16-bit d = 128 problems; 64 and 256 rows on request) and streams the
+// key/value tiles that tile needs through
 // LDS.  Scores never leave the compute unit; only O and the per-row
 // logsumexp are written.  The pages' pseudocode runs key/value blocks in the
 // outer loop and carries per-query-block state through memory; here the
@@ -669,7 +670,7 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   return launch_fwd_combine<T, D>(pb, t, splits);
 }
 
-// Query rows per tile (work-group): 128 by default; 64 and 256 on request;
+// Query rows per tile (work-group): 128 or 256 (chosen on the host), 64 on request;
 // 32 (one wave, 16-bit types) for inference with few queries.
 template <typename T, int D>
 hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
