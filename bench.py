@@ -32,7 +32,9 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
-                                   fa_forward, fa_forward_blocksparse, fa_forward_kv,
+                                   fa_forward, fa_forward_blocksparse,
+                                   fa_forward_blocksparse_split,
+                                   fa_forward_blocksparse_split_workspace_bytes, fa_forward_kv,
                                    fa_forward_kv_workspace_bytes, fa_forward_varlen,
                                    fa_forward_block_rows_for, fa_kernel_name,
                                    fa_set_forward_block_rows, fa_timing_enable, fa_timing_read,
@@ -500,7 +502,7 @@ def main():
         print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30}))
         return
 
-    for k in ("fwd", "bwd_dkdv", "bwd_dq"):
+    for k in ("fwd", "fwd_combine", "bwd_dkdv", "bwd_dq"):
         KERNEL_NAMES[k] = fa_kernel_name(k)
 
     if args.standard:
@@ -527,9 +529,21 @@ def main():
     ws = torch.empty(fa_backward_workspace_bytes(prob.B, prob.H, prob.N, prob.d),
                      dtype=torch.uint8, device=dev)
     scale = float(prob.scale)
+    # The long structured masks give one query tile per head the whole key
+    # range: its forward is split four ways over work-groups (measured best
+    # of 4K, 8K and 16K keys per split at N = 32K and 64K).
+    key_chunk = 0
+    if prob.name.startswith("block_sparse_long"):
+        key_chunk = -(-prob.N // (4 * 64)) * 64
+        split_ws = torch.empty(max(fa_forward_blocksparse_split_workspace_bytes(
+            prob.B, prob.H, prob.N, prob.d, key_chunk), 1), dtype=torch.uint8, device=dev)
 
     def fwd():
-        if bm is not None:
+        if key_chunk:
+            fa_forward_blocksparse_split(q, k, v, bm, prob.block_size, key_chunk=key_chunk,
+                                         scale=scale, causal=prob.causal, key_lens=kl, o=o,
+                                         lse=lse, workspace=split_ws)
+        elif bm is not None:
             fa_forward_blocksparse(q, k, v, bm, prob.block_size, scale=scale, causal=prob.causal,
                                    key_lens=kl, o=o, lse=lse)
         else:
@@ -602,11 +616,12 @@ def main():
                    "causal": prob.causal,
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
-                   "fwd_block_rows": fwd_rows, "parallelism": "none"},
+                   "fwd_block_rows": fwd_rows, "fwd_key_chunk": key_chunk or None,
+                   "parallelism": "none"},
         "fwd_ms": round(ms_fwd, 4),
         "fwd_tflops": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12, 2),
         "frac_of_peak_fwd_bwd": round(value / PEAK_TFLOPS[prob.dtype], 4),
-        "kernels_us": {v["name"]: round(v["avg_us"], 2) for v in kernels.values()},
+        "kernels_us": {v["name"]: round(v["avg_us"], 2) for v in kernels.values() if v["launches"]},
         "roofline": roof,
     }
     if args.cpu_budget > 0:

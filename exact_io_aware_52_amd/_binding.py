@@ -42,6 +42,10 @@ def load_library():
     P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     lib.fa_forward.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, I, P]
     lib.fa_forward_blocksparse.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P]
+    lib.fa_forward_blocksparse_split.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I,
+                                                 P, Z, P]
+    lib.fa_forward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_forward_blocksparse_split_workspace_bytes.restype = Z
     lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = Z
@@ -60,7 +64,8 @@ def load_library():
     lib.fa_forward_kv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.fa_forward_kv_workspace_bytes.restype = Z
     lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
-    for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_backward,
+    for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_forward_blocksparse_split,
+               lib.fa_backward,
                lib.fa_timing_enable, lib.fa_timing_read, lib.fa_set_forward_block_rows,
                lib.fa_get_forward_block_rows, lib.fa_forward_block_rows_for, lib.fa_forward_kv,
                lib.fa_forward_varlen):
@@ -168,6 +173,41 @@ def fa_forward_blocksparse(q, k, v, block_mask, block_size=128, scale=None, caus
         raise ValueError("block_mask is required")
     return _forward("fa_forward_blocksparse", q, k, v, scale, causal, key_lens, block_mask,
                     block_size, o, lse)
+
+
+def fa_forward_blocksparse_split_workspace_bytes(B, H, N, d, key_chunk):
+    return int(load_library().fa_forward_blocksparse_split_workspace_bytes(B, H, N, d,
+                                                                          int(key_chunk)))
+
+
+def fa_forward_blocksparse_split(q, k, v, block_mask, block_size=128, key_chunk=16384, scale=None,
+                                 causal=False, key_lens=None, o=None, lse=None, workspace=None):
+    """Block-sparse forward with each query tile's key range split into
+    key_chunk-key pieces over work-groups, merged by a second pass (for masks
+    with a few very long rows).  workspace: uint8 device tensor of at least
+    fa_forward_blocksparse_split_workspace_bytes(...) bytes, allocated here
+    when not given."""
+    if block_mask is None:
+        raise ValueError("block_mask is required")
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    o = torch.empty_like(q) if o is None else _like("o", o, q)
+    lse = (torch.empty((B, H, N), dtype=torch.float32, device=q.device) if lse is None
+           else _like("lse", lse, q, (B, H, N), torch.float32))
+    need = fa_forward_blocksparse_split_workspace_bytes(B, H, N, d, key_chunk)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    kl = _lens(key_lens, B, q.device)
+    bm = _mask(block_mask, N, block_size, q.device)
+    st = lib.fa_forward_blocksparse_split(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d, _scale(scale, d),
+        int(bool(causal)), _ptr(kl), _ptr(bm), int(block_size), int(key_chunk),
+        _DTYPE_CODE[q.dtype], _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream(q.device))
+    _check("fa_forward_blocksparse_split", st)
+    return o, lse
 
 
 def fa_forward_kv_workspace_bytes(B, H, Nq, Nk, d, dtype):

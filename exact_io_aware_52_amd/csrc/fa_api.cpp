@@ -122,10 +122,30 @@ int check_block(const uint8_t* block_mask, int block_size, int N, bool required)
   return FA_OK;
 }
 
+size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Key-range splits of the block-sparse forward with key_chunk keys each, and
+// the workspace their fp32 partial O and LSE take ([splits][B*H][N][d], then
+// [splits][B*H][N], each rounded up to 256 bytes).
+constexpr int kMaxSplits = 1024;
+int sparse_splits(int N, int key_chunk) { return (N + key_chunk - 1) / key_chunk; }
+size_t split_workspace(int B, int H, int N, int d, int splits) {
+  if (splits <= 1) return 0;
+  const size_t rows = (size_t)splits * B * H * N;
+  return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
+}
+
+// Key-range split of one forward call (splits = 1: none).
+struct SplitArgs {
+  int key_chunk = 0;
+  void* workspace = nullptr;
+  size_t workspace_bytes = 0;
+};
+
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const int32_t* key_lens,
                  const uint8_t* block_mask, int block_size, bool sparse, fa_dtype dtype,
-                 hipStream_t stream) {
+                 hipStream_t stream, const SplitArgs& split = SplitArgs()) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
@@ -142,13 +162,28 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
     return st;
   if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
   fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream, rows};
+  const int splits = split.key_chunk > 0 ? sparse_splits(N, split.key_chunk) : 1;
+  if (splits > 1) {
+    const size_t need = split_workspace(B, H, N, d, splits);
+    if (!split.workspace)
+      return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+    if (!aligned(split.workspace, 16))
+      return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+    if (split.workspace_bytes < need)
+      return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", split.workspace_bytes,
+                  need);
+    const size_t prow = (size_t)splits * B * H * N;
+    p.splits = splits;
+    p.chunk = split.key_chunk;
+    p.opart = static_cast<float*>(split.workspace);
+    p.lpart = reinterpret_cast<float*>(static_cast<char*>(split.workspace) +
+                                       round_up(prow * d * sizeof(float), 256));
+  }
   fa::FwdTensors t{q, k, v, o, lse};
   hipError_t e = fa::launch_forward(p, t);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "forward launch: %s", hipGetErrorString(e));
   return FA_OK;
 }
-
-size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 // Inference forward plan: query rows per work-group and key-range splits.
 // Few queries against a long cache leave too few work-groups to fill the
@@ -192,6 +227,15 @@ size_t kv_workspace(int B, int H, int Nq, int d, const KvPlan& pl) {
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
+int check_key_chunk(int key_chunk, int N) {
+  if (key_chunk <= 0 || key_chunk % 64 != 0)
+    return fail(FA_ERR_UNSUPPORTED, "key_chunk=%d (a positive multiple of 64)", key_chunk);
+  if (N > 0 && sparse_splits(N, key_chunk) > kMaxSplits)
+    return fail(FA_ERR_UNSUPPORTED, "N=%d with key_chunk=%d gives more than %d splits", N,
+                key_chunk, kMaxSplits);
+  return FA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -209,6 +253,29 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
                            fa_dtype dtype, hipStream_t stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
                       block_size, true, dtype, stream);
+}
+
+size_t fa_forward_blocksparse_split_workspace_bytes(int B, int H, int N, int d, int key_chunk) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || key_chunk <= 0 || key_chunk % 64 != 0) return 0;
+  const int splits = sparse_splits(N, key_chunk);
+  if (splits > kMaxSplits) return 0;
+  return split_workspace(B, H, N, d, splits);
+}
+
+int fa_forward_blocksparse_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int H, int N, int d, float scale, int causal,
+                                 const int32_t* key_lens, const uint8_t* block_mask,
+                                 int block_size, int key_chunk, fa_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  g_detail[0] = 0;
+  const int st = check_key_chunk(key_chunk, N);
+  if (st != FA_OK) return st;
+  SplitArgs split;
+  split.key_chunk = key_chunk;
+  split.workspace = workspace;
+  split.workspace_bytes = workspace_bytes;
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
+                      block_size, true, dtype, stream, split);
 }
 
 size_t fa_forward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dtype dtype) {

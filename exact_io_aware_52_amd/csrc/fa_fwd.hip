@@ -534,18 +534,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   const float l_tot = pair_sum(l_run);
   if (p.opart && myq < N) {
     // One split of the key range: fp32 partial results for the combine pass.
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+    // A row that saw no key in this split gets LSE = -inf only: the combine
+    // pass never reads the partial O of such a row.
     const size_t prow = ((size_t)blockIdx.y * p.BH + bh) * N + myq;
-    float* Op = p.opart + prow * D;
+    if (l_tot > 0.f) {
+      const float inv = 1.f / l_tot;
+      float* Op = p.opart + prow * D;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+      for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 out;
+        for (int g = 0; g < 4; ++g) {
+          f32x4 out;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) out[u] = oacc[db][4 * g + u] * inv;
-        *reinterpret_cast<f32x4*>(Op + db * 32 + 8 * g + 4 * hh) = out;
-      }
+          for (int u = 0; u < 4; ++u) out[u] = oacc[db][4 * g + u] * inv;
+          *reinterpret_cast<f32x4*>(Op + db * 32 + 8 * g + 4 * hh) = out;
+        }
+    }
     if (hh == 0) p.lpart[prow] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
   } else if (myq < N) {
     const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;

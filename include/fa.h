@@ -90,6 +90,28 @@ int fa_forward_blocksparse(const void* q, const void* k, const void* v, void* o,
                            fa_dtype dtype, hipStream_t stream);
 
 /*
+ * fa_forward_blocksparse with the key range of every query tile split over
+ * ceil(N / key_chunk) work-groups, whose float32 partial O and LSE a second
+ * pass merges (the online-softmax merge of per-block states, taken across
+ * work-groups).  For masks that give a few query tiles far more kept blocks
+ * than the rest (a global row), whose single work-group would otherwise run
+ * the whole key range alone.  key_chunk: keys per split, a positive multiple
+ * of 64 (FA_ERR_UNSUPPORTED otherwise, or beyond 1024 splits); a split with
+ * no kept block contributes nothing.  workspace: caller-owned device memory
+ * of at least fa_forward_blocksparse_split_workspace_bytes(B,H,N,d,key_chunk)
+ * bytes, 16-byte aligned, not initialised (NULL when that is 0, i.e. one
+ * split: then the call is fa_forward_blocksparse); calls that share it must
+ * be ordered on one stream.  Same results as fa_forward_blocksparse up to the
+ * rounding of the merge.
+ */
+int fa_forward_blocksparse_split(const void* q, const void* k, const void* v, void* o, float* lse,
+                                 int B, int H, int N, int d, float scale, int causal,
+                                 const int32_t* key_lens, const uint8_t* block_mask,
+                                 int block_size, int key_chunk, fa_dtype dtype, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+size_t fa_forward_blocksparse_split_workspace_bytes(int B, int H, int N, int d, int key_chunk);
+
+/*
  * Inference forward: Nq new queries against a key/value cache of Nk entries
  * (review page, "Caveats": the kernel later became central to inference
  * stacks; "Agent Infrastructure Takeaways": for long contexts, memory
@@ -144,7 +166,7 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
  * L = sum(dout * o): with P = exp(S - LSE), D = rowsum(dout * o),
  * dV = P^T dout, dP = dout V^T, dS = P * (dP - D), dQ = scale * dS K,
  * dK = scale * dS^T Q.
- * o and lse must come from fa_forward / fa_forward_blocksparse called with
+ * o and lse must come from fa_forward / fa_forward_blocksparse(_split) called with
  * the same q, k, v, sizes, scale and masks.  block_mask may be NULL (dense);
  * block_size is ignored then.  Overwrites dq, dk, dv (dtype).
  * workspace: device memory of at least fa_backward_workspace_bytes(B,H,N,d)

@@ -93,6 +93,32 @@ def test_blocksparse_validation(lib):
     assert "1024" in detail(lib)
 
 
+def test_blocksparse_split_validation(lib):
+    f = lib.fa_forward_blocksparse_split
+
+    def call(N=256, chunk=128, ws=FAKE, ws_bytes=0):
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 2, N, 64, 0.1, 0, None, FAKE, 128, chunk, 2, ws,
+                 ws_bytes, None)
+
+    for chunk in (0, -64, 100, 65):
+        assert call(chunk=chunk) == _binding.FA_ERR_UNSUPPORTED
+        assert "key_chunk" in detail(lib)
+    assert call(N=65600, chunk=64) == _binding.FA_ERR_UNSUPPORTED     # 1025 splits
+    assert "1024" in detail(lib)
+    need = lib.fa_forward_blocksparse_split_workspace_bytes(1, 2, 256, 64, 128)
+    # 2 splits x 2 heads x 256 rows: fp32 O (d = 64), then fp32 LSE, each rounded to 256 bytes
+    assert need == 2 * 2 * 256 * 64 * 4 + 2 * 2 * 256 * 4
+    assert call(ws=None) == _binding.FA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == _binding.FA_ERR_WORKSPACE
+    assert str(need) in detail(lib)
+    assert call(ws=BAD_ALIGN, ws_bytes=need) == _binding.FA_ERR_INVALID_ARG
+    ws_bytes = lib.fa_forward_blocksparse_split_workspace_bytes
+    assert ws_bytes(1, 2, 256, 64, 256) == 0        # one split: no workspace
+    assert ws_bytes(1, 2, 256, 64, 100) == 0        # invalid chunk
+    assert ws_bytes(3, 1, 300, 128, 128) == (3 * 3 * 300 * 128 * 4) + \
+        ((3 * 3 * 300 * 4 + 255) // 256 * 256)
+
+
 def bwd(lib, ws=FAKE, ws_bytes=1 << 30, dq=FAKE, bm=None, bs=128, d=64, N=100):
     return lib.fa_backward(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, 2, 3, N, d, 0.1, 1,
                            None, bm, bs, 1, ws, ws_bytes, None)

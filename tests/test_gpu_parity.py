@@ -16,7 +16,8 @@ import torch
 
 import oracle
 from exact_io_aware_52_amd import (fa_backward, fa_forward, fa_forward_blocksparse,
-                                   fa_set_forward_block_rows, inputs)
+                                   fa_forward_blocksparse_split, fa_set_forward_block_rows,
+                                   inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -290,6 +291,66 @@ def test_config_block_sparse_long(n):
             bound_k = 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0)))
             assert np.all(dev_k <= bound_k), (b, h, "sum dK", dev_k.max(), bound_k.min())
     log(f"[parity] block_sparse_long N={n}: dK, dV sums within bounds on all heads")
+
+
+# ----------------------------------------------------------------------------- split key ranges
+
+SPLIT_CASES = [
+    # B, H, N, d, dtype, causal, key_len_range, keep_p, band, global, key_chunk
+    (1, 2, 384, 64, "bf16", False, None, 0.5, None, 0, 128),
+    (2, 1, 300, 128, "fp16", True, (1, 300), 0.6, None, 0, 64),
+    (1, 2, 200, 64, "fp32", True, None, 0.7, None, 0, 128),
+    (1, 2, 1024, 64, "bf16", False, None, 1 / 32, 1, 1, 256),   # band + global row/column
+    (1, 1, 1000, 128, "bf16", False, (500, 1000), 0.25, None, 0, 320),
+]
+
+
+@pytest.mark.parametrize("case", SPLIT_CASES,
+                         ids=lambda c: "B{}H{}N{}d{}_{}_chunk{}".format(*c[:5], c[10]))
+def test_blocksparse_split(case):
+    # The key range of every query tile split over work-groups and merged:
+    # against the oracle, and against the unsplit block-sparse forward.
+    B, H, N, d, dtype, causal, klr, keep, band, glob, chunk = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=301 + N + chunk, causal=causal,
+                               key_len_range=klr, block_keep_p=keep, block_band=band,
+                               block_global=glob)
+    q, k, v = (dev(x, dtype) for x in (prob.q, prob.k, prob.v))
+    kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
+    bm = torch.from_numpy(prob.block_mask).cuda()
+    kw = dict(scale=float(prob.scale), causal=causal, key_lens=kl)
+    o, lse = fa_forward_blocksparse_split(q, k, v, bm, prob.block_size, key_chunk=chunk, **kw)
+    o1, lse1 = fa_forward_blocksparse(q, k, v, bm, prob.block_size, **kw)
+    torch.cuda.synchronize()
+    got = {"o": o.double().cpu().numpy(), "lse": lse.double().cpu().numpy()}
+    compare(got, run_oracle(prob, backward=False), TOL[dtype],
+            label=f"split forward {case}", magnitude_scaled=klr is not None and klr[0] < 4)
+    compare(got, {"o": o1.double().cpu().numpy(), "lse": lse1.double().cpu().numpy()},
+            TOL[dtype], label=f"split vs unsplit {case}")
+
+
+@pytest.mark.parametrize("n", [32768, 65536])
+def test_config_block_sparse_long_split(n):
+    # The long structured workloads through the split forward (16384 keys per
+    # split, the launch the bench times): sampled rows of O and LSE against the
+    # oracle's row function, every row against the unsplit forward.
+    prob = inputs.workload("block_sparse_long", n)
+    q, k, v = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v))
+    bm = torch.from_numpy(prob.block_mask).cuda()
+    o, lse = fa_forward_blocksparse_split(q, k, v, bm, prob.block_size, key_chunk=16384,
+                                          scale=float(prob.scale))
+    o1, lse1 = fa_forward_blocksparse(q, k, v, bm, prob.block_size, scale=float(prob.scale))
+    torch.cuda.synchronize()
+    compare({"o": o.double().cpu().numpy(), "lse": lse.double().cpu().numpy()},
+            {"o": o1.double().cpu().numpy(), "lse": lse1.double().cpu().numpy()}, TOL["bf16"],
+            label=f"block_sparse_long N={n} split vs unsplit")
+    rows = np.array([0, 1, 127, 128, n // 2, n - 129, n - 1])
+    for b, h in [(0, 3)]:
+        ro, rl, _ = oracle.head_rows(*(x[b, h].astype(np.float64)
+                                       for x in (prob.q, prob.k, prob.v, prob.do)),
+                                     float(prob.scale), rows, block_mask=prob.block_mask,
+                                     block_size=prob.block_size)
+        compare({"o": o[b, h].double().cpu().numpy()[rows], "lse": lse[b, h].double().cpu().numpy()[rows]},
+                {"o": ro, "lse": rl}, TOL["bf16"], label=f"block_sparse_long N={n} split rows")
 
 
 # ----------------------------------------------------------------------------- maximum sizes
