@@ -448,6 +448,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     // loop, on every step, which also stalls on the tiles just requested.
     wait_vmcnt<0>();
     int cur = 0, nxt = PD;  // ring slots of tile i and of tile i + PD
+    // One ring tile seen in full by this wave: NSUB sub-tiles, each with its
+    // scores, exponentials and P V products.
+    auto full_tile = [&](const raw* Kc, const raw* Vc) {
+#pragma unroll
+      for (int h = 0; h < NSUB; ++h) {
+        f32x16 sc;
+        frag_t<T> pf[2];
+        scores(Kc, h, sc);
+        const float rs = expo(sc, pf, false);
+        if (h > 0) {
+          // This block also holds the P V products of sub-tile h-1 (after
+          // its settle branch): score reads and products first, then each
+          // P V product beside a share of the exponentials.
+          __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+          __builtin_amdgcn_sched_group_barrier(0x100, 4 * D / 32, 0);
+#pragma unroll
+          for (int i = 0; i < 2 * D / 32; ++i) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * D / 32), 0);
+          }
+        }
+        settle(sc, pf, rs, false);
+        pv(Vc, h, pf);
+      }
+    };
     // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
     int lo = nkt, hi = -1;
     if (!sparse) {
@@ -466,28 +492,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         const uint32_t nb = ring_lds + nxt * L::SLOT_BYTES;
         kplan.issue(Kg + (size_t)(t + PD) * BT * D, nb);
         vplan.issue(Vg + (size_t)(t + PD) * BT * D, nb + L::TILE_BYTES);
-#pragma unroll
-        for (int h = 0; h < NSUB; ++h) {
-          f32x16 sc;
-          frag_t<T> pf[2];
-          scores(Kc, h, sc);
-          const float rs = expo(sc, pf, false);
-          if (h > 0) {
-            // This block also holds the P V products of sub-tile h-1 (after
-            // its settle branch): score reads and products first, then each
-            // P V product beside a share of the exponentials.
-            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
-            __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 4 * D / 32, 0);
-#pragma unroll
-            for (int i = 0; i < 2 * D / 32; ++i) {
-              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-              __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * D / 32), 0);
-            }
-          }
-          settle(sc, pf, rs, false);
-          pv(Vc, h, pf);
-        }
+        full_tile(Kc, Vc);
 #pragma unroll
         for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
         tl[PD] = min(t + PD + 1, nkt);
@@ -507,6 +512,14 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();  // every wave is done with step i-1: slot nxt is free
         if (tl[PD] < nkt) issue(tl[PD], nxt);
+        // A tile this wave sees in full (every sub-tile active and unmasked;
+        // wave-uniform) takes the interior's interleaved order.
+        bool full = true;
+#pragma unroll
+        for (int h = 0; h < NSUB; ++h) full = full && active(t, h) && !masked(t, h);
+        if (full) {
+          full_tile(Kc, Vc);
+        } else {
 #pragma unroll
         for (int h = 0; h < NSUB; ++h) {
           if (active(t, h)) {
@@ -519,6 +532,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
             settle(sc, pf, rs, mc);
             pv(Vc, h, pf);
           }
+        }
         }
 #pragma unroll
         for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
