@@ -206,25 +206,26 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
   const float c = p.c;
   typedef f32x16 qblk[BQ / 32];
+  // -D of the accumulator rows of query block qb of the tile in `slot`
+  // (queries qb*32 + 8g + 4hh + u), read from the words staged beside Q, dO.
+  auto dneg_of = [&](const char* slot, int qb) {
+    const float* dns = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES) + 64;
+    f32x16 dneg;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const float4 d4 = *reinterpret_cast<const float4*>(dns + qb * 32 + 8 * g + 4 * hh);
+      dneg[4 * g] = d4.x;
+      dneg[4 * g + 1] = d4.y;
+      dneg[4 * g + 2] = d4.z;
+      dneg[4 * g + 3] = d4.w;
+    }
+    return dneg;
+  };
   // S (queries x keys) and dP = dO V^T of the query tile in `slot`, with
   // queries as accumulator rows.
   auto sdp = [&](const char* slot, qblk& sacc, qblk& pacc) {
     const raw* Qs = reinterpret_cast<const raw*>(slot);
     const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
-    const float* dns = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES) + 64;
-    // -D of the accumulator rows of block qb (queries qb*32 + 8g + 4hh + u)
-    auto dneg_of = [&](int qb) {
-      f32x16 dneg;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const float4 d4 = *reinterpret_cast<const float4*>(dns + qb * 32 + 8 * g + 4 * hh);
-        dneg[4 * g] = d4.x;
-        dneg[4 * g + 1] = d4.y;
-        dneg[4 * g + 2] = d4.z;
-        dneg[4 * g + 3] = d4.w;
-      }
-      return dneg;
-    };
     if constexpr (L::PREFETCH) {
       // groups of GK k-steps of one query block, read one group ahead
       constexpr int GK = L::GK, NG = D / 16 / GK;
@@ -242,7 +243,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
       for (int g = 0; g < BQ / 32 * NG; ++g) {
         const int qb = g / NG, k0 = (g % NG) * GK;
-        if (k0 == 0) dneg = dneg_of(qb);
+        if (k0 == 0) dneg = dneg_of(slot, qb);
         if (g + 1 < BQ / 32 * NG) ld(g + 1, (g + 1) & 1);
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -256,7 +257,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     } else {
 #pragma unroll
       for (int qb = 0; qb < BQ / 32; ++qb) {
-        const f32x16 dneg = dneg_of(qb);
+        const f32x16 dneg = dneg_of(slot, qb);
 #pragma unroll
         for (int kc = 0; kc < D / 16; ++kc) {
           const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
@@ -366,7 +367,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     const raw* Qs = reinterpret_cast<const raw*>(slot);
     const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
     const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
-    const float* dns = lse2s + 64;
     qblk sacc, pacc;
     qfrag pf, sf;
     auto soft_half = [&](int qb, int t) {
@@ -427,16 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int g = 0; g < NGRP; ++g) {
       const int qb = g / NG, k0 = (g % NG) * GK;
-      if (k0 == 0) {
-#pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          const float4 d4 = *reinterpret_cast<const float4*>(dns + qb * 32 + 8 * g4 + 4 * hh);
-          dneg[4 * g4] = d4.x;
-          dneg[4 * g4 + 1] = d4.y;
-          dneg[4 * g4 + 2] = d4.z;
-          dneg[4 * g4 + 3] = d4.w;
-        }
-      }
+      if (k0 == 0) dneg = dneg_of(slot, qb);
       if (g + 1 < NGRP) ld(g + 1, (g + 1) & 1);
       else gld(0, 0);
       __builtin_amdgcn_sched_barrier(0);
