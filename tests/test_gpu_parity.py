@@ -328,6 +328,26 @@ def test_blocksparse_split(case):
             TOL[dtype], label=f"split vs unsplit {case}")
 
 
+def test_blocksparse_split_edge_cases():
+    # key_chunk >= N: one split, no workspace, the unsplit forward's results;
+    # an all-ones block mask through the split path equals the dense forward.
+    prob = inputs.make_problem(1, 2, 520, 64, "bf16", seed=503, causal=True)
+    q, k, v = (dev(x, "bf16") for x in (prob.q, prob.k, prob.v))
+    nb = (520 + 127) // 128
+    ones = torch.ones(nb, nb, dtype=torch.uint8, device="cuda")
+    kw = dict(scale=float(prob.scale), causal=True)
+    o1, l1 = fa_forward_blocksparse_split(q, k, v, ones, 128, key_chunk=1024, **kw)
+    o2, l2 = fa_forward_blocksparse_split(q, k, v, ones, 128, key_chunk=192, **kw)
+    od, ld = fa_forward(q, k, v, **kw)
+    torch.cuda.synchronize()
+    dense = {"o": od.double().cpu().numpy(), "lse": ld.double().cpu().numpy()}
+    one = {"o": o1.double().cpu().numpy(), "lse": l1.double().cpu().numpy()}
+    assert np.array_equal(one["o"], dense["o"]) and np.array_equal(one["lse"], dense["lse"])
+    compare({"o": o2.double().cpu().numpy(), "lse": l2.double().cpu().numpy()}, dense,
+            TOL["bf16"], label="3 splits, all-ones mask vs dense")
+    compare(dense, run_oracle(prob, backward=False), TOL["bf16"], label="dense vs oracle")
+
+
 @pytest.mark.parametrize("n", [32768, 65536])
 def test_config_block_sparse_long_split(n):
     # The long structured workloads through the split forward (16384 keys per
