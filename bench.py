@@ -2,26 +2,33 @@
 
 One step = one forward (fa_forward) plus one backward (fa_backward) over one
 batch of synthetic inputs already resident in HBM.  The default workload is
-GPT-2-small-shaped causal self-attention (B=8, H=12, N=1024, d=64, bf16).
+the largest point of the metric's sequence-length range: long-context causal
+self-attention, B=2, H=8, N=16384, d=64, bf16.
 
-    python bench.py [--steps K] [--warmup W] [--config NAME [--n N --d D]]
+    python bench.py [--steps K] [--warmup W] [--config NAME [--n N --d D]] [--no-sweep]
 
 Prints one JSON line.  ``value`` is algorithmic forward+backward TFLOP/s
-(14 * d flops per kept query-key pair) of the whole job.  The inference
-workloads (``--config kv_decode`` / ``kv_chunk``: new queries against a
-key/value cache, fa_forward_kv; ``varlen_prefill``: packed sequences of
-several lengths, fa_forward_varlen) have no backward: there a step is one
-inference forward and ``value`` its algorithmic TFLOP/s (4 * d per pair).  ``roofline``
-describes the kernel that takes most of the step, timed with the library's
-per-launch HIP events over a second pass of the same K steps; ``cpu_baseline``
-times the fp64 oracle on the host on a bounded sample of the same workload.
+(14 * d flops per kept query-key pair) of the whole job.  ``sweep`` repeats
+the forward and forward+backward timing at every point of the metric (the
+GPT-2-shaped N=1024 workload and the long-context points N = 2K..16K,
+d = 64 and 128).  The inference workloads (``--config kv_decode`` /
+``kv_chunk``: new queries against a key/value cache, fa_forward_kv;
+``varlen_prefill``: packed sequences of several lengths, fa_forward_varlen)
+have no backward: there a step is one inference forward and ``value`` its
+algorithmic TFLOP/s (4 * d per pair).
+
+Kernel times: each kernel is launched through its own entry point (the
+forward, the backward's dQ pass, the backward's dK/dV pass) K times back to
+back between two HIP events recorded on the launch stream, so no event sits
+between two launches; ``kernels_sum_us`` reports their sum beside the step
+time.  ``roofline`` describes the kernel that takes most of the step;
+``cpu_baseline`` times the fp64 oracle on the host on a bounded sample of the
+same workload.
 """
 
 import argparse
-import hashlib
 import json
 import os
-import re
 import sys
 import time
 
@@ -31,14 +38,13 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-from exact_io_aware_52_amd import (accounting, fa_backward, fa_backward_workspace_bytes,  # noqa: E402
-                                   fa_forward, fa_forward_blocksparse,
+from exact_io_aware_52_amd import (accounting, build_lib, fa_backward,  # noqa: E402
+                                   fa_backward_dkdv, fa_backward_dq,
+                                   fa_backward_workspace_bytes, fa_forward,
                                    fa_forward_blocksparse_split,
-                                   fa_forward_blocksparse_split_workspace_bytes, fa_forward_kv,
-                                   fa_forward_kv_workspace_bytes, fa_forward_varlen,
-                                   fa_forward_block_rows_for, fa_kernel_name,
-                                   fa_set_forward_block_rows, fa_timing_enable, fa_timing_read,
-                                   inputs)
+                                   fa_forward_blocksparse_split_workspace_bytes, fa_forward_ex,
+                                   fa_forward_kv, fa_forward_kv_workspace_bytes,
+                                   fa_forward_varlen, fa_forward_block_rows_for, inputs)
 
 PEAK_TFLOPS = {"bf16": 2500.0, "fp16": 2500.0, "fp32": 157.3}   # dense MFMA, MI355X
 PEAK_HBM_GBS = 8000.0
@@ -47,31 +53,24 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 # forward S and PV; the dK/dV pass does the recomputed S, dP, dV and dK; the
 # dQ pass contributes the dQ product only (its S and dP repeat the dK/dV pass).
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
-KERNEL_SOURCES = {
-    "fwd": ["fa_fwd.hip", "fa_common.h"],
-    "fwd_combine": ["fa_fwd.hip", "fa_common.h"],
-    "bwd_dkdv": ["fa_bwd_impl.h", "fa_common.h"],
-    "bwd_dq": ["fa_bwd_impl.h", "fa_common.h"],
-}
+KERNEL_NAMES = {"fwd": "fa_fwd_kernel", "fwd_combine": "fa_fwd_combine_kernel",
+                "bwd_dq": "fa_bwd_dq_kernel", "bwd_dkdv": "fa_bwd_dkdv_kernel"}
+METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak"
 
 
-def source_hash(kind):
-    """Hash of the code (comments and whitespace removed) of the sources a
-    kernel is built from: a counter summary stays valid across comment-only
-    edits and is dropped when the code changes."""
-    h = hashlib.sha256()
-    for f in KERNEL_SOURCES[kind]:
-        with open(os.path.join(ROOT, "exact_io_aware_52_amd", "csrc", f), encoding="utf-8") as fh:
-            text = fh.read()
-        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
-        text = re.sub(r"//[^\n]*", " ", text)
-        h.update(" ".join(text.split()).encode())
-    return h.hexdigest()[:16]
+def code_hashes():
+    """Hashes of the built kernels' machine code (written by the build)."""
+    try:
+        with open(build_lib.CODE_MANIFEST) as fh:
+            return json.load(fh)
+    except (OSError, ValueError):
+        return {}
 
 
 def read_traffic(kernel, workload):
     """HBM bytes per launch from a committed counter summary, or None when
-    there is none or the kernel source changed since it was taken."""
+    there is none or the kernel's machine code differs from the code the
+    counters were taken on."""
     path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
@@ -80,8 +79,8 @@ def read_traffic(kernel, workload):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    kind = {v: k for k, v in KERNEL_NAMES.items()}.get(kernel)
-    if kind is None or fields.get("source_sha256") != source_hash(kind):
+    built = code_hashes().get(kernel)
+    if built is None or fields.get("code_sha256") != built:
         return None
     try:
         return float(fields["traffic_bytes_per_launch"])
@@ -89,7 +88,17 @@ def read_traffic(kernel, workload):
         return None
 
 
-KERNEL_NAMES = {}
+def event_time_ms(fn, n):
+    """Average milliseconds of fn() over n back-to-back calls, between two
+    HIP events on the current stream (the stream the library launches on)."""
+    stream = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n
 
 
 def make_workload(args):
@@ -281,7 +290,6 @@ def bench_kv(args, dev):
     """One step = one fa_forward_kv call (new queries against a key/value
     cache); no backward.  The roofline names the bound with the longer time
     at peak for the forward kernel's work: HBM bytes or matrix flops."""
-    KERNEL_NAMES["fwd_combine"] = fa_kernel_name("fwd_combine")
     prob = inputs.kv_workload(args.config)
     dt = TORCH_DT[prob.dtype]
     q, k, v = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v))
@@ -304,23 +312,15 @@ def bench_kv(args, dev):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-
-    fa_timing_enable(True)
-    for kind in ("fwd", "fwd_combine"):
-        fa_timing_read(kind)
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    fa_timing_enable(False)
-    kernels = {}
-    for kind in ("fwd", "fwd_combine"):
-        total, n = fa_timing_read(kind)
-        kernels[kind] = {"name": KERNEL_NAMES[kind], "avg_us": 1e3 * total / max(n, 1),
-                         "launches": n}
+    # The call is the forward kernel plus, when the key range is split, the
+    # merge kernel; both are timed together between two events.
+    call_us = 1e3 * event_time_ms(step, args.steps)
+    splits = kv_splits(prob)
+    unit = KERNEL_NAMES["fwd"] + (" + " + KERNEL_NAMES["fwd_combine"] if splits > 1 else "")
+    kernels = {"fwd": {"name": unit, "avg_us": call_us}}
 
     pairs = accounting.kv_kept_pairs(prob)
     flops = 4 * prob.d * pairs
-    splits = kv_splits(prob)
     nbytes = accounting.kv_forward_bytes(prob, splits)
     t_fwd = kernels["fwd"]["avg_us"] * 1e-6
     peak = PEAK_TFLOPS[prob.dtype]
@@ -332,12 +332,12 @@ def bench_kv(args, dev):
         achieved = flops / t_fwd / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                 "unit": "TFLOP/s", "frac": round(achieved / peak, 4)}
-    roof["traffic"] = read_traffic(KERNEL_NAMES["fwd"], prob.name)
-    roof["kernel"] = KERNEL_NAMES["fwd"]
+    roof["traffic"] = read_traffic(KERNEL_NAMES["fwd"], prob.name) if splits == 1 else None
+    roof["kernel"] = unit
     roof["kernel_avg_us"] = round(kernels["fwd"]["avg_us"], 2)
     roof["algorithmic_bytes"] = nbytes
     result = {
-        "metric": "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak",
+        "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 3),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -385,14 +385,7 @@ def bench_varlen(args, dev):
         step()
     torch.cuda.synchronize()
     ms_step = (time.perf_counter() - t0) * 1e3 / args.steps
-    fa_timing_enable(True)
-    fa_timing_read("fwd")
-    for _ in range(args.steps):
-        step()
-    torch.cuda.synchronize()
-    fa_timing_enable(False)
-    total, n = fa_timing_read("fwd")
-    avg_us = 1e3 * total / max(n, 1)
+    avg_us = 1e3 * event_time_ms(step, args.steps)   # one kernel per call
     pairs = accounting.varlen_kept_pairs(prob)
     flops = 4 * prob.d * pairs
     peak = PEAK_TFLOPS[prob.dtype]
@@ -402,7 +395,7 @@ def bench_varlen(args, dev):
             "traffic": read_traffic(KERNEL_NAMES["fwd"], prob.name),
             "kernel": KERNEL_NAMES["fwd"], "kernel_avg_us": round(avg_us, 2)}
     result = {
-        "metric": "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak",
+        "metric": METRIC,
         "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -456,21 +449,127 @@ def cpu_baseline_varlen(prob, budget_s):
                       f"fp64 forward, {dt:.1f} s"}
 
 
+class Runner:
+    """Device buffers and launch closures for one self-attention workload."""
+
+    def __init__(self, prob, dev, fwd_block_rows=0):
+        self.prob = prob
+        dt = TORCH_DT[prob.dtype]
+        self.q, self.k, self.v, self.do = (torch.from_numpy(x).to(dt).to(dev)
+                                           for x in (prob.q, prob.k, prob.v, prob.do))
+        self.kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).to(dev)
+        self.bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).to(dev)
+        self.o = torch.empty_like(self.q)
+        self.lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=dev)
+        self.dq, self.dk, self.dv = (torch.empty_like(self.q) for _ in range(3))
+        self.ws = torch.empty(fa_backward_workspace_bytes(prob.B, prob.H, prob.N, prob.d),
+                              dtype=torch.uint8, device=dev)
+        self.scale = float(prob.scale)
+        self.rows = fwd_block_rows
+        self.fwd_rows = fwd_block_rows or fa_forward_block_rows_for(
+            prob.B, prob.H, prob.N, prob.d, dt, prob.block_mask is not None)
+        # The long structured masks give one query tile per head the whole key
+        # range: its forward is split four ways over work-groups (measured best
+        # of 4K, 8K and 16K keys per split at N = 32K and 64K).
+        self.key_chunk = 0
+        if prob.name.startswith("block_sparse_long"):
+            self.key_chunk = -(-prob.N // (4 * 64)) * 64
+            self.split_ws = torch.empty(max(fa_forward_blocksparse_split_workspace_bytes(
+                prob.B, prob.H, prob.N, prob.d, self.key_chunk), 1), dtype=torch.uint8,
+                device=dev)
+        self.kw = dict(scale=self.scale, causal=prob.causal, key_lens=self.kl,
+                       block_mask=self.bm, block_size=prob.block_size)
+
+    def fwd(self):
+        if self.key_chunk:
+            fa_forward_blocksparse_split(self.q, self.k, self.v, self.bm, self.prob.block_size,
+                                         key_chunk=self.key_chunk, scale=self.scale,
+                                         causal=self.prob.causal, key_lens=self.kl, o=self.o,
+                                         lse=self.lse, workspace=self.split_ws)
+        else:
+            fa_forward_ex(self.q, self.k, self.v, block_rows=self.rows, o=self.o, lse=self.lse,
+                          **self.kw)
+
+    def bwd_dq(self):
+        fa_backward_dq(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq,
+                       workspace=self.ws, **self.kw)
+
+    def bwd_dkdv(self):
+        fa_backward_dkdv(self.q, self.k, self.v, self.do, self.ws, dk=self.dk, dv=self.dv,
+                         **self.kw)
+
+    def step(self):
+        self.fwd()
+        fa_backward(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq, dk=self.dk,
+                    dv=self.dv, workspace=self.ws, **self.kw)
+
+
+def wall_ms(fn, n):
+    """Average milliseconds of fn() over n calls, host clock, synchronised
+    on both sides."""
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(n):
+        fn()
+    torch.cuda.synchronize()
+    return (time.perf_counter() - t0) * 1e3 / n
+
+
+def measure(run, steps, warmup, kernels=True):
+    """Step time, forward time and (optionally) per-kernel times of a Runner."""
+    for _ in range(warmup):
+        run.step()
+    out = {"ms_step": wall_ms(run.step, steps), "ms_fwd": wall_ms(run.fwd, steps)}
+    if kernels:
+        out["kernels_us"] = {
+            "fwd": 1e3 * event_time_ms(run.fwd, steps),
+            "bwd_dq": 1e3 * event_time_ms(run.bwd_dq, steps),
+            "bwd_dkdv": 1e3 * event_time_ms(run.bwd_dkdv, steps),
+        }
+    return out
+
+
+def sweep(dev, steps, warmup):
+    """Forward and forward+backward TFLOP/s at every point of the metric."""
+    points = [("gpt2_small", None, None)] + [("long_causal", n, d) for n, d in inputs.LONG_POINTS]
+    rows = []
+    for name, n, d in points:
+        prob = inputs.workload(name, n, d)
+        run = Runner(prob, dev)
+        m = measure(run, steps, warmup, kernels=False)
+        pairs = accounting.kept_pairs(prob)
+        peak = PEAK_TFLOPS[prob.dtype]
+        fwd_tf = 4 * prob.d * pairs / (m["ms_fwd"] * 1e-3) / 1e12
+        fb_tf = 14 * prob.d * pairs / (m["ms_step"] * 1e-3) / 1e12
+        rows.append({"workload": prob.name, "N": prob.N, "d": prob.d, "causal": prob.causal,
+                     "fwd_ms": round(m["ms_fwd"], 4), "fwd_tflops": round(fwd_tf, 1),
+                     "fwd_frac": round(fwd_tf / peak, 4),
+                     "fwdbwd_ms": round(m["ms_step"], 4), "fwdbwd_tflops": round(fb_tf, 1),
+                     "fwdbwd_frac": round(fb_tf / peak, 4), "fwd_block_rows": run.fwd_rows})
+        print(f"[sweep] {prob.name}: fwd {fwd_tf:.0f} TFLOP/s, fwd+bwd {fb_tf:.0f} TFLOP/s",
+              file=sys.stderr, flush=True)
+        del run
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--config", default="gpt2_small",
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="long_causal",
                     choices=["tiny", "gpt2_small", "bert_large_padded", "long_causal",
                              "block_sparse", "block_sparse_long", "kv_decode", "kv_chunk",
                              "varlen_prefill"])
-    ap.add_argument("--n", type=int, default=4096)
+    ap.add_argument("--n", type=int, default=16384)
     ap.add_argument("--d", type=int, default=64)
     ap.add_argument("--fwd-block-rows", type=int, default=0, choices=[0, 64, 128, 256],
                     help="query rows per forward work-group (tile height); 0 = chosen per problem")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of host work for the oracle baseline (0 disables)")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the timing sweep over the metric's other points")
     ap.add_argument("--standard", action="store_true",
                     help="time standard (materialising) attention on the workload beside the "
                          "tiled kernels")
@@ -501,10 +600,6 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30}))
         return
-
-    for k in ("fwd", "fwd_combine", "bwd_dkdv", "bwd_dq"):
-        KERNEL_NAMES[k] = fa_kernel_name(k)
-
     if args.standard:
         bench_standard(args, dev)
         return
@@ -515,92 +610,28 @@ def main():
         bench_varlen(args, dev)
         return
 
-    fa_set_forward_block_rows(args.fwd_block_rows)
     prob = make_workload(args)
-    fwd_rows = fa_forward_block_rows_for(prob.B, prob.H, prob.N, prob.d, TORCH_DT[prob.dtype],
-                                         prob.block_mask is not None)
-    dt = TORCH_DT[prob.dtype]
-    q, k, v, do = (torch.from_numpy(x).to(dt).to(dev) for x in (prob.q, prob.k, prob.v, prob.do))
-    kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).to(dev)
-    bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).to(dev)
-    o = torch.empty_like(q)
-    lse = torch.empty(prob.B, prob.H, prob.N, dtype=torch.float32, device=dev)
-    dq, dk, dv = (torch.empty_like(q) for _ in range(3))
-    ws = torch.empty(fa_backward_workspace_bytes(prob.B, prob.H, prob.N, prob.d),
-                     dtype=torch.uint8, device=dev)
-    scale = float(prob.scale)
-    # The long structured masks give one query tile per head the whole key
-    # range: its forward is split four ways over work-groups (measured best
-    # of 4K, 8K and 16K keys per split at N = 32K and 64K).
-    key_chunk = 0
-    if prob.name.startswith("block_sparse_long"):
-        key_chunk = -(-prob.N // (4 * 64)) * 64
-        split_ws = torch.empty(max(fa_forward_blocksparse_split_workspace_bytes(
-            prob.B, prob.H, prob.N, prob.d, key_chunk), 1), dtype=torch.uint8, device=dev)
-
-    def fwd():
-        if key_chunk:
-            fa_forward_blocksparse_split(q, k, v, bm, prob.block_size, key_chunk=key_chunk,
-                                         scale=scale, causal=prob.causal, key_lens=kl, o=o,
-                                         lse=lse, workspace=split_ws)
-        elif bm is not None:
-            fa_forward_blocksparse(q, k, v, bm, prob.block_size, scale=scale, causal=prob.causal,
-                                   key_lens=kl, o=o, lse=lse)
-        else:
-            fa_forward(q, k, v, scale=scale, causal=prob.causal, key_lens=kl, o=o, lse=lse)
-
-    def step():
-        fwd()
-        fa_backward(q, k, v, o, do, lse, scale=scale, causal=prob.causal, key_lens=kl,
-                    block_mask=bm, block_size=prob.block_size, dq=dq, dk=dk, dv=dv,
-                    workspace=ws)
-
-    def timed(fn, n):
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(n):
-            fn()
-        torch.cuda.synchronize()
-        return (time.perf_counter() - t0) * 1e3 / n
-
-    for _ in range(args.warmup):
-        step()
-    ms_step = timed(step, args.steps)
-    ms_fwd = timed(fwd, args.steps)
-
-    # Second pass with per-launch HIP events (recorded on the launch stream).
-    fa_timing_enable(True)
-    for kind in KERNEL_NAMES:
-        fa_timing_read(kind)
-    timed(step, args.steps)
-    fa_timing_enable(False)
-    kernels = {}
-    for kind in KERNEL_NAMES:
-        total, n = fa_timing_read(kind)
-        kernels[kind] = {"name": KERNEL_NAMES[kind], "avg_us": 1e3 * total / max(n, 1),
-                         "launches": n}
-
+    run = Runner(prob, dev, args.fwd_block_rows)
+    m = measure(run, args.steps, args.warmup)
+    ms_step, ms_fwd, kus = m["ms_step"], m["ms_fwd"], m["kernels_us"]
     pairs = accounting.kept_pairs(prob)
     flops_step = 14 * prob.d * pairs
     value = flops_step / (ms_step * 1e-3) / 1e12
-    dom = max((k for k in kernels if kernels[k]["launches"]), key=lambda k: kernels[k]["avg_us"])
-    if dom in KERNEL_FLOPS_PER_PAIR_D:
-        work = KERNEL_FLOPS_PER_PAIR_D[dom] * prob.d * pairs
-        achieved = work / (kernels[dom]["avg_us"] * 1e-6) / 1e12
-        peak = PEAK_TFLOPS[prob.dtype]
-        roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
-                "frac": round(achieved / peak, 4)}
-    else:
-        work = accounting.ELEM_BYTES[prob.dtype] * 2 * prob.B * prob.H * prob.N * prob.d
-        achieved = work / (kernels[dom]["avg_us"] * 1e-6) / 1e9
-        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_HBM_GBS,
-                "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4)}
-    roof["traffic"] = read_traffic(KERNEL_NAMES[dom], prob.name)
-    roof["kernel"] = KERNEL_NAMES[dom]
-    roof["kernel_avg_us"] = round(kernels[dom]["avg_us"], 2)
+    dom = max(kus, key=kus.get)
+    fwd_unit = KERNEL_NAMES["fwd"] + (" + " + KERNEL_NAMES["fwd_combine"] if run.key_chunk else "")
+    names = dict(KERNEL_NAMES, fwd=fwd_unit)
+    work = KERNEL_FLOPS_PER_PAIR_D[dom] * prob.d * pairs
+    achieved = work / (kus[dom] * 1e-6) / 1e12
+    peak = PEAK_TFLOPS[prob.dtype]
+    roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(achieved / peak, 4),
+            "traffic": (read_traffic(KERNEL_NAMES[dom], prob.name)
+                        if not (dom == "fwd" and run.key_chunk) else None),
+            "kernel": names[dom], "kernel_avg_us": round(kus[dom], 2),
+            "algorithmic_flops_per_launch": work}
 
     result = {
-        "metric": "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak",
+        "metric": METRIC,
         "value": round(value, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
@@ -616,14 +647,20 @@ def main():
                    "causal": prob.causal,
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
-                   "fwd_block_rows": fwd_rows, "fwd_key_chunk": key_chunk or None,
+                   "fwd_block_rows": run.fwd_rows, "fwd_key_chunk": run.key_chunk or None,
                    "parallelism": "none"},
         "fwd_ms": round(ms_fwd, 4),
         "fwd_tflops": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12, 2),
-        "frac_of_peak_fwd_bwd": round(value / PEAK_TFLOPS[prob.dtype], 4),
-        "kernels_us": {v["name"]: round(v["avg_us"], 2) for v in kernels.values() if v["launches"]},
+        "frac_of_peak_fwd": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12 / peak, 4),
+        "frac_of_peak_fwd_bwd": round(value / peak, 4),
+        "kernels_us": {names[k]: round(v, 2) for k, v in kus.items()},
+        "kernels_sum_us": round(sum(kus.values()), 2),
         "roofline": roof,
     }
+    del run
+    torch.cuda.empty_cache()
+    if not args.no_sweep and args.config == "long_causal":
+        result["sweep"] = sweep(dev, max(5, args.steps // 2), max(2, args.warmup // 2))
     if args.cpu_budget > 0:
         result["cpu_baseline"] = cpu_baseline(prob, args.cpu_budget)
     print(json.dumps(result), flush=True)

@@ -10,9 +10,8 @@ declared in ``include/fa.h``); this package only marshals torch tensors
 
 from ._binding import (  # noqa: F401
     FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP,
-    FaError, library_path, load_library, fa_forward, fa_forward_blocksparse,
+    FaError, library_path, load_library, fa_forward, fa_forward_ex, fa_forward_blocksparse,
     fa_forward_blocksparse_split, fa_forward_blocksparse_split_workspace_bytes, fa_backward,
-    fa_backward_workspace_bytes, fa_timing_enable, fa_timing_read, fa_kernel_name,
-    fa_set_forward_block_rows, fa_get_forward_block_rows, fa_forward_block_rows_for, fa_forward_kv,
-    fa_forward_kv_workspace_bytes, fa_forward_varlen, KERNEL_KINDS,
+    fa_backward_dq, fa_backward_dkdv, fa_backward_workspace_bytes, fa_forward_block_rows_for,
+    fa_forward_kv, fa_forward_kv_workspace_bytes, fa_forward_varlen,
 )

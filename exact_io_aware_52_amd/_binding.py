@@ -10,11 +10,11 @@ import ctypes
 import math
 import os
 
+import numpy as np
 import torch
 
 FA_OK, FA_ERR_INVALID_ARG, FA_ERR_UNSUPPORTED, FA_ERR_WORKSPACE, FA_ERR_HIP = range(5)
 _DTYPE_CODE = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}
-KERNEL_KINDS = {"fwd": 0, "bwd_dkdv": 1, "bwd_dq": 2, "fwd_combine": 3}
 
 _LIB = None
 
@@ -32,9 +32,14 @@ def library_path():
 def load_library():
     """Load libfa.so (once) and declare the C signatures."""
     global _LIB
-    if _LIB is not None:
-        return _LIB
-    path = library_path()
+    if _LIB is None:
+        _LIB = open_library(library_path())
+    return _LIB
+
+
+def open_library(path):
+    """Load a build of the library (libfa.so, or the race-check build
+    libfa_serial.so) with the C signatures declared; raises if it is missing."""
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is missing: build it with "
                            "`python -m exact_io_aware_52_amd.build_lib`")
@@ -47,30 +52,24 @@ def load_library():
     lib.fa_forward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_forward_blocksparse_split_workspace_bytes.restype = Z
     lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
+    lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
+    lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
+    lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P]
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = Z
     lib.fa_status_string.argtypes = [I]
     lib.fa_status_string.restype = ctypes.c_char_p
     lib.fa_last_error_detail.argtypes = []
     lib.fa_last_error_detail.restype = ctypes.c_char_p
-    lib.fa_timing_enable.argtypes = [I]
-    lib.fa_timing_read.argtypes = [I, ctypes.POINTER(ctypes.c_double), ctypes.POINTER(I)]
-    lib.fa_kernel_name.argtypes = [I]
-    lib.fa_kernel_name.restype = ctypes.c_char_p
-    lib.fa_set_forward_block_rows.argtypes = [I]
-    lib.fa_get_forward_block_rows.argtypes = []
     lib.fa_forward_block_rows_for.argtypes = [I, I, I, I, I, I]
     lib.fa_forward_kv.argtypes = [P, P, P, P, P, I, I, I, I, I, F, I, P, I, P, Z, P]
     lib.fa_forward_kv_workspace_bytes.argtypes = [I, I, I, I, I, I]
     lib.fa_forward_kv_workspace_bytes.restype = Z
     lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_forward_blocksparse_split,
-               lib.fa_backward,
-               lib.fa_timing_enable, lib.fa_timing_read, lib.fa_set_forward_block_rows,
-               lib.fa_get_forward_block_rows, lib.fa_forward_block_rows_for, lib.fa_forward_kv,
-               lib.fa_forward_varlen):
+               lib.fa_forward_ex, lib.fa_backward, lib.fa_backward_dq, lib.fa_backward_dkdv,
+               lib.fa_forward_block_rows_for, lib.fa_forward_kv, lib.fa_forward_varlen):
         fn.restype = I
-    _LIB = lib
     return lib
 
 
@@ -144,7 +143,8 @@ def _scale(scale, d):
     return float(1.0 / math.sqrt(d)) if scale is None else float(scale)
 
 
-def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, lse):
+def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, lse,
+             block_rows=0):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     o = torch.empty_like(q) if o is None else _like("o", o, q)
@@ -153,9 +153,11 @@ def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, 
     kl = _lens(key_lens, B, q.device)
     args = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse), B, H, N, d,
             _scale(scale, d), int(bool(causal)), _ptr(kl)]
-    if name == "fa_forward_blocksparse":
+    if name in ("fa_forward_blocksparse", "fa_forward_ex"):
         bm = _mask(block_mask, N, block_size, q.device)
         args += [_ptr(bm), int(block_size)]
+    if name == "fa_forward_ex":
+        args += [int(block_rows)]
     args += [_DTYPE_CODE[q.dtype], _stream(q.device)]
     _check(name, getattr(lib, name)(*args))
     return o, lse
@@ -173,6 +175,14 @@ def fa_forward_blocksparse(q, k, v, block_mask, block_size=128, scale=None, caus
         raise ValueError("block_mask is required")
     return _forward("fa_forward_blocksparse", q, k, v, scale, causal, key_lens, block_mask,
                     block_size, o, lse)
+
+
+def fa_forward_ex(q, k, v, block_mask=None, block_size=128, block_rows=0, scale=None,
+                  causal=False, key_lens=None, o=None, lse=None):
+    """Forward with the query rows per work-group (64, 128, 256; 0 = the
+    library's choice) given per call; block_mask optional."""
+    return _forward("fa_forward_ex", q, k, v, scale, causal, key_lens, block_mask, block_size,
+                    o, lse, block_rows)
 
 
 def fa_forward_blocksparse_split_workspace_bytes(B, H, N, d, key_chunk):
@@ -269,6 +279,18 @@ def fa_forward_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, scale=N
     for name, t in (("q", q), ("k", k), ("v", v)):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
+    # The kernel's grid covers max_seqlen_q rows per sequence; a longer
+    # sequence would be left partly unwritten.  The library cannot see device
+    # prefix sums; check them here whenever they come from the host.
+    for name, cu in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if isinstance(cu, torch.Tensor) and cu.device.type != "cpu":
+            continue
+        lens = np.diff(np.asarray(cu, dtype=np.int64))
+        if lens.size and np.any(lens < 0):
+            raise ValueError(f"{name} must be non-decreasing")
+        if name == "cu_seqlens_q" and lens.size and int(lens.max()) > int(max_seqlen_q):
+            raise ValueError(f"max_seqlen_q={int(max_seqlen_q)} is below the longest "
+                             f"query sequence ({int(lens.max())})")
     if q.dtype not in _DTYPE_CODE:
         raise ValueError(f"unsupported dtype {q.dtype}")
     if q.device.type != "cuda":
@@ -292,41 +314,66 @@ def fa_backward_workspace_bytes(B, H, N, d):
     return int(load_library().fa_backward_workspace_bytes(B, H, N, d))
 
 
-def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
-                block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None):
-    """Backward pass: returns (dQ, dK, dV) in q.dtype."""
+def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, block_size,
+              dq, dk, dv, workspace):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
-    _like("o", o, q)
     _like("dout", dout, q)
-    _like("lse", lse, q, (B, H, N), torch.float32)
-    dq = torch.empty_like(q) if dq is None else _like("dq", dq, q)
-    dk = torch.empty_like(q) if dk is None else _like("dk", dk, q)
-    dv = torch.empty_like(q) if dv is None else _like("dv", dv, q)
+    if name != "fa_backward_dkdv":
+        _like("o", o, q)
+        _like("lse", lse, q, (B, H, N), torch.float32)
+    if name != "fa_backward_dkdv":
+        dq = torch.empty_like(q) if dq is None else _like("dq", dq, q)
+    if name != "fa_backward_dq":
+        dk = torch.empty_like(q) if dk is None else _like("dk", dk, q)
+        dv = torch.empty_like(q) if dv is None else _like("dv", dv, q)
     need = fa_backward_workspace_bytes(B, H, N, d)
     if workspace is None:
+        if name == "fa_backward_dkdv":
+            raise ValueError("fa_backward_dkdv reads the workspace fa_backward_dq filled")
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     elif workspace.device != q.device or not workspace.is_contiguous():
         raise ValueError("workspace must be a contiguous tensor on the device of q")
     kl = _lens(key_lens, B, q.device)
     bm = _mask(block_mask, N, block_size, q.device)
-    st = lib.fa_backward(_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse),
-                         _ptr(dq), _ptr(dk), _ptr(dv), B, H, N, d, _scale(scale, d),
-                         int(bool(causal)), _ptr(kl), _ptr(bm), int(block_size),
-                         _DTYPE_CODE[q.dtype], _ptr(workspace),
-                         workspace.numel() * workspace.element_size(), _stream(q.device))
-    _check("fa_backward", st)
+    tail = [B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm),
+            int(block_size), _DTYPE_CODE[q.dtype], _ptr(workspace),
+            workspace.numel() * workspace.element_size(), _stream(q.device)]
+    if name == "fa_backward":
+        head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
+                _ptr(dv)]
+    elif name == "fa_backward_dq":
+        head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq)]
+    else:
+        head = [_ptr(q), _ptr(k), _ptr(v), _ptr(dout), _ptr(dk), _ptr(dv)]
+    _check(name, getattr(lib, name)(*(head + tail)))
+    return dq, dk, dv, workspace
+
+
+def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
+                block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None):
+    """Backward pass: returns (dQ, dK, dV) in q.dtype."""
+    dq, dk, dv, _ = _backward("fa_backward", q, k, v, o, dout, lse, scale, causal, key_lens,
+                              block_mask, block_size, dq, dk, dv, workspace)
     return dq, dk, dv
 
 
-def fa_set_forward_block_rows(rows):
-    """Query rows per forward work-group: 64, 128, 256, or 0 (default) to
-    choose per call."""
-    _check("fa_set_forward_block_rows", load_library().fa_set_forward_block_rows(int(rows)))
+def fa_backward_dq(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
+                   block_mask=None, block_size=128, dq=None, workspace=None):
+    """First backward pass: returns (dQ, workspace); the workspace then holds
+    -D and LSE * log2(e) for fa_backward_dkdv."""
+    dq, _, _, ws = _backward("fa_backward_dq", q, k, v, o, dout, lse, scale, causal, key_lens,
+                             block_mask, block_size, dq, None, None, workspace)
+    return dq, ws
 
 
-def fa_get_forward_block_rows():
-    return int(load_library().fa_get_forward_block_rows())
+def fa_backward_dkdv(q, k, v, dout, workspace, scale=None, causal=False, key_lens=None,
+                     block_mask=None, block_size=128, dk=None, dv=None):
+    """Second backward pass, from the workspace fa_backward_dq filled:
+    returns (dK, dV)."""
+    _, dk, dv, _ = _backward("fa_backward_dkdv", q, k, v, None, dout, None, scale, causal,
+                             key_lens, block_mask, block_size, None, dk, dv, workspace)
+    return dk, dv
 
 
 def fa_forward_block_rows_for(B, H, N, d, dtype, sparse=False):
@@ -334,22 +381,3 @@ def fa_forward_block_rows_for(B, H, N, d, dtype, sparse=False):
     return int(load_library().fa_forward_block_rows_for(int(B), int(H), int(N), int(d),
                                                         (_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)),
                                                         int(bool(sparse))))
-
-
-def fa_timing_enable(enable=True):
-    _check("fa_timing_enable", load_library().fa_timing_enable(int(bool(enable))))
-
-
-def fa_timing_read(kind):
-    """(total_ms, launches) of one kernel kind since the last read."""
-    lib = load_library()
-    ms = ctypes.c_double()
-    n = ctypes.c_int()
-    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
-    _check("fa_timing_read", lib.fa_timing_read(k, ctypes.byref(ms), ctypes.byref(n)))
-    return ms.value, n.value
-
-
-def fa_kernel_name(kind):
-    k = KERNEL_KINDS[kind] if isinstance(kind, str) else int(kind)
-    return load_library().fa_kernel_name(k).decode()

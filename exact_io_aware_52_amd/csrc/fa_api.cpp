@@ -1,5 +1,6 @@
 // C ABI of the tiled attention library: argument validation, dispatch to the
-// kernel launchers, status strings and the optional kernel timing hooks.
+// kernel launchers and status strings.  No state is kept between calls apart
+// from the thread-local detail text of the last failure.
 // Every check runs on the host before any HIP call, so a rejected call has
 // launched nothing.
 
@@ -11,7 +12,6 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
-#include <vector>
 
 #include "fa_internal.h"
 
@@ -29,55 +29,20 @@ int fail(int status, const char* fmt, ...) {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-// ---------------------------------------------------------------- timing hooks
-struct EventPair {
-  hipEvent_t start = nullptr, stop = nullptr;
-};
-struct KindTimes {
-  std::vector<EventPair> pool;  // events created so far (reused after a read)
-  size_t used = 0;              // pairs recorded since the last read
-};
-bool g_timing = false;
-int g_fwd_rows = 0;  // fa_set_forward_block_rows (0: chosen per problem)
-
-// Query rows per forward work-group when none is set.  256-row tiles halve
-// the K/V bytes each query reads at L2 and, at 16-bit d = 128, run as fast or
-// faster than 128 once the grid still holds two rounds of work-groups (one
-// 256-row work-group fits a compute unit): measured N = 8K -4.3%, 16K -3.5%
-// forward time, but N = 4K (one round) +14%.  Otherwise 128.
+// Query rows per forward work-group when the caller leaves the choice to the
+// library.  256-row tiles halve the K/V bytes each query reads at L2 and, at
+// 16-bit d = 128, run as fast or faster than 128 once the grid still holds
+// two rounds of work-groups (one 256-row work-group fits a compute unit):
+// measured N = 8K -4.3%, 16K -3.5% forward time, but N = 4K (one round)
+// +14%.  Otherwise 128.
 constexpr long long kAutoTallMinGroups = 2LL * 256;  // two per CU of MI355X's 256
-int auto_fwd_rows(int B, int H, int N, int d, fa_dtype dtype, const uint8_t* block_mask) {
-  if (dtype == FA_F32 || d != 128 || block_mask) return 128;
+int auto_fwd_rows(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
+  if (dtype == FA_F32 || d != 128 || sparse) return 128;
   const long long groups = (long long)B * H * ((N + 255) / 256);
   return groups >= kAutoTallMinGroups ? 256 : 128;
 }
-KindTimes g_times[fa::kNumKernelKinds];
 
 }  // namespace
-
-namespace fa {
-
-void timing_begin(KernelKind kind, hipStream_t stream) {
-  if (!g_timing) return;
-  KindTimes& t = g_times[kind];
-  if (t.used == t.pool.size()) {
-    EventPair e;
-    if (hipEventCreate(&e.start) != hipSuccess || hipEventCreate(&e.stop) != hipSuccess) return;
-    t.pool.push_back(e);
-  }
-  (void)hipEventRecord(t.pool[t.used].start, stream);
-}
-
-void timing_end(KernelKind kind, hipStream_t stream) {
-  if (!g_timing) return;
-  KindTimes& t = g_times[kind];
-  if (t.used < t.pool.size()) {
-    (void)hipEventRecord(t.pool[t.used].stop, stream);
-    ++t.used;
-  }
-}
-
-}  // namespace fa
 
 namespace {
 
@@ -145,13 +110,17 @@ struct SplitArgs {
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const int32_t* key_lens,
                  const uint8_t* block_mask, int block_size, bool sparse, fa_dtype dtype,
-                 hipStream_t stream, const SplitArgs& split = SplitArgs()) {
+                 hipStream_t stream, const SplitArgs& split = SplitArgs(), int block_rows = 0) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
   if (st != FA_OK) return st;
   if ((st = check_block(block_mask, block_size, N, sparse)) != FA_OK) return st;
-  const int rows = g_fwd_rows ? g_fwd_rows : auto_fwd_rows(B, H, N, d, dtype, block_mask);
+  if (block_rows != 0 && block_rows != 64 && block_rows != 128 && block_rows != 256)
+    return fail(FA_ERR_UNSUPPORTED,
+                "block_rows=%d (supported: 0 = automatic, 64, 128, 256)", block_rows);
+  const int rows =
+      block_rows ? block_rows : auto_fwd_rows(B, H, N, d, dtype, block_mask != nullptr);
   if (block_mask && rows > 128)
     return fail(FA_ERR_UNSUPPORTED, "block-sparse forward with %d query rows per tile (at most 128)",
                 rows);
@@ -233,6 +202,46 @@ int check_key_chunk(int key_chunk, int N) {
   if (N > 0 && sparse_splits(N, key_chunk) > kMaxSplits)
     return fail(FA_ERR_UNSUPPORTED, "N=%d with key_chunk=%d gives more than %d splits", N,
                 key_chunk, kMaxSplits);
+  return FA_OK;
+}
+
+}  // namespace
+
+namespace {
+
+// Shared by fa_backward and its two passes.  Pointers a pass does not read
+// (passes = the dQ pass only: dk, dv; the dK/dV pass only: o, lse, dq) are
+// not checked and may be NULL.
+int backward_impl(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                  const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                  float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
+                  int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                  hipStream_t stream, int passes) {
+  g_detail[0] = 0;
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK) return st;
+  if ((st = check_block(block_mask, block_size, N, false)) != FA_OK) return st;
+  if (empty) return FA_OK;
+  const bool pdq = (passes & fa::kPassDq) != 0, pkv = (passes & fa::kPassDkDv) != 0;
+  if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
+      (st = check_tensor(v, "v", 16)) || (st = check_tensor(dout, "dout", 16)))
+    return st;
+  if (pdq && ((st = check_tensor(o, "o", 16)) || (st = check_tensor(lse, "lse", 4)) ||
+              (st = check_tensor(dq, "dq", 16))))
+    return st;
+  if (pkv && ((st = check_tensor(dk, "dk", 16)) || (st = check_tensor(dv, "dv", 16)))) return st;
+  if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
+  const size_t need = fa_backward_workspace_bytes(B, H, N, d);
+  if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
+  if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
+  if (workspace_bytes < need)
+    return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
+  fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
+  p.bwd_passes = passes;
+  fa::BwdTensors t{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace)};
+  hipError_t e = fa::launch_backward(p, t);
+  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
   return FA_OK;
 }
 
@@ -357,20 +366,16 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
   return FA_OK;
 }
 
-int fa_set_forward_block_rows(int rows) {
-  if (rows != 0 && rows != 64 && rows != 128 && rows != 256)
-    return fail(FA_ERR_UNSUPPORTED, "forward block rows %d (supported: 0 = automatic, 64, 128, 256)",
-                rows);
-  g_fwd_rows = rows;
-  return FA_OK;
+int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
+                  int N, int d, float scale, int causal, const int32_t* key_lens,
+                  const uint8_t* block_mask, int block_size, int block_rows, fa_dtype dtype,
+                  hipStream_t stream) {
+  return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
+                      block_size, false, dtype, stream, SplitArgs(), block_rows);
 }
 
-int fa_get_forward_block_rows(void) { return g_fwd_rows; }
-
 int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse) {
-  if (g_fwd_rows) return g_fwd_rows;
-  static const uint8_t any_mask = 1;
-  return auto_fwd_rows(B, H, N, d, dtype, sparse ? &any_mask : nullptr);
+  return auto_fwd_rows(B, H, N, d, dtype, sparse != 0);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
@@ -383,29 +388,29 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
                 int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                 hipStream_t stream) {
-  g_detail[0] = 0;
-  bool empty = false;
-  int st = check_common(B, H, N, d, scale, dtype, &empty);
-  if (st != FA_OK) return st;
-  if ((st = check_block(block_mask, block_size, N, false)) != FA_OK) return st;
-  if (empty) return FA_OK;
-  if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
-      (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||
-      (st = check_tensor(dout, "dout", 16)) || (st = check_tensor(lse, "lse", 4)) ||
-      (st = check_tensor(dq, "dq", 16)) || (st = check_tensor(dk, "dk", 16)) ||
-      (st = check_tensor(dv, "dv", 16)))
-    return st;
-  if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
-  const size_t need = fa_backward_workspace_bytes(B, H, N, d);
-  if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
-  if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
-  if (workspace_bytes < need)
-    return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
-  fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
-  fa::BwdTensors t{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace)};
-  hipError_t e = fa::launch_backward(p, t);
-  if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
-  return FA_OK;
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
+                       block_mask, block_size, dtype, workspace, workspace_bytes, stream,
+                       fa::kPassBoth);
+}
+
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, int B, int H, int N, int d, float scale,
+                   int causal, const int32_t* key_lens, const uint8_t* block_mask,
+                   int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal,
+                       key_lens, block_mask, block_size, dtype, workspace, workspace_bytes,
+                       stream, fa::kPassDq);
+}
+
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
+                     void* dv, int B, int H, int N, int d, float scale, int causal,
+                     const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                     fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     hipStream_t stream) {
+  return backward_impl(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, B, H, N, d, scale,
+                       causal, key_lens, block_mask, block_size, dtype, workspace,
+                       workspace_bytes, stream, fa::kPassDkDv);
 }
 
 const char* fa_status_string(int status) {
@@ -420,39 +425,5 @@ const char* fa_status_string(int status) {
 }
 
 const char* fa_last_error_detail(void) { return g_detail; }
-
-int fa_timing_enable(int enable) {
-  g_timing = enable != 0;
-  return FA_OK;
-}
-
-int fa_timing_read(int kernel, double* total_ms, int* launches) {
-  if (kernel < 0 || kernel >= fa::kNumKernelKinds || !total_ms || !launches)
-    return fail(FA_ERR_INVALID_ARG, "bad timing query");
-  KindTimes& t = g_times[kernel];
-  double total = 0.0;
-  for (size_t i = 0; i < t.used; ++i) {
-    if (hipEventSynchronize(t.pool[i].stop) != hipSuccess)
-      return fail(FA_ERR_HIP, "hipEventSynchronize failed");
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, t.pool[i].start, t.pool[i].stop) != hipSuccess)
-      return fail(FA_ERR_HIP, "hipEventElapsedTime failed");
-    total += ms;
-  }
-  *total_ms = total;
-  *launches = (int)t.used;
-  t.used = 0;
-  return FA_OK;
-}
-
-const char* fa_kernel_name(int kernel) {
-  switch (kernel) {
-    case fa::kFwd: return "fa_fwd_kernel";
-    case fa::kBwdDkDv: return "fa_bwd_dkdv_kernel";
-    case fa::kBwdDq: return "fa_bwd_dq_kernel";
-    case fa::kFwdCombine: return "fa_fwd_combine_kernel";
-  }
-  return "unknown";
-}
 
 }  // extern "C"

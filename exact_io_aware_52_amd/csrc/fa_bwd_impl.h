@@ -469,6 +469,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (tl[0] < t_end) {
     issue(tl[0], 0);
     if (tl[1] < t_end) issue(tl[1], 1);
+    FA_STAGE_FENCE();
     // The K and V fragments arrived by ordinary loads issued before these
     // copies.  Waiting for everything once here tells the compiler they have
     // landed; otherwise it waits for them (vmcnt(0)) at their first use
@@ -492,9 +493,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         const int qn = (t + 2) * BQ;
         plan.issue(Qg + (size_t)qn * D, base);
         plan.issue(dOg + (size_t)qn * D, base + L::TILE_BYTES);
+        // 64 words per copy; with 32-row tiles (fp32, d = 128) lanes 32..63
+        // would reach past the head, so the row is clamped as in issue().
         if (w < 2)
-          dma4s((uint32_t)(qn + lane) * 4u, w == 0 ? (const void*)lse2g : (const void*)dvecg,
+          dma4s((uint32_t)min(qn + lane, N - 1) * 4u,
+                w == 0 ? (const void*)lse2g : (const void*)dvecg,
                 base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
+        FA_STAGE_FENCE();
         if constexpr (L::ILV) {
           step_ilv(slot_of(step), t * BQ, false);
         } else {
@@ -512,6 +517,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         wait_tiles(tl[1] < t_end ? 1 : 0);  // tile t landed; tl[1] may be in flight
         __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
         if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+        FA_STAGE_FENCE();
         if (active(t)) {
           if constexpr (L::ILV) {
             step_ilv(slot_of(step), t * BQ, masked(t));
@@ -528,6 +534,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         tl[1] = tl[2];
         tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
       }
+      FA_STAGE_FENCE();
       ++step;
       if (tl[0] >= t_end) break;
     }
@@ -786,6 +793,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     issue(tl[0], 0);
     if (tl[1] < nkt) issue(tl[1], 1);
     if (tl[2] < nkt) issue(tl[2], 2);
+    FA_STAGE_FENCE();
     // As in the dK/dV pass: the Q and dO fragments came by ordinary loads;
     // wait for them here, once, rather than inside the loop.
     wait_vmcnt<0>();
@@ -794,11 +802,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
       wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));
       __syncthreads();  // every wave is done with step i-1
       if (step > 0 && tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+      FA_STAGE_FENCE();
       const int kt0 = tl[0] * BC;
       if (!p.causal || kt0 <= qw0 + 31) step_math(ring + (step & 3) * L::SLOT_BYTES, kt0);
       tl[0] = tl[1];
       tl[1] = tl[2];
       tl[2] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+      FA_STAGE_FENCE();
       ++step;
       if (tl[0] >= nkt) break;
     }
@@ -840,16 +850,18 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   p.causal = pb.causal;
 
   const unsigned tiles128 = (unsigned)((pb.N + 127) / 128);
-  timing_begin(kBwdDq, pb.stream);
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
-  hipError_t e = hipGetLastError();
-  timing_end(kBwdDq, pb.stream);
-  if (e != hipSuccess) return e;
-
-  timing_begin(kBwdDkDv, pb.stream);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream, p);
-  e = hipGetLastError();
-  timing_end(kBwdDkDv, pb.stream);
+  hipError_t e = hipSuccess;
+  if (pb.bwd_passes & kPassDq) {
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream,
+                       p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (pb.bwd_passes & kPassDkDv) {
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0,
+                       pb.stream, p);
+    e = hipGetLastError();
+  }
   return e;
 }
 

@@ -153,6 +153,23 @@ template <int N> __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((N & 15) | (((N >> 4) & 3) << 14) | (7 << 4) | (15 << 8));
 }
 
+// Race check build (FA_SERIALIZE_STAGES): every LDS ring stage is fenced on
+// both sides, each copy completed and the whole work-group synchronised right
+// after it is issued and again after each step's reads, so no tile is read
+// before it lands or overwritten while read.  Same arithmetic in the same
+// order; the results must equal the normal build's bit for bit.
+#ifdef FA_SERIALIZE_STAGES
+#define FA_STAGE_FENCE() \
+  do {                   \
+    wait_vmcnt<0>();     \
+    __syncthreads();     \
+  } while (0)
+#else
+#define FA_STAGE_FENCE() \
+  do {                   \
+  } while (0)
+#endif
+
 // 4-byte variant (lane i's word lands at LDS byte lds + 4 i).
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"

@@ -387,6 +387,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
       issue(tl[0], 0);
       if (tl[1] < nkt) issue(tl[1], 1);
       if (tl[2] < nkt) issue(tl[2], 2);
+      FA_STAGE_FENCE();
       // wait for tile 0 (later tiles may stay in flight)
       if (tl[2] < nkt) wait_vmcnt<2 * LPT>();
       else if (tl[1] < nkt) wait_vmcnt<LPT>();
@@ -410,6 +411,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
         if (tl[3] < nkt) issue(tl[3], (step + 3) & 3);
+        FA_STAGE_FENCE();
         const raw* Kc = ktile(step & 3);
         const raw* Kn = ktile((step + 1) & 3);
         const raw* Vc = vtile(step & 3);
@@ -424,6 +426,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         tl[1] = tl[2];
         tl[2] = tl[3];
         tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+        FA_STAGE_FENCE();
         ++step;
       };
       while (true) {
@@ -442,6 +445,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
     for (int k = 0; k < PD; ++k)
       if (tl[k] < nkt) issue(tl[k], k);
+    FA_STAGE_FENCE();
     // The Q fragments arrived by ordinary loads issued before these copies.
     // Waiting for everything once here tells the compiler they have landed;
     // otherwise it waits for them (vmcnt(0)) at their first use inside the
@@ -492,6 +496,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         const uint32_t nb = ring_lds + nxt * L::SLOT_BYTES;
         kplan.issue(Kg + (size_t)(t + PD) * BT * D, nb);
         vplan.issue(Vg + (size_t)(t + PD) * BT * D, nb + L::TILE_BYTES);
+        FA_STAGE_FENCE();
         full_tile(Kc, Vc);
 #pragma unroll
         for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
@@ -512,6 +517,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         }
         __syncthreads();  // every wave is done with step i-1: slot nxt is free
         if (tl[PD] < nkt) issue(tl[PD], nxt);
+        FA_STAGE_FENCE();
         // A tile this wave sees in full (every sub-tile active and unmasked;
         // wave-uniform) takes the interior's interleaved order.
         bool full = true;
@@ -538,6 +544,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
         tl[PD] = tl[PD] < nkt ? next_kept(tl[PD] + 1) : nkt;
       }
+      FA_STAGE_FENCE();
       cur = cur + 1 == NS ? 0 : cur + 1;
       nxt = nxt + 1 == NS ? 0 : nxt + 1;
       if (tl[0] >= nkt) break;
@@ -643,11 +650,8 @@ hipError_t launch_fwd_combine(const Problem& pb, const FwdTensors& t, int splits
   c.rows = pb.B * pb.H * pb.N;
   c.splits = splits;
   const unsigned grid = (unsigned)((c.rows + RPB - 1) / RPB);
-  timing_begin(kFwdCombine, pb.stream);
   hipLaunchKernelGGL((fa_fwd_combine_kernel<T, D>), dim3(grid), dim3(256), 0, pb.stream, c);
-  hipError_t e = hipGetLastError();
-  timing_end(kFwdCombine, pb.stream);
-  return e;
+  return hipGetLastError();
 }
 
 template <typename T, int D, int NW>
@@ -679,11 +683,9 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.Tq = pb.Tq;
   p.Tk = pb.Tk;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
-  timing_begin(kFwd, pb.stream);
   hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid, splits), dim3(64 * NW), 0, pb.stream,
                      p);
   hipError_t e = hipGetLastError();
-  timing_end(kFwd, pb.stream);
   if (e != hipSuccess || splits == 1) return e;
   return launch_fwd_combine<T, D>(pb, t, splits);
 }

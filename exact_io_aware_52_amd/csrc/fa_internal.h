@@ -8,7 +8,10 @@
 
 namespace fa {
 
-enum KernelKind { kFwd = 0, kBwdDkDv = 1, kBwdDq = 2, kFwdCombine = 3, kNumKernelKinds = 4 };
+// Backward passes a call launches (Problem::bwd_passes): the dQ pass (which
+// also writes -D and LSE * log2(e) to the workspace) and the dK/dV pass that
+// reads them.
+enum BwdPass { kPassDq = 1, kPassDkDv = 2, kPassBoth = 3 };
 
 struct Problem {
   int B, H, N, d;
@@ -31,6 +34,7 @@ struct Problem {
   const int32_t* cu_q = nullptr;
   const int32_t* cu_k = nullptr;
   int Tq = 0, Tk = 0;
+  int bwd_passes = kPassBoth;  // backward: which passes to launch (BwdPass bits)
 };
 
 // Heads per XCD dispatched together (map_tile's group).  The XCDs of MI355X
@@ -66,10 +70,6 @@ struct BwdTensors {
   float* workspace;  // caller's workspace: -D = -rowsum(dO * O), then LSE * log2(e),
                     // each float32 [B, H, N]
 };
-
-// Event bracketing of launches (active only while timing is enabled).
-void timing_begin(KernelKind kind, hipStream_t stream);
-void timing_end(KernelKind kind, hipStream_t stream);
 
 hipError_t launch_forward(const Problem& p, const FwdTensors& t);
 hipError_t launch_backward(const Problem& p, const BwdTensors& t);

@@ -4,6 +4,9 @@
  * C ABI of libfa.so.  Every tensor argument is a DEVICE pointer owned by the
  * caller; the library never allocates, frees or synchronises memory it was
  * handed, and it launches all work asynchronously on the caller's stream.
+ * It keeps no settings between calls (the only state is the thread-local
+ * text of fa_last_error_detail), so calls from several threads are safe as
+ * long as calls sharing a workspace are ordered on one stream.
  * Asynchronous kernel faults surface at the caller's next synchronisation.
  *
  * Method (FlashAttention, as summarised by the review page "FlashAttention"
@@ -130,7 +133,7 @@ size_t fa_forward_blocksparse_split_workspace_bytes(int B, int H, int N, int d, 
  * fa_forward_kv_workspace_bytes(B,H,Nq,Nk,d,dtype) bytes, 16-byte aligned,
  * need not be initialised.  workspace may be NULL when that size is 0.
  * Calls that share a workspace must be ordered on one stream.  The tile
- * height is chosen from Nq (fa_set_forward_block_rows does not apply).
+ * height is chosen from Nq.
  */
 int fa_forward_kv(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int Nq, int Nk, int d, float scale, int causal,
@@ -152,8 +155,10 @@ size_t fa_forward_kv_workspace_bytes(int B, int H, int Nq, int Nk, int d, fa_dty
  * counts; causal aligned bottom-right, top-left when they are equal).
  * Offsets are clamped into [0, Tq] / [0, Tk] on the device.  max_seqlen_q
  * must be at least every sequence's query count (it sizes the grid; query
- * rows of a longer sequence past it, rounded up to the tile, are not
- * written).  Rows outside every sequence are not written.  No workspace.
+ * rows of a longer sequence past it, rounded up to the tile, would not be
+ * written; the library cannot check it, since the prefix sums live on the
+ * device, and the Python binding checks it when they are given on the host).
+ * Rows outside every sequence are not written.  No workspace.
  */
 int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                       const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k,
@@ -183,25 +188,57 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 hipStream_t stream);
 
 /*
- * Query rows per forward work-group, the tile height B_r of the tiled IO
- * analysis (review page, claims C2 and C3: tiling reduces HBM reads and
- * writes, with an IO cost that depends on the on-chip memory size; K and V
- * are read once per query tile, so that traffic falls as B_r grows): 64,
- * 128 or 256, or 0 (the default) to choose per call: 256 for 16-bit d = 128
- * dense problems whose 256-row grid holds at least 512 work-groups, else 128.
- * A tuning and measurement setting; results agree to rounding for every
- * value.  The block-sparse forward supports 64 and 128 (a 128-token mask
- * block holds a whole tile; the automatic choice takes 128 there) and returns
- * FA_ERR_UNSUPPORTED for 256.  Process-wide, read at each forward call, not
- * synchronised between threads.  Returns FA_OK, or FA_ERR_UNSUPPORTED for any
- * other value (the setting is kept).  fa_get_forward_block_rows returns the
- * setting (0 when automatic).
+ * The two passes of fa_backward, for callers that schedule them separately
+ * (and for timing each).  fa_backward is fa_backward_dq followed by
+ * fa_backward_dkdv on the same stream, with the same arguments and workspace.
+ *   fa_backward_dq    writes dq; fills the workspace with -D = -rowsum(dout * o)
+ *                     and LSE * log2(e) (float32 [B,H,N] each).  Reads q, k, v,
+ *                     o, dout, lse.
+ *   fa_backward_dkdv  writes dk, dv; reads q, k, v, dout and the workspace
+ *                     that a preceding fa_backward_dq with the same q, k, v,
+ *                     o, dout, lse, sizes, scale and masks filled (unchanged
+ *                     since).  It may be called again on that workspace.
+ * Arguments, validation and errors as fa_backward.
  */
-int fa_set_forward_block_rows(int rows);
-int fa_get_forward_block_rows(void);
-/* Query rows per work-group that fa_forward (sparse = 0) or
- * fa_forward_blocksparse (sparse != 0) would use for these sizes under the
- * current setting.  Host only; no validation beyond that of the rule. */
+int fa_backward_dq(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                   fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout,
+                     void* dk, void* dv, int B, int H, int N, int d, float scale,
+                     int causal, const int32_t* key_lens, const uint8_t* block_mask,
+                     int block_size, fa_dtype dtype, void* workspace,
+                     size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Forward with the tile height chosen per call (review page, claims C2 and
+ * C3: tiling reduces HBM reads and writes, and the IO cost depends on the
+ * on-chip memory size; K and V are read once per query tile, so that traffic
+ * falls as the tile height B_r grows).  As fa_forward, plus:
+ *   block_mask, block_size  as fa_forward_blocksparse, or block_mask NULL
+ *                           (dense; block_size is then ignored);
+ *   block_rows  query rows per work-group: 64, 128 or 256, or 0 to let the
+ *               library choose (fa_forward_block_rows_for).  The block-sparse
+ *               forward takes 64 or 128 (FA_ERR_UNSUPPORTED for 256, since a
+ *               128-token mask block must hold a whole tile); any other value
+ *               is FA_ERR_UNSUPPORTED.
+ * A tuning and measurement option: results agree to rounding for every
+ * value.  fa_forward and fa_forward_blocksparse are this call with
+ * block_rows = 0.
+ */
+int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
+                  int B, int H, int N, int d, float scale, int causal,
+                  const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                  int block_rows, fa_dtype dtype, hipStream_t stream);
+
+/*
+ * Query rows per work-group that a forward of these sizes uses when
+ * block_rows is 0 (sparse != 0: a block mask is given): 256 for 16-bit
+ * d = 128 dense problems whose 256-row grid holds at least 512 work-groups,
+ * else 128.  Host arithmetic only.
+ */
 int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
 
 /* Workspace bytes fa_backward needs for these sizes (0 for an empty problem). */
@@ -212,19 +249,6 @@ const char* fa_status_string(int status);
 
 /* Detail of the last non-OK return on the calling thread ("" if none). */
 const char* fa_last_error_detail(void);
-
-/*
- * Kernel timing.  While enabled, every kernel the library launches is
- * bracketed by a pair of HIP events recorded on the launch stream.
- * fa_timing_read() waits for the recorded events of one kernel kind, returns
- * the summed elapsed milliseconds and the launch count, and clears them.
- * kernel: 0 forward, 1 backward dK/dV, 2 backward dQ (which also forms D
- * and LSE * log2(e) for the dK/dV pass), 3 the merge of split forward
- * results (fa_forward_kv).  Not thread-safe; meant for benchmarks.
- */
-int fa_timing_enable(int enable);
-int fa_timing_read(int kernel, double* total_ms, int* launches);
-const char* fa_kernel_name(int kernel);
 
 #ifdef __cplusplus
 }

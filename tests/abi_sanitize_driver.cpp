@@ -1,0 +1,174 @@
+// Host-only driver for fa_api.cpp (argument validation, planning, status
+// strings), built with AddressSanitizer and UndefinedBehaviorSanitizer by
+// tests/test_abi_sanitize.py.  The kernel launchers are replaced by stubs
+// that record the problem they were handed, so every path of the C ABI layer
+// runs without a GPU: rejected arguments, empty problems, the tile-height
+// rule, the inference split plan, the split workspace layout and a launch
+// failure.  Pointers are fake and never dereferenced (the layer only checks
+// them).  Exit status 0 when every check holds.
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_internal.h"
+
+namespace {
+int g_calls = 0;
+hipError_t g_result = hipSuccess;
+fa::Problem g_last{};
+int g_failures = 0;
+
+void check(bool ok, const char* what, int line) {
+  if (!ok) {
+    std::fprintf(stderr, "FAIL line %d: %s (detail: %s)\n", line, what, fa_last_error_detail());
+    ++g_failures;
+  }
+}
+#define CHECK(x) check((x), #x, __LINE__)
+
+void* P(uintptr_t x) { return reinterpret_cast<void*>(x); }
+const uintptr_t kA = 0x10000;       // 16-byte aligned fake address
+const uintptr_t kBad = 0x10002;     // misaligned
+}  // namespace
+
+namespace fa {
+hipError_t launch_forward(const Problem& p, const FwdTensors&) {
+  ++g_calls;
+  g_last = p;
+  return g_result;
+}
+hipError_t launch_backward(const Problem& p, const BwdTensors&) {
+  ++g_calls;
+  g_last = p;
+  return g_result;
+}
+}  // namespace fa
+
+extern "C" const char* hipGetErrorString(hipError_t) { return "stub launch error"; }
+
+int main() {
+  void* a = P(kA);
+  float* f = static_cast<float*>(a);
+  // ---- forward: rejections launch nothing
+  g_calls = 0;
+  CHECK(fa_forward(nullptr, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) ==
+        FA_ERR_INVALID_ARG);
+  CHECK(std::strstr(fa_last_error_detail(), "q is NULL") != nullptr);
+  CHECK(fa_forward(P(kBad), a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) ==
+        FA_ERR_INVALID_ARG);
+  CHECK(fa_forward(a, a, a, a, f, -1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) ==
+        FA_ERR_INVALID_ARG);
+  CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 96, 0.1f, 0, nullptr, FA_BF16, nullptr) ==
+        FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, -1.f, 0, nullptr, FA_BF16, nullptr) ==
+        FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 1.f / 0.f, 0, nullptr, FA_BF16, nullptr) ==
+        FA_ERR_INVALID_ARG);
+  CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, (fa_dtype)9, nullptr) ==
+        FA_ERR_INVALID_ARG);
+  CHECK(fa_forward(a, a, a, a, f, 1 << 20, 1 << 12, 1 << 16, 64, 0.1f, 0, nullptr, FA_BF16,
+                   nullptr) == FA_ERR_INVALID_ARG);  // grid beyond 2^31 work-groups
+  CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, reinterpret_cast<const int32_t*>(kA + 2),
+                   FA_BF16, nullptr) == FA_ERR_INVALID_ARG);
+  CHECK(fa_forward(nullptr, nullptr, nullptr, nullptr, nullptr, 0, 1, 64, 64, 0.1f, 0, nullptr,
+                   FA_BF16, nullptr) == FA_OK);  // empty: nothing checked, nothing launched
+  CHECK(g_calls == 0);
+  // ---- forward: accepted calls and the tile-height rule
+  CHECK(fa_forward(a, a, a, a, f, 2, 8, 16384, 128, 0.1f, 1, nullptr, FA_BF16, nullptr) == FA_OK);
+  CHECK(g_calls == 1 && g_last.fwd_rows == 256 && g_last.splits == 1 && g_last.causal == 1);
+  CHECK(fa_forward(a, a, a, a, f, 2, 8, 4096, 128, 0.1f, 1, nullptr, FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.fwd_rows == 128);
+  for (int rows : {64, 128, 256}) {
+    CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, rows,
+                        FA_F16, nullptr) == FA_OK);
+    CHECK(g_last.fwd_rows == rows);
+  }
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 32, FA_F16,
+                      nullptr) == FA_ERR_UNSUPPORTED);
+  const uint8_t* bm = static_cast<const uint8_t*>(a);
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 256, FA_F16,
+                      nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 300, 64, 0.1f, 0, nullptr, nullptr, 128,
+                               FA_BF16, nullptr) == FA_ERR_INVALID_ARG);  // mask required
+  CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 300, 64, 0.1f, 0, nullptr, bm, 64, FA_BF16,
+                               nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 131073, 64, 0.1f, 0, nullptr, bm, 128,
+                               FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 131072, 64, 0.1f, 0, nullptr, bm, 128,
+                               FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.block_mask == bm && g_last.fwd_rows == 128);
+  // ---- split block-sparse forward: workspace layout
+  const size_t wsz = fa_forward_blocksparse_split_workspace_bytes(1, 8, 65536, 64, 16384);
+  CHECK(wsz == 4ull * 8 * 65536 * 64 * 4 + 4ull * 8 * 65536 * 4);
+  CHECK(fa_forward_blocksparse_split_workspace_bytes(1, 8, 1000, 64, 1024) == 0);  // one split
+  CHECK(fa_forward_blocksparse_split_workspace_bytes(1, 8, 1000, 64, 100) == 0);   // bad chunk
+  CHECK(fa_forward_blocksparse_split(a, a, a, a, f, 1, 8, 65536, 64, 0.1f, 0, nullptr, bm, 128,
+                                     16384, FA_BF16, a, wsz - 1, nullptr) == FA_ERR_WORKSPACE);
+  CHECK(fa_forward_blocksparse_split(a, a, a, a, f, 1, 8, 65536, 64, 0.1f, 0, nullptr, bm, 128,
+                                     16384, FA_BF16, a, wsz, nullptr) == FA_OK);
+  CHECK(g_last.splits == 4 && g_last.chunk == 16384 && g_last.opart == f &&
+        reinterpret_cast<char*>(g_last.lpart) == static_cast<char*>(a) + 4ull * 8 * 65536 * 64 * 4);
+  CHECK(fa_forward_blocksparse_split(a, a, a, a, f, 1, 1, 65536, 64, 0.1f, 0, nullptr, bm, 128,
+                                     64, FA_BF16, a, 1ull << 40, nullptr) == FA_OK);  // 1024 splits
+  CHECK(fa_forward_blocksparse_split(a, a, a, a, f, 1, 1, 65600, 64, 0.1f, 0, nullptr, bm, 128,
+                                     64, FA_BF16, a, 1ull << 40, nullptr) == FA_ERR_UNSUPPORTED);
+  // ---- inference forward: split plan and workspace
+  const size_t kvw = fa_forward_kv_workspace_bytes(16, 16, 1, 8192, 128, FA_BF16);
+  CHECK(kvw > 0 && kvw % 256 == 0);
+  CHECK(fa_forward_kv(a, a, a, a, f, 16, 16, 1, 8192, 128, 0.1f, 1, nullptr, FA_BF16, a, kvw,
+                      nullptr) == FA_OK);
+  CHECK(g_last.splits > 1 && g_last.fwd_rows == 32 && g_last.causal_br == 1 &&
+        g_last.nk == 8192 && g_last.chunk % 64 == 0 &&
+        (long long)g_last.splits * g_last.chunk >= 8192);
+  CHECK(fa_forward_kv(a, a, a, a, f, 16, 16, 1, 8192, 128, 0.1f, 1, nullptr, FA_BF16, a, kvw - 1,
+                      nullptr) == FA_ERR_WORKSPACE);
+  CHECK(fa_forward_kv(a, nullptr, nullptr, a, f, 2, 2, 5, 0, 64, 0.1f, 1, nullptr, FA_BF16,
+                      nullptr, 0, nullptr) == FA_OK);  // empty cache: k, v unused
+  CHECK(fa_forward_kv(a, a, a, a, f, 2, 2, 5, -1, 64, 0.1f, 1, nullptr, FA_BF16, nullptr, 0,
+                      nullptr) == FA_ERR_INVALID_ARG);
+  // ---- packed variable-length forward
+  const int32_t* cu = static_cast<const int32_t*>(a);
+  CHECK(fa_forward_varlen(a, a, a, a, f, cu, cu, 16, 16, 25815, 25815, 4096, 128, 0.1f, 1,
+                          FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.cu_q == cu && g_last.Tq == 25815 && g_last.N == 4096 && g_last.fwd_rows == 128);
+  CHECK(fa_forward_varlen(a, a, a, a, f, cu, cu, 16, 16, 100, 100, 101, 128, 0.1f, 1, FA_BF16,
+                          nullptr) == FA_ERR_INVALID_ARG);
+  // ---- backward and its passes
+  const size_t bw = fa_backward_workspace_bytes(2, 3, 100, 64);
+  CHECK(bw == 2 * 2 * 3 * 100 * 4 + 256 - (2 * 2 * 3 * 100 * 4) % 256);
+  CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                    FA_BF16, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_passes == fa::kPassBoth);
+  CHECK(fa_backward_dq(a, a, a, a, a, f, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_passes == fa::kPassDq);
+  CHECK(fa_backward_dkdv(a, a, a, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                         FA_BF16, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_passes == fa::kPassDkDv);
+  CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                    FA_BF16, a, bw - 1, nullptr) == FA_ERR_WORKSPACE);
+  CHECK(fa_backward(a, a, a, a, a, f, nullptr, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr,
+                    128, FA_BF16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+  CHECK(fa_backward_dkdv(a, a, a, a, nullptr, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                         FA_BF16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+  // ---- a failed launch is reported, with its message
+  g_result = hipErrorInvalidValue;
+  CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) == FA_ERR_HIP);
+  CHECK(std::strstr(fa_last_error_detail(), "stub launch error") != nullptr);
+  CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                    FA_BF16, a, bw, nullptr) == FA_ERR_HIP);
+  g_result = hipSuccess;
+  // ---- status strings and the automatic tile height
+  for (int st = -1; st < 7; ++st) CHECK(fa_status_string(st) != nullptr);
+  CHECK(fa_forward_block_rows_for(2, 8, 16384, 128, FA_BF16, 0) == 256);
+  CHECK(fa_forward_block_rows_for(2, 8, 16384, 128, FA_BF16, 1) == 128);
+  CHECK(fa_forward_block_rows_for(2, 8, 16384, 64, FA_BF16, 0) == 128);
+  if (g_failures) {
+    std::fprintf(stderr, "%d check(s) failed\n", g_failures);
+    return 1;
+  }
+  std::printf("abi sanitize driver: all checks passed\n");
+  return 0;
+}

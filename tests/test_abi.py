@@ -3,10 +3,10 @@ declares, and rejects bad arguments on the host before any HIP call (so no
 GPU is needed).  Pointers passed here are never dereferenced: each call is
 built to fail validation."""
 
-import ctypes
 import os
 import re
 
+import numpy as np
 import pytest
 
 from exact_io_aware_52_amd import _binding, build_lib
@@ -137,18 +137,40 @@ def test_backward_validation(lib):
     assert bwd(lib, d=80) == _binding.FA_ERR_UNSUPPORTED
 
 
-def test_status_strings_and_timing(lib):
+def test_status_strings(lib):
     assert lib.fa_status_string(0) == b"FA_OK"
     assert lib.fa_status_string(3) == b"FA_ERR_WORKSPACE"
     assert lib.fa_status_string(99) == b"FA_ERR_UNKNOWN"
-    assert lib.fa_kernel_name(0) == b"fa_fwd_kernel"
-    ms, n = ctypes.c_double(), ctypes.c_int()
-    assert lib.fa_timing_read(2, ctypes.byref(ms), ctypes.byref(n)) == 0
-    assert lib.fa_timing_read(3, ctypes.byref(ms), ctypes.byref(n)) == 0
-    assert lib.fa_kernel_name(3) == b"fa_fwd_combine_kernel"
-    assert lib.fa_timing_read(4, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
-    assert n.value == 0 and ms.value == 0.0
-    assert lib.fa_timing_read(9, ctypes.byref(ms), ctypes.byref(n)) == _binding.FA_ERR_INVALID_ARG
+
+
+def test_backward_pass_validation(lib):
+    # The two passes check only the pointers they use: the dQ pass needs o,
+    # lse, dq (not dk, dv); the dK/dV pass needs dk, dv (not o, lse, dq).
+    need = lib.fa_backward_workspace_bytes(2, 3, 100, 64)
+
+    def dq_pass(o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=need):
+        return lib.fa_backward_dq(FAKE, FAKE, FAKE, o, FAKE, lse, dq, 2, 3, 100, 64, 0.1, 1,
+                                  None, None, 128, 2, ws, ws_bytes, None)
+
+    def kv_pass(dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=need, q=FAKE):
+        return lib.fa_backward_dkdv(q, FAKE, FAKE, FAKE, dk, dv, 2, 3, 100, 64, 0.1, 1, None,
+                                    None, 128, 2, ws, ws_bytes, None)
+
+    for bad in (dict(o=None), dict(lse=None), dict(dq=None), dict(dq=BAD_ALIGN), dict(ws=None),
+                dict(ws_bytes=need - 1)):
+        assert dq_pass(**bad) != _binding.FA_OK, bad
+    for bad in (dict(dk=None), dict(dv=BAD_ALIGN), dict(ws=None), dict(ws_bytes=need - 1),
+                dict(q=None)):
+        assert kv_pass(**bad) != _binding.FA_OK, bad
+    assert "q is NULL" in detail(lib)
+
+
+def test_no_process_wide_settings(lib):
+    # The library keeps no settings between calls: no setter or timing hook
+    # is exported.
+    for gone in ("fa_set_forward_block_rows", "fa_get_forward_block_rows", "fa_timing_enable",
+                 "fa_timing_read", "fa_kernel_name"):
+        assert not hasattr(lib, gone), gone
 
 
 def kv(lib, q=FAKE, k=FAKE, B=2, H=3, Nq=1, Nk=1000, d=64, dtype=2, ws=FAKE, ws_bytes=1 << 30,
@@ -202,32 +224,34 @@ def test_forward_varlen_validation(lib):
     assert varlen(lib, q=None, cq=None, mq=0) == _binding.FA_OK
 
 
-def test_forward_block_rows_setting(lib):
-    assert lib.fa_get_forward_block_rows() == 0   # chosen per problem
-    for bad in (32, 96, 512, -128):
-        assert lib.fa_set_forward_block_rows(bad) == _binding.FA_ERR_UNSUPPORTED
-        assert lib.fa_get_forward_block_rows() == 0
-    try:
-        for rows in (64, 256, 128):
-            assert lib.fa_set_forward_block_rows(rows) == _binding.FA_OK
-            assert lib.fa_get_forward_block_rows() == rows
-            for sparse in (0, 1):
-                assert lib.fa_forward_block_rows_for(2, 8, 16384, 128, 2, sparse) == rows
-        # 256-row tiles span two 128-token mask blocks: not for the block-sparse forward
-        assert lib.fa_set_forward_block_rows(256) == _binding.FA_OK
-        f = lib.fa_forward_blocksparse
-        assert f(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 64, 0.1, 0, None, FAKE, 128, 2, None) \
-            == _binding.FA_ERR_UNSUPPORTED
-        assert "256" in detail(lib)
-    finally:
-        lib.fa_set_forward_block_rows(0)
+def fwd_ex(lib, rows, bm=None, N=256, q=FAKE):
+    return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, N, 64, 0.1, 0, None, bm, 128, rows,
+                             2, None)
+
+
+def test_forward_ex_block_rows_validation(lib):
+    for bad in (32, 96, 512, -128, 1):
+        assert fwd_ex(lib, bad) == _binding.FA_ERR_UNSUPPORTED, bad
+        assert "block_rows" in detail(lib)
+    # valid heights pass the row check (and then fail on the null q, before
+    # any launch)
+    for rows in (0, 64, 128, 256):
+        assert fwd_ex(lib, rows, q=None) == _binding.FA_ERR_INVALID_ARG
+        assert "q is NULL" in detail(lib)
+    # 256-row tiles span two 128-token mask blocks: not with a block mask
+    assert fwd_ex(lib, 256, bm=FAKE) == _binding.FA_ERR_UNSUPPORTED
+    assert "256" in detail(lib)
+    assert fwd_ex(lib, 128, bm=FAKE, q=None) == _binding.FA_ERR_INVALID_ARG
+    # a block mask too long for the on-chip row cache
+    assert fwd_ex(lib, 0, bm=FAKE, N=131073) == _binding.FA_ERR_UNSUPPORTED
+    # empty problem: nothing checked beyond the sizes, nothing launched
+    assert fwd_ex(lib, 64, N=0, q=None) == _binding.FA_OK
 
 
 def test_forward_block_rows_automatic(lib):
     # 256-row tiles only for 16-bit d=128 dense problems with at least 512
     # work-groups of 256 rows; 128 otherwise
     rows_for = lib.fa_forward_block_rows_for
-    assert lib.fa_set_forward_block_rows(0) == _binding.FA_OK
     assert rows_for(2, 8, 16384, 128, 2, 0) == 256     # 1024 work-groups
     assert rows_for(2, 8, 8192, 128, 1, 0) == 256      # 512
     assert rows_for(2, 8, 7937, 128, 2, 0) == 256      # 16 x 32 (ragged last tile)
@@ -243,3 +267,16 @@ def test_binding_refuses_cpu_tensors():
     q = torch.zeros(1, 1, 8, 64)
     with pytest.raises(Exception):
         _binding.fa_forward(q, q, q)          # no silent CPU fallback
+
+
+def test_varlen_binding_checks_max_seqlen():
+    # A sequence longer than max_seqlen_q would be left partly unwritten by
+    # the kernel's grid: the binding refuses it when the prefix sums are on
+    # the host (before any device work).
+    import torch
+    q = torch.zeros(2, 300, 64)
+    cu = np.array([0, 100, 300], np.int32)
+    with pytest.raises(ValueError, match="max_seqlen_q"):
+        _binding.fa_forward_varlen(q, q, q, cu, cu, 150)
+    with pytest.raises(ValueError, match="non-decreasing"):
+        _binding.fa_forward_varlen(q, q, q, np.array([0, 200, 100], np.int32), cu, 300)

@@ -1,9 +1,17 @@
-"""Host logic of bench.py: the kernel-source hash that keeps a counter summary
-valid is blind to comments and whitespace and sees every code change."""
+"""Host logic of bench.py and the build: counter summaries are tied to the
+machine code of the kernel they were taken on.  The build hashes each
+kernel's gfx950 code; the bench reads a summary's traffic only while the
+hash it carries equals the built one."""
 
 import importlib.util
+import json
 import os
 import shutil
+import subprocess
+
+import pytest
+
+from exact_io_aware_52_amd import build_lib
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -15,21 +23,51 @@ def load_bench():
     return mod
 
 
-def test_source_hash_ignores_comments_not_code(tmp_path):
+def test_manifest_names_every_kernel():
+    if not os.path.exists(build_lib.CODE_MANIFEST):
+        build_lib.build()
+    hashes = json.load(open(build_lib.CODE_MANIFEST))
+    assert set(hashes) == set(build_lib.KERNELS)
+    assert all(isinstance(h, str) and len(h) == 16 for h in hashes.values())
+
+
+def test_read_traffic_only_for_matching_code(tmp_path, monkeypatch):
     bench = load_bench()
-    csrc = tmp_path / "exact_io_aware_52_amd" / "csrc"
-    shutil.copytree(os.path.join(ROOT, "exact_io_aware_52_amd", "csrc"), csrc)
-    bench.ROOT = str(tmp_path)
-    base = {k: bench.source_hash(k) for k in bench.KERNEL_SOURCES}
-    f = csrc / "fa_common.h"
-    text = f.read_text()
-    f.write_text("// a new comment line\n" + text.replace("namespace fa {", "namespace fa {  /* x */\n\n", 1))
-    assert {k: bench.source_hash(k) for k in bench.KERNEL_SOURCES} == base
-    f.write_text(text.replace("kCusPerXcd = 32", "kCusPerXcd = 16", 1))
-    changed = {k: bench.source_hash(k) for k in bench.KERNEL_SOURCES}
-    assert all(changed[k] != base[k] for k in base)   # every kernel includes fa_common.h
-    f.write_text(text)
-    b = csrc / "fa_bwd_impl.h"
-    b.write_text(b.read_text().replace("constexpr int NS = 4;", "constexpr int NS = 3;", 1))
-    after = {k: bench.source_hash(k) for k in bench.KERNEL_SOURCES}
-    assert after["fwd"] == base["fwd"] and after["bwd_dkdv"] != base["bwd_dkdv"]
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    monkeypatch.setattr(bench, "code_hashes", lambda: {"fa_bwd_dkdv_kernel": "abcd" * 4})
+    path = tmp_path / "profiles" / "fa_bwd_dkdv_kernel_w_traffic.txt"
+    path.write_text("kernel: fa_bwd_dkdv_kernel\ncode_sha256: " + "abcd" * 4 +
+                    "\ntraffic_bytes_per_launch: 1234.5\n")
+    assert bench.read_traffic("fa_bwd_dkdv_kernel", "w") == 1234.5
+    path.write_text("code_sha256: " + "ffff" * 4 + "\ntraffic_bytes_per_launch: 1234.5\n")
+    assert bench.read_traffic("fa_bwd_dkdv_kernel", "w") is None
+    assert bench.read_traffic("fa_bwd_dkdv_kernel", "other") is None
+
+
+KERNEL = """#include <hip/hip_runtime.h>
+%s
+__global__ void fa_probe_kernelI(float* x) { x[threadIdx.x] = x[threadIdx.x] * %s + 1.f; }
+"""
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="hipcc not available")
+def test_code_hash_sees_code_not_comments(tmp_path, monkeypatch):
+    # The hash is over machine code: a comment changes nothing, a constant does.
+    monkeypatch.setattr(build_lib, "BUILD", str(tmp_path))
+    monkeypatch.setattr(build_lib, "KERNELS", ("fa_probe_kernel",))
+
+    def hash_of(comment, factor, name):
+        src = tmp_path / f"{name}.hip"
+        src.write_text(KERNEL % (comment, factor))
+        obj = tmp_path / f"{name}.o"
+        subprocess.run([build_lib.hipcc(), "-O3", f"--offload-arch={build_lib.ARCH}", "-c",
+                        str(src), "-o", str(obj)], check=True, capture_output=True)
+        # the probe's mangled name carries the kernel name followed by 'I'
+        return build_lib.kernel_code_hashes([str(obj)])["fa_probe_kernel"]
+
+    a = hash_of("", "2.f", "a")
+    b = hash_of("// a comment\n/* and another */", "2.f", "b")
+    c = hash_of("", "3.f", "c")
+    assert a is not None and a == b and a != c

@@ -4,8 +4,13 @@ same seeded, dtype-rounded inputs.
 Bar: max-abs error <= 1e-5 for fp32 inputs and <= 2e-2 for bf16/fp16 inputs,
 on O, LSE, dQ, dK and dV (unit-variance data).  Small cases span several
 tiles with ragged tails and are compared element by element in full; the
-five workloads run at full size in the launch configuration the bench times,
-and the oracle recomputes whole sampled heads.
+five workloads run at full size in the launch configuration the bench times.
+Up to N = 4096 every head is compared in full; beyond, every head is
+compared on sampled query rows (the first and last row of every tile among
+them) and through the two sum identities of the gradient, and one whole head
+in full.  Every output buffer starts as NaN, so an element no work-group
+writes cannot pass: all heads are checked for NaN and for the -inf pattern
+of LSE (rows without a visible key) before any sampled comparison.
 """
 
 import sys
@@ -16,8 +21,7 @@ import torch
 
 import oracle
 from exact_io_aware_52_amd import (fa_backward, fa_forward, fa_forward_blocksparse,
-                                   fa_forward_blocksparse_split, fa_set_forward_block_rows,
-                                   inputs)
+                                   fa_forward_blocksparse_split, fa_forward_ex, inputs)
 
 pytestmark = pytest.mark.gpu
 
@@ -35,22 +39,61 @@ def dev(x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).to(TORCH_DT[dtype]).cuda()
 
 
-def run_gpu(prob, backward=True):
+def nan_like(t):
+    return torch.full_like(t, float("nan"))
+
+
+def run_gpu(prob, backward=True, block_rows=None):
+    """Forward (and backward) through the C ABI into NaN-filled outputs."""
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
     bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).cuda()
     kw = dict(scale=float(prob.scale), causal=prob.causal, key_lens=kl)
-    if bm is not None:
-        o, lse = fa_forward_blocksparse(q, k, v, bm, prob.block_size, **kw)
+    o = nan_like(q)
+    lse = torch.full((prob.B, prob.H, prob.N), float("nan"), dtype=torch.float32, device="cuda")
+    if block_rows is not None:
+        fa_forward_ex(q, k, v, bm, prob.block_size, block_rows=block_rows, o=o, lse=lse, **kw)
+    elif bm is not None:
+        fa_forward_blocksparse(q, k, v, bm, prob.block_size, o=o, lse=lse, **kw)
     else:
-        o, lse = fa_forward(q, k, v, **kw)
+        fa_forward(q, k, v, o=o, lse=lse, **kw)
     out = {"o": o, "lse": lse}
     if backward:
-        dq, dk, dv = fa_backward(q, k, v, o, do, lse, block_mask=bm,
-                                 block_size=prob.block_size, **kw)
+        dq, dk, dv = (nan_like(q) for _ in range(3))
+        fa_backward(q, k, v, o, do, lse, block_mask=bm, block_size=prob.block_size, dq=dq, dk=dk,
+                    dv=dv, **kw)
         out.update(dq=dq, dk=dk, dv=dv)
     torch.cuda.synchronize()
     return {n: t.double().cpu().numpy() for n, t in out.items()}
+
+
+def rows_without_keys(prob, b, chunk=2048):
+    """Boolean [N]: query rows of batch b that see no key (from the oracle's
+    visibility rule, a chunk of rows at a time)."""
+    kl = None if prob.key_lens is None else int(prob.key_lens[b])
+    out = np.zeros(prob.N, dtype=bool)
+    for r0 in range(0, prob.N, chunk):
+        rows = np.arange(r0, min(prob.N, r0 + chunk))
+        vis = oracle.visibility(prob.N, prob.causal, kl, prob.block_mask, prob.block_size,
+                                rows=rows)
+        out[rows] = ~vis.any(axis=1)
+    return out
+
+
+def check_all_heads(prob, gpu, label=""):
+    """Every head: no NaN left in any output (each element was written), LSE
+    is -inf exactly on the rows without a visible key, everything else finite."""
+    for n, g in gpu.items():
+        assert not np.isnan(g).any(), f"{label} {n}: {int(np.isnan(g).sum())} elements never written"
+    lse = gpu["lse"]
+    for b in range(prob.B):
+        empty = rows_without_keys(prob, b)
+        ninf = np.isneginf(lse[b])
+        assert np.array_equal(ninf, np.broadcast_to(empty, ninf.shape)), f"{label} b={b}: -inf rows"
+        assert np.all(np.isfinite(lse[b][:, ~empty])), f"{label} b={b}: LSE not finite"
+    for n in gpu:
+        if n != "lse":
+            assert np.all(np.isfinite(gpu[n])), f"{label} {n}: non-finite values"
 
 
 def run_oracle(prob, heads=None, row_chunk=None, backward=True):
@@ -76,6 +119,8 @@ def compare(gpu, ref, tol, heads=None, label="", magnitude_scaled=False):
     for n in ref:
         g, r = gpu[n], ref[n]
         if heads is not None:
+            # unsampled heads: at least every element written and finite
+            assert not np.isnan(g).any(), f"{label} {n}: elements never written"
             g = np.stack([g[b, h] for b, h in heads])
             r = np.stack([r[b, h] for b, h in heads])
         # rows without a visible key: LSE must be -inf on both sides
@@ -115,11 +160,17 @@ SMALL = [
     (1, 1, 1, 128, "fp16", True, None, None),
     # Very short key lengths: each row attends to 1-3 keys, so dV and dK sum
     # O(N) rows of one key and leave the unit-variance regime (compared with
-    # the tolerance scaled by the output magnitude).  Not in bf16: there D is
-    # formed from the bf16-rounded O (about 1.6e-2 error on D at d=64), which
-    # with probabilities near 1/2 reaches dS and dK undamped.
+    # the tolerance scaled by the output magnitude).  The bf16 form of this
+    # case has its own test below (test_short_keys_bf16).
     (3, 2, 130, 64, "fp16", False, (1, 3), None),
     (3, 2, 130, 128, "fp32", True, (1, 3), None),
+    # B * H a multiple of 8: the tile schedule's XCD-aware branch (every tile
+    # of a head on one XCD), with several tiles per head and ragged tails,
+    # compared in full.
+    (2, 4, 600, 64, "bf16", True, None, None),
+    (2, 8, 333, 128, "fp16", False, (100, 333), None),
+    (1, 16, 520, 64, "bf16", False, None, 0.5),
+    (4, 2, 257, 64, "fp32", True, None, None),
 ]
 
 
@@ -134,7 +185,66 @@ def test_small_cases(case):
     # Key lengths of 1-3 concentrate each head's attention on a few keys, so
     # dV sums O(N) unit rows and leaves the unit-variance regime.
     short = klr is not None and klr[1] <= 8
-    compare(run_gpu(prob), run_oracle(prob), TOL[dtype], label=str(case), magnitude_scaled=short)
+    gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, str(case))
+    compare(gpu, run_oracle(prob), TOL[dtype], label=str(case), magnitude_scaled=short)
+
+
+GROUPED = [
+    # B, H, N, d, dtype, causal, key_len_range: B * H = 24, three heads per
+    # XCD whose streamed K/V (or Q/dO) exceed the XCD's 4 MB of L2, so the
+    # schedule takes them two at a time (groups of 2 and 1) in every kernel.
+    (3, 8, 2800, 128, "bf16", True, None),
+    (4, 6, 2900, 128, "fp16", False, (1000, 2900)),
+]
+
+
+@pytest.mark.parametrize("case", GROUPED, ids=lambda c: "B{}H{}N{}d{}_{}".format(*c[:5]))
+def test_grouped_head_schedule(case):
+    B, H, N, d, dtype, causal, klr = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=2000 + N, causal=causal,
+                               key_len_range=klr)
+    log(f"[case] grouped heads {case}")
+    gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, f"grouped {case}")
+    compare(gpu, run_oracle(prob, row_chunk=1024), TOL[dtype], label=f"grouped {case}")
+
+
+def test_short_keys_bf16():
+    # bf16 with key lengths 1-3.  Beyond the compute error covered by the
+    # magnitude-scaled tolerance, dQ and dK carry the error of
+    # D = rowsum(dO * O) formed from the O the forward stored in bf16.  To
+    # first order (u = 2^-8, the bf16 unit roundoff): the stored O differs
+    # from the exact one by at most u (sum_j P_ij |v_jk| + 2 |O_ik|) (P and
+    # O each rounded once, plus the normalisation), so
+    # |dD_i| <= u sum_k |dO_ik| (sum_j P_ij |v_jk| + 2 |O_ik|), which reaches
+    # dQ_i = scale sum_j dS_ij k_j and dK_j = scale sum_i dS_ij q_i through
+    # dS_ij = P_ij (dP_ij - D_i) as
+    #   |d dQ_i| <= scale |dD_i| sum_j P_ij |k_j|,
+    #   |d dK_j| <= scale sum_i P_ij |dD_i| |q_i|.
+    # The test allows that propagated bound, element by element, on top of
+    # the scaled tolerance (all terms from the oracle's P and O and the inputs).
+    prob = inputs.make_problem(3, 2, 130, 64, "bf16", seed=1194, key_len_range=(1, 3))
+    gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, "short keys bf16")
+    ref = run_oracle(prob)
+    tol, u, sc = TOL["bf16"], 2.0 ** -8, float(prob.scale)
+    for b in range(prob.B):
+        for h in range(prob.H):
+            q, k, v, do = (x[b, h].astype(np.float64) for x in (prob.q, prob.k, prob.v, prob.do))
+            P = oracle.head_probabilities(q, k, sc, key_len=int(prob.key_lens[b]))
+            dD = u * (np.abs(do) * (P @ np.abs(v) + 2 * np.abs(ref["o"][b, h]))).sum(axis=1)
+            extra = {"dq": sc * dD[:, None] * (P @ np.abs(k)),
+                     "dk": sc * (P.T @ (dD[:, None] * np.abs(q))),
+                     "dv": 0.0, "o": 0.0}
+            for n, e in extra.items():
+                g, r = gpu[n][b, h], ref[n][b, h]
+                bound = tol * max(1.0, float(np.abs(ref[n]).max())) + e
+                over = np.abs(g - r) - bound
+                log(f"[parity] short keys bf16 ({b},{h}) {n}: max err "
+                    f"{np.abs(g - r).max():.3g}, worst margin {over.max():.3g}")
+                assert np.all(over <= 0), (b, h, n, float(over.max()))
+            assert np.abs(gpu["lse"][b, h] - ref["lse"][b, h]).max() <= tol
 
 
 @pytest.mark.parametrize("dtype,lens", [("bf16", [0, 200, 150]), ("fp32", [0, 200, 5])])
@@ -160,9 +270,9 @@ def test_block_mask_with_empty_rows():
 @pytest.mark.parametrize("dtype,d,causal", [("fp16", 64, True), ("fp16", 128, False),
                                              ("bf16", 64, False), ("bf16", 128, True)])
 def test_large_scale(dtype, d, causal):
-    # scale * log2(e) > 1: fp16 keeps Q unscaled and scales each score (the
-    # pre-scaled product could overflow fp16); bf16 still pre-scales.  Scores
-    # have standard deviation sqrt(d), so rows are close to one-hot.
+    # scale = 1: Q stays unscaled in every dtype and each fp32 score is
+    # multiplied by scale * log2(e) before the exponential.  Scores have
+    # standard deviation sqrt(d), so rows are close to one-hot.
     prob = inputs.make_problem(1, 2, 300, d, dtype, seed=83 + d, causal=causal, scale=1.0)
     compare(run_gpu(prob), run_oracle(prob), TOL[dtype], label=f"scale 1 {dtype} d{d}",
             magnitude_scaled=True)
@@ -187,11 +297,8 @@ def test_forward_block_rows(case):
     rows, B, H, N, d, dtype, causal, klr, bkp = case
     prob = inputs.make_problem(B, H, N, d, dtype, seed=97 + rows + N, causal=causal,
                                key_len_range=klr, block_keep_p=bkp)
-    fa_set_forward_block_rows(rows)
-    try:
-        gpu = run_gpu(prob)
-    finally:
-        fa_set_forward_block_rows(0)
+    gpu = run_gpu(prob, block_rows=rows)
+    check_all_heads(prob, gpu, f"{rows} rows")
     compare(gpu, run_oracle(prob), TOL[dtype], label=f"{rows} rows {case[1:]}",
             magnitude_scaled=klr is not None and klr[0] < 4)
 
@@ -226,31 +333,90 @@ def test_config_tiny_full():
 
 def test_config_gpt2_small():
     prob = inputs.workload("gpt2_small")
-    heads = [(0, 0), (3, 5), (7, 11)]
-    compare(run_gpu(prob), run_oracle(prob, heads=heads), TOL["bf16"], heads, "gpt2_small")
+    gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, "gpt2_small")
+    compare(gpu, run_oracle(prob), TOL["bf16"], label="gpt2_small, all 96 heads")
 
 
 def test_config_bert_large_padded():
     prob = inputs.workload("bert_large_padded")
-    b_short = int(np.argmin(prob.key_lens))
-    b_long = int(np.argmax(prob.key_lens))
-    heads = [(b_short, 0), (b_long, 15), (5, 7)]
-    compare(run_gpu(prob), run_oracle(prob, heads=heads), TOL["fp16"], heads, "bert_large_padded")
+    gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, "bert_large_padded")
+    compare(gpu, run_oracle(prob), TOL["fp16"], label="bert_large_padded, all 256 heads")
+
+
+def tile_edge_rows(n, tile=128, extra=16, seed=0):
+    """First and last row of every tile, plus a few random rows."""
+    t0 = np.arange(0, n, tile)
+    rows = np.concatenate([t0, np.minimum(t0 + tile - 1, n - 1),
+                           np.random.default_rng(seed).integers(0, n, extra)])
+    return np.unique(rows)
+
+
+def check_sampled_rows(prob, gpu, rows, label, heads=None):
+    """O, LSE and dQ of the given query rows of every head (or ``heads``)
+    against the oracle's row function."""
+    worst = {}
+    todo = heads or [(b, h) for b in range(prob.B) for h in range(prob.H)]
+    for b, h in todo:
+        kl = None if prob.key_lens is None else int(prob.key_lens[b])
+        o, lse, dq = oracle.head_rows(*(x[b, h].astype(np.float64)
+                                        for x in (prob.q, prob.k, prob.v, prob.do)),
+                                      float(prob.scale), rows, causal=prob.causal, key_len=kl,
+                                      block_mask=prob.block_mask, block_size=prob.block_size)
+        ref = {"o": o, "lse": lse, "dq": dq}
+        got = {n: gpu[n][b, h][rows] for n in ref}
+        for n, e in compare(got, ref, TOL[prob.dtype], label=f"{label} rows of ({b},{h})").items():
+            worst[n] = max(worst.get(n, 0.0), e)
+    log(f"[parity] {label}: {len(rows)} rows on {len(todo)} heads, worst {worst}")
+
+
+def check_sum_identities(prob, gpu, label):
+    """Every head: sum_j dV_j = sum_i dO_i and sum_j dK_j = 0 (over the rows
+    that see a key; here every row does), within the spread that bf16 or
+    fp16 rounding of the stored values (and of P, O) leaves in such sums."""
+    u = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11, "fp32": 2.0 ** -24}[prob.dtype]
+    for b in range(prob.B):
+        assert not rows_without_keys(prob, b).any(), "identities below assume every row sees a key"
+        for h in range(prob.H):
+            dv, dk, do = gpu["dv"][b, h], gpu["dk"][b, h], prob.do[b, h].astype(np.float64)
+            q, o = prob.q[b, h].astype(np.float64), gpu["o"][b, h]
+            dev_v = np.abs(dv.sum(axis=0) - do.sum(axis=0))
+            bound_v = 6 * u * (np.sqrt((dv ** 2).sum(axis=0)) + np.sqrt((do ** 2).sum(axis=0)))
+            assert np.all(dev_v <= bound_v), (label, b, h, "sum dV", dev_v.max(), bound_v.min())
+            # sum_j dS_ij = D_i(exact O) - D_i(rounded O): spread |dO_i| |O_i| u per row
+            spread = float(prob.scale) * np.sqrt(((np.abs(q) * (np.abs(do) * np.abs(o)).sum(
+                axis=1, keepdims=True) * u) ** 2).sum(axis=0))
+            dev_k = np.abs(dk.sum(axis=0))
+            bound_k = 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0)))
+            assert np.all(dev_k <= bound_k), (label, b, h, "sum dK", dev_k.max(), bound_k.min())
+    log(f"[parity] {label}: dK, dV sums within bounds on all {prob.B * prob.H} heads")
 
 
 @pytest.mark.parametrize("point", inputs.LONG_POINTS, ids=lambda p: f"N{p[0]}_d{p[1]}")
 def test_config_long_causal(point):
     prob = inputs.workload("long_causal", *point)
-    heads = [(1, 7)] if point[0] > 4096 else [(0, 0), (1, 7)]
-    compare(run_gpu(prob), run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads,
-            f"long_causal {point}")
+    gpu = run_gpu(prob)
+    label = f"long_causal {point}"
+    check_all_heads(prob, gpu, label)
+    if point[0] <= 4096:
+        compare(gpu, run_oracle(prob, row_chunk=2048), TOL["bf16"], label=label + ", all heads")
+        return
+    heads = [(1, 7)]
+    compare(gpu, run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads, label)
+    check_sampled_rows(prob, gpu, tile_edge_rows(point[0], seed=point[0] + point[1]), label)
+    check_sum_identities(prob, gpu, label)
 
 
 def test_config_block_sparse():
     prob = inputs.workload("block_sparse")
+    gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, "block_sparse")
     heads = [(0, 3)]
-    compare(run_gpu(prob), run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads,
+    compare(gpu, run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads,
             "block_sparse")
+    check_sampled_rows(prob, gpu, tile_edge_rows(prob.N, seed=5), "block_sparse")
+    check_sum_identities(prob, gpu, "block_sparse")
 
 
 @pytest.mark.parametrize("n", inputs.SPARSE_LONG_N)
@@ -263,34 +429,16 @@ def test_config_block_sparse_long(n):
     # rounding the stored values (and P, O) to bf16 leaves in such sums.
     prob = inputs.workload("block_sparse_long", n)
     gpu = run_gpu(prob)
+    label = f"block_sparse_long N={n}"
+    check_all_heads(prob, gpu, label)
     if n <= 32768:
         heads = [(0, 5)]
-        compare(gpu, run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads,
-                f"block_sparse_long N={n}")
+        compare(gpu, run_oracle(prob, heads=heads, row_chunk=2048), TOL["bf16"], heads, label)
     rng = np.random.default_rng(11)
     rows = np.unique(np.concatenate([[0, 1, 127, 128, 129, n // 2, n // 2 + 1, n - 129, n - 128,
                                       n - 1], rng.integers(0, n, 22)]))
-    for b, h in [(0, 2), (0, 7)]:
-        o, lse, dq = oracle.head_rows(*(x[b, h].astype(np.float64) for x in (prob.q, prob.k, prob.v, prob.do)),
-                                      float(prob.scale), rows, block_mask=prob.block_mask,
-                                      block_size=prob.block_size)
-        ref = {"o": o, "lse": lse, "dq": dq}
-        got = {k: gpu[k][b, h][rows] for k in ref}
-        compare(got, ref, TOL["bf16"], label=f"block_sparse_long N={n} rows of head ({b},{h})")
-    u = 2.0 ** -8      # bf16 unit roundoff
-    for b in range(prob.B):
-        for h in range(prob.H):
-            dv, dk, do = gpu["dv"][b, h], gpu["dk"][b, h], prob.do[b, h].astype(np.float64)
-            q, o = prob.q[b, h].astype(np.float64), gpu["o"][b, h]
-            dev_v = np.abs(dv.sum(axis=0) - do.sum(axis=0))
-            bound_v = 6 * u * (np.sqrt((dv ** 2).sum(axis=0)) + np.sqrt((do ** 2).sum(axis=0)))
-            assert np.all(dev_v <= bound_v), (b, h, "sum dV", dev_v.max(), bound_v.min())
-            # sum_j dS_ij = D_i(exact O) - D_i(bf16 O): spread |dO_i| |O_i| u per row
-            spread = float(prob.scale) * np.sqrt(((np.abs(q) * (np.abs(do) * np.abs(o)).sum(axis=1, keepdims=True) * u) ** 2).sum(axis=0))
-            dev_k = np.abs(dk.sum(axis=0))
-            bound_k = 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0)))
-            assert np.all(dev_k <= bound_k), (b, h, "sum dK", dev_k.max(), bound_k.min())
-    log(f"[parity] block_sparse_long N={n}: dK, dV sums within bounds on all heads")
+    check_sampled_rows(prob, gpu, rows, label)
+    check_sum_identities(prob, gpu, label)
 
 
 # ----------------------------------------------------------------------------- split key ranges
@@ -382,27 +530,19 @@ def test_max_block_mask_length():
     n = 131072
     prob = inputs.make_problem(1, 1, n, 64, "bf16", seed=91, block_keep_p=1 / 128, block_band=1)
     gpu = run_gpu(prob)
+    check_all_heads(prob, gpu, f"N={n}")
     rng = np.random.default_rng(12)
     rows = np.unique(np.concatenate([[0, 127, 128, n // 2, n - 129, n - 128, n - 1],
                                      rng.integers(0, n, 9)]))
-    o, lse, dq = oracle.head_rows(*(x[0, 0].astype(np.float64) for x in (prob.q, prob.k, prob.v, prob.do)),
-                                  float(prob.scale), rows, block_mask=prob.block_mask,
-                                  block_size=prob.block_size)
-    got = {k: gpu[k][0, 0][rows] for k in ("o", "lse", "dq")}
-    compare(got, {"o": o, "lse": lse, "dq": dq}, TOL["bf16"], label=f"N={n} block mask, sampled rows")
-    u = 2.0 ** -8
-    dv, dk, do = gpu["dv"][0, 0], gpu["dk"][0, 0], prob.do[0, 0].astype(np.float64)
-    dev_v = np.abs(dv.sum(axis=0) - do.sum(axis=0))
-    assert np.all(dev_v <= 6 * u * (np.sqrt((dv ** 2).sum(axis=0)) + np.sqrt((do ** 2).sum(axis=0))))
-    q, ov = prob.q[0, 0].astype(np.float64), gpu["o"][0, 0]
-    spread = float(prob.scale) * np.sqrt(((np.abs(q) * (np.abs(do) * np.abs(ov)).sum(axis=1, keepdims=True) * u) ** 2).sum(axis=0))
-    assert np.all(np.abs(dk.sum(axis=0)) <= 6 * (spread + u * np.sqrt((dk ** 2).sum(axis=0))))
+    check_sampled_rows(prob, gpu, rows, f"N={n} block mask")
+    check_sum_identities(prob, gpu, f"N={n} block mask")
 
 
 def test_many_heads():
     # 4096 (b, h) heads of 130 rows (a ragged second tile): the largest grids of
     # the five workloads have ~2K work-groups; this launches 8K per pass.
+    # B * H is a multiple of 8 (the XCD-aware schedule, 512 heads per XCD).
     prob = inputs.make_problem(64, 64, 130, 64, "bf16", seed=92, causal=True)
     gpu = run_gpu(prob)
-    heads = [(0, 0), (7, 63), (31, 5), (63, 63), (40, 17)]
-    compare(gpu, run_oracle(prob, heads=heads), TOL["bf16"], heads, label="4096 heads")
+    check_all_heads(prob, gpu, "4096 heads")
+    compare(gpu, run_oracle(prob), TOL["bf16"], label="4096 heads, all compared")
