@@ -52,6 +52,8 @@ def open_library(path):
     lib.fa_forward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_forward_blocksparse_split_workspace_bytes.restype = Z
     lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
+    lib.fa_backward_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P,
+                                   Z, P]
     lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P]
@@ -67,7 +69,8 @@ def open_library(path):
     lib.fa_forward_kv_workspace_bytes.restype = Z
     lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_forward_blocksparse_split,
-               lib.fa_forward_ex, lib.fa_backward, lib.fa_backward_dq, lib.fa_backward_dkdv,
+               lib.fa_forward_ex, lib.fa_backward, lib.fa_backward_ex, lib.fa_backward_dq,
+               lib.fa_backward_dkdv,
                lib.fa_forward_block_rows_for, lib.fa_forward_kv, lib.fa_forward_varlen):
         fn.restype = I
     return lib
@@ -315,18 +318,26 @@ def fa_backward_workspace_bytes(B, H, N, d):
 
 
 def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, block_size,
-              dq, dk, dv, workspace):
+              dq, dk, dv, workspace, grad_dtype=None):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     _like("dout", dout, q)
     if name != "fa_backward_dkdv":
         _like("o", o, q)
         _like("lse", lse, q, (B, H, N), torch.float32)
+    gdt = q.dtype if grad_dtype is None else grad_dtype
+    if gdt not in (q.dtype, torch.float32):
+        raise ValueError(f"grad_dtype must be {q.dtype} or torch.float32")
+    if gdt != q.dtype:
+        name = "fa_backward_ex"
+
+    def grad(t, nm):
+        return (torch.empty(q.shape, dtype=gdt, device=q.device) if t is None
+                else _like(nm, t, q, dtype=gdt))
     if name != "fa_backward_dkdv":
-        dq = torch.empty_like(q) if dq is None else _like("dq", dq, q)
+        dq = grad(dq, "dq")
     if name != "fa_backward_dq":
-        dk = torch.empty_like(q) if dk is None else _like("dk", dk, q)
-        dv = torch.empty_like(q) if dv is None else _like("dv", dv, q)
+        dk, dv = grad(dk, "dk"), grad(dv, "dv")
     need = fa_backward_workspace_bytes(B, H, N, d)
     if workspace is None:
         if name == "fa_backward_dkdv":
@@ -337,9 +348,11 @@ def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, 
     kl = _lens(key_lens, B, q.device)
     bm = _mask(block_mask, N, block_size, q.device)
     tail = [B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm),
-            int(block_size), _DTYPE_CODE[q.dtype], _ptr(workspace),
-            workspace.numel() * workspace.element_size(), _stream(q.device)]
-    if name == "fa_backward":
+            int(block_size), _DTYPE_CODE[q.dtype]]
+    if name == "fa_backward_ex":
+        tail.append(_DTYPE_CODE[gdt])
+    tail += [_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)]
+    if name in ("fa_backward", "fa_backward_ex"):
         head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
                 _ptr(dv)]
     elif name == "fa_backward_dq":
@@ -351,10 +364,13 @@ def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, 
 
 
 def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
-                block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None):
-    """Backward pass: returns (dQ, dK, dV) in q.dtype."""
+                block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None,
+                grad_dtype=None):
+    """Backward pass: returns (dQ, dK, dV) in q.dtype, or in float32 with
+    grad_dtype=torch.float32 (fa_backward_ex: the same computation without the
+    final rounding to the 16-bit type)."""
     dq, dk, dv, _ = _backward("fa_backward", q, k, v, o, dout, lse, scale, causal, key_lens,
-                              block_mask, block_size, dq, dk, dv, workspace)
+                              block_mask, block_size, dq, dk, dv, workspace, grad_dtype)
     return dq, dk, dv
 
 

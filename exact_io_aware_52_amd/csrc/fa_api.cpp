@@ -216,11 +216,14 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                   float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
                   int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream, int passes) {
+                  hipStream_t stream, int passes, fa_dtype grad_dtype) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
   if (st != FA_OK) return st;
+  if (grad_dtype != dtype && grad_dtype != FA_F32)
+    return fail(FA_ERR_INVALID_ARG, "grad_dtype %d (the input dtype %d or FA_F32)",
+                (int)grad_dtype, (int)dtype);
   if ((st = check_block(block_mask, block_size, N, false)) != FA_OK) return st;
   if (empty) return FA_OK;
   const bool pdq = (passes & fa::kPassDq) != 0, pkv = (passes & fa::kPassDkDv) != 0;
@@ -239,6 +242,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
     return fail(FA_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
   fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
   p.bwd_passes = passes;
+  p.grad_f32 = grad_dtype == FA_F32 && dtype != FA_F32;
   fa::BwdTensors t{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace)};
   hipError_t e = fa::launch_backward(p, t);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
@@ -390,7 +394,17 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
                 hipStream_t stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
                        block_mask, block_size, dtype, workspace, workspace_bytes, stream,
-                       fa::kPassBoth);
+                       fa::kPassBoth, dtype);
+}
+
+int fa_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
+                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
+                   float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
+                   int block_size, fa_dtype dtype, fa_dtype grad_dtype, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
+                       block_mask, block_size, dtype, workspace, workspace_bytes, stream,
+                       fa::kPassBoth, grad_dtype);
 }
 
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
@@ -400,7 +414,7 @@ int fa_backward_dq(const void* q, const void* k, const void* v, const void* o, c
                    hipStream_t stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal,
                        key_lens, block_mask, block_size, dtype, workspace, workspace_bytes,
-                       stream, fa::kPassDq);
+                       stream, fa::kPassDq, dtype);
 }
 
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
@@ -410,7 +424,7 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* do
                      hipStream_t stream) {
   return backward_impl(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, B, H, N, d, scale,
                        causal, key_lens, block_mask, block_size, dtype, workspace,
-                       workspace_bytes, stream, fa::kPassDkDv);
+                       workspace_bytes, stream, fa::kPassDkDv, dtype);
 }
 
 const char* fa_status_string(int status) {

@@ -103,7 +103,10 @@ struct DkDvCfg {
   static constexpr bool ILV = D == 128 && sizeof(raw) == 2;
 };
 
-template <typename T, int D>
+// GF32: store dK, dV as float32 (16-bit inputs; an option for exact
+// comparisons, compiled as separate instances so that the usual instances'
+// register allocation is untouched).
+template <typename T, int D, bool GF32 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     DkDvCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
   typedef raw_t<T> raw;
@@ -547,8 +550,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   // dK, dV bytes written and as much again fetched).  Each tensor goes through
   // LDS instead (the ring is idle by now), one at a time, and is stored as
   // whole rows: every store instruction writes 64 lanes x 16 bytes of
-  // complete rows.
-  {
+  // complete rows.  With float32 gradients requested (an option for exact
+  // comparisons, not a fast path), each lane stores its fp32 values directly.
+  if constexpr (GF32) {
+    if (myk < N) {
+      float* const dkg = reinterpret_cast<float*>(p.dk) + head + (size_t)myk * D;
+      float* const dvg = reinterpret_cast<float*>(p.dv) + head + (size_t)myk * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 k4, v4;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            k4[u] = dk_acc[db][4 * g + u] * p.scale;
+            v4[u] = dv_acc[db][4 * g + u];
+          }
+          *reinterpret_cast<f32x4*>(dkg + db * 32 + 8 * g + 4 * hh) = k4;
+          *reinterpret_cast<f32x4*>(dvg + db * 32 + 8 * g + 4 * hh) = v4;
+        }
+    }
+  } else {
     constexpr int RB = D * (int)sizeof(raw);  // bytes per row
     constexpr int RS = RB + 16;               // padded LDS row stride
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
@@ -602,7 +624,7 @@ struct DqCfg {
   static constexpr int GK = (sizeof(raw) == 2 && D == 128) ? 1 : 0;
 };
 
-template <typename T, int D>
+template <typename T, int D, bool GF32 = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     DqCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
   typedef raw_t<T> raw;
@@ -814,7 +836,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
-  if (myq < N) {
+  if constexpr (GF32) {
+    if (myq < N) {
+      float* const dQg = reinterpret_cast<float*>(p.dq) + head + (size_t)myq * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 out;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) out[u] = dq_acc[db][4 * g + u] * p.scale;
+          *reinterpret_cast<f32x4*>(dQg + db * 32 + 8 * g + 4 * hh) = out;
+        }
+    }
+  } else if (myq < N) {
     raw* dQg = reinterpret_cast<raw*>(p.dq) + head + (size_t)myq * D;
 #pragma unroll
     for (int db = 0; db < D / 32; ++db)
@@ -829,7 +864,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <typename T, int D>
+template <typename T, int D, bool GF32 = false>
 hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   BwdParams p;
   p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.dout = t.dout; p.lse = t.lse;
@@ -852,13 +887,13 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   const unsigned tiles128 = (unsigned)((pb.N + 127) / 128);
   hipError_t e = hipSuccess;
   if (pb.bwd_passes & kPassDq) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0, pb.stream,
-                       p);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32>), dim3(tiles128 * p.BH), dim3(256), 0,
+                       pb.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (pb.bwd_passes & kPassDkDv) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D>), dim3(tiles128 * p.BH), dim3(256), 0,
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32>), dim3(tiles128 * p.BH), dim3(256), 0,
                        pb.stream, p);
     e = hipGetLastError();
   }

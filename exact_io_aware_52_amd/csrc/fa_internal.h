@@ -35,6 +35,7 @@ struct Problem {
   const int32_t* cu_k = nullptr;
   int Tq = 0, Tk = 0;
   int bwd_passes = kPassBoth;  // backward: which passes to launch (BwdPass bits)
+  int grad_f32 = 0;            // backward, 16-bit inputs: float32 dQ, dK, dV
 };
 
 // Heads per XCD dispatched together (map_tile's group).  The XCDs of MI355X

@@ -188,6 +188,24 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 hipStream_t stream);
 
 /*
+ * fa_backward with the gradients' storage type chosen: grad_dtype is the
+ * input dtype (then this is fa_backward) or FA_F32, which writes dq, dk, dv
+ * as float32 [B,H,N,d] (4-byte elements, 16-byte aligned).  The computation
+ * is the same; only the final rounding to a 16-bit type is left out, so the
+ * 16-bit results of fa_backward are exactly the round-to-nearest-even of
+ * these.  Meant for callers that accumulate gradients in float32 and for
+ * measuring the computation's error apart from the output rounding (the
+ * output rounding of a bf16 value of magnitude 4 to 8 is already 2^-6).
+ * Any other grad_dtype is FA_ERR_INVALID_ARG.
+ */
+int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
+                   const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                   int B, int H, int N, int d, float scale, int causal,
+                   const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                   fa_dtype dtype, fa_dtype grad_dtype, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream);
+
+/*
  * The two passes of fa_backward, for callers that schedule them separately
  * (and for timing each).  fa_backward is fa_backward_dq followed by
  * fa_backward_dkdv on the same stream, with the same arguments and workspace.

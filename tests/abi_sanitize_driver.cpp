@@ -44,6 +44,10 @@ hipError_t launch_backward(const Problem& p, const BwdTensors&) {
   g_last = p;
   return g_result;
 }
+hipError_t scratch_workspace(void** ptr) {
+  *ptr = reinterpret_cast<void*>(0x200000);
+  return hipSuccess;
+}
 }  // namespace fa
 
 extern "C" const char* hipGetErrorString(hipError_t) { return "stub launch error"; }
@@ -153,6 +157,18 @@ int main() {
                     128, FA_BF16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
   CHECK(fa_backward_dkdv(a, a, a, a, nullptr, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
                          FA_BF16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+  // ---- float32 gradients for 16-bit inputs
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_F32, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.grad_f32 == 1 && g_last.bwd_passes == fa::kPassBoth);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_BF16, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.grad_f32 == 0);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_F16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_F32, FA_F32, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.grad_f32 == 0);  // float32 inputs: float32 gradients already
   // ---- a failed launch is reported, with its message
   g_result = hipErrorInvalidValue;
   CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) == FA_ERR_HIP);
