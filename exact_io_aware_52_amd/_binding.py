@@ -54,6 +54,10 @@ def open_library(path):
     lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_backward_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P,
                                    Z, P]
+    lib.fa_backward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I,
+                                        P]
+    lib.fa_backward_noalloc_max_rows.argtypes = []
+    lib.fa_backward_noalloc_max_rows.restype = Z
     lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P]
@@ -70,7 +74,7 @@ def open_library(path):
     lib.fa_forward_varlen.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, F, I, I, P]
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_forward_blocksparse_split,
                lib.fa_forward_ex, lib.fa_backward, lib.fa_backward_ex, lib.fa_backward_dq,
-               lib.fa_backward_dkdv,
+               lib.fa_backward_dkdv, lib.fa_backward_noalloc,
                lib.fa_forward_block_rows_for, lib.fa_forward_kv, lib.fa_forward_varlen):
         fn.restype = I
     return lib

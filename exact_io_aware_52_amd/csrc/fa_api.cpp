@@ -427,6 +427,33 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* do
                        workspace_bytes, stream, fa::kPassDkDv, dtype);
 }
 
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv, int B,
+                        int H, int N, int d, float scale, int causal, const int32_t* key_lens,
+                        const uint8_t* block_mask, int block_size, fa_dtype dtype,
+                        hipStream_t stream) {
+  g_detail[0] = 0;
+  bool empty = false;
+  int st = check_common(B, H, N, d, scale, dtype, &empty);
+  if (st != FA_OK) return st;
+  if (empty) return FA_OK;
+  const size_t need = fa_backward_workspace_bytes(B, H, N, d);
+  if (need > fa::kScratchBytes)
+    return fail(FA_ERR_UNSUPPORTED,
+                "problem needs %zu bytes of scratch; the allocation-free backward holds %zu "
+                "(B*H*N <= %zu)",
+                need, fa::kScratchBytes, fa::kScratchBytes / 8);
+  void* ws = nullptr;
+  const hipError_t e = fa::scratch_workspace(&ws);
+  if (e != hipSuccess)
+    return fail(FA_ERR_HIP, "scratch address lookup: %s", hipGetErrorString(e));
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
+                       block_mask, block_size, dtype, ws, fa::kScratchBytes, stream,
+                       fa::kPassBoth, dtype);
+}
+
+size_t fa_backward_noalloc_max_rows(void) { return fa::kScratchBytes / 8; }
+
 const char* fa_status_string(int status) {
   switch (status) {
     case FA_OK: return "FA_OK";

@@ -72,6 +72,12 @@ struct BwdTensors {
                     // each float32 [B, H, N]
 };
 
+// Device scratch of the allocation-free backward (fa_backward_noalloc): its
+// size, and its address on the current device (looked up once per device;
+// thread-safe).  It holds the backward workspace of any problem up to that size.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_workspace(void** ptr);
+
 hipError_t launch_forward(const Problem& p, const FwdTensors& t);
 hipError_t launch_backward(const Problem& p, const BwdTensors& t);
 

@@ -259,6 +259,28 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
  */
 int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
 
+/*
+ * fa_backward for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same computation and results, with the workspace taken from a device array
+ * inside the library instead of a caller buffer.  Calls no allocating
+ * routine.  The array holds 16 MiB on each GPU the library runs on, until the
+ * process ends; problems whose workspace (fa_backward_workspace_bytes, 8 bytes
+ * per query row) exceeds it, i.e. B * H * N > fa_backward_noalloc_max_rows(),
+ * return FA_ERR_UNSUPPORTED before anything is launched.  The array of the
+ * current device is used, so stream must belong to the current device.
+ * Every call on a GPU shares that GPU's array: calls that overlap on one GPU
+ * (different streams, or other threads) race and must not be made; calls
+ * ordered on one stream are safe.  Nothing in the array needs clearing
+ * between calls (the first pass writes every entry the second reads).
+ */
+int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,
+                        const void* dout, const float* lse, void* dq, void* dk, void* dv,
+                        int B, int H, int N, int d, float scale, int causal,
+                        const int32_t* key_lens, const uint8_t* block_mask, int block_size,
+                        fa_dtype dtype, hipStream_t stream);
+size_t fa_backward_noalloc_max_rows(void);
+
 /* Workspace bytes fa_backward needs for these sizes (0 for an empty problem). */
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d);
 

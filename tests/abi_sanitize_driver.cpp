@@ -169,6 +169,16 @@ int main() {
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
                        FA_F32, FA_F32, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 0);  // float32 inputs: float32 gradients already
+  // ---- allocation-free backward: the library's device scratch, size-limited
+  const size_t max_rows = fa_backward_noalloc_max_rows();
+  CHECK(max_rows == (size_t(16) << 20) / 8);
+  CHECK(fa_backward_noalloc(a, a, a, a, a, f, a, a, a, 2, 8, 16384, 128, 0.1f, 1, nullptr,
+                            nullptr, 128, FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.bwd_passes == fa::kPassBoth);
+  CHECK(fa_backward_noalloc(a, a, a, a, a, f, a, a, a, 1, 1, (int)max_rows + 256, 64, 0.1f, 1,
+                            nullptr, nullptr, 128, FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_noalloc(a, a, a, a, a, f, nullptr, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr,
+                            nullptr, 128, FA_BF16, nullptr) == FA_ERR_INVALID_ARG);
   // ---- a failed launch is reported, with its message
   g_result = hipErrorInvalidValue;
   CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) == FA_ERR_HIP);
