@@ -53,7 +53,8 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 # forward S and PV; the dK/dV pass does the recomputed S, dP, dV and dK; the
 # dQ pass contributes the dQ product only (its S and dP repeat the dK/dV pass).
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
-KERNEL_NAMES = {"fwd": "fa_fwd_kernel", "fwd_combine": "fa_fwd_combine_kernel",
+KERNEL_NAMES = {"fwd": "fa_fwd_kernel", "fwd_pp": "fa_fwd_pp_kernel",
+                "fwd_combine": "fa_fwd_combine_kernel",
                 "bwd_dq": "fa_bwd_dq_kernel", "bwd_dkdv": "fa_bwd_dkdv_kernel"}
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak"
 
@@ -472,6 +473,9 @@ class Runner:
         # range: its forward is split four ways over work-groups (measured best
         # of 4K, 8K and 16K keys per split at N = 32K and 64K).
         self.key_chunk = 0
+        # 256-row tiles of dense 16-bit self-attention run the ping-pong kernel.
+        self.fwd_kernel = KERNEL_NAMES["fwd_pp" if self.fwd_rows == 256 and prob.dtype != "fp32"
+                                       and prob.block_mask is None else "fwd"]
         if prob.name.startswith("block_sparse_long"):
             self.key_chunk = -(-prob.N // (4 * 64)) * 64
             self.split_ws = torch.empty(max(fa_forward_blocksparse_split_workspace_bytes(
@@ -618,14 +622,14 @@ def main():
     flops_step = 14 * prob.d * pairs
     value = flops_step / (ms_step * 1e-3) / 1e12
     dom = max(kus, key=kus.get)
-    fwd_unit = KERNEL_NAMES["fwd"] + (" + " + KERNEL_NAMES["fwd_combine"] if run.key_chunk else "")
+    fwd_unit = run.fwd_kernel + (" + " + KERNEL_NAMES["fwd_combine"] if run.key_chunk else "")
     names = dict(KERNEL_NAMES, fwd=fwd_unit)
     work = KERNEL_FLOPS_PER_PAIR_D[dom] * prob.d * pairs
     achieved = work / (kus[dom] * 1e-6) / 1e12
     peak = PEAK_TFLOPS[prob.dtype]
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
-            "traffic": (read_traffic(KERNEL_NAMES[dom], prob.name)
+            "traffic": (read_traffic(dict(KERNEL_NAMES, fwd=run.fwd_kernel)[dom], prob.name)
                         if not (dom == "fwd" and run.key_chunk) else None),
             "kernel": names[dom], "kernel_avg_us": round(kus[dom], 2),
             "algorithmic_flops_per_launch": work}

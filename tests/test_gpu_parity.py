@@ -328,6 +328,24 @@ def test_forward_block_rows(case):
             magnitude_scaled=klr is not None and klr[0] < 4)
 
 
+@pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, True), ("fp16", 128, False),
+                                             ("bf16", 128, True)])
+def test_forward_far_keys_take_the_recompute_path(dtype, d, causal):
+    # 256-row tiles of dense 16-bit problems fix each row's reference point at
+    # the largest score among the first 32 keys.  Here a few later keys are
+    # scaled so that their scores exceed that reference by far more than
+    # 2^32 allows: those waves recompute their rows with a moving reference.
+    # Both paths must agree with the oracle (rows then attend almost only to
+    # the planted keys, so O leaves the unit-variance regime: scaled bound).
+    prob = inputs.make_problem(1, 2, 700, d, dtype, seed=611 + d, causal=causal, scale=1.0)
+    prob.k[:, :, 300:304] *= 6.0
+    prob.k = inputs.round_to_dtype(prob.k, dtype)
+    gpu = run_gpu(prob, block_rows=256)
+    check_all_heads(prob, gpu, f"far keys {dtype} d{d}")
+    compare(gpu, run_oracle(prob), TOL[dtype], label=f"far keys {dtype} d{d}",
+            magnitude_scaled=True)
+
+
 def test_scale_zero_is_uniform_attention():
     prob = inputs.make_problem(1, 2, 200, 64, "fp32", seed=79, causal=True, scale=0.0)
     compare(run_gpu(prob), run_oracle(prob), TOL["fp32"], label="scale 0")
