@@ -217,7 +217,7 @@ __device__ __forceinline__ void dma_tile(const raw* __restrict__ g, int row0, in
     const int r = pos / CPR, cs = pos % CPR;
     const int c = cs ^ swz<CPR, KIND>(r);
     const int row = min(row0 + r, N - 1);
-    dma16(g + (size_t)row * D + c * VEC, lds + blk * 1024);
+    dma16(g + (size_t)row * D + c * VEC, __builtin_amdgcn_readfirstlane(lds + blk * 1024));
   }
 }
 
@@ -243,8 +243,14 @@ struct DmaPlan {
     }
   }
   __device__ __forceinline__ void issue(const raw* first_row, uint32_t lds) const {
+    // The base address and the LDS address are wave-uniform; stating it keeps
+    // them in scalar registers wherever the compiler cannot prove it.
+    const uint64_t a = (uint64_t)first_row;
+    const raw* base = (const raw*)(((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32)) << 32) |
+                                   (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a));
 #pragma unroll
-    for (int i = 0; i < NI; ++i) dma16s(off[i], first_row, lds + (i * NW + wave) * 1024);
+    for (int i = 0; i < NI; ++i)
+      dma16s(off[i], base, __builtin_amdgcn_readfirstlane(lds + (i * NW + wave) * 1024));
   }
   // rows row0 .. row0+ROWS-1 of g, or the clamped copy if the tile is ragged
   __device__ __forceinline__ void copy(const raw* g, int row0, int N, uint32_t lds,

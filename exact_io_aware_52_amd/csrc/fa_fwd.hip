@@ -42,8 +42,11 @@
 // every lane's sum of its probabilities is at most 2^8 (which bounds each
 // one), so no per-tile max is taken; only otherwise, or before a row's first
 // visible key, is the sub-tile max formed and the reference moved, with the
-// accumulator and denominator rescaled.  The result is the same exact
-// softmax: the reference cancels in O = acc / l.  (Pre-multiplying Q by c
+// accumulator and denominator rescaled.  Dense self-attention first tries
+// an unchecked sweep with the reference fixed from each row's first 32 keys
+// and falls back to the checked one only if a denominator passes 2^64 or an
+// accumulator is not finite.  The result is the same exact softmax either
+// way: the reference cancels in O = acc / l.  (Pre-multiplying Q by c
 // would save the multiply but round c q to the input type, an error that
 // grows with the size of the scores.)
 //
@@ -53,6 +56,8 @@
 
 #include "fa_common.h"
 #include "fa_internal.h"
+
+#include <type_traits>
 
 namespace fa {
 namespace {
@@ -116,8 +121,10 @@ struct FwdCfg {
   // height: 64-row tiles (NW = 2) hold half the default's waves per CU (6 at
   // d = 64, 4 at d = 128), and 256-row tiles (NW = 8) one work-group, 8
   // waves, since two of them would need more VGPRs than a SIMD holds.  The
-  // fp32 instances (accuracy, not speed) take the whole register file.
-  static constexpr int WAVES_PER_SIMD = B16 ? (D == 64 ? 3 : 2) : 1;
+  // fp32 instances (accuracy, not speed) take the whole register file, and
+  // so does the one-wave d = 128 tile (inference with few queries), which
+  // would spill to fit two.
+  static constexpr int WAVES_PER_SIMD = B16 ? (D == 64 ? 3 : (NW == 1 ? 1 : 2)) : 1;
   static constexpr int NS = B16 ? (D == 64 ? 3 : 2) : 4;
   static constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);  // one K or V tile
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
@@ -158,6 +165,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 
   __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
   __shared__ uint8_t mask_row[kMaxMaskBlocks];
+  __shared__ int wg_redo;  // unchecked sweep overflowed somewhere in the work-group
   const uint32_t ring_lds = lds_addr(ring);
   auto ktile = [&](int s) { return reinterpret_cast<const raw*>(ring + s * L::SLOT_BYTES); };
   auto vtile = [&](int s) {
@@ -233,7 +241,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   DmaPlan<raw, BT, D, VSWZ, NW> vplan;
   kplan.init(w, lane);
   vplan.init(w, lane);
-  auto issue = [&](int t, int s) {
+  auto issue = [&](int t, int s) __attribute__((always_inline)) {
     const uint32_t base = ring_lds + s * L::SLOT_BYTES;
     kplan.copy(Kg, t * BT, NK, base, lane);
     vplan.copy(Vg, t * BT, NK, base + L::TILE_BYTES, lane);
@@ -429,115 +437,179 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     // Without the pipeline: step i forms, exponentiates and multiplies into
     // O the scores of tile i, from ring slot i % NS, with the next NS - 1
     // tiles requested ahead (several work-groups per CU hide the latency).
+    //
+    // Dense self-attention first takes an unchecked sweep: each row's
+    // reference point is fixed at the largest score among keys 0 .. 31
+    // (key 0 is visible to every row here) and no sub-tile is checked on the
+    // way, so a step has no branch and the compiler interleaves its matrix and
+    // vector work across both sub-tiles.  Probabilities may then exceed 1.
+    // The sweep is kept if every row's denominator is at most 2^64 and every
+    // accumulator is finite: no probability, product or sum has then lost
+    // range.  Otherwise the work-group starts over with the checked sweep
+    // (the lazy reference above), which is also the only sweep for masked,
+    // split or packed problems.
     constexpr int NS = L::NS, PD = NS - 1;
     static_assert(PD >= 1 && PD <= 3, "ring of 2 to 4 slots");
+    auto sweep = [&](auto checked_c) {
+      constexpr bool CHECKED = decltype(checked_c)::value;
+      int tl[PD + 1];
+      tl[0] = next_kept(t0);
 #pragma unroll
-    for (int k = 0; k < PD; ++k)
-      if (tl[k] < nkt) issue(tl[k], k);
-    FA_STAGE_FENCE();
-    // The Q fragments arrived by ordinary loads issued before these copies.
-    // Waiting for everything once here tells the compiler they have landed;
-    // otherwise it waits for them (vmcnt(0)) at their first use inside the
-    // loop, on every step, which also stalls on the tiles just requested.
-    wait_vmcnt<0>();
-    int cur = 0, nxt = PD;  // ring slots of tile i and of tile i + PD
-    // One ring tile seen in full by this wave: NSUB sub-tiles, each with its
-    // scores, exponentials and P V products.
-    auto full_tile = [&](const raw* Kc, const raw* Vc) {
+      for (int k = 1; k <= PD; ++k) tl[k] = tl[k - 1] < nkt ? next_kept(tl[k - 1] + 1) : nkt;
+      // (tile indices are wave-uniform; the copies take them as scalars)
 #pragma unroll
-      for (int h = 0; h < NSUB; ++h) {
+      for (int k = 0; k <= PD; ++k) tl[k] = __builtin_amdgcn_readfirstlane(tl[k]);
+#pragma unroll
+      for (int k = 0; k < PD; ++k)
+        if (tl[k] < nkt) issue(tl[k], k);
+      FA_STAGE_FENCE();
+      // The Q fragments arrived by ordinary loads issued before these copies.
+      // Waiting for everything once here tells the compiler they have landed;
+      // otherwise it waits for them (vmcnt(0)) at their first use inside the
+      // loop, on every step, which also stalls on the tiles just requested.
+      wait_vmcnt<0>();
+      if constexpr (!CHECKED) {
+        // Reference points: sub-tile 0 of tile 0, the keys each row sees.
+        __syncthreads();
         f32x16 sc;
-        frag_t<T> pf[2];
-        scores(Kc, h, sc);
-        const float rs = expo(sc, pf, false);
-        if (h > 0) {
-          // This block also holds the P V products of sub-tile h-1 (after
-          // its settle branch): score reads and products first, then each
-          // P V product beside a share of the exponentials.
-          __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
-          __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
-          __builtin_amdgcn_sched_group_barrier(0x100, 4 * D / 32, 0);
+        scores(ktile(0), 0, sc);
+        apply_mask(0, 0, sc);
+        float mx = kNegInf;
 #pragma unroll
-          for (int i = 0; i < 2 * D / 32; ++i) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * D / 32), 0);
-          }
-        }
-        settle(sc, pf, rs, false);
-        pv(Vc, h, pf);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+        ra = pair_max(mx) * c;
       }
-    };
-    // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
-    int lo = nkt, hi = -1;
-    if (!sparse) {
-      lo = t0;
-      hi = min(min(nkt, NK / BT) - 1 - PD, kend / BT - 1);
-      // whole tile visible to query i0: (t + 1) BT - 1 <= i0 + shift
-      if (p.causal) hi = min(hi, i0 + shift + 1 >= 0 ? (i0 + shift + 1) / BT - 1 : -1);
-    }
-    for (;;) {
-      const int t = tl[0];
-      const raw* Kc = ktile(cur);
-      const raw* Vc = vtile(cur);
-      if (t >= lo && t <= hi) {
-        wait_vmcnt<(PD - 1) * LPT>();  // tile t landed; t+1 .. t+PD-1 may be in flight
-        __syncthreads();               // every wave is done with step i-1: slot nxt is free
-        const uint32_t nb = ring_lds + nxt * L::SLOT_BYTES;
-        kplan.issue(Kg + (size_t)(t + PD) * BT * D, nb);
-        vplan.issue(Vg + (size_t)(t + PD) * BT * D, nb + L::TILE_BYTES);
-        FA_STAGE_FENCE();
-        full_tile(Kc, Vc);
-#pragma unroll
-        for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
-        tl[PD] = min(t + PD + 1, nkt);
-      } else {
-        int inflight = 0;  // later tiles requested so far (at most PD - 1)
-#pragma unroll
-        for (int k = 1; k < PD; ++k) inflight += tl[k] < nkt;
-        if constexpr (PD >= 3) {
-          if (inflight >= 2) wait_vmcnt<2 * LPT>();
-          else if (inflight == 1) wait_vmcnt<LPT>();
-          else wait_vmcnt<0>();
-        } else if constexpr (PD == 2) {
-          if (inflight == 1) wait_vmcnt<LPT>();
-          else wait_vmcnt<0>();
-        } else {
-          wait_vmcnt<0>();
-        }
-        __syncthreads();  // every wave is done with step i-1: slot nxt is free
-        if (tl[PD] < nkt) issue(tl[PD], nxt);
-        FA_STAGE_FENCE();
-        // A tile this wave sees in full (every sub-tile active and unmasked;
-        // wave-uniform) takes the interior's interleaved order.
-        bool full = true;
-#pragma unroll
-        for (int h = 0; h < NSUB; ++h) full = full && active(t, h) && !masked(t, h);
-        if (full) {
-          full_tile(Kc, Vc);
-        } else {
+      // Per sub-tile bookkeeping: the checked sweep's settle, or the sum.
+      auto take = [&](const f32x16& s, frag_t<T> (&pf)[2], float rs, bool has_mask) {
+        if constexpr (CHECKED) settle(s, pf, rs, has_mask);
+        else l_run += rs;
+      };
+      int cur = 0, nxt = PD;  // ring slots of tile i and of tile i + PD
+      // One ring tile seen in full by this wave: NSUB sub-tiles, each with its
+      // scores, exponentials and P V products.
+      auto full_tile = [&](const raw* Kc, const raw* Vc) {
 #pragma unroll
         for (int h = 0; h < NSUB; ++h) {
-          if (active(t, h)) {
-            f32x16 sc;
-            frag_t<T> pf[2];
-            scores(Kc, h, sc);
-            const bool mc = masked(t, h);
-            if (mc) apply_mask(t, h, sc);
-            const float rs = expo(sc, pf, mc);
-            settle(sc, pf, rs, mc);
-            pv(Vc, h, pf);
-          }
-        }
-        }
+          f32x16 sc;
+          frag_t<T> pf[2];
+          scores(Kc, h, sc);
+          const float rs = expo(sc, pf, false);
+          if (CHECKED && h > 0) {
+            // This block also holds the P V products of sub-tile h-1 (after
+            // its settle branch): score reads and products first, then each
+            // P V product beside a share of the exponentials.
+            __builtin_amdgcn_sched_group_barrier(0x100, D / 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x008, D / 16, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 4 * D / 32, 0);
 #pragma unroll
-        for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
-        tl[PD] = tl[PD] < nkt ? next_kept(tl[PD] + 1) : nkt;
+            for (int i = 0; i < 2 * D / 32; ++i) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x002, 40 / (2 * D / 32), 0);
+            }
+          }
+          take(sc, pf, rs, false);
+          pv(Vc, h, pf);
+        }
+      };
+      // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
+      int lo = nkt, hi = -1;
+      if (!sparse) {
+        lo = t0;
+        hi = min(min(nkt, NK / BT) - 1 - PD, kend / BT - 1);
+        // whole tile visible to query i0: (t + 1) BT - 1 <= i0 + shift
+        if (p.causal) hi = min(hi, i0 + shift + 1 >= 0 ? (i0 + shift + 1) / BT - 1 : -1);
       }
-      FA_STAGE_FENCE();
-      cur = cur + 1 == NS ? 0 : cur + 1;
-      nxt = nxt + 1 == NS ? 0 : nxt + 1;
-      if (tl[0] >= nkt) break;
+      for (;;) {
+        const int t = __builtin_amdgcn_readfirstlane(tl[0]);
+        const raw* Kc = ktile(cur);
+        const raw* Vc = vtile(cur);
+        if (t >= lo && t <= hi) {
+          wait_vmcnt<(PD - 1) * LPT>();  // tile t landed; t+1 .. t+PD-1 may be in flight
+          __syncthreads();               // every wave is done with step i-1: slot nxt is free
+          const uint32_t nb = ring_lds + nxt * L::SLOT_BYTES;
+          kplan.issue(Kg + (size_t)(t + PD) * BT * D, nb);
+          vplan.issue(Vg + (size_t)(t + PD) * BT * D, nb + L::TILE_BYTES);
+          FA_STAGE_FENCE();
+          full_tile(Kc, Vc);
+#pragma unroll
+          for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
+          tl[PD] = min(t + PD + 1, nkt);
+        } else {
+          int inflight = 0;  // later tiles requested so far (at most PD - 1)
+#pragma unroll
+          for (int k = 1; k < PD; ++k) inflight += tl[k] < nkt;
+          if constexpr (PD >= 3) {
+            if (inflight >= 2) wait_vmcnt<2 * LPT>();
+            else if (inflight == 1) wait_vmcnt<LPT>();
+            else wait_vmcnt<0>();
+          } else if constexpr (PD == 2) {
+            if (inflight == 1) wait_vmcnt<LPT>();
+            else wait_vmcnt<0>();
+          } else {
+            wait_vmcnt<0>();
+          }
+          __syncthreads();  // every wave is done with step i-1: slot nxt is free
+          if (tl[PD] < nkt) issue(tl[PD], nxt);
+          FA_STAGE_FENCE();
+          // A tile this wave sees in full (every sub-tile active and unmasked;
+          // wave-uniform) takes the interior's interleaved order.
+          bool full = true;
+#pragma unroll
+          for (int h = 0; h < NSUB; ++h) full = full && active(t, h) && !masked(t, h);
+          if (full) {
+            full_tile(Kc, Vc);
+          } else {
+#pragma unroll
+            for (int h = 0; h < NSUB; ++h) {
+              if (active(t, h)) {
+                f32x16 sc;
+                frag_t<T> pf[2];
+                scores(Kc, h, sc);
+                const bool mc = masked(t, h);
+                if (mc) apply_mask(t, h, sc);
+                const float rs = expo(sc, pf, mc);
+                take(sc, pf, rs, mc);
+                pv(Vc, h, pf);
+              }
+            }
+          }
+#pragma unroll
+          for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
+          tl[PD] = __builtin_amdgcn_readfirstlane(tl[PD] < nkt ? next_kept(tl[PD] + 1) : nkt);
+        }
+        FA_STAGE_FENCE();
+        cur = cur + 1 == NS ? 0 : cur + 1;
+        nxt = nxt + 1 == NS ? 0 : nxt + 1;
+        if (tl[0] >= nkt) break;
+      }
+    };
+    // (One-wave tiles, for inference with few queries, keep only the checked
+    // sweep: both would not fit its registers at d = 128.)
+    bool checked = NW == 1 || sparse || p.causal_br || p.cu_q || p.opart;
+    if constexpr (NW > 1) {
+      if (!checked) {
+        sweep(std::false_type{});
+        bool bad = !(l_run <= 0x1p64f);
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) bad = bad || !(__builtin_fabsf(oacc[db][r]) <= 0x1p127f);
+        // Work-group wide: every wave is done with the ring before the flag is
+        // read, and any wave's overflow sends the whole work-group back.
+        if (tid == 0) wg_redo = 0;
+        __syncthreads();
+        if (__builtin_amdgcn_ballot_w64(bad) != 0 && lane == 0) wg_redo = 1;
+        __syncthreads();
+        checked = __builtin_amdgcn_readfirstlane(wg_redo) != 0;
+        if (checked) {
+          ra = 0.f;
+          l_run = 0.f;
+#pragma unroll
+          for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
+        }
+      }
     }
+    if (checked) sweep(std::true_type{});
   }
 
   // Epilogue: O = acc / l, LSE = ln(2^ra l) = ra ln(2) + ln(l).
@@ -598,7 +670,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 // each row's reference once; probabilities are exp2(c s - ra) from then on,
 // with no rescaling in the loop.  The result is the same softmax (the
 // reference cancels in O = acc / l).  A wave whose sub-tile sums ever exceed
-// 2^32 (scores far above those of the first keys) marks itself and, after
+// 2^32 (bf16; 2^15 for fp16, whose largest value is 65504) (scores far
+// above those of the first keys) marks itself and, after
 // the loop, recomputes its rows alone with the moving reference of
 // fa_fwd_kernel, staging K and V through its own part of the ring.
 //
@@ -616,7 +689,10 @@ __global__ __launch_bounds__(512) void fa_fwd_pp_kernel(FwdParams p) {
   constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);
   constexpr int SLOT_BYTES = 2 * TILE_BYTES;
   constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);  // DMA instructions per wave per tile
-  constexpr float kOverflow = 4294967296.f;          // 2^32
+  // Bound on a sub-tile's probabilities (their sum bounds each one) before
+  // they are rounded to T for the P V products: 2^32 for bf16; fp16 tops
+  // out at 65504, so 2^15 there.
+  constexpr float kOverflow = std::is_same<T, _Float16>::value ? 32768.f : 4294967296.f;
 
   __shared__ __attribute__((aligned(1024))) char ring[NS * SLOT_BYTES];
   const uint32_t ring_lds = lds_addr(ring);

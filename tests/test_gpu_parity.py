@@ -328,22 +328,34 @@ def test_forward_block_rows(case):
             magnitude_scaled=klr is not None and klr[0] < 4)
 
 
+@pytest.mark.parametrize("boost", [1.5, 6.0])
+@pytest.mark.parametrize("rows", [128, 256])
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, True), ("fp16", 128, False),
                                              ("bf16", 128, True)])
-def test_forward_far_keys_take_the_recompute_path(dtype, d, causal):
-    # 256-row tiles of dense 16-bit problems fix each row's reference point at
-    # the largest score among the first 32 keys.  Here a few later keys are
-    # scaled so that their scores exceed that reference by far more than
-    # 2^32 allows: those waves recompute their rows with a moving reference.
-    # Both paths must agree with the oracle (rows then attend almost only to
+def test_forward_far_keys_take_the_recompute_path(dtype, d, causal, rows, boost):
+    # Dense 16-bit forwards fix each row's reference point at the largest
+    # score among the first 32 keys it sees (256-row tiles, and the unchecked
+    # sweep of 128-row tiles).  Here a few later keys are scaled so that their
+    # scores exceed that reference.  With boost 6 they do so by far more than
+    # either allows (2^32 for 256-row tiles, a denominator of 2^64 for 128-row
+    # ones) and those rows are recomputed with a moving reference; with boost
+    # 1.5 the 128-row sweep keeps probabilities of up to 2^49 as they are.
+    # Every path must agree with the oracle (rows then attend almost only to
     # the planted keys, so O leaves the unit-variance regime: scaled bound).
     prob = inputs.make_problem(1, 2, 700, d, dtype, seed=611 + d, causal=causal, scale=1.0)
-    prob.k[:, :, 300:304] *= 6.0
+    prob.k[:, :, 300:304] *= boost
     prob.k = inputs.round_to_dtype(prob.k, dtype)
-    gpu = run_gpu(prob, block_rows=256)
-    check_all_heads(prob, gpu, f"far keys {dtype} d{d}")
-    compare(gpu, run_oracle(prob), TOL[dtype], label=f"far keys {dtype} d{d}",
-            magnitude_scaled=True)
+    # How far above the fixed reference the planted scores reach (log2 units).
+    s = np.einsum("bhid,bhjd->bhij", prob.q.astype(np.float64), prob.k.astype(np.float64))
+    s = s * prob.scale * np.log2(np.e)
+    first = s[..., :32].max(axis=-1)
+    later = s[..., 300:304].max(axis=-1)
+    margin = (later - first)[..., 300:].max()
+    assert margin > 64 + 8 if boost > 2 else 16 < margin < 60
+    gpu = run_gpu(prob, block_rows=rows)
+    label = f"far keys x{boost} {dtype} d{d} rows {rows}"
+    check_all_heads(prob, gpu, label)
+    compare(gpu, run_oracle(prob), TOL[dtype], label=label, magnitude_scaled=True)
 
 
 def test_scale_zero_is_uniform_attention():
