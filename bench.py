@@ -39,6 +39,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import (accounting, build_lib, fa_backward,  # noqa: E402
+                                   fa_backward_blocksparse_split,
+                                   fa_backward_blocksparse_split_workspace_bytes,
                                    fa_backward_dkdv, fa_backward_dq,
                                    fa_backward_workspace_bytes, fa_forward,
                                    fa_forward_blocksparse_split,
@@ -52,8 +54,12 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 # Algorithmic flops per kept pair, in units of d, that each kernel performs:
 # forward S and PV; the dK/dV pass does the recomputed S, dP, dV and dK; the
 # dQ pass contributes the dQ product only (its S and dP repeat the dK/dV pass).
-KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2}
+# The split block-sparse backward is one call (both passes and their
+# reductions), timed as one unit: 10 d.
+KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2, "bwd": 10}
 KERNEL_NAMES = {"fwd": "fa_fwd_kernel", "fwd_pp": "fa_fwd_pp_kernel",
+                "bwd": "fa_bwd_split_prep_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel "
+                       "+ fa_bwd_split_reduce_kernel (split backward)",
                 "fwd_combine": "fa_fwd_combine_kernel",
                 "bwd_dq": "fa_bwd_dq_kernel", "bwd_dkdv": "fa_bwd_dkdv_kernel"}
 METRIC = "attention TFLOP/s fwd & fwd+bwd (bf16, d=64, N=1K\u201316K) and % of MFMA peak"
@@ -476,10 +482,19 @@ class Runner:
         # 256-row tiles of dense 16-bit self-attention run the ping-pong kernel.
         self.fwd_kernel = KERNEL_NAMES["fwd_pp" if self.fwd_rows == 256 and prob.dtype != "fp32"
                                        and prob.block_mask is None else "fwd"]
+        # Their backward is split by kept mask blocks, 64 per work-group (measured
+        # at 32K: 911, 979 and 1217 us for 32, 64 and 128 against 1346 unsplit; at
+        # 64K all within 1% of unsplit, the passes bound by HBM reads of sparse
+        # tiles; 64 keeps the float32 partial workspace at 3 GB for 64K).
+        self.chunk_blocks = 0
         if prob.name.startswith("block_sparse_long"):
             self.key_chunk = -(-prob.N // (4 * 64)) * 64
             self.split_ws = torch.empty(max(fa_forward_blocksparse_split_workspace_bytes(
                 prob.B, prob.H, prob.N, prob.d, self.key_chunk), 1), dtype=torch.uint8,
+                device=dev)
+            self.chunk_blocks = 64
+            self.bsplit_ws = torch.empty(fa_backward_blocksparse_split_workspace_bytes(
+                prob.B, prob.H, prob.N, prob.d, self.chunk_blocks), dtype=torch.uint8,
                 device=dev)
         self.kw = dict(scale=self.scale, causal=prob.causal, key_lens=self.kl,
                        block_mask=self.bm, block_size=prob.block_size)
@@ -502,10 +517,20 @@ class Runner:
         fa_backward_dkdv(self.q, self.k, self.v, self.do, self.ws, dk=self.dk, dv=self.dv,
                          **self.kw)
 
+    def bwd(self):
+        if self.chunk_blocks:
+            fa_backward_blocksparse_split(self.q, self.k, self.v, self.o, self.do, self.lse,
+                                          self.bm, self.prob.block_size, self.chunk_blocks,
+                                          scale=self.scale, causal=self.prob.causal,
+                                          key_lens=self.kl, dq=self.dq, dk=self.dk, dv=self.dv,
+                                          workspace=self.bsplit_ws)
+        else:
+            fa_backward(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq,
+                        dk=self.dk, dv=self.dv, workspace=self.ws, **self.kw)
+
     def step(self):
         self.fwd()
-        fa_backward(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq, dk=self.dk,
-                    dv=self.dv, workspace=self.ws, **self.kw)
+        self.bwd()
 
 
 def wall_ms(fn, n):
@@ -524,7 +549,12 @@ def measure(run, steps, warmup, kernels=True):
     for _ in range(warmup):
         run.step()
     out = {"ms_step": wall_ms(run.step, steps), "ms_fwd": wall_ms(run.fwd, steps)}
-    if kernels:
+    if kernels and run.chunk_blocks:
+        out["kernels_us"] = {
+            "fwd": 1e3 * event_time_ms(run.fwd, steps),
+            "bwd": 1e3 * event_time_ms(run.bwd, steps),
+        }
+    elif kernels:
         out["kernels_us"] = {
             "fwd": 1e3 * event_time_ms(run.fwd, steps),
             "bwd_dq": 1e3 * event_time_ms(run.bwd_dq, steps),
@@ -630,7 +660,7 @@ def main():
     roof = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak, "unit": "TFLOP/s",
             "frac": round(achieved / peak, 4),
             "traffic": (read_traffic(dict(KERNEL_NAMES, fwd=run.fwd_kernel)[dom], prob.name)
-                        if not (dom == "fwd" and run.key_chunk) else None),
+                        if not (dom == "bwd" or (dom == "fwd" and run.key_chunk)) else None),
             "kernel": names[dom], "kernel_avg_us": round(kus[dom], 2),
             "algorithmic_flops_per_launch": work}
 
@@ -652,6 +682,7 @@ def main():
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
                    "fwd_block_rows": run.fwd_rows, "fwd_key_chunk": run.key_chunk or None,
+                   "bwd_chunk_blocks": run.chunk_blocks or None,
                    "parallelism": "none"},
         "fwd_ms": round(ms_fwd, 4),
         "fwd_tflops": round(4 * prob.d * pairs / (ms_fwd * 1e-3) / 1e12, 2),

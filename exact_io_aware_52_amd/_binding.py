@@ -61,6 +61,10 @@ def open_library(path):
     lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P]
+    lib.fa_backward_blocksparse_split.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I,
+                                                  P, P, I, I, I, P, Z, P]
+    lib.fa_backward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.fa_backward_blocksparse_split_workspace_bytes.restype = Z
     lib.fa_backward_workspace_bytes.argtypes = [I, I, I, I]
     lib.fa_backward_workspace_bytes.restype = Z
     lib.fa_status_string.argtypes = [I]
@@ -394,6 +398,46 @@ def fa_backward_dkdv(q, k, v, dout, workspace, scale=None, causal=False, key_len
     _, dk, dv, _ = _backward("fa_backward_dkdv", q, k, v, None, dout, None, scale, causal,
                              key_lens, block_mask, block_size, None, dk, dv, workspace)
     return dk, dv
+
+
+def fa_backward_blocksparse_split_workspace_bytes(B, H, N, d, chunk_blocks):
+    return int(load_library().fa_backward_blocksparse_split_workspace_bytes(
+        B, H, N, d, int(chunk_blocks)))
+
+
+def fa_backward_blocksparse_split(q, k, v, o, dout, lse, block_mask, block_size=128,
+                                  chunk_blocks=64, scale=None, causal=False, key_lens=None,
+                                  dq=None, dk=None, dv=None, workspace=None):
+    """Block-sparse backward with each mask row (dQ pass) and column (dK/dV
+    pass) handed out in items of chunk_blocks kept blocks over work-groups,
+    longer ones reduced from float32 partials (for masks with a few very long
+    rows or columns).  Returns (dQ, dK, dV) in q.dtype.  workspace: uint8
+    device tensor of at least fa_backward_blocksparse_split_workspace_bytes(...)
+    bytes, allocated here when not given."""
+    if block_mask is None:
+        raise ValueError("block_mask is required")
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    for nm, t in (("o", o), ("dout", dout)):
+        _like(nm, t, q)
+    _like("lse", lse, q, (B, H, N), torch.float32)
+    dq = torch.empty_like(q) if dq is None else _like("dq", dq, q)
+    dk = torch.empty_like(q) if dk is None else _like("dk", dk, q)
+    dv = torch.empty_like(q) if dv is None else _like("dv", dv, q)
+    need = fa_backward_blocksparse_split_workspace_bytes(B, H, N, d, chunk_blocks)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    elif workspace.device != q.device or not workspace.is_contiguous():
+        raise ValueError("workspace must be a contiguous tensor on the device of q")
+    kl = _lens(key_lens, B, q.device)
+    bm = _mask(block_mask, N, block_size, q.device)
+    st = lib.fa_backward_blocksparse_split(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm), int(block_size),
+        int(chunk_blocks), _DTYPE_CODE[q.dtype], _ptr(workspace),
+        workspace.numel() * workspace.element_size(), _stream(q.device))
+    _check("fa_backward_blocksparse_split", st)
+    return dq, dk, dv
 
 
 def fa_forward_block_rows_for(B, H, N, d, dtype, sparse=False):

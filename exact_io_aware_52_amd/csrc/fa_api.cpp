@@ -100,6 +100,22 @@ size_t split_workspace(int B, int H, int N, int d, int splits) {
   return round_up(rows * d * sizeof(float), 256) + round_up(rows * sizeof(float), 256);
 }
 
+// Block-sparse backward split: items per mask row or column, and the bytes of
+// one float32 partial array [items][B*H][N][d] (rounded up to 256 bytes).
+int bwd_split_items(int N, int chunk_blocks) {
+  const int nblk = (N + 127) / 128;
+  return (nblk + chunk_blocks - 1) / chunk_blocks;
+}
+size_t bwd_split_part_bytes(int B, int H, int N, int d, int chunk_blocks) {
+  return round_up((size_t)bwd_split_items(N, chunk_blocks) * B * H * N * d * sizeof(float), 256);
+}
+// Kept-block counts per mask row and column (int32 [2][nblk]), then the
+// transposed mask ([nblk][nblk] bytes), each rounded up to 256 bytes.
+size_t bwd_split_mask_bytes(int N) {
+  const size_t nblk = (size_t)(N + 127) / 128;
+  return round_up(2 * nblk * sizeof(int32_t), 256) + round_up(nblk * nblk, 256);
+}
+
 // Key-range split of one forward call (splits = 1: none).
 struct SplitArgs {
   int key_chunk = 0;
@@ -216,7 +232,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                   float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
                   int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream, int passes, fa_dtype grad_dtype) {
+                  hipStream_t stream, int passes, fa_dtype grad_dtype, int chunk_blocks = 0) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
@@ -235,7 +251,9 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
     return st;
   if (pkv && ((st = check_tensor(dk, "dk", 16)) || (st = check_tensor(dv, "dv", 16)))) return st;
   if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
-  const size_t need = fa_backward_workspace_bytes(B, H, N, d);
+  const size_t need = chunk_blocks > 0
+                         ? fa_backward_blocksparse_split_workspace_bytes(B, H, N, d, chunk_blocks)
+                         : fa_backward_workspace_bytes(B, H, N, d);
   if (!workspace) return fail(FA_ERR_WORKSPACE, "workspace is NULL (%zu bytes needed)", need);
   if (!aligned(workspace, 16)) return fail(FA_ERR_INVALID_ARG, "workspace is not 16-byte aligned");
   if (workspace_bytes < need)
@@ -243,6 +261,20 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
   p.bwd_passes = passes;
   p.grad_f32 = grad_dtype == FA_F32 && dtype != FA_F32;
+  if (chunk_blocks > 0) {
+    const size_t base = fa_backward_workspace_bytes(B, H, N, d);
+    const size_t part = bwd_split_part_bytes(B, H, N, d, chunk_blocks);
+    char* const w = static_cast<char*>(workspace);
+    p.chunk_blocks = chunk_blocks;
+    p.split_items = bwd_split_items(N, chunk_blocks);
+    p.part_dq = reinterpret_cast<float*>(w + base);
+    p.part_dk = reinterpret_cast<float*>(w + base + part);
+    p.part_dv = reinterpret_cast<float*>(w + base + 2 * part);
+    const size_t nblk = (size_t)(N + 127) / 128;
+    p.split_counts = reinterpret_cast<int32_t*>(w + base + 3 * part);
+    p.mask_t = reinterpret_cast<uint8_t*>(w + base + 3 * part +
+                                          round_up(2 * nblk * sizeof(int32_t), 256));
+  }
   fa::BwdTensors t{q, k, v, o, dout, lse, dq, dk, dv, static_cast<float*>(workspace)};
   hipError_t e = fa::launch_backward(p, t);
   if (e != hipSuccess) return fail(FA_ERR_HIP, "backward launch: %s", hipGetErrorString(e));
@@ -425,6 +457,34 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* do
   return backward_impl(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, B, H, N, d, scale,
                        causal, key_lens, block_mask, block_size, dtype, workspace,
                        workspace_bytes, stream, fa::kPassDkDv, dtype);
+}
+
+size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,
+                                                     int chunk_blocks) {
+  if (B <= 0 || H <= 0 || N <= 0 || d <= 0 || chunk_blocks <= 0) return 0;
+  if (bwd_split_items(N, chunk_blocks) > kMaxSplits) return 0;
+  return fa_backward_workspace_bytes(B, H, N, d) +
+         3 * bwd_split_part_bytes(B, H, N, d, chunk_blocks) + bwd_split_mask_bytes(N);
+}
+
+int fa_backward_blocksparse_split(const void* q, const void* k, const void* v, const void* o,
+                                  const void* dout, const float* lse, void* dq, void* dk,
+                                  void* dv, int B, int H, int N, int d, float scale, int causal,
+                                  const int32_t* key_lens, const uint8_t* block_mask,
+                                  int block_size, int chunk_blocks, fa_dtype dtype,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  g_detail[0] = 0;
+  if (chunk_blocks <= 0)
+    return fail(FA_ERR_UNSUPPORTED, "chunk_blocks=%d (at least 1)", chunk_blocks);
+  if (N > 0 && bwd_split_items(N, chunk_blocks) > kMaxSplits)
+    return fail(FA_ERR_UNSUPPORTED, "N=%d with chunk_blocks=%d gives more than %d items", N,
+                chunk_blocks, kMaxSplits);
+  if (dtype == FA_F32)
+    return fail(FA_ERR_UNSUPPORTED, "split backward for float32 inputs (use fa_backward)");
+  if (!block_mask) return fail(FA_ERR_INVALID_ARG, "block_mask is NULL");
+  return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
+                       block_mask, block_size, dtype, workspace, workspace_bytes, stream,
+                       fa::kPassBoth, dtype, chunk_blocks);
 }
 
 int fa_backward_noalloc(const void* q, const void* k, const void* v, const void* o,

@@ -9,6 +9,15 @@ namespace fa {
 hipError_t launch_backward_f32(const Problem& p, const BwdTensors& t);  // fa_bwd_f32.hip
 
 hipError_t launch_backward(const Problem& p, const BwdTensors& t) {
+  if (p.chunk_blocks > 0) {  // block-sparse split (16-bit types; checked by the caller)
+    switch (p.dtype * 1000 + p.d) {
+      case 1 * 1000 + 64: return launch_bwd_t<_Float16, 64, false, true>(p, t);
+      case 1 * 1000 + 128: return launch_bwd_t<_Float16, 128, false, true>(p, t);
+      case 2 * 1000 + 64: return launch_bwd_t<__bf16, 64, false, true>(p, t);
+      case 2 * 1000 + 128: return launch_bwd_t<__bf16, 128, false, true>(p, t);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (p.dtype * 1000 + p.d) {
     case 0 * 1000 + 64:
     case 0 * 1000 + 128: return launch_backward_f32(p, t);

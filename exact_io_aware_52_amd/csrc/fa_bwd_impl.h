@@ -28,6 +28,16 @@
 // straight into a 4-slot LDS ring by direct-to-LDS loads, requested two steps
 // before use; one barrier per step.
 //
+// Long block-sparse rows and columns (a "global" block row attends every key
+// block, a global column is seen by every query block) would make one
+// work-group's sweep the whole kernel's critical path.  The split instances
+// (SPLIT) therefore hand out each row (dQ pass) or column (dK/dV pass) in
+// items of chunk_blocks kept mask blocks, one work-group per item
+// (gridDim.y = items of the longest row).  A tile with at most chunk_blocks
+// kept blocks is one item and writes its result directly; the items of a
+// longer one write fp32 partials that fa_bwd_split_reduce_kernel sums in item
+// order, so the result stays deterministic.
+//
 // Masks: tiles that straddle a causal, padding or sequence boundary apply the
 // element mask after the exponentials, in a loop of their own behind one
 // wave-uniform branch (or as selects in the interleaved step); a run-time
@@ -73,7 +83,72 @@ struct BwdParams {
   float scale;
   float c;  // scale * log2(e)
   int causal;
+  // Split by kept mask blocks (SPLIT instances): work-group (tile, item)
+  // takes kept blocks item * chunk_blocks .. of its row or column; tiles
+  // with more than chunk_blocks kept blocks write fp32 partials
+  // [item][BH][N][d] (dK scaled), summed by fa_bwd_split_reduce_kernel.
+  int chunk_blocks;
+  float* part_dq;
+  float* part_dk;
+  float* part_dv;
+  // Written by fa_bwd_split_prep_kernel: kept blocks of each mask row, then
+  // of each column ([2][nblk], whole rows and columns: an upper bound on
+  // what a pass counts, enough to drop items that cannot exist before they
+  // load anything), and the mask transposed ([nblk][nblk], so that the dK/dV
+  // pass reads its column contiguously).
+  int* split_counts;
+  uint8_t* mask_t;
 };
+
+// Split backward, before both passes: per mask row and column the kept
+// blocks, and the transposed mask.  One work-group per mask row r.
+__global__ __launch_bounds__(256) void fa_bwd_split_prep_kernel(BwdParams p) {
+  const int r = (int)blockIdx.x, nb = p.nblk;
+  int rows = 0, cols = 0;
+  for (int base = 0; base < nb; base += 256) {
+    const int i = base + (int)threadIdx.x;
+    const bool in = i < nb;
+    const uint8_t mr = in ? p.block_mask[(size_t)r * nb + i] : 0;
+    const uint8_t mc = in ? p.block_mask[(size_t)i * nb + r] : 0;
+    if (in) p.mask_t[(size_t)r * nb + i] = mc;
+    rows += __syncthreads_count(mr != 0);
+    cols += __syncthreads_count(mc != 0);
+  }
+  if (threadIdx.x == 0) {
+    p.split_counts[r] = rows;
+    p.split_counts[nb + r] = cols;
+  }
+}
+
+// Kept blocks among m[lo, hi) (LDS copy of a mask row or column; every wave
+// computes the same wave-uniform count).
+__device__ __forceinline__ int count_kept(const uint8_t* m, int lo, int hi, int lane) {
+  int n = 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    n += __builtin_popcountll(__builtin_amdgcn_ballot_w64(i < hi && m[i] != 0));
+  }
+  return n;
+}
+
+// Index of the kept block of rank `rank` (0-based) among m[lo, hi), or hi if
+// there are not that many.
+__device__ __forceinline__ int kth_kept(const uint8_t* m, int lo, int hi, int rank, int lane) {
+  int before = 0;
+  for (int base = lo; base < hi; base += 64) {
+    const int i = base + lane;
+    const bool kept = i < hi && m[i] != 0;
+    const uint64_t bits = __builtin_amdgcn_ballot_w64(kept);
+    const int n = __builtin_popcountll(bits);
+    if (rank < before + n) {
+      const int r = __builtin_popcountll(bits & ((1ull << lane) - 1ull));
+      const uint64_t hit = __builtin_amdgcn_ballot_w64(kept && r == rank - before);
+      return base + (int)__builtin_ctzll(hit);
+    }
+    before += n;
+  }
+  return hi;
+}
 
 // ----------------------------------------------------------------------------
 // dK, dV.  Work-group: 4 waves x 32 keys; query tiles of BQ rows.
@@ -106,7 +181,7 @@ struct DkDvCfg {
 // GF32: store dK, dV as float32 (16-bit inputs; an option for exact
 // comparisons, compiled as separate instances so that the usual instances'
 // register allocation is untouched).
-template <typename T, int D, bool GF32 = false>
+template <typename T, int D, bool GF32 = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     DkDvCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
   typedef raw_t<T> raw;
@@ -131,6 +206,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
   int kt, bh;
   map_tile(blockIdx.x, nkt, p.BH, false, p.hgroup, kt, bh);
+  if constexpr (SPLIT) {
+    // an item past every kept block of this column: nothing to do
+    if (blockIdx.y > 0 && (int)blockIdx.y * p.chunk_blocks >= p.split_counts[p.nblk + kt]) return;
+  }
   const int b = bh / p.H;
   const int j0 = kt * BK;
   const int kw0 = j0 + 32 * w;  // first key of this wave
@@ -150,12 +229,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   // Query tiles that see keys [j0, j0 + BK); the block-mask column of this
   // key block is cached in LDS.
   const int nqt = (N + BQ - 1) / BQ;
-  const int t_begin = p.causal ? j0 / BQ : 0;
-  const int t_end = j0 < kend ? nqt : t_begin;  // no visible key in this tile: nothing to do
+  int t_begin = p.causal ? j0 / BQ : 0;
+  int t_end = j0 < kend ? nqt : t_begin;  // no visible key in this tile: nothing to do
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     for (int i = tid; i < p.nblk; i += 256)
-      mask_col[i] = p.block_mask[(size_t)i * p.nblk + j0 / kMaskBlock];
+      mask_col[i] = SPLIT ? p.mask_t[(size_t)(j0 / kMaskBlock) * p.nblk + i]
+                          : p.block_mask[(size_t)i * p.nblk + j0 / kMaskBlock];
   }
 
   f32x16 dk_acc[D / 32], dv_acc[D / 32];
@@ -173,6 +253,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     vf[kc] = ok ? load_frag<T>(Vg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
   }
   __syncthreads();  // mask_col visible
+
+  // Split: this work-group's item of the column's kept query blocks.
+  bool multi = false;  // the column has more than one item: write partials
+  const int item = SPLIT ? (int)blockIdx.y : 0;
+  if constexpr (SPLIT) {
+    const int qlo = (t_begin * BQ) / kMaskBlock;
+    const int qhi = min((t_end * BQ + kMaskBlock - 1) / kMaskBlock, p.nblk);
+    const int total = count_kept(mask_col, qlo, qhi, lane);
+    const int C = p.chunk_blocks;
+    if (item > 0 && item * C >= total) return;  // whole work-group, no barrier pending
+    multi = total > C;
+    const int b0 = kth_kept(mask_col, qlo, qhi, item * C, lane);
+    const int b1 = kth_kept(mask_col, qlo, qhi, (item + 1) * C, lane);
+    t_begin = max(t_begin, b0 * (kMaskBlock / BQ));
+    t_end = min(t_end, b1 * (kMaskBlock / BQ));
+    if (t_end < t_begin) t_end = t_begin;
+  }
 
   auto next_kept = [&](int t) {
     if (!sparse) return t;
@@ -465,13 +562,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
   // Kept query tiles in order; tl[k] is the tile of step i + k.  Step i
   // forms S and dP of tile i, its softmax, then the dV, dK products.
-  int tl[3];
+  // The split instances (long sparse masks, whose tiles come from HBM rather
+  // than L2) request tiles three steps ahead, using the ring's fourth slot;
+  // the others two.
+  constexpr bool LA3 = SPLIT;
+  int tl[4];
   tl[0] = t_begin < t_end ? next_kept(t_begin) : t_end;
   tl[1] = tl[0] < t_end ? next_kept(tl[0] + 1) : t_end;
   tl[2] = tl[1] < t_end ? next_kept(tl[1] + 1) : t_end;
+  tl[3] = LA3 && tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
   if (tl[0] < t_end) {
     issue(tl[0], 0);
     if (tl[1] < t_end) issue(tl[1], 1);
+    if (LA3 && tl[2] < t_end) issue(tl[2], 2);
     FA_STAGE_FENCE();
     // The K and V fragments arrived by ordinary loads issued before these
     // copies.  Waiting for everything once here tells the compiler they have
@@ -517,9 +620,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         tl[1] = t + 2;
         tl[2] = min(t + 3, t_end);
       } else {
-        wait_tiles(tl[1] < t_end ? 1 : 0);  // tile t landed; tl[1] may be in flight
-        __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
-        if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+        if constexpr (LA3) {
+          wait_tiles((tl[1] < t_end) + (tl[2] < t_end));  // tile t landed
+          __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
+          if (tl[3] < t_end) issue(tl[3], (step + 3) & 3);
+        } else {
+          wait_tiles(tl[1] < t_end ? 1 : 0);  // tile t landed; tl[1] may be in flight
+          __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
+          if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+        }
         FA_STAGE_FENCE();
         if (active(t)) {
           if constexpr (L::ILV) {
@@ -535,7 +644,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
         }
         tl[0] = tl[1];
         tl[1] = tl[2];
-        tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+        if constexpr (LA3) {
+          tl[2] = tl[3];
+          tl[3] = tl[3] < t_end ? next_kept(tl[3] + 1) : t_end;
+        } else {
+          tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+        }
       }
       FA_STAGE_FENCE();
       ++step;
@@ -543,6 +657,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     }
   }
 
+  if constexpr (SPLIT) {
+    if (multi) {
+      // One item of a long column: fp32 partials of scale * dK and dV.
+      if (myk < N) {
+        const size_t prow = ((size_t)item * p.BH + bh) * N + myk;
+        float* const dkg = p.part_dk + prow * D;
+        float* const dvg = p.part_dv + prow * D;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            f32x4 k4, v4;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+              k4[u] = dk_acc[db][4 * g + u] * p.scale;
+              v4[u] = dv_acc[db][4 * g + u];
+            }
+            *reinterpret_cast<f32x4*>(dkg + db * 32 + 8 * g + 4 * hh) = k4;
+            *reinterpret_cast<f32x4*>(dvg + db * 32 + 8 * g + 4 * hh) = v4;
+          }
+      }
+      return;
+    }
+  }
   // Store dK = scale * dK and dV.  A lane holds four consecutive d of one key
   // (key `myk`), so storing straight from the accumulators makes every
   // instruction write 16 bytes into each of 32 rows; lines that leave L2 half
@@ -624,7 +762,7 @@ struct DqCfg {
   static constexpr int GK = (sizeof(raw) == 2 && D == 128) ? 1 : 0;
 };
 
-template <typename T, int D, bool GF32 = false>
+template <typename T, int D, bool GF32 = false, bool SPLIT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     DqCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
   typedef raw_t<T> raw;
@@ -649,6 +787,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
   int qt, bh;
   map_tile(blockIdx.x, nq, p.BH, p.causal != 0, p.hgroup, qt, bh, p.causal != 0);
+  if constexpr (SPLIT) {
+    // an item past every kept block of this row: nothing to do
+    if (blockIdx.y > 0 && (int)blockIdx.y * p.chunk_blocks >= p.split_counts[qt]) return;
+  }
   const int b = bh / p.H;
   const int i0 = qt * BR;
   const int qw0 = i0 + 32 * w;
@@ -658,7 +800,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
   int kv_end = kend;
   if (p.causal) kv_end = min(kv_end, i0 + BR);
-  const int nkt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
+  int nkt = kv_end > 0 ? (kv_end + BC - 1) / BC : 0;
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
@@ -695,7 +837,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
   const float dneg = -pair_sum(part);  // -D
-  if (myq < N && hh == 0) {
+  if (myq < N && hh == 0 && (!SPLIT || blockIdx.y == 0)) {
     p.dvec[(size_t)bh * N + myq] = dneg;
     p.lse2[(size_t)bh * N + myq] = lse2;
   }
@@ -703,6 +845,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int r = 0; r < 16; ++r) dinit[r] = dneg;
   __syncthreads();  // mask_row visible
+
+  // Split: this work-group's item of the row's kept key blocks.
+  int kt_first = 0;
+  bool multi = false;  // the row has more than one item: write partials
+  const int item = SPLIT ? (int)blockIdx.y : 0;
+  if constexpr (SPLIT) {
+    const int nb = min((max(kv_end, 0) + kMaskBlock - 1) / kMaskBlock, p.nblk);
+    const int total = count_kept(mask_row, 0, nb, lane);
+    const int C = p.chunk_blocks;
+    if (item > 0 && item * C >= total) return;  // whole work-group, no barrier pending
+    multi = total > C;
+    const int b0 = kth_kept(mask_row, 0, nb, item * C, lane);
+    const int b1 = kth_kept(mask_row, 0, nb, (item + 1) * C, lane);
+    kt_first = b0 * (kMaskBlock / BC);
+    nkt = min(nkt, b1 * (kMaskBlock / BC));
+  }
 
   auto next_kept = [&](int j) {
     if (!sparse) return j;
@@ -807,36 +965,65 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  int tl[3];
-  tl[0] = next_kept(0);
+  // As in the dK/dV pass: three tiles ahead in the split instances.
+  constexpr bool LA3 = SPLIT;
+  int tl[4];
+  tl[0] = kt_first < nkt ? next_kept(kt_first) : nkt;
   tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
   tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
+  tl[3] = LA3 && tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
   if (tl[0] < nkt) {
     issue(tl[0], 0);
     if (tl[1] < nkt) issue(tl[1], 1);
     if (tl[2] < nkt) issue(tl[2], 2);
+    if (LA3 && tl[3] < nkt) issue(tl[3], 3);
     FA_STAGE_FENCE();
     // As in the dK/dV pass: the Q and dO fragments came by ordinary loads;
     // wait for them here, once, rather than inside the loop.
     wait_vmcnt<0>();
     int step = 0;
     while (true) {
-      wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));
-      __syncthreads();  // every wave is done with step i-1
-      if (step > 0 && tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+      if constexpr (LA3) {
+        wait_tiles((tl[1] < nkt) + (tl[2] < nkt));
+        __syncthreads();  // every wave is done with step i-1
+        if (step > 0 && tl[3] < nkt) issue(tl[3], (step + 3) & 3);
+      } else {
+        wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));
+        __syncthreads();  // every wave is done with step i-1
+        if (step > 0 && tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+      }
       FA_STAGE_FENCE();
       const int kt0 = tl[0] * BC;
       if (!p.causal || kt0 <= qw0 + 31) step_math(ring + (step & 3) * L::SLOT_BYTES, kt0);
       tl[0] = tl[1];
       tl[1] = tl[2];
-      tl[2] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+      if constexpr (LA3) {
+        tl[2] = tl[3];
+        tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+      } else {
+        tl[2] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+      }
       FA_STAGE_FENCE();
       ++step;
       if (tl[0] >= nkt) break;
     }
   }
 
-  if constexpr (GF32) {
+  if (SPLIT && multi) {
+    // One item of a long row: fp32 partial of scale * dQ.
+    if (myq < N) {
+      float* const dQg = p.part_dq + (((size_t)item * p.BH + bh) * N + myq) * D;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 out;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) out[u] = dq_acc[db][4 * g + u] * p.scale;
+          *reinterpret_cast<f32x4*>(dQg + db * 32 + 8 * g + 4 * hh) = out;
+        }
+    }
+  } else if constexpr (GF32) {
     if (myq < N) {
       float* const dQg = reinterpret_cast<float*>(p.dq) + head + (size_t)myq * D;
 #pragma unroll
@@ -864,8 +1051,71 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   }
 }
 
-template <typename T, int D, bool GF32 = false>
+// Sums, in item order, the fp32 partials of the tiles whose mask row (dQ;
+// COLS false) or column (dK and dV; COLS true) has more than chunk_blocks
+// kept blocks, and writes the gradients of those tiles.  One work-group per
+// 128-row tile of a head; the kept blocks are counted over the same range as
+// in the pass that wrote the partials, so both agree on which tiles are split.
+template <typename T, int D, bool COLS>
+__global__ __launch_bounds__(256) void fa_bwd_split_reduce_kernel(BwdParams p) {
+  typedef raw_t<T> raw;
+  typedef raw4_t<T> raw4;
+  const int N = p.N;
+  const int nt = (N + 127) / 128;
+  const int tile = (int)blockIdx.x % nt;
+  const int bh = (int)blockIdx.x / nt;
+  const int b = bh / p.H;
+  int kend = N;
+  if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
+  const int r0 = tile * 128;
+  if (p.split_counts[(COLS ? p.nblk : 0) + tile] <= p.chunk_blocks) return;  // one item at most
+  int lo, hi;
+  if constexpr (!COLS) {
+    const int kv_end = p.causal ? min(kend, r0 + 128) : kend;
+    lo = 0;
+    hi = min((max(kv_end, 0) + kMaskBlock - 1) / kMaskBlock, p.nblk);
+  } else {
+    constexpr int BQ = DkDvCfg<T, D>::BQ;
+    const int nqt = (N + BQ - 1) / BQ;
+    const int t_begin = p.causal ? r0 / BQ : 0;
+    const int t_end = r0 < kend ? nqt : t_begin;
+    lo = (t_begin * BQ) / kMaskBlock;
+    hi = min((t_end * BQ + kMaskBlock - 1) / kMaskBlock, p.nblk);
+  }
+  int total = 0;
+  for (int base = lo; base < hi; base += 256) {
+    const int i = base + (int)threadIdx.x;
+    const bool kept = i < hi && (COLS ? p.mask_t : p.block_mask)[(size_t)tile * p.nblk + i] != 0;
+    total += __syncthreads_count(kept);
+  }
+  const int C = p.chunk_blocks;
+  if (total <= C) return;  // one item: its pass wrote the gradients directly
+  const int items = (total + C - 1) / C;
+  const int rows = min(128, N - r0);
+  constexpr int V4 = D / 4;  // float4 per row
+  for (int e = (int)threadIdx.x; e < rows * V4; e += 256) {
+    const int r = e / V4, c4 = e - r * V4;
+    const size_t row = (size_t)bh * N + r0 + r;
+#pragma unroll
+    for (int o = 0; o < (COLS ? 2 : 1); ++o) {
+      const float* part = COLS ? (o ? p.part_dv : p.part_dk) : p.part_dq;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < items; ++s)
+        acc += *reinterpret_cast<const f32x4*>(part + ((size_t)s * p.BH * N + row) * D + 4 * c4);
+      raw4 out;
+#pragma unroll
+      for (int u = 0; u < 4; ++u) out[u] = __builtin_bit_cast(raw, (T)acc[u]);
+      raw* dst = reinterpret_cast<raw*>(COLS ? (o ? p.dv : p.dk) : p.dq);
+      *reinterpret_cast<raw4*>(dst + row * D + 4 * c4) = out;
+    }
+  }
+}
+
+// SPLIT: the split instances, launched with one work-group per item
+// (gridDim.y = pb.split_items), each pass followed by its reduce kernel.
+template <typename T, int D, bool GF32 = false, bool SPLIT = false>
 hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
+  static_assert(!(GF32 && SPLIT), "split backward: gradients in the input type");
   BwdParams p;
   p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.dout = t.dout; p.lse = t.lse;
   p.dq = t.dq; p.dk = t.dk; p.dv = t.dv;
@@ -883,19 +1133,43 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   p.scale = pb.scale;
   p.c = pb.scale * kLog2e;
   p.causal = pb.causal;
+  p.chunk_blocks = SPLIT ? pb.chunk_blocks : 0;
+  p.part_dq = pb.part_dq;
+  p.part_dk = pb.part_dk;
+  p.part_dv = pb.part_dv;
+  p.split_counts = pb.split_counts;
+  p.mask_t = pb.mask_t;
 
   const unsigned tiles128 = (unsigned)((pb.N + 127) / 128);
+  if constexpr (SPLIT) {
+    hipLaunchKernelGGL(fa_bwd_split_prep_kernel, dim3(p.nblk), dim3(256), 0, pb.stream, p);
+    hipError_t e0 = hipGetLastError();
+    if (e0 != hipSuccess) return e0;
+  }
+  const unsigned items = SPLIT ? (unsigned)pb.split_items : 1u;
   hipError_t e = hipSuccess;
   if (pb.bwd_passes & kPassDq) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32>), dim3(tiles128 * p.BH), dim3(256), 0,
-                       pb.stream, p);
+    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32, SPLIT>), dim3(tiles128 * p.BH, items),
+                       dim3(256), 0, pb.stream, p);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
+    if constexpr (SPLIT) {
+      hipLaunchKernelGGL((fa_bwd_split_reduce_kernel<T, D, false>), dim3(tiles128 * p.BH),
+                         dim3(256), 0, pb.stream, p);
+      e = hipGetLastError();
+      if (e != hipSuccess) return e;
+    }
   }
   if (pb.bwd_passes & kPassDkDv) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32>), dim3(tiles128 * p.BH), dim3(256), 0,
-                       pb.stream, p);
+    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT>), dim3(tiles128 * p.BH, items),
+                       dim3(256), 0, pb.stream, p);
     e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if constexpr (SPLIT) {
+      hipLaunchKernelGGL((fa_bwd_split_reduce_kernel<T, D, true>), dim3(tiles128 * p.BH),
+                         dim3(256), 0, pb.stream, p);
+      e = hipGetLastError();
+    }
   }
   return e;
 }

@@ -36,6 +36,16 @@ struct Problem {
   int Tq = 0, Tk = 0;
   int bwd_passes = kPassBoth;  // backward: which passes to launch (BwdPass bits)
   int grad_f32 = 0;            // backward, 16-bit inputs: float32 dQ, dK, dV
+  // Block-sparse backward split by kept mask blocks (chunk_blocks > 0): items
+  // of chunk_blocks kept blocks per mask row (dQ) or column (dK, dV), at most
+  // split_items per tile; fp32 partials [split_items][B*H][N][d] each.
+  int chunk_blocks = 0;
+  int split_items = 1;
+  float* part_dq = nullptr;
+  float* part_dk = nullptr;
+  float* part_dv = nullptr;
+  int* split_counts = nullptr;  // [2][ceil(N/128)] kept blocks per mask row, column
+  uint8_t* mask_t = nullptr;    // [ceil(N/128)]^2 transposed block mask
 };
 
 // Heads per XCD dispatched together (map_tile's group).  The XCDs of MI355X

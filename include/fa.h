@@ -231,6 +231,43 @@ int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* do
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * Block-sparse backward for masks with a few very long block rows or columns
+ * (visual guide, block-sparse paragraph: long-context results; a "global"
+ * row attends every key block, a global column is seen by every query
+ * block).  As fa_backward with block_mask required, except that each mask
+ * row (dQ pass) and each mask column (dK/dV pass) is handed out in items of
+ * chunk_blocks kept blocks, one work-group per item, instead of one
+ * work-group sweeping the whole row or column.  A row or column with at most
+ * chunk_blocks kept blocks is one item and writes its gradients directly;
+ * the items of a longer one write float32 partials to the workspace, which a
+ * reduction sums in item order (deterministic).  Arguments:
+ *   chunk_blocks  kept mask blocks per item, >= 1 (FA_ERR_UNSUPPORTED
+ *                 otherwise, or beyond 1024 items per row);
+ *   dtype         FA_F16 or FA_BF16 (FA_F32: FA_ERR_UNSUPPORTED; gradients
+ *                 come back in dtype);
+ *   workspace     caller-owned device memory of at least
+ *                 fa_backward_blocksparse_split_workspace_bytes(B,H,N,d,
+ *                 chunk_blocks) bytes, 16-byte aligned, not initialised:
+ *                 fa_backward's workspace, then three float32 partial arrays
+ *                 [items][B,H,N,d] (items = ceil(ceil(N/128) / chunk_blocks)),
+ *                 of which only split rows and columns touch their part, then
+ *                 the kept-block counts of every mask row and column and the
+ *                 transposed mask.  Calls that share a workspace must be
+ *                 ordered on one stream.
+ * Same results as fa_backward up to the rounding of the partial sums.
+ */
+int fa_backward_blocksparse_split(const void* q, const void* k, const void* v,
+                                  const void* o, const void* dout, const float* lse,
+                                  void* dq, void* dk, void* dv, int B, int H, int N,
+                                  int d, float scale, int causal,
+                                  const int32_t* key_lens, const uint8_t* block_mask,
+                                  int block_size, int chunk_blocks, fa_dtype dtype,
+                                  void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream);
+size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,
+                                                     int chunk_blocks);
+
+/*
  * Forward with the tile height chosen per call (review page, claims C2 and
  * C3: tiling reduces HBM reads and writes, and the IO cost depends on the
  * on-chip memory size; K and V are read once per query tile, so that traffic

@@ -179,6 +179,43 @@ int main() {
                             nullptr, nullptr, 128, FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward_noalloc(a, a, a, a, a, f, nullptr, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr,
                             nullptr, 128, FA_BF16, nullptr) == FA_ERR_INVALID_ARG);
+  // ---- block-sparse backward split by kept blocks: item count and the
+  // three float32 partial arrays placed after the unsplit workspace
+  {
+    const uint8_t* bm2 = reinterpret_cast<const uint8_t*>(a);
+    const size_t base = fa_backward_workspace_bytes(1, 8, 65536, 64);
+    const size_t part = 8ull * 8 * 65536 * 64 * 4;  // 512 blocks per row in items of 64: 8
+    const size_t need = fa_backward_blocksparse_split_workspace_bytes(1, 8, 65536, 64, 64);
+    const size_t masks = 4096 + 512ull * 512;  // int32 counts [2][512], transposed mask
+    CHECK(need == base + 3 * part + masks);
+    char* ws = static_cast<char*>(a);
+    CHECK(fa_backward_blocksparse_split(a, a, a, a, a, f, a, a, a, 1, 8, 65536, 64, 0.1f, 0,
+                                        nullptr, bm2, 128, 64, FA_BF16, ws, need,
+                                        nullptr) == FA_OK);
+    CHECK(g_last.chunk_blocks == 64 && g_last.split_items == 8 &&
+          g_last.part_dq == reinterpret_cast<float*>(ws + base) &&
+          g_last.part_dk == reinterpret_cast<float*>(ws + base + part) &&
+          g_last.part_dv == reinterpret_cast<float*>(ws + base + 2 * part) &&
+          g_last.split_counts == reinterpret_cast<int*>(ws + base + 3 * part) &&
+          g_last.mask_t == reinterpret_cast<uint8_t*>(ws + base + 3 * part + 4096) &&
+          g_last.bwd_passes == fa::kPassBoth && g_last.grad_f32 == 0);
+    CHECK(fa_backward_blocksparse_split(a, a, a, a, a, f, a, a, a, 1, 8, 65536, 64, 0.1f, 0,
+                                        nullptr, bm2, 128, 64, FA_BF16, ws, need - 1,
+                                        nullptr) == FA_ERR_WORKSPACE);
+    CHECK(fa_backward_blocksparse_split(a, a, a, a, a, f, a, a, a, 1, 8, 65536, 64, 0.1f, 0,
+                                        nullptr, nullptr, 128, 64, FA_BF16, ws, need,
+                                        nullptr) == FA_ERR_INVALID_ARG);
+    CHECK(fa_backward_blocksparse_split(a, a, a, a, a, f, a, a, a, 1, 8, 65536, 64, 0.1f, 0,
+                                        nullptr, bm2, 128, 0, FA_BF16, ws, need,
+                                        nullptr) == FA_ERR_UNSUPPORTED);
+    CHECK(fa_backward_blocksparse_split(a, a, a, a, a, f, a, a, a, 1, 8, 65536, 64, 0.1f, 0,
+                                        nullptr, bm2, 128, 64, FA_F32, ws, need,
+                                        nullptr) == FA_ERR_UNSUPPORTED);
+    // a later unsplit call carries no split state
+    CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                      FA_BF16, a, bw, nullptr) == FA_OK);
+    CHECK(g_last.chunk_blocks == 0 && g_last.part_dq == nullptr);
+  }
   // ---- a failed launch is reported, with its message
   g_result = hipErrorInvalidValue;
   CHECK(fa_forward(a, a, a, a, f, 1, 1, 64, 64, 0.1f, 0, nullptr, FA_BF16, nullptr) == FA_ERR_HIP);

@@ -137,6 +137,37 @@ def test_backward_validation(lib):
     assert bwd(lib, d=80) == _binding.FA_ERR_UNSUPPORTED
 
 
+def test_backward_blocksparse_split_validation(lib):
+    f = lib.fa_backward_blocksparse_split
+
+    def call(N=1000, chunk=2, ws=FAKE, ws_bytes=1 << 40, bm=FAKE, dtype=2, d=64):
+        return f(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 2, 3, N, d, 0.1, 0, None,
+                 bm, 128, chunk, dtype, ws, ws_bytes, None)
+
+    for chunk in (0, -1):
+        assert call(chunk=chunk) == _binding.FA_ERR_UNSUPPORTED
+        assert "chunk_blocks" in detail(lib)
+    assert call(N=131072 + 128, chunk=1) == _binding.FA_ERR_UNSUPPORTED  # 1025 items per row
+    assert "1024" in detail(lib)
+    assert call(dtype=0) == _binding.FA_ERR_UNSUPPORTED                   # float32 inputs
+    assert call(bm=None) == _binding.FA_ERR_INVALID_ARG
+    ws_bytes = lib.fa_backward_blocksparse_split_workspace_bytes
+    base = lib.fa_backward_workspace_bytes(2, 3, 1000, 64)
+    # 8 mask blocks per row in items of 2: 4 items; three fp32 [4][2*3][1000][64] arrays,
+    # then int32 counts [2][8] and the transposed 8 x 8 mask, each rounded to 256 bytes
+    part = 4 * 2 * 3 * 1000 * 64 * 4
+    masks = 256 + 256
+    assert ws_bytes(2, 3, 1000, 64, 2) == base + 3 * part + masks
+    assert ws_bytes(2, 3, 1000, 64, 8) == base + 3 * (part // 4) + masks   # one item
+    assert ws_bytes(2, 3, 1000, 64, 0) == 0
+    need = ws_bytes(2, 3, 1000, 64, 2)
+    assert call(ws=None) == _binding.FA_ERR_WORKSPACE
+    assert call(ws_bytes=need - 1) == _binding.FA_ERR_WORKSPACE
+    assert str(need) in detail(lib)
+    assert call(ws=BAD_ALIGN, ws_bytes=need) == _binding.FA_ERR_INVALID_ARG
+    assert call(d=96, ws_bytes=need) == _binding.FA_ERR_UNSUPPORTED
+
+
 def test_status_strings(lib):
     assert lib.fa_status_string(0) == b"FA_OK"
     assert lib.fa_status_string(3) == b"FA_ERR_WORKSPACE"

@@ -69,3 +69,42 @@ def test_serialized_stages_bitwise(case):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (
             f"{name} {n}: {int((a != b).sum())} elements differ between the builds")
     log(f"[race] {name}: all outputs bitwise equal")
+
+
+def run_split(lib, prob, chunk_blocks):
+    q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
+    bm = torch.from_numpy(prob.block_mask).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((prob.B, prob.H, prob.N), dtype=torch.float32, device="cuda")
+    dq, dk, dv = (torch.full_like(q, float("nan")) for _ in range(3))
+    need = lib.fa_backward_blocksparse_split_workspace_bytes(prob.B, prob.H, prob.N, prob.d,
+                                                             chunk_blocks)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    common = (prob.B, prob.H, prob.N, prob.d, float(prob.scale), int(prob.causal), None)
+    st = lib.fa_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), *common, ptr(bm),
+                           prob.block_size, 0, CODE[prob.dtype], stream)
+    assert st == 0, lib.fa_last_error_detail()
+    st = lib.fa_backward_blocksparse_split(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse),
+                                           ptr(dq), ptr(dk), ptr(dv), *common, ptr(bm),
+                                           prob.block_size, chunk_blocks, CODE[prob.dtype],
+                                           ptr(ws), need, stream)
+    assert st == 0, lib.fa_last_error_detail()
+    torch.cuda.synchronize()
+    return {n: t.cpu() for n, t in (("dq", dq), ("dk", dk), ("dv", dv))}
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_serialized_stages_split_backward(causal):
+    # The split backward's passes (three tiles ahead in the ring), its
+    # preparation and reduction kernels, fenced and unfenced: bit for bit.
+    prob = inputs.make_problem(1, 2, 4096, 64, "bf16", seed=41 + causal, causal=causal,
+                               block_keep_p=1 / 8, block_band=1, block_global=1)
+    log(f"[race] split backward causal={causal}")
+    main = run_split(_binding.load_library(), prob, 3)
+    serial = run_split(_binding.open_library(build_lib.SERIAL_LIB), prob, 3)
+    for n in main:
+        a, b = main[n], serial[n]
+        assert not torch.isnan(a).any(), n
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), (
+            f"split {n}: {int((a != b).sum())} elements differ between the builds")
