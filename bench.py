@@ -27,6 +27,7 @@ same workload.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -38,6 +39,7 @@ import torch
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
+from exact_io_aware_52_amd import _binding  # noqa: E402
 from exact_io_aware_52_amd import (accounting, build_lib, fa_backward,  # noqa: E402
                                    fa_backward_blocksparse_split,
                                    fa_backward_blocksparse_split_workspace_bytes,
@@ -587,6 +589,73 @@ def sweep(dev, steps, warmup):
     return rows
 
 
+STAMP_SEGMENTS = {(5, 1): "loop", (5, 11): "loop", (1, 2): "wait_tile", (2, 3): "barrier",
+                  (3, 4): "math", (4, 1): "loop", (4, 11): "loop", (4, 20): "loop",
+                  (11, 12): "wait_tile", (12, 13): "barrier", (13, 14): "math",
+                  (14, 11): "loop", (14, 1): "loop", (14, 20): "loop", (20, 21): "epilogue"}
+
+
+def step_stamps(args, dev):
+    """Forward step timeline (the stamps build of the forward kernel): for
+    the heaviest, a middle and the lightest work-groups of the grid, waves 0-3
+    record the shader clock at each step's start, after its tile wait, after
+    its barrier and after its math.  Prints, per work-group and wave, the
+    total and median cycles of each segment and the clock they imply."""
+    prob = make_workload(args)
+    lib = _binding.open_library(build_lib.STAMPS_LIB)
+    lib.fa_stamps_arm.argtypes = [ctypes.c_void_p]
+    lib.fa_stamps_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t]
+    run = Runner(prob, dev, args.fwd_block_rows)
+    rows = run.fwd_rows
+    nwg = prob.B * prob.H * -(-prob.N // rows)
+    wgs = np.array([0, 1, 2, nwg // 3, nwg // 2, nwg - 3, nwg - 2, nwg - 1], dtype=np.int32)
+    assert lib.fa_stamps_arm(wgs.ctypes.data) == 0
+    dt = TORCH_DT[prob.dtype]
+    st = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    bm = None if run.bm is None else ctypes.c_void_p(run.bm.data_ptr())
+    kl = None if run.kl is None else ctypes.c_void_p(run.kl.data_ptr())
+    code = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[dt]
+
+    def fwd():
+        assert lib.fa_forward_ex(ctypes.c_void_p(run.q.data_ptr()), ctypes.c_void_p(run.k.data_ptr()),
+                                 ctypes.c_void_p(run.v.data_ptr()), ctypes.c_void_p(run.o.data_ptr()),
+                                 ctypes.c_void_p(run.lse.data_ptr()), prob.B, prob.H, prob.N, prob.d,
+                                 run.scale, int(prob.causal), kl, bm, prob.block_size, rows, code,
+                                 st) == 0
+    for _ in range(max(args.warmup, 1)):
+        fwd()
+    torch.cuda.synchronize()
+    kernel_us = 1e3 * event_time_ms(fwd, max(args.steps, 1))
+    buf = np.zeros((32, 3 * 340), dtype=np.uint64)
+    assert lib.fa_stamps_read(buf.ctypes.data, buf.nbytes) == 0
+    out = []
+    for slot, wg in enumerate(wgs):
+        for w in range(4):
+            r = buf[slot * 4 + w].reshape(-1, 3).astype(np.int64)
+            n = int(np.argmax(r[:, 0] == 0)) if (r[:, 0] == 0).any() else len(r)
+            r = r[:n]
+            if n < 2:
+                continue
+            cyc, rt, codes = r[:, 0], r[:, 1], r[:, 2]
+            seg = {}
+            for i in range(n - 1):
+                key = STAMP_SEGMENTS.get((int(codes[i]), int(codes[i + 1])))
+                if key is None and codes[i] >= 1000:
+                    key = "prologue"
+                if key:
+                    seg.setdefault(key, []).append(int(cyc[i + 1] - cyc[i]))
+            ns = 10 * int(rt[-1] - rt[0])
+            out.append({"work_group": int(wg), "wave": w,
+                        "query_tile": int(codes[0] - 1000) if codes[0] >= 1000 else None,
+                        "steps": int(sum(c in (1, 11) for c in codes)),
+                        "recorded_events": n, "wall_ns": ns, "cycles": int(cyc[-1] - cyc[0]),
+                        "clock_ghz": round((cyc[-1] - cyc[0]) / ns, 3) if ns else None,
+                        "segments": {k: {"total": int(sum(v)), "median": float(np.median(v)),
+                                         "count": len(v)} for k, v in seg.items()}})
+    print(json.dumps({"workload": prob.name, "fwd_block_rows": rows, "work_groups": nwg,
+                      "kernel_us_stamps_build": round(kernel_us, 2), "timeline": out}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -613,6 +682,9 @@ def main():
                     help="with --standard: run only the standard attention (counter runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--step-stamps", action="store_true",
+                    help="forward step timeline of chosen work-groups from the stamps build "
+                         "(libfa_stamps.so)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -633,6 +705,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30}))
+        return
+    if args.step_stamps:
+        step_stamps(args, dev)
         return
     if args.standard:
         bench_standard(args, dev)

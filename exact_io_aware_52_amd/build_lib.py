@@ -25,6 +25,9 @@ LIB = os.path.join(PKG, "libfa.so")
 # Race-check build: the same sources with every LDS ring stage fenced
 # (FA_SERIALIZE_STAGES); its results must equal libfa.so's bit for bit.
 SERIAL_LIB = os.path.join(PKG, "libfa_serial.so")
+# Step timeline build: the forward with FA_STEP_STAMPS (per-step clock stamps
+# of chosen work-groups, read by bench.py --step-stamps), the rest as libfa.so.
+STAMPS_LIB = os.path.join(PKG, "libfa_stamps.so")
 # Hash of each kernel's gfx950 machine code (all instances of one kernel
 # template together), written at every build.  Counter summaries under
 # profiles/ carry the hash of the code they were taken on, and the bench
@@ -71,6 +74,8 @@ def _compile(src, variant=""):
         del flags[i - 1:i + 1]
     if variant == "serial":
         flags.append("-DFA_SERIALIZE_STAGES")
+    if variant == "stamps":
+        flags.append("-DFA_STEP_STAMPS")
     cmd = [hipcc()] + flags + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     noise = "packed-fp32-ops' is not a recognized feature"
@@ -148,23 +153,28 @@ def kernel_code_hashes(objects):
 
 
 def build(verbose=False):
-    """Compile libfa.so and the race-check build libfa_serial.so."""
-    os.makedirs(os.path.join(BUILD, "serial"), exist_ok=True)
-    jobs = [(src, "") for src in SOURCES] + [(src, "serial") for src in SOURCES]
-    with ThreadPoolExecutor(max_workers=min(8, len(jobs))) as ex:
+    """Compile libfa.so, the race-check build libfa_serial.so and the step
+    timeline build libfa_stamps.so."""
+    for var in ("serial", "stamps"):
+        os.makedirs(os.path.join(BUILD, var), exist_ok=True)
+    jobs = ([(src, "") for src in SOURCES] + [(src, "serial") for src in SOURCES] +
+            [("fa_fwd.hip", "stamps")])
+    with ThreadPoolExecutor(max_workers=min(9, len(jobs))) as ex:
         results = list(ex.map(lambda j: _compile(*j), jobs))
     for obj, err in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
     main = [o for (o, _), (_, var) in zip(results, jobs) if not var]
-    serial = [o for (o, _), (_, var) in zip(results, jobs) if var]
+    serial = [o for (o, _), (_, var) in zip(results, jobs) if var == "serial"]
+    stamps_fwd = [o for (o, _), (_, var) in zip(results, jobs) if var == "stamps"]
     _link(main, LIB)
     _link(serial, SERIAL_LIB)
+    _link([o for o in main if not o.endswith("fa_fwd.o")] + stamps_fwd, STAMPS_LIB)
     hashes = kernel_code_hashes(main)
     with open(CODE_MANIFEST, "w") as fh:
         json.dump(hashes, fh, indent=1, sort_keys=True)
     if verbose:
-        print(f"built {LIB} and {SERIAL_LIB}")
+        print(f"built {LIB}, {SERIAL_LIB} and {STAMPS_LIB}")
         print(f"kernel code hashes: {hashes}")
     return LIB
 

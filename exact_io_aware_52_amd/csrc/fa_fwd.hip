@@ -99,6 +99,21 @@ struct FwdParams {
 
 constexpr int kMaxMaskBlocks = 1024;    // block-mask row cached in LDS (N <= 131072)
 
+// Step timeline build (FA_STEP_STAMPS, a separate library for measurement
+// only): lane 0 of waves 0..3 of up to eight chosen work-groups records
+// (shader clock, 100 MHz wall clock, event code) at fixed points of
+// fa_fwd_kernel's sweep into a device buffer that fa_stamps_read returns.
+// Codes: 1000 + query tile at the start; 5 prologue done (first tiles
+// landed); interior step: 1 top, 2 tile landed, 3 past the barrier, 4 math
+// done; generic step: 11 top, 12 tile landed, 13 past the barrier, 14 math
+// done; 20 epilogue start, 21 end.  The stores add to the wave's count of
+// memory operations in flight, so the waits for tiles are stricter there.
+#ifdef FA_STEP_STAMPS
+constexpr int kStampWgs = 8, kStampEvents = 340;
+__device__ unsigned long long g_stamps[kStampWgs * 4][3 * kStampEvents];
+__device__ int g_stamp_wgs[kStampWgs];
+#endif
+
 // NW waves per work-group, 32 query rows each (BR = 32 NW rows per tile).
 template <typename T, int D, int NW>
 struct FwdCfg {
@@ -180,6 +195,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 
   int qt, bh;
   map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, p.hgroup, qt, bh);
+#ifdef FA_STEP_STAMPS
+  int stamp_slot = -1;
+  for (int i = 0; i < kStampWgs; ++i)
+    if (g_stamp_wgs[i] == (int)blockIdx.x && blockIdx.y == 0) stamp_slot = i;
+  int stamp_ev = 0;
+  auto stamp = [&](int code) {
+    __builtin_amdgcn_sched_barrier(0);
+    const unsigned long long t = __builtin_readcyclecounter();
+    const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
+    if (stamp_slot >= 0 && w < 4 && lane == 0 && stamp_ev < kStampEvents) {
+      unsigned long long* rec = g_stamps[stamp_slot * 4 + w] + 3 * stamp_ev;
+      rec[0] = t;
+      rec[1] = rt;
+      rec[2] = (unsigned long long)code;
+    }
+    ++stamp_ev;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#else
+  auto stamp = [](int) {};
+#endif
+  stamp(1000 + qt);
   const int b = bh / p.H;
   int N = p.N;    // query rows of this head
   int NK = p.nk;  // key rows
@@ -468,6 +505,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
       // otherwise it waits for them (vmcnt(0)) at their first use inside the
       // loop, on every step, which also stalls on the tiles just requested.
       wait_vmcnt<0>();
+      stamp(5);
       if constexpr (!CHECKED) {
         // Reference points: sub-tile 0 of tile 0, the keys each row sees.
         __syncthreads();
@@ -524,17 +562,22 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         const raw* Kc = ktile(cur);
         const raw* Vc = vtile(cur);
         if (t >= lo && t <= hi) {
+          stamp(1);
           wait_vmcnt<(PD - 1) * LPT>();  // tile t landed; t+1 .. t+PD-1 may be in flight
+          stamp(2);
           __syncthreads();               // every wave is done with step i-1: slot nxt is free
+          stamp(3);
           const uint32_t nb = ring_lds + nxt * L::SLOT_BYTES;
           kplan.issue(Kg + (size_t)(t + PD) * BT * D, nb);
           vplan.issue(Vg + (size_t)(t + PD) * BT * D, nb + L::TILE_BYTES);
           FA_STAGE_FENCE();
           full_tile(Kc, Vc);
+          stamp(4);
 #pragma unroll
           for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
           tl[PD] = min(t + PD + 1, nkt);
         } else {
+          stamp(11);
           int inflight = 0;  // later tiles requested so far (at most PD - 1)
 #pragma unroll
           for (int k = 1; k < PD; ++k) inflight += tl[k] < nkt;
@@ -548,7 +591,9 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
           } else {
             wait_vmcnt<0>();
           }
+          stamp(12);
           __syncthreads();  // every wave is done with step i-1: slot nxt is free
+          stamp(13);
           if (tl[PD] < nkt) issue(tl[PD], nxt);
           FA_STAGE_FENCE();
           // A tile this wave sees in full (every sub-tile active and unmasked;
@@ -573,6 +618,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
               }
             }
           }
+          stamp(14);
 #pragma unroll
           for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
           tl[PD] = __builtin_amdgcn_readfirstlane(tl[PD] < nkt ? next_kept(tl[PD] + 1) : nkt);
@@ -612,6 +658,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     if (checked) sweep(std::true_type{});
   }
 
+  stamp(20);
   // Epilogue: O = acc / l, LSE = ln(2^ra l) = ra ln(2) + ln(l).
   const float l_tot = pair_sum(l_run);
   if (p.opart && myq < N) {
@@ -652,6 +699,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
       p.lse[lrow + myq] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
     }
   }
+  stamp(21);
 }
 
 // Ping-pong forward for 16-bit dense self-attention (no block mask, no key
@@ -1113,6 +1161,25 @@ hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
 }
 
 }  // namespace
+
+#ifdef FA_STEP_STAMPS
+// Step timeline build only (not part of the C ABI): choose the work-groups
+// (blockIdx.x, up to 8; -1 unused) and clear the buffer, then read it back
+// after the launches ([32][3 * 340] uint64: work-group slot * 4 + wave).
+extern "C" int fa_stamps_arm(const int* wgs) {
+  static unsigned long long zero[kStampWgs * 4][3 * kStampEvents];
+  hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_stamps), zero, sizeof(zero), 0,
+                                   hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpyToSymbol(HIP_SYMBOL(g_stamp_wgs), wgs, kStampWgs * sizeof(int), 0,
+                          hipMemcpyHostToDevice);
+  return (int)e;
+}
+extern "C" int fa_stamps_read(void* host, size_t bytes) {
+  if (bytes > sizeof(g_stamps)) bytes = sizeof(g_stamps);
+  return (int)hipMemcpyFromSymbol(host, HIP_SYMBOL(g_stamps), bytes, 0, hipMemcpyDeviceToHost);
+}
+#endif
 
 hipError_t launch_forward(const Problem& p, const FwdTensors& t) {
   switch (p.dtype * 1000 + p.d) {
