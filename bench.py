@@ -88,7 +88,9 @@ def read_traffic(kernel, workload):
         if ":" in line:
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    built = code_hashes().get(kernel)
+    # the hash of the instance the counters were taken on, else of the template
+    inst = fields.get("instance")
+    built = code_hashes().get("instance:" + inst if inst else kernel)
     if built is None or fields.get("code_sha256") != built:
         return None
     try:

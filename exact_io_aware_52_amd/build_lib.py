@@ -127,7 +127,9 @@ def _elf_functions(path):
 
 def kernel_code_hashes(objects):
     """sha256 (16 hex digits) of each kernel template's gfx950 code, over all
-    its instances, from the device code objects bundled in the objects."""
+    its instances (key: the kernel name), and of each instance alone (key:
+    "instance:" + its mangled name), from the device code objects bundled in
+    the objects."""
     funcs = {}
     tmp = os.path.join(BUILD, "code")
     os.makedirs(tmp, exist_ok=True)
@@ -148,6 +150,9 @@ def kernel_code_hashes(objects):
         for n in names:
             h.update(n.encode())
             h.update(funcs[n])
+            # each instance on its own as well: a counter summary names the
+            # instance it was taken on, which other instances do not change
+            hashes["instance:" + n] = hashlib.sha256(n.encode() + funcs[n]).hexdigest()[:16]
         hashes[kern] = h.hexdigest()[:16] if names else None
     return hashes
 
@@ -175,7 +180,7 @@ def build(verbose=False):
         json.dump(hashes, fh, indent=1, sort_keys=True)
     if verbose:
         print(f"built {LIB}, {SERIAL_LIB} and {STAMPS_LIB}")
-        print(f"kernel code hashes: {hashes}")
+        print(f"kernel code hashes: { {k: v for k, v in hashes.items() if ':' not in k} }")
     return LIB
 
 

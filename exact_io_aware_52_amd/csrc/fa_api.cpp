@@ -140,6 +140,10 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (block_mask && rows > 128)
     return fail(FA_ERR_UNSUPPORTED, "block-sparse forward with %d query rows per tile (at most 128)",
                 rows);
+  // Eight fp32 waves at d = 128 need more registers than a CU holds.
+  if (dtype == FA_F32 && d == 128 && rows > 128)
+    return fail(FA_ERR_UNSUPPORTED, "float32 forward at d=128 with %d query rows per tile "
+                "(at most 128)", rows);
   if (empty) return FA_OK;
   if ((st = check_tensor(q, "q", 16)) || (st = check_tensor(k, "k", 16)) ||
       (st = check_tensor(v, "v", 16)) || (st = check_tensor(o, "o", 16)) ||

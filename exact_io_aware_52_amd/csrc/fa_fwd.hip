@@ -1155,7 +1155,10 @@ hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
       if constexpr (sizeof(T) == 2) return launch_fwd_t<T, D, 1>(pb, t);
       else return launch_fwd_t<T, D, 2>(pb, t);
     case 64: return launch_fwd_t<T, D, 2>(pb, t);
-    case 256: return launch_fwd_t<T, D, 8>(pb, t);
+    case 256:
+      // (float32 at d = 128 takes at most 128 rows: refused by the caller)
+      if constexpr (sizeof(T) == 4 && D == 128) return hipErrorInvalidValue;
+      else return launch_fwd_t<T, D, 8>(pb, t);
     default: return launch_fwd_t<T, D, 4>(pb, t);
   }
 }

@@ -277,7 +277,9 @@ size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,
  *   block_rows  query rows per work-group: 64, 128 or 256, or 0 to let the
  *               library choose (fa_forward_block_rows_for).  The block-sparse
  *               forward takes 64 or 128 (FA_ERR_UNSUPPORTED for 256, since a
- *               128-token mask block must hold a whole tile); any other value
+ *               128-token mask block must hold a whole tile), and so does the
+ *               float32 forward at d = 128 (eight float32 waves would need
+ *               more registers than a compute unit holds); any other value
  *               is FA_ERR_UNSUPPORTED.
  * A tuning and measurement option: results agree to rounding for every
  * value.  fa_forward and fa_forward_blocksparse are this call with

@@ -277,6 +277,14 @@ def test_forward_ex_block_rows_validation(lib):
     assert fwd_ex(lib, 0, bm=FAKE, N=131073) == _binding.FA_ERR_UNSUPPORTED
     # empty problem: nothing checked beyond the sizes, nothing launched
     assert fwd_ex(lib, 64, N=0, q=None) == _binding.FA_OK
+    # float32 at d = 128: at most 128 rows per tile
+
+    def f32(rows, q=FAKE):
+        return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 128, 0.1, 0, None, None,
+                                 128, rows, 0, None)
+    assert f32(256) == _binding.FA_ERR_UNSUPPORTED
+    assert "float32" in detail(lib)
+    assert f32(128, q=None) == _binding.FA_ERR_INVALID_ARG
 
 
 def test_forward_block_rows_automatic(lib):

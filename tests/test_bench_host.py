@@ -27,8 +27,10 @@ def test_manifest_names_every_kernel():
     if not os.path.exists(build_lib.CODE_MANIFEST):
         build_lib.build()
     hashes = json.load(open(build_lib.CODE_MANIFEST))
-    assert set(hashes) == set(build_lib.KERNELS)
+    assert {k for k in hashes if not k.startswith("instance:")} == set(build_lib.KERNELS)
     assert all(isinstance(h, str) and len(h) == 16 for h in hashes.values())
+    for kern in build_lib.KERNELS:   # every kernel has its instances hashed one by one
+        assert any(k.startswith("instance:") and kern + "I" in k for k in hashes), kern
 
 
 def test_read_traffic_only_for_matching_code(tmp_path, monkeypatch):
@@ -43,6 +45,14 @@ def test_read_traffic_only_for_matching_code(tmp_path, monkeypatch):
     path.write_text("code_sha256: " + "ffff" * 4 + "\ntraffic_bytes_per_launch: 1234.5\n")
     assert bench.read_traffic("fa_bwd_dkdv_kernel", "w") is None
     assert bench.read_traffic("fa_bwd_dkdv_kernel", "other") is None
+    # a summary naming its instance is matched against that instance's hash
+    monkeypatch.setattr(bench, "code_hashes", lambda: {"fa_bwd_dkdv_kernel": "abcd" * 4,
+                                                       "instance:_Zinst": "1234" * 4})
+    path.write_text("kernel: fa_bwd_dkdv_kernel\ninstance: _Zinst\ncode_sha256: " + "1234" * 4 +
+                    "\ntraffic_bytes_per_launch: 99.0\n")
+    assert bench.read_traffic("fa_bwd_dkdv_kernel", "w") == 99.0
+    path.write_text("instance: _Zinst\ncode_sha256: " + "abcd" * 4 + "\ntraffic_bytes_per_launch: 9\n")
+    assert bench.read_traffic("fa_bwd_dkdv_kernel", "w") is None
 
 
 KERNEL = """#include <hip/hip_runtime.h>

@@ -311,7 +311,7 @@ ROW_CASES = [
     (64, 1, 1, 200, 64, "fp32", True, None, None),
     (256, 1, 2, 600, 64, "bf16", True, None, None),
     (256, 2, 1, 520, 128, "bf16", False, (100, 520), None),
-    (256, 1, 1, 300, 128, "fp32", True, None, None),
+    (256, 1, 1, 300, 64, "fp32", True, None, None),
 ]
 
 
