@@ -59,7 +59,7 @@ TORCH_DT = {"fp32": torch.float32, "fp16": torch.float16, "bf16": torch.bfloat16
 # The split block-sparse backward is one call (both passes and their
 # reductions), timed as one unit: 10 d.
 KERNEL_FLOPS_PER_PAIR_D = {"fwd": 4, "bwd_dkdv": 8, "bwd_dq": 2, "bwd": 10}
-KERNEL_NAMES = {"fwd": "fa_fwd_kernel", "fwd_pp": "fa_fwd_pp_kernel",
+KERNEL_NAMES = {"fwd": "fa_fwd_kernel",
                 "bwd": "fa_bwd_split_prep_kernel + fa_bwd_dq_kernel + fa_bwd_dkdv_kernel "
                        "+ fa_bwd_split_reduce_kernel (split backward)",
                 "fwd_combine": "fa_fwd_combine_kernel",
@@ -483,9 +483,7 @@ class Runner:
         # range: its forward is split four ways over work-groups (measured best
         # of 4K, 8K and 16K keys per split at N = 32K and 64K).
         self.key_chunk = 0
-        # 256-row tiles of dense 16-bit self-attention run the ping-pong kernel.
-        self.fwd_kernel = KERNEL_NAMES["fwd_pp" if self.fwd_rows == 256 and prob.dtype != "fp32"
-                                       and prob.block_mask is None else "fwd"]
+        self.fwd_kernel = KERNEL_NAMES["fwd"]
         # Their backward is split by kept mask blocks, 64 per work-group (measured
         # at 32K: 911, 979 and 1217 us for 32, 64 and 128 against 1346 unsplit; at
         # 64K all within 1% of unsplit, the passes bound by HBM reads of sparse

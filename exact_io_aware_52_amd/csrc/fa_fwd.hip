@@ -702,327 +702,6 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   stamp(21);
 }
 
-// Ping-pong forward for 16-bit dense self-attention (no block mask, no key
-// splits; causal top-left and key lengths supported): 8 waves and 256 query
-// rows per work-group, two waves on each SIMD.  A wave's work per 32-key
-// sub-tile n alternates between a matrix phase M(n) (the P V products of
-// sub-tile n-1 and the scores of sub-tile n, operands already in registers)
-// and a vector phase V(n) (the exponentials of sub-tile n, while the
-// operands of M(n+1) are read from LDS).  Waves 4..7 run one phase behind
-// waves 0..3 and every phase ends at a work-group barrier, so on each SIMD
-// one wave's vector phase runs beside the other wave's matrix phase.  K/V
-// tiles (64 keys) stream through a 4-slot ring: the slot of tile T is
-// refilled at M(2T+3) and the new tile waited for at the end of M(2T+7).
-//
-// Reference point: the row max of sub-tile 0 (every row sees key 0) fixes
-// each row's reference once; probabilities are exp2(c s - ra) from then on,
-// with no rescaling in the loop.  The result is the same softmax (the
-// reference cancels in O = acc / l).  A wave whose sub-tile sums ever exceed
-// 2^32 (bf16; 2^15 for fp16, whose largest value is 65504) (scores far
-// above those of the first keys) marks itself and, after
-// the loop, recomputes its rows alone with the moving reference of
-// fa_fwd_kernel, staging K and V through its own part of the ring.
-//
-// The interior loop (sub-tiles every wave sees in full) has no branches:
-// accumulators updated under a condition force the register allocator to
-// copy them at every join.  Sub-tiles on the causal diagonal or the key
-// length run a second loop that masks by selects.
-template <typename T, int D>
-__global__ __launch_bounds__(512) void fa_fwd_pp_kernel(FwdParams p) {
-  typedef raw_t<T> raw;
-  typedef raw4_t<T> raw4;
-  typedef Traits<T> Tr;
-  static_assert(sizeof(raw) == 2, "16-bit types only");
-  constexpr int NW = 8, BR = 32 * NW, BT = 64, NS = 4;
-  constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);
-  constexpr int SLOT_BYTES = 2 * TILE_BYTES;
-  constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);  // DMA instructions per wave per tile
-  // Bound on a sub-tile's probabilities (their sum bounds each one) before
-  // they are rounded to T for the P V products: 2^32 for bf16; fp16 tops
-  // out at 65504, so 2^15 there.
-  constexpr float kOverflow = std::is_same<T, _Float16>::value ? 32768.f : 4294967296.f;
-
-  __shared__ __attribute__((aligned(1024))) char ring[NS * SLOT_BYTES];
-  const uint32_t ring_lds = lds_addr(ring);
-  auto ktile = [&](int s) { return reinterpret_cast<const raw*>(ring + s * SLOT_BYTES); };
-  auto vtile = [&](int s) {
-    return reinterpret_cast<const raw*>(ring + s * SLOT_BYTES + TILE_BYTES);
-  };
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int late = w >> 2;  // waves 4..7 run one phase behind
-  const int col = lane & 31;
-  const int hh = lane >> 5;
-
-  int qt, bh;
-  map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, p.hgroup, qt, bh);
-  const int b = bh / p.H;
-  const int N = p.N;
-  const size_t head = (size_t)bh * N * D;
-  const int i0 = qt * BR;
-  const int qw0 = i0 + 32 * w;
-  const int myq = qw0 + col;
-  int kend = N;
-  if (p.key_lens) kend = min(max(p.key_lens[b], 0), N);
-  int kv_end = kend;
-  if (p.causal) kv_end = min(kv_end, i0 + BR);
-  const int nkt = kv_end > 0 ? (kv_end + BT - 1) / BT : 0;  // key tiles of this work-group
-  const int nsub = 2 * nkt;                                 // 32-key sub-tiles
-  // Sub-tiles every row of the work-group sees in full: keys below kend and,
-  // under the causal mask, below the first row i0.
-  int nint = min(kend, p.causal ? i0 : kend) / 32;
-  nint = max(1, min(nint, nsub));  // sub-tile 0 (peeled) counts as interior
-  // First key this lane's query does not see.
-  const int lim = p.causal ? min(kend, myq + 1) : kend;
-  const raw* __restrict__ Qg = reinterpret_cast<const raw*>(p.q) + head;
-  const raw* __restrict__ Kg = reinterpret_cast<const raw*>(p.k) + head;
-  const raw* __restrict__ Vg = reinterpret_cast<const raw*>(p.v) + head;
-  const float c = p.c;
-
-  frag_t<T> qf[D / 16];
-#pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc)
-    qf[kc] = myq < N ? load_frag<T>(Qg + (size_t)myq * D + kc * 16 + hh * 8) : zero_frag<T>();
-
-  DmaPlan<raw, BT, D, kRows, NW> kplan;
-  DmaPlan<raw, BT, D, kTr, NW> vplan;
-  kplan.init(w, lane);
-  vplan.init(w, lane);
-  auto issue = [&](int t) {
-    const uint32_t base = ring_lds + (t % NS) * SLOT_BYTES;
-    kplan.copy(Kg, t * BT, N, base, lane);
-    vplan.copy(Vg, t * BT, N, base + TILE_BYTES, lane);
-  };
-#pragma unroll
-  for (int t = 0; t < NS; ++t)
-    if (t < nkt) issue(t);
-  wait_vmcnt<0>();  // the first tiles and the Q fragments (see fa_fwd_kernel)
-  __syncthreads();
-
-  f32x16 oacc[D / 32];
-#pragma unroll
-  for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-  float ra = 0.f, l_run = 0.f;
-  bool bad = false;  // a sub-tile sum exceeded the overflow bound (wave-uniform)
-  f32x16 sc;
-  frag_t<T> pf[2];
-  frag_t<T> kn[D / 16];     // K operands of the next matrix phase's scores
-  frag_t<T> vn[2][D / 32];  // V^T operands of the next matrix phase's P V
-  auto load_k = [&](int n) {
-    const raw* Ks = ktile((n >> 1) % NS);
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc)
-      kn[kc] = load_frag_swz<T, D, kRows>(Ks, 32 * (n & 1) + col, kc * 16 + hh * 8);
-  };
-  auto load_v = [&](int n) {
-    const raw* Vs = vtile((n >> 1) % NS);
-#pragma unroll
-    for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-        vn[kc][db] = load_frag_tr<T, D, kTr>(Vs, 32 * (n & 1) + kc * 16, db * 32, lane);
-  };
-  // M(n): P V of sub-tile n-1 (pv) and the scores of sub-tile n (sc), the two
-  // products interleaved so that neither waits on its own previous result.
-  auto matrix = [&](bool pv, bool sc_new) {
-#pragma unroll
-    for (int kc = 0; kc < D / 16; ++kc) {
-      if (sc_new) sc = Tr::mma(kn[kc], qf[kc], kc == 0 ? zero16() : sc);
-      if (pv && kc < 2 * (D / 32)) {
-        const int vk = kc / (D / 32), db = kc % (D / 32);
-        oacc[db] = Tr::mma(vn[vk][db], pf[vk], oacc[db]);
-      }
-    }
-    if (pv) {
-#pragma unroll
-      for (int i = D / 16; i < 2 * (D / 32); ++i) {
-        const int vk = i / (D / 32), db = i % (D / 32);
-        oacc[db] = Tr::mma(vn[vk][db], pf[vk], oacc[db]);
-      }
-    }
-  };
-  // V(n): probabilities of sc against the fixed reference; masked sub-tiles
-  // select 0 for keys at or past this lane's limit.  Returns the lane's sum.
-  auto probs = [&](int n, bool mask) {
-    float e[16];
-#pragma unroll
-    for (int h2 = 0; h2 < 2; ++h2) {
-      frag_t<T> f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        float v = fast_exp2(fmaf(sc[8 * h2 + u], c, -ra));
-        if (mask) v = 32 * n + acc_row(8 * h2 + u, hh) < lim ? v : 0.f;
-        e[8 * h2 + u] = v;
-        f[u] = (T)v;
-      }
-      pf[h2] = f;
-    }
-    return sum16(e);
-  };
-  auto check = [&](float rs) {
-    bad = bad || __builtin_amdgcn_ballot_w64(!(rs <= kOverflow)) != 0;
-  };
-  auto wait_tile = [&](int u) {  // tiles up to u + 2 have been requested by now
-    if (u + 2 < nkt) wait_vmcnt<2 * LPT>();
-    else if (u + 1 < nkt) wait_vmcnt<LPT>();
-    else wait_vmcnt<0>();
-  };
-  auto phase_end = [&]() {
-    __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS reads are done
-    __builtin_amdgcn_sched_barrier(0);
-    __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // The matrix phase's side duties: refill the slot freed two sub-tiles ago
-  // (odd n >= 3) and wait for the tile the next vector phase starts reading.
-  auto m_duties_pre = [&](int n) {
-    if ((n & 1) && n >= 3) {
-      const int t = (n - 3) / 2 + NS;
-      if (t < nkt) issue(t);
-    }
-  };
-  auto m_duties_post = [&](int n) {
-    if ((n & 1) && (n + 1) / 2 < nkt) wait_tile((n + 1) / 2);
-  };
-
-  if (late) phase_end();
-  if (nsub > 0) {
-    // ---- M(0), V(0): sub-tile 0 fixes each row's reference.
-    load_k(0);
-    matrix(false, true);
-    phase_end();
-    load_k(1);
-    load_v(0);
-    {
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_row(r, hh) < lim ? sc[r] : kNegInf);
-      mx = pair_max(mx);
-      ra = mx == kNegInf ? 0.f : mx * c;  // rows without keys (kend = 0) never get here
-      const float rs = probs(0, true);
-      check(rs);
-      l_run = rs;
-    }
-    phase_end();
-    // ---- interior: sub-tiles 1 .. nint-1, no conditions
-    int n = 1;
-    for (; n < nint; ++n) {
-      m_duties_pre(n);
-      matrix(true, true);
-      m_duties_post(n);
-      phase_end();
-      if (n + 1 < nsub) load_k(n + 1);
-      load_v(n);
-      const float rs = probs(n, false);
-      check(rs);
-      l_run += rs;
-      phase_end();
-    }
-    // ---- boundary: sub-tiles nint .. nsub-1 (masked by selects), then the
-    // last P V.
-    for (;; ++n) {
-      m_duties_pre(n);
-      matrix(true, n < nsub);
-      m_duties_post(n);
-      phase_end();
-      if (n >= nsub) break;
-      if (n + 1 < nsub) load_k(n + 1);
-      load_v(n);
-      const float rs = probs(n, true);
-      check(rs);
-      l_run += rs;
-      phase_end();
-    }
-  } else {
-    phase_end();  // the single matrix phase of an empty range
-  }
-  if (!late) phase_end();
-
-  if (bad) {
-    // Rare: recompute this wave's rows with a moving reference (rescaling
-    // the accumulator whenever a sub-tile would exceed 2^8 against it), K and
-    // V of each 32-key sub-tile staged through this wave's 1/8 of the ring.
-    // Every wave is past the last barrier, so the ring is free.
-    const uint32_t my_lds = ring_lds + w * (NS * SLOT_BYTES / NW);
-    const raw* Ks = reinterpret_cast<const raw*>(ring + w * (NS * SLOT_BYTES / NW));
-    const raw* Vs = Ks + 32 * D;
-    static_assert(2 * 32 * D * (int)sizeof(raw) <= NS * SLOT_BYTES / NW, "staging fits");
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db) oacc[db] = zero16();
-    ra = 0.f;
-    l_run = 0.f;
-    bool ref = false;
-    const int nsw = min(kend, p.causal ? qw0 + 32 : kend);  // keys this wave can see
-    for (int n = 0; 32 * n < nsw; ++n) {
-      dma_tile<raw, 32, D, kRows, 1>(Kg, 32 * n, N, my_lds, 0, lane);
-      dma_tile<raw, 32, D, kTr, 1>(Vg, 32 * n, N, my_lds + 32 * D * (int)sizeof(raw), 0, lane);
-      wait_vmcnt<0>();
-#pragma unroll
-      for (int kc = 0; kc < D / 16; ++kc)
-        sc = Tr::mma(load_frag_swz<T, D, kRows>(Ks, col, kc * 16 + hh * 8), qf[kc],
-                     kc == 0 ? zero16() : sc);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) sc[r] = 32 * n + acc_row(r, hh) < lim ? sc[r] : kNegInf;
-      float mx = kNegInf;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-      mx = pair_max(mx);
-      const float m2 = mx == kNegInf ? kNegInf : mx * c;
-      const bool move = m2 != kNegInf && (!ref || m2 > ra + 8.f);
-      const float alpha = move && ref ? fast_exp2(ra - m2) : 1.f;
-      ra = move ? m2 : ra;
-      ref = ref || move;
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) oacc[db][r] *= alpha;
-      float e[16];
-#pragma unroll
-      for (int h2 = 0; h2 < 2; ++h2) {
-        frag_t<T> f;
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-          const float x = sc[8 * h2 + u];
-          e[8 * h2 + u] = x == kNegInf ? 0.f : fast_exp2(fmaf(x, c, -ra));
-          f[u] = (T)e[8 * h2 + u];
-        }
-        pf[h2] = f;
-      }
-      l_run += sum16(e);
-#pragma unroll
-      for (int kc = 0; kc < 2; ++kc)
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db)
-          oacc[db] = Tr::mma(load_frag_tr<T, D, kTr>(Vs, kc * 16, db * 32, lane), pf[kc], oacc[db]);
-      // the next sub-tile's copies overwrite this staging area
-      __builtin_amdgcn_s_waitcnt(0xc07f);
-    }
-  }
-
-  // Epilogue: O = acc / l, LSE = ra ln(2) + ln(l).
-  const float l_tot = pair_sum(l_run);
-  if (myq < N) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-    raw* Og = reinterpret_cast<raw*>(p.o) + head + (size_t)myq * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        raw4 out;
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const T val = (T)(oacc[db][4 * g + u] * inv);
-          out[u] = __builtin_bit_cast(raw, val);
-        }
-        *reinterpret_cast<raw4*>(Og + db * 32 + 8 * g + 4 * hh) = out;
-      }
-    if (hh == 0) p.lse[(size_t)bh * N + myq] = l_tot > 0.f ? ra * kLn2 + __logf(l_tot) : kNegInf;
-  }
-}
-
 // Merge of the key-range splits of one query row (the online-softmax merge of
 // per-block states, applied across work-groups): with split results (O_s,
 // LSE_s), LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.  A row
@@ -1120,36 +799,10 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   return launch_fwd_combine<T, D>(pb, t, splits);
 }
 
-// The ping-pong forward for dense 16-bit self-attention with 256-row tiles.
-template <typename T, int D>
-hipError_t launch_fwd_pp(const Problem& pb, const FwdTensors& t) {
-  FwdParams p = {};
-  p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.lse = t.lse;
-  p.key_lens = pb.key_lens;
-  p.H = pb.H;
-  p.N = pb.N;
-  p.nk = pb.N;
-  p.BH = pb.B * pb.H;
-  p.hgroup = head_group(p.BH, 2LL * pb.N * D * (long long)sizeof(raw_t<T>));
-  p.nq = (pb.N + 255) / 256;
-  p.scale = pb.scale;
-  p.c = pb.scale * kLog2e;
-  p.causal = pb.causal;
-  const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
-  hipLaunchKernelGGL((fa_fwd_pp_kernel<T, D>), dim3(grid), dim3(512), 0, pb.stream, p);
-  return hipGetLastError();
-}
-
 // Query rows per tile (work-group): 128 or 256 (chosen on the host), 64 on request;
-// 32 (one wave, 16-bit types) for inference with few queries.  256-row tiles of
-// dense 16-bit self-attention take the ping-pong kernel.
+// 32 (one wave, 16-bit types) for inference with few queries.
 template <typename T, int D>
 hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
-  if constexpr (sizeof(T) == 2) {
-    if (pb.fwd_rows == 256 && !pb.block_mask && pb.splits <= 1 && !pb.cu_q && !pb.causal_br &&
-        (pb.nk < 0 || pb.nk == pb.N))
-      return launch_fwd_pp<T, D>(pb, t);
-  }
   switch (pb.fwd_rows) {
     case 32:
       if constexpr (sizeof(T) == 2) return launch_fwd_t<T, D, 1>(pb, t);

@@ -333,15 +333,16 @@ def test_forward_block_rows(case):
 @pytest.mark.parametrize("dtype,d,causal", [("bf16", 64, True), ("fp16", 128, False),
                                              ("bf16", 128, True)])
 def test_forward_far_keys_take_the_recompute_path(dtype, d, causal, rows, boost):
-    # Dense 16-bit forwards fix each row's reference point at the largest
-    # score among the first 32 keys it sees (256-row tiles, and the unchecked
-    # sweep of 128-row tiles).  Here a few later keys are scaled so that their
-    # scores exceed that reference.  With boost 6 they do so by far more than
-    # either allows (2^32 for 256-row tiles, a denominator of 2^64 for 128-row
-    # ones) and those rows are recomputed with a moving reference; with boost
-    # 1.5 the 128-row sweep keeps probabilities of up to 2^49 as they are.
-    # Every path must agree with the oracle (rows then attend almost only to
-    # the planted keys, so O leaves the unit-variance regime: scaled bound).
+    # Dense 16-bit forwards first sweep with each row's reference point fixed
+    # at the largest score among the first 32 keys it sees (the unchecked
+    # sweep).  Here a few later keys are scaled so that their scores exceed
+    # that reference.  With boost 6 they do so by far more than the sweep
+    # allows (a denominator of 2^64; fp16 probabilities overflow sooner and
+    # leave the accumulator infinite) and the work-group starts over with the
+    # checked sweep; with boost 1.5 bf16 keeps probabilities of up to 2^49 as
+    # they are, while fp16 falls back.  Every path must agree with the oracle
+    # (rows then attend almost only to the planted keys, so O leaves the
+    # unit-variance regime: scaled bound).
     prob = inputs.make_problem(1, 2, 700, d, dtype, seed=611 + d, causal=causal, scale=1.0)
     prob.k[:, :, 300:304] *= boost
     prob.k = inputs.round_to_dtype(prob.k, dtype)
