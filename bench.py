@@ -463,7 +463,7 @@ def cpu_baseline_varlen(prob, budget_s):
 class Runner:
     """Device buffers and launch closures for one self-attention workload."""
 
-    def __init__(self, prob, dev, fwd_block_rows=0):
+    def __init__(self, prob, dev, fwd_block_rows=0, fwd_block_keys=0, bwd_rows=0):
         self.prob = prob
         dt = TORCH_DT[prob.dtype]
         self.q, self.k, self.v, self.do = (torch.from_numpy(x).to(dt).to(dev)
@@ -479,11 +479,19 @@ class Runner:
         self.rows = fwd_block_rows
         self.fwd_rows = fwd_block_rows or fa_forward_block_rows_for(
             prob.B, prob.H, prob.N, prob.d, dt, prob.block_mask is not None)
+        # Keys per K/V tile: 64 by default (16-bit); 32 and 128 run as
+        # fa_fwd_keys_kernel with 128-row tiles.
+        self.keys = fwd_block_keys
+        # Backward tile heights (dQ query rows, dK/dV keys per work-group).
+        self.dq_rows = self.dkdv_rows = bwd_rows
+        other_keys = fwd_block_keys not in (0, 64)
+        if other_keys:
+            self.fwd_rows = 128
         # The long structured masks give one query tile per head the whole key
         # range: its forward is split four ways over work-groups (measured best
         # of 4K, 8K and 16K keys per split at N = 32K and 64K).
         self.key_chunk = 0
-        self.fwd_kernel = KERNEL_NAMES["fwd"]
+        self.fwd_kernel = "fa_fwd_keys_kernel" if other_keys else KERNEL_NAMES["fwd"]
         # Their backward is split by kept mask blocks, 64 per work-group (measured
         # at 32K: 911, 979 and 1217 us for 32, 64 and 128 against 1346 unsplit; at
         # 64K all within 1% of unsplit, the passes bound by HBM reads of sparse
@@ -508,16 +516,16 @@ class Runner:
                                          causal=self.prob.causal, key_lens=self.kl, o=self.o,
                                          lse=self.lse, workspace=self.split_ws)
         else:
-            fa_forward_ex(self.q, self.k, self.v, block_rows=self.rows, o=self.o, lse=self.lse,
-                          **self.kw)
+            fa_forward_ex(self.q, self.k, self.v, block_rows=self.rows, block_keys=self.keys,
+                          o=self.o, lse=self.lse, **self.kw)
 
     def bwd_dq(self):
         fa_backward_dq(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq,
-                       workspace=self.ws, **self.kw)
+                       workspace=self.ws, rows=self.dq_rows, **self.kw)
 
     def bwd_dkdv(self):
         fa_backward_dkdv(self.q, self.k, self.v, self.do, self.ws, dk=self.dk, dv=self.dv,
-                         **self.kw)
+                         rows=self.dkdv_rows, **self.kw)
 
     def bwd(self):
         if self.chunk_blocks:
@@ -527,8 +535,9 @@ class Runner:
                                           key_lens=self.kl, dq=self.dq, dk=self.dk, dv=self.dv,
                                           workspace=self.bsplit_ws)
         else:
-            fa_backward(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq,
-                        dk=self.dk, dv=self.dv, workspace=self.ws, **self.kw)
+            fa_backward_ex(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq,
+                           dk=self.dk, dv=self.dv, workspace=self.ws, dq_rows=self.dq_rows,
+                           dkdv_rows=self.dkdv_rows, **self.kw)
 
     def step(self):
         self.fwd()
@@ -620,8 +629,8 @@ def step_stamps(args, dev):
         assert lib.fa_forward_ex(ctypes.c_void_p(run.q.data_ptr()), ctypes.c_void_p(run.k.data_ptr()),
                                  ctypes.c_void_p(run.v.data_ptr()), ctypes.c_void_p(run.o.data_ptr()),
                                  ctypes.c_void_p(run.lse.data_ptr()), prob.B, prob.H, prob.N, prob.d,
-                                 run.scale, int(prob.causal), kl, bm, prob.block_size, rows, code,
-                                 st) == 0
+                                 run.scale, int(prob.causal), kl, bm, prob.block_size, rows, 0,
+                                 code, st) == 0
     for _ in range(max(args.warmup, 1)):
         fwd()
     torch.cuda.synchronize()
@@ -669,6 +678,12 @@ def main():
     ap.add_argument("--d", type=int, default=64)
     ap.add_argument("--fwd-block-rows", type=int, default=0, choices=[0, 64, 128, 256],
                     help="query rows per forward work-group (tile height); 0 = chosen per problem")
+    ap.add_argument("--fwd-block-keys", type=int, default=0, choices=[0, 32, 64, 128],
+                    help="keys per forward K/V tile (B_c); 0 = the default (64); 32 and 128 "
+                         "take 128-row tiles")
+    ap.add_argument("--bwd-rows", type=int, default=0, choices=[0, 64, 128, 256],
+                    help="backward tile height: query rows per dQ work-group and keys per dK/dV "
+                         "work-group; 0 = 128")
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of host work for the oracle baseline (0 disables)")
     ap.add_argument("--no-sweep", action="store_true",
@@ -720,7 +735,7 @@ def main():
         return
 
     prob = make_workload(args)
-    run = Runner(prob, dev, args.fwd_block_rows)
+    run = Runner(prob, dev, args.fwd_block_rows, args.fwd_block_keys, args.bwd_rows)
     m = measure(run, args.steps, args.warmup)
     ms_step, ms_fwd, kus = m["ms_step"], m["ms_fwd"], m["kernels_us"]
     pairs = accounting.kept_pairs(prob)
@@ -756,7 +771,9 @@ def main():
                    "causal": prob.causal,
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
-                   "fwd_block_rows": run.fwd_rows, "fwd_key_chunk": run.key_chunk or None,
+                   "fwd_block_rows": run.fwd_rows, "fwd_block_keys": run.keys or 64,
+                   "bwd_rows": run.dq_rows or 128,
+                   "fwd_key_chunk": run.key_chunk or None,
                    "bwd_chunk_blocks": run.chunk_blocks or None,
                    "parallelism": "none"},
         "fwd_ms": round(ms_fwd, 4),

@@ -52,15 +52,15 @@ def open_library(path):
     lib.fa_forward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.fa_forward_blocksparse_split_workspace_bytes.restype = Z
     lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
-    lib.fa_backward_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P,
-                                   Z, P]
+    lib.fa_backward_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, I,
+                                   I, P, Z, P]
     lib.fa_backward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I,
                                         P]
     lib.fa_backward_noalloc_max_rows.argtypes = []
     lib.fa_backward_noalloc_max_rows.restype = Z
-    lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
-    lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
-    lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P]
+    lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P, Z, P]
+    lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P, Z, P]
+    lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, I, P]
     lib.fa_backward_blocksparse_split.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I,
                                                   P, P, I, I, I, P, Z, P]
     lib.fa_backward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -155,7 +155,7 @@ def _scale(scale, d):
 
 
 def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, lse,
-             block_rows=0):
+             block_rows=0, block_keys=0):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     o = torch.empty_like(q) if o is None else _like("o", o, q)
@@ -168,7 +168,7 @@ def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, 
         bm = _mask(block_mask, N, block_size, q.device)
         args += [_ptr(bm), int(block_size)]
     if name == "fa_forward_ex":
-        args += [int(block_rows)]
+        args += [int(block_rows), int(block_keys)]
     args += [_DTYPE_CODE[q.dtype], _stream(q.device)]
     _check(name, getattr(lib, name)(*args))
     return o, lse
@@ -189,11 +189,12 @@ def fa_forward_blocksparse(q, k, v, block_mask, block_size=128, scale=None, caus
 
 
 def fa_forward_ex(q, k, v, block_mask=None, block_size=128, block_rows=0, scale=None,
-                  causal=False, key_lens=None, o=None, lse=None):
+                  causal=False, key_lens=None, o=None, lse=None, block_keys=0):
     """Forward with the query rows per work-group (64, 128, 256; 0 = the
-    library's choice) given per call; block_mask optional."""
+    library's choice) and the keys per K/V tile (32, 64, 128; 0 = the type's
+    default) given per call; block_mask optional."""
     return _forward("fa_forward_ex", q, k, v, scale, causal, key_lens, block_mask, block_size,
-                    o, lse, block_rows)
+                    o, lse, block_rows, block_keys)
 
 
 def fa_forward_blocksparse_split_workspace_bytes(B, H, N, d, key_chunk):
@@ -326,7 +327,7 @@ def fa_backward_workspace_bytes(B, H, N, d):
 
 
 def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, block_size,
-              dq, dk, dv, workspace, grad_dtype=None):
+              dq, dk, dv, workspace, grad_dtype=None, dq_rows=0, dkdv_rows=0):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     _like("dout", dout, q)
@@ -336,7 +337,7 @@ def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, 
     gdt = q.dtype if grad_dtype is None else grad_dtype
     if gdt not in (q.dtype, torch.float32):
         raise ValueError(f"grad_dtype must be {q.dtype} or torch.float32")
-    if gdt != q.dtype:
+    if name == "fa_backward" and (gdt != q.dtype or dq_rows or dkdv_rows):
         name = "fa_backward_ex"
 
     def grad(t, nm):
@@ -358,7 +359,9 @@ def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, 
     tail = [B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm),
             int(block_size), _DTYPE_CODE[q.dtype]]
     if name == "fa_backward_ex":
-        tail.append(_DTYPE_CODE[gdt])
+        tail += [_DTYPE_CODE[gdt], int(dq_rows), int(dkdv_rows)]
+    elif name in ("fa_backward_dq", "fa_backward_dkdv"):
+        tail.append(int(dq_rows if name == "fa_backward_dq" else dkdv_rows))
     tail += [_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)]
     if name in ("fa_backward", "fa_backward_ex"):
         head = [_ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk),
@@ -382,21 +385,60 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
     return dq, dk, dv
 
 
+def fa_backward_ex(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
+                   block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None,
+                   grad_dtype=None, dq_rows=0, dkdv_rows=0):
+    """Backward with the gradients' dtype (q.dtype or torch.float32) and the
+    tile sizes (query rows per dQ work-group, keys per dK/dV work-group: 64,
+    128, 256; 0 = 128) given per call: returns (dQ, dK, dV)."""
+    dq, dk, dv, _ = _backward("fa_backward_ex", q, k, v, o, dout, lse, scale, causal, key_lens,
+                              block_mask, block_size, dq, dk, dv, workspace, grad_dtype,
+                              dq_rows, dkdv_rows)
+    return dq, dk, dv
+
+
+def fa_backward_noalloc_max_rows():
+    return int(load_library().fa_backward_noalloc_max_rows())
+
+
+def fa_backward_noalloc(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
+                        block_mask=None, block_size=128, dq=None, dk=None, dv=None):
+    """fa_backward with its workspace in the library's per-device scratch (no
+    allocation by the library; B*H*N at most fa_backward_noalloc_max_rows()).
+    Calls on one device share that scratch: they must not overlap."""
+    lib = load_library()
+    B, H, N, d = _shape(q, k, v)
+    _like("dout", dout, q)
+    _like("o", o, q)
+    _like("lse", lse, q, (B, H, N), torch.float32)
+    dq, dk, dv = (torch.empty_like(q) if t is None else _like(nm, t, q)
+                  for t, nm in ((dq, "dq"), (dk, "dk"), (dv, "dv")))
+    kl = _lens(key_lens, B, q.device)
+    bm = _mask(block_mask, N, block_size, q.device)
+    _check("fa_backward_noalloc", lib.fa_backward_noalloc(
+        _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(dout), _ptr(lse), _ptr(dq), _ptr(dk), _ptr(dv),
+        B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm), int(block_size),
+        _DTYPE_CODE[q.dtype], _stream(q.device)))
+    return dq, dk, dv
+
+
 def fa_backward_dq(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
-                   block_mask=None, block_size=128, dq=None, workspace=None):
+                   block_mask=None, block_size=128, dq=None, workspace=None, rows=0):
     """First backward pass: returns (dQ, workspace); the workspace then holds
-    -D and LSE * log2(e) for fa_backward_dkdv."""
+    -D and LSE * log2(e) for fa_backward_dkdv.  rows: query rows per
+    work-group (64, 128, 256; 0 = 128)."""
     dq, _, _, ws = _backward("fa_backward_dq", q, k, v, o, dout, lse, scale, causal, key_lens,
-                             block_mask, block_size, dq, None, None, workspace)
+                             block_mask, block_size, dq, None, None, workspace, dq_rows=rows)
     return dq, ws
 
 
 def fa_backward_dkdv(q, k, v, dout, workspace, scale=None, causal=False, key_lens=None,
-                     block_mask=None, block_size=128, dk=None, dv=None):
+                     block_mask=None, block_size=128, dk=None, dv=None, rows=0):
     """Second backward pass, from the workspace fa_backward_dq filled:
-    returns (dK, dV)."""
+    returns (dK, dV).  rows: keys per work-group (64, 128, 256; 0 = 128)."""
     _, dk, dv, _ = _backward("fa_backward_dkdv", q, k, v, None, dout, None, scale, causal,
-                             key_lens, block_mask, block_size, None, dk, dv, workspace)
+                             key_lens, block_mask, block_size, None, dk, dv, workspace,
+                             dkdv_rows=rows)
     return dk, dv
 
 

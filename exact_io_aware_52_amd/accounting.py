@@ -87,6 +87,75 @@ def tiled_forward_bytes(prob, block_rows):
     return compulsory_bytes(prob, "fwd") + prob.B * prob.H * tiles * 2 * frac * n * d * s
 
 
+def _limits(prob, b):
+    """Per query row i of batch b: keys [0, limit_i) pass the causal and
+    key-length masks."""
+    n = prob.N
+    lim = np.full(n, n, dtype=np.int64)
+    if prob.causal:
+        lim = np.minimum(lim, np.arange(n, dtype=np.int64) + 1)
+    if prob.key_lens is not None:
+        lim = np.minimum(lim, max(0, min(int(prob.key_lens[b]), n)))
+    return lim
+
+
+def streamed_rows(prob, which, rows):
+    """Rows of the other side that the backward pass ``which`` streams through
+    on-chip memory, summed over its work-groups of ``rows`` rows and over every
+    head: the dQ pass ('dq', work-groups of queries) reads each key that some
+    query of the work-group keeps; the dK/dV pass ('dkdv', work-groups of keys)
+    reads each query that keeps some key of the work-group."""
+    n, bs = prob.N, prob.block_size
+    bm = None if prob.block_mask is None else np.asarray(prob.block_mask) != 0
+    total = 0
+    for b in range(prob.B):
+        lim = _limits(prob, b)
+        qblk = np.arange(n) // bs
+        for r0 in range(0, n, rows):
+            r1 = min(n, r0 + rows)
+            if which == "dq":
+                if bm is None:
+                    total += int(lim[r0:r1].max())   # the union of [0, limit_i)
+                    continue
+                # per key block, the furthest key some query of the tile keeps
+                cover = np.zeros(bm.shape[1], dtype=np.int64)
+                for qb in range(r0 // bs, (r1 - 1) // bs + 1):
+                    m = int(lim[max(r0, qb * bs):min(r1, (qb + 1) * bs)].max())
+                    cover = np.maximum(cover, np.where(bm[qb], m, 0))
+                starts = np.arange(bm.shape[1], dtype=np.int64) * bs
+                total += int(np.clip(cover - starts, 0, bs).sum())
+            else:
+                # query i keeps key j of the tile iff j < limit_i (and j's
+                # mask block is kept for i's): some key iff limit_i exceeds
+                # the first key of a kept block within the tile
+                if bm is None:
+                    total += int((lim > r0).sum())
+                    continue
+                keeps = np.zeros(n, dtype=bool)
+                for kb in range(r0 // bs, (r1 - 1) // bs + 1):
+                    keeps |= bm[qblk, kb] & (lim > max(r0, kb * bs))
+                total += int(keeps.sum())
+    return total * prob.H
+
+
+def tiled_backward_pass_bytes(prob, which, rows):
+    """HBM bytes one backward pass reads and writes when each work-group of
+    ``rows`` rows reads the other side's rows it needs once (streamed_rows):
+    the backward's form of the Theta(N^2 d^2 / M) re-read term, plus the
+    pass's own rows.  dQ pass: Q, dO, O rows and the logsumexp read, dQ, -D
+    and LSE * log2(e) written; K and V rows streamed (2 d s bytes each).  dK/dV
+    pass: K and V read, dK and dV written; Q and dO rows streamed with their
+    LSE * log2(e) and -D words (2 d s + 8 bytes each)."""
+    s = ELEM_BYTES[prob.dtype]
+    heads = prob.B * prob.H
+    n, d = prob.N, prob.d
+    if which == "dq":
+        own = heads * (4 * n * d * s + 12 * n)
+        return own + streamed_rows(prob, "dq", rows) * 2 * d * s
+    own = heads * (4 * n * d * s)
+    return own + streamed_rows(prob, "dkdv", rows) * (2 * d * s + 8)
+
+
 # ----------------------------------------------------------------------------- inference
 
 def kv_fill(prob, b):

@@ -126,7 +126,8 @@ struct SplitArgs {
 int forward_impl(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                  int N, int d, float scale, int causal, const int32_t* key_lens,
                  const uint8_t* block_mask, int block_size, bool sparse, fa_dtype dtype,
-                 hipStream_t stream, const SplitArgs& split = SplitArgs(), int block_rows = 0) {
+                 hipStream_t stream, const SplitArgs& split = SplitArgs(), int block_rows = 0,
+                 int block_keys = 0) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
@@ -135,8 +136,22 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (block_rows != 0 && block_rows != 64 && block_rows != 128 && block_rows != 256)
     return fail(FA_ERR_UNSUPPORTED,
                 "block_rows=%d (supported: 0 = automatic, 64, 128, 256)", block_rows);
-  const int rows =
-      block_rows ? block_rows : auto_fwd_rows(B, H, N, d, dtype, block_mask != nullptr);
+  if (block_keys != 0 && block_keys != 32 && block_keys != 64 && block_keys != 128)
+    return fail(FA_ERR_UNSUPPORTED,
+                "block_keys=%d (supported: 0 = the type's default, 32, 64, 128)", block_keys);
+  // Key tiles other than the type's default (64 keys for 16-bit types, 32 for
+  // float32) exist for 16-bit types with 128-row tiles.
+  const int default_keys = dtype == FA_F32 ? 32 : 64;
+  const bool other_keys = block_keys != 0 && block_keys != default_keys;
+  if (other_keys && dtype == FA_F32)
+    return fail(FA_ERR_UNSUPPORTED, "float32 forward with %d keys per tile (32 only)", block_keys);
+  if (other_keys && block_rows != 0 && block_rows != 128)
+    return fail(FA_ERR_UNSUPPORTED,
+                "%d keys per tile with %d query rows per tile (128 rows only)", block_keys,
+                block_rows);
+  const int rows = other_keys ? 128
+                   : block_rows ? block_rows
+                                : auto_fwd_rows(B, H, N, d, dtype, block_mask != nullptr);
   if (block_mask && rows > 128)
     return fail(FA_ERR_UNSUPPORTED, "block-sparse forward with %d query rows per tile (at most 128)",
                 rows);
@@ -151,6 +166,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
     return st;
   if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
   fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream, rows};
+  p.fwd_keys = other_keys ? block_keys : 0;
   const int splits = split.key_chunk > 0 ? sparse_splits(N, split.key_chunk) : 1;
   if (splits > 1) {
     const size_t need = split_workspace(B, H, N, d, splits);
@@ -236,7 +252,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
                   const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                   float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
                   int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                  hipStream_t stream, int passes, fa_dtype grad_dtype, int chunk_blocks = 0) {
+                  hipStream_t stream, int passes, fa_dtype grad_dtype, int chunk_blocks = 0,
+                  int dq_rows = 0, int dkdv_rows = 0) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
@@ -244,6 +261,21 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   if (grad_dtype != dtype && grad_dtype != FA_F32)
     return fail(FA_ERR_INVALID_ARG, "grad_dtype %d (the input dtype %d or FA_F32)",
                 (int)grad_dtype, (int)dtype);
+  // Tile sizes of the two passes: 128 rows by default; 64 and 256 for 16-bit
+  // inputs with gradients in the input type, 256 without a block mask (a
+  // work-group's rows then span two 128-token mask blocks).
+  for (int i = 0; i < 2; ++i) {
+    const int rows = i == 0 ? dq_rows : dkdv_rows;
+    const char* name = i == 0 ? "dq_rows" : "dkdv_rows";
+    if (rows != 0 && rows != 64 && rows != 128 && rows != 256)
+      return fail(FA_ERR_UNSUPPORTED, "%s=%d (supported: 0 = 128, 64, 128, 256)", name, rows);
+    if (rows == 0 || rows == 128) continue;
+    if (dtype == FA_F32 || grad_dtype != dtype)
+      return fail(FA_ERR_UNSUPPORTED, "%s=%d needs 16-bit inputs and gradients (128 only "
+                  "otherwise)", name, rows);
+    if (rows == 256 && block_mask)
+      return fail(FA_ERR_UNSUPPORTED, "%s=256 with a block mask (at most 128)", name);
+  }
   if ((st = check_block(block_mask, block_size, N, false)) != FA_OK) return st;
   if (empty) return FA_OK;
   const bool pdq = (passes & fa::kPassDq) != 0, pkv = (passes & fa::kPassDkDv) != 0;
@@ -265,6 +297,8 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream};
   p.bwd_passes = passes;
   p.grad_f32 = grad_dtype == FA_F32 && dtype != FA_F32;
+  p.bwd_dq_rows = dq_rows ? dq_rows : 128;
+  p.bwd_dkdv_rows = dkdv_rows ? dkdv_rows : 128;
   if (chunk_blocks > 0) {
     const size_t base = fa_backward_workspace_bytes(B, H, N, d);
     const size_t part = bwd_split_part_bytes(B, H, N, d, chunk_blocks);
@@ -408,10 +442,10 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
 
 int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, int d, float scale, int causal, const int32_t* key_lens,
-                  const uint8_t* block_mask, int block_size, int block_rows, fa_dtype dtype,
-                  hipStream_t stream) {
+                  const uint8_t* block_mask, int block_size, int block_rows, int block_keys,
+                  fa_dtype dtype, hipStream_t stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
-                      block_size, false, dtype, stream, SplitArgs(), block_rows);
+                      block_size, false, dtype, stream, SplitArgs(), block_rows, block_keys);
 }
 
 int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse) {
@@ -436,31 +470,31 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o, cons
 int fa_backward_ex(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                    float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
-                   int block_size, fa_dtype dtype, fa_dtype grad_dtype, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream) {
+                   int block_size, fa_dtype dtype, fa_dtype grad_dtype, int dq_rows,
+                   int dkdv_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
                        block_mask, block_size, dtype, workspace, workspace_bytes, stream,
-                       fa::kPassBoth, grad_dtype);
+                       fa::kPassBoth, grad_dtype, 0, dq_rows, dkdv_rows);
 }
 
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,
                    const float* lse, void* dq, int B, int H, int N, int d, float scale,
                    int causal, const int32_t* key_lens, const uint8_t* block_mask,
-                   int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
-                   hipStream_t stream) {
+                   int block_size, fa_dtype dtype, int rows, void* workspace,
+                   size_t workspace_bytes, hipStream_t stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, nullptr, nullptr, B, H, N, d, scale, causal,
                        key_lens, block_mask, block_size, dtype, workspace, workspace_bytes,
-                       stream, fa::kPassDq, dtype);
+                       stream, fa::kPassDq, dtype, 0, rows, 0);
 }
 
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout, void* dk,
                      void* dv, int B, int H, int N, int d, float scale, int causal,
                      const int32_t* key_lens, const uint8_t* block_mask, int block_size,
-                     fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                     fa_dtype dtype, int rows, void* workspace, size_t workspace_bytes,
                      hipStream_t stream) {
   return backward_impl(q, k, v, nullptr, dout, nullptr, nullptr, dk, dv, B, H, N, d, scale,
                        causal, key_lens, block_mask, block_size, dtype, workspace,
-                       workspace_bytes, stream, fa::kPassDkDv, dtype);
+                       workspace_bytes, stream, fa::kPassDkDv, dtype, 0, 0, rows);
 }
 
 size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,

@@ -151,8 +151,9 @@ __device__ __forceinline__ int kth_kept(const uint8_t* m, int lo, int hi, int ra
 }
 
 // ----------------------------------------------------------------------------
-// dK, dV.  Work-group: 4 waves x 32 keys; query tiles of BQ rows.
-template <typename T, int D>
+// dK, dV.  Work-group: NW waves x 32 keys (4 by default; 2 and 8 are a
+// tile-size option); query tiles of BQ rows.
+template <typename T, int D, int NW = 4>
 struct DkDvCfg {
   typedef raw_t<T> raw;
   static constexpr int BQ = (sizeof(raw) == 4 && D == 128) ? 32 : 64;
@@ -160,7 +161,7 @@ struct DkDvCfg {
   static constexpr int TILE_BYTES = BQ * D * (int)sizeof(raw);   // one of Q, dO
   static constexpr int ROWV_BYTES = 64 * 4;                      // LSE2 or D words (one DMA)
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES + 2 * ROWV_BYTES;
-  static constexpr int LPT = 2 * TILE_BYTES / 4096;              // 16-byte DMAs per wave per tile
+  static constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);       // 16-byte DMAs per wave per tile
   // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
   // accumulators: 192 VGPRs) only fits one wave per SIMD.
   static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
@@ -181,15 +182,16 @@ struct DkDvCfg {
 // GF32: store dK, dV as float32 (16-bit inputs; an option for exact
 // comparisons, compiled as separate instances so that the usual instances'
 // register allocation is untouched).
-template <typename T, int D, bool GF32 = false, bool SPLIT = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    DkDvCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
+template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
+    DkDvCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef DkDvCfg<T, D> L;
+  typedef DkDvCfg<T, D, NW> L;
   constexpr int BQ = L::BQ;
-  constexpr int BK = 128;
+  constexpr int BK = 32 * NW;  // keys of this work-group (at most one mask block)
+  static_assert(BK <= kMaskBlock || !SPLIT, "split columns come in whole mask blocks");
   constexpr int LPT = L::LPT;
 
   __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
@@ -233,7 +235,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   int t_end = j0 < kend ? nqt : t_begin;  // no visible key in this tile: nothing to do
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
-    for (int i = tid; i < p.nblk; i += 256)
+    for (int i = tid; i < p.nblk; i += 64 * NW)
       mask_col[i] = SPLIT ? p.mask_t[(size_t)(j0 / kMaskBlock) * p.nblk + i]
                           : p.block_mask[(size_t)i * p.nblk + j0 / kMaskBlock];
   }
@@ -277,7 +279,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     return t;
   };
 
-  DmaPlan<raw, BQ, D, kBoth> plan;
+  DmaPlan<raw, BQ, D, kBoth, NW> plan;
   plan.init(w, lane);
   // Q, dO rows of tile t, plus (waves 0 and 1) its LSE2 and D words.
   auto issue = [&](int t, int s) {
@@ -713,7 +715,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     constexpr int RS = RB + 16;               // padded LDS row stride
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;             // rows per store instruction
-    static_assert(4 * 32 * RS <= L::NS * L::SLOT_BYTES, "staging fits in the ring");
+    static_assert(NW * 32 * RS <= L::NS * L::SLOT_BYTES, "staging fits in the ring");
     char* const stage = ring + w * 32 * RS;
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 
 // ----------------------------------------------------------------------------
 // dQ (and D).  Work-group: 4 waves x 32 queries; key tiles of BC rows.
-template <typename T, int D>
+template <typename T, int D, int NW = 4>
 struct DqCfg {
   typedef raw_t<T> raw;
   // 64 keys per step at d = 64; 32 at d = 128 (two work-groups per CU).
@@ -753,7 +755,7 @@ struct DqCfg {
   static constexpr int NS = 4;
   static constexpr int TILE_BYTES = BC * D * (int)sizeof(raw);   // one of K, V
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;
-  static constexpr int LPT = 2 * TILE_BYTES / 4096;
+  static constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);
   static constexpr int WAVES_PER_SIMD = sizeof(raw) == 4 ? 1 : 2;
   // Score/dP operand prefetch group (k-steps; 0: read each operand just
   // before its product).  One k-step ahead at 16-bit d = 128 (dQ 3.6%
@@ -762,15 +764,18 @@ struct DqCfg {
   static constexpr int GK = (sizeof(raw) == 2 && D == 128) ? 1 : 0;
 };
 
-template <typename T, int D, bool GF32 = false, bool SPLIT = false>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
-    DqCfg<T, D>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
+// Work-group: NW waves x 32 queries (4 by default; 2 and 8 are a tile-size
+// option); key tiles of BC rows.
+template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
+    DqCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef DqCfg<T, D> L;
+  typedef DqCfg<T, D, NW> L;
   constexpr int BC = L::BC;
-  constexpr int BR = 128;
+  constexpr int BR = 32 * NW;  // queries of this work-group (at most one mask block)
+  static_assert(BR <= kMaskBlock || !SPLIT, "split rows come in whole mask blocks");
   constexpr int LPT = L::LPT;
 
   __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
@@ -804,7 +809,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
-    for (int i = tid; i < p.nblk; i += 256) mask_row[i] = bm[i];
+    for (int i = tid; i < p.nblk; i += 64 * NW) mask_row[i] = bm[i];
   }
 
   const size_t head = (size_t)bh * N * D;
@@ -872,8 +877,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq_acc[db] = zero16();
 
-  DmaPlan<raw, BC, D, kBoth> kplan;
-  DmaPlan<raw, BC, D, kRows> vplan;
+  DmaPlan<raw, BC, D, kBoth, NW> kplan;
+  DmaPlan<raw, BC, D, kRows, NW> vplan;
   kplan.init(w, lane);
   vplan.init(w, lane);
   auto issue = [&](int t, int s) {
@@ -1113,6 +1118,22 @@ __global__ __launch_bounds__(256) void fa_bwd_split_reduce_kernel(BwdParams p) {
 
 // SPLIT: the split instances, launched with one work-group per item
 // (gridDim.y = pb.split_items), each pass followed by its reduce kernel.
+// One pass with NW waves (32 NW rows) per work-group.
+template <typename T, int D, bool GF32, bool SPLIT, int NW>
+hipError_t launch_dq_pass(const BwdParams& p, const Problem& pb, unsigned items) {
+  const unsigned tiles = (unsigned)((pb.N + 32 * NW - 1) / (32 * NW));
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32, SPLIT, NW>), dim3(tiles * p.BH, items),
+                     dim3(64 * NW), 0, pb.stream, p);
+  return hipGetLastError();
+}
+template <typename T, int D, bool GF32, bool SPLIT, int NW>
+hipError_t launch_dkdv_pass(const BwdParams& p, const Problem& pb, unsigned items) {
+  const unsigned tiles = (unsigned)((pb.N + 32 * NW - 1) / (32 * NW));
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT, NW>), dim3(tiles * p.BH, items),
+                     dim3(64 * NW), 0, pb.stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int D, bool GF32 = false, bool SPLIT = false>
 hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   static_assert(!(GF32 && SPLIT), "split backward: gradients in the input type");
@@ -1148,10 +1169,17 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   }
   const unsigned items = SPLIT ? (unsigned)pb.split_items : 1u;
   hipError_t e = hipSuccess;
+  // Other tile heights than 128 rows: 16-bit inputs and gradients, unsplit
+  // (checked by the caller).
+  constexpr bool kRowsOption = sizeof(T) == 2 && !GF32 && !SPLIT;
   if (pb.bwd_passes & kPassDq) {
-    hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32, SPLIT>), dim3(tiles128 * p.BH, items),
-                       dim3(256), 0, pb.stream, p);
-    e = hipGetLastError();
+    if constexpr (kRowsOption) {
+      e = pb.bwd_dq_rows == 64    ? launch_dq_pass<T, D, false, false, 2>(p, pb, items)
+          : pb.bwd_dq_rows == 256 ? launch_dq_pass<T, D, false, false, 8>(p, pb, items)
+                                  : launch_dq_pass<T, D, false, false, 4>(p, pb, items);
+    } else {
+      e = launch_dq_pass<T, D, GF32, SPLIT, 4>(p, pb, items);
+    }
     if (e != hipSuccess) return e;
     if constexpr (SPLIT) {
       hipLaunchKernelGGL((fa_bwd_split_reduce_kernel<T, D, false>), dim3(tiles128 * p.BH),
@@ -1161,9 +1189,13 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
     }
   }
   if (pb.bwd_passes & kPassDkDv) {
-    hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT>), dim3(tiles128 * p.BH, items),
-                       dim3(256), 0, pb.stream, p);
-    e = hipGetLastError();
+    if constexpr (kRowsOption) {
+      e = pb.bwd_dkdv_rows == 64    ? launch_dkdv_pass<T, D, false, false, 2>(p, pb, items)
+          : pb.bwd_dkdv_rows == 256 ? launch_dkdv_pass<T, D, false, false, 8>(p, pb, items)
+                                    : launch_dkdv_pass<T, D, false, false, 4>(p, pb, items);
+    } else {
+      e = launch_dkdv_pass<T, D, GF32, SPLIT, 4>(p, pb, items);
+    }
     if (e != hipSuccess) return e;
     if constexpr (SPLIT) {
       hipLaunchKernelGGL((fa_bwd_split_reduce_kernel<T, D, true>), dim3(tiles128 * p.BH),

@@ -115,14 +115,19 @@ __device__ int g_stamp_wgs[kStampWgs];
 #endif
 
 // NW waves per work-group, 32 query rows each (BR = 32 NW rows per tile).
-template <typename T, int D, int NW>
+// BC: keys per K/V tile, or 0 for the default width.
+template <typename T, int D, int NW, int BC = 0>
 struct FwdCfg {
   typedef raw_t<T> raw;
   static constexpr int BR = 32 * NW;
   static constexpr bool B16 = sizeof(raw) == 2;
   // BT keys per ring slot (one DMA tile, one barrier); the math runs on
-  // 32-key sub-tiles, NSUB per slot.
-  static constexpr int BT = B16 ? 64 : 32;
+  // 32-key sub-tiles, NSUB per slot.  By default 64 keys (16-bit) or 32
+  // (fp32); the key-tile width option of the 16-bit forward also takes 32
+  // and 128 (tile-size sweeps: the width sets the step count and the ring's
+  // granularity, not the bytes each query tile reads).
+  static constexpr int BT = BC ? BC : (B16 ? 64 : 32);
+  static_assert(BT == 32 || (B16 && (BT == 64 || BT == 128)), "key tile of 32, 64 or 128 keys");
   static constexpr int NSUB = BT / 32;
   // Software pipelining across sub-tiles (a second score buffer); the 16-bit
   // instances instead keep more waves resident, which interleave matrix and
@@ -140,7 +145,11 @@ struct FwdCfg {
   // so does the one-wave d = 128 tile (inference with few queries), which
   // would spill to fit two.
   static constexpr int WAVES_PER_SIMD = B16 ? (D == 64 ? 3 : (NW == 1 ? 1 : 2)) : 1;
-  static constexpr int NS = B16 ? (D == 64 ? 3 : 2) : 4;
+  // (Other key-tile widths keep the default ring's bytes where 2 to 4 slots
+  // allow it: 4 slots of 32 keys, 2 of 128.)
+  static constexpr int RING_TARGET = D == 64 ? 3 * 2 * 64 * 64 * 2 : 2 * 2 * 64 * 128 * 2;
+  static constexpr int NS_FIT = RING_TARGET / (2 * BT * D * (int)sizeof(raw));
+  static constexpr int NS = B16 ? (NS_FIT < 2 ? 2 : (NS_FIT > 4 ? 4 : NS_FIT)) : 4;
   static constexpr int TILE_BYTES = BT * D * (int)sizeof(raw);  // one K or V tile
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES;             // K then V
   static constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);      // DMA instructions per wave per tile
@@ -164,13 +173,13 @@ __device__ __forceinline__ float sum16(const float (&e)[16]) {
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-template <typename T, int D, int NW>
-__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
-    FwdCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
+// One work-group's query tile (the body of both forward kernels below).
+template <typename T, int D, int NW, int BC>
+__device__ __forceinline__ void fwd_tile(FwdParams p) {
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef FwdCfg<T, D, NW> L;
+  typedef FwdCfg<T, D, NW, BC> L;
   constexpr int BR = L::BR;
   constexpr int BT = L::BT;
   constexpr int NSUB = L::NSUB;
@@ -702,6 +711,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   stamp(21);
 }
 
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
+    FwdCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_fwd_kernel(FwdParams p) {
+  fwd_tile<T, D, NW, 0>(p);
+}
+
+// 128-row tiles with another key-tile width (16-bit types; tile-size option).
+template <typename T, int D, int BC>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
+    FwdCfg<T, D, 4, BC>::WAVES_PER_SIMD))) void fa_fwd_keys_kernel(FwdParams p) {
+  fwd_tile<T, D, 4, BC>(p);
+}
+
 // Merge of the key-range splits of one query row (the online-softmax merge of
 // per-block states, applied across work-groups): with split results (O_s,
 // LSE_s), LSE = ln sum_s exp(LSE_s) and O = sum_s exp(LSE_s - LSE) O_s.  A row
@@ -763,9 +785,9 @@ hipError_t launch_fwd_combine(const Problem& pb, const FwdTensors& t, int splits
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW>
+template <typename T, int D, int NW, int BC = 0>
 hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
-  constexpr int BR = FwdCfg<T, D, NW>::BR;
+  constexpr int BR = FwdCfg<T, D, NW, BC>::BR;
   FwdParams p;
   p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.lse = t.lse;
   p.key_lens = pb.key_lens;
@@ -792,8 +814,14 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.Tq = pb.Tq;
   p.Tk = pb.Tk;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
-  hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid, splits), dim3(64 * NW), 0, pb.stream,
-                     p);
+  if constexpr (BC != 0) {
+    static_assert(NW == 4, "other key-tile widths come with 128-row tiles");
+    hipLaunchKernelGGL((fa_fwd_keys_kernel<T, D, BC>), dim3(grid, splits), dim3(256), 0,
+                       pb.stream, p);
+  } else {
+    hipLaunchKernelGGL((fa_fwd_kernel<T, D, NW>), dim3(grid, splits), dim3(64 * NW), 0,
+                       pb.stream, p);
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || splits == 1) return e;
   return launch_fwd_combine<T, D>(pb, t, splits);
@@ -803,6 +831,11 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
 // 32 (one wave, 16-bit types) for inference with few queries.
 template <typename T, int D>
 hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
+  if constexpr (sizeof(T) == 2) {
+    // 128-row tiles of 32 or 128 keys (checked by the caller)
+    if (pb.fwd_keys == 32) return launch_fwd_t<T, D, 4, 32>(pb, t);
+    if (pb.fwd_keys == 128) return launch_fwd_t<T, D, 4, 128>(pb, t);
+  }
   switch (pb.fwd_rows) {
     case 32:
       if constexpr (sizeof(T) == 2) return launch_fwd_t<T, D, 1>(pb, t);

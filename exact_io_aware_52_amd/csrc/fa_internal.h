@@ -22,6 +22,7 @@ struct Problem {
   int dtype;                  // fa_dtype
   hipStream_t stream;
   int fwd_rows = 128;         // forward: query rows per work-group (32, 64, 128, 256)
+  int fwd_keys = 0;           // forward: keys per K/V tile (0: the type's default)
   // Forward of N queries against nk keys (inference): nk < 0 means nk = N.
   int nk = -1;
   int causal_br = 0;          // causal aligned bottom-right to the visible key count
@@ -36,6 +37,8 @@ struct Problem {
   int Tq = 0, Tk = 0;
   int bwd_passes = kPassBoth;  // backward: which passes to launch (BwdPass bits)
   int grad_f32 = 0;            // backward, 16-bit inputs: float32 dQ, dK, dV
+  int bwd_dq_rows = 128;       // backward: query rows per dQ work-group (64, 128, 256)
+  int bwd_dkdv_rows = 128;     // backward: keys per dK/dV work-group (64, 128, 256)
   // Block-sparse backward split by kept mask blocks (chunk_blocks > 0): items
   // of chunk_blocks kept blocks per mask row (dQ) or column (dK, dV), at most
   // split_items per tile; fp32 partials [split_items][B*H][N][d] each.

@@ -188,22 +188,35 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
                 hipStream_t stream);
 
 /*
- * fa_backward with the gradients' storage type chosen: grad_dtype is the
- * input dtype (then this is fa_backward) or FA_F32, which writes dq, dk, dv
- * as float32 [B,H,N,d] (4-byte elements, 16-byte aligned).  The computation
- * is the same; only the final rounding to a 16-bit type is left out, so the
- * 16-bit results of fa_backward are exactly the round-to-nearest-even of
- * these.  Meant for callers that accumulate gradients in float32 and for
- * measuring the computation's error apart from the output rounding (the
- * output rounding of a bf16 value of magnitude 4 to 8 is already 2^-6).
- * Any other grad_dtype is FA_ERR_INVALID_ARG.
+ * fa_backward with the gradients' storage type and the tile sizes chosen
+ * per call.
+ *   grad_dtype  the input dtype (then this is fa_backward) or FA_F32, which
+ *               writes dq, dk, dv as float32 [B,H,N,d] (4-byte elements,
+ *               16-byte aligned).  The computation is the same; only the
+ *               final rounding to a 16-bit type is left out, so the 16-bit
+ *               results of fa_backward are exactly the round-to-nearest-even
+ *               of these.  Meant for callers that accumulate gradients in
+ *               float32 and for measuring the computation's error apart from
+ *               the output rounding (the output rounding of a bf16 value of
+ *               magnitude 4 to 8 is already 2^-6).  Any other grad_dtype is
+ *               FA_ERR_INVALID_ARG.
+ *   dq_rows     query rows per work-group of the dQ pass, and
+ *   dkdv_rows   keys per work-group of the dK/dV pass: 0 (= 128), 64, 128 or
+ *               256 (review page, claims C2 and C3, applied to the backward:
+ *               each work-group streams the other side's tiles through
+ *               on-chip memory once, so those re-reads fall as its rows
+ *               grow).  64 and 256 take 16-bit inputs with grad_dtype = dtype,
+ *               256 no block mask; other combinations and values are
+ *               FA_ERR_UNSUPPORTED.  Results agree to rounding for every
+ *               value (the accumulation order over tiles is unchanged, so
+ *               they are in fact bitwise equal).
  */
 int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    int B, int H, int N, int d, float scale, int causal,
                    const int32_t* key_lens, const uint8_t* block_mask, int block_size,
-                   fa_dtype dtype, fa_dtype grad_dtype, void* workspace,
-                   size_t workspace_bytes, hipStream_t stream);
+                   fa_dtype dtype, fa_dtype grad_dtype, int dq_rows, int dkdv_rows,
+                   void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
  * The two passes of fa_backward, for callers that schedule them separately
@@ -216,18 +229,21 @@ int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
  *                     that a preceding fa_backward_dq with the same q, k, v,
  *                     o, dout, lse, sizes, scale and masks filled (unchanged
  *                     since).  It may be called again on that workspace.
- * Arguments, validation and errors as fa_backward.
+ *   rows              the pass's tile height: dq_rows or dkdv_rows of
+ *                     fa_backward_ex (0 = 128), under the same rules; the
+ *                     workspace does not depend on it.
+ * Other arguments, validation and errors as fa_backward.
  */
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq,
                    int B, int H, int N, int d, float scale, int causal,
                    const int32_t* key_lens, const uint8_t* block_mask, int block_size,
-                   fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                   fa_dtype dtype, int rows, void* workspace, size_t workspace_bytes,
                    hipStream_t stream);
 int fa_backward_dkdv(const void* q, const void* k, const void* v, const void* dout,
                      void* dk, void* dv, int B, int H, int N, int d, float scale,
                      int causal, const int32_t* key_lens, const uint8_t* block_mask,
-                     int block_size, fa_dtype dtype, void* workspace,
+                     int block_size, fa_dtype dtype, int rows, void* workspace,
                      size_t workspace_bytes, hipStream_t stream);
 
 /*
@@ -268,10 +284,11 @@ size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,
                                                      int chunk_blocks);
 
 /*
- * Forward with the tile height chosen per call (review page, claims C2 and
+ * Forward with the tile sizes chosen per call (review page, claims C2 and
  * C3: tiling reduces HBM reads and writes, and the IO cost depends on the
  * on-chip memory size; K and V are read once per query tile, so that traffic
- * falls as the tile height B_r grows).  As fa_forward, plus:
+ * falls as the tile height B_r grows, whatever the key-tile width B_c).  As
+ * fa_forward, plus:
  *   block_mask, block_size  as fa_forward_blocksparse, or block_mask NULL
  *                           (dense; block_size is then ignored);
  *   block_rows  query rows per work-group: 64, 128 or 256, or 0 to let the
@@ -281,14 +298,19 @@ size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,
  *               float32 forward at d = 128 (eight float32 waves would need
  *               more registers than a compute unit holds); any other value
  *               is FA_ERR_UNSUPPORTED.
- * A tuning and measurement option: results agree to rounding for every
+ *   block_keys  keys per K/V tile streamed through on-chip memory: 0 for the
+ *               default (64 for 16-bit types, 32 for float32), or 32, 64,
+ *               128.  Widths other than the default take 16-bit types and
+ *               128 query rows per tile (block_rows 0 or 128; 0 then means
+ *               128); other combinations and values are FA_ERR_UNSUPPORTED.
+ * Tuning and measurement options: results agree to rounding for every
  * value.  fa_forward and fa_forward_blocksparse are this call with
- * block_rows = 0.
+ * block_rows = 0 and block_keys = 0.
  */
 int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int N, int d, float scale, int causal,
                   const int32_t* key_lens, const uint8_t* block_mask, int block_size,
-                  int block_rows, fa_dtype dtype, hipStream_t stream);
+                  int block_rows, int block_keys, fa_dtype dtype, hipStream_t stream);
 
 /*
  * Query rows per work-group that a forward of these sizes uses when

@@ -85,15 +85,31 @@ int main() {
   CHECK(fa_forward(a, a, a, a, f, 2, 8, 4096, 128, 0.1f, 1, nullptr, FA_BF16, nullptr) == FA_OK);
   CHECK(g_last.fwd_rows == 128);
   for (int rows : {64, 128, 256}) {
-    CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, rows,
+    CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, rows, 0,
                         FA_F16, nullptr) == FA_OK);
-    CHECK(g_last.fwd_rows == rows);
+    CHECK(g_last.fwd_rows == rows && g_last.fwd_keys == 0);
   }
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 32, FA_F16,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 32, 0, FA_F16,
                       nullptr) == FA_ERR_UNSUPPORTED);
+  // key-tile widths: 32 and 128 with 128-row tiles (0 rows means 128); 64,
+  // the 16-bit default, is no option at all
+  for (int keys : {32, 64, 128}) {
+    CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 16384, 128, 0.1f, 1, nullptr, nullptr, 128, 0, keys,
+                        FA_BF16, nullptr) == FA_OK);
+    CHECK(g_last.fwd_keys == (keys == 64 ? 0 : keys) && g_last.fwd_rows == (keys == 64 ? 256 : 128));
+  }
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 256, 128,
+                      FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 0, 128,
+                      FA_F32, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 0, 256,
+                      FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
   const uint8_t* bm = static_cast<const uint8_t*>(a);
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 256, FA_F16,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 256, 0, FA_F16,
                       nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 0, 32, FA_F16,
+                      nullptr) == FA_OK);
+  CHECK(g_last.fwd_keys == 32 && g_last.fwd_rows == 128 && g_last.block_mask == bm);
   CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 300, 64, 0.1f, 0, nullptr, nullptr, 128,
                                FA_BF16, nullptr) == FA_ERR_INVALID_ARG);  // mask required
   CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 300, 64, 0.1f, 0, nullptr, bm, 64, FA_BF16,
@@ -146,29 +162,67 @@ int main() {
                     FA_BF16, a, bw, nullptr) == FA_OK);
   CHECK(g_last.bwd_passes == fa::kPassBoth);
   CHECK(fa_backward_dq(a, a, a, a, a, f, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, a, bw, nullptr) == FA_OK);
-  CHECK(g_last.bwd_passes == fa::kPassDq);
+                       FA_BF16, 0, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_passes == fa::kPassDq && g_last.bwd_dq_rows == 128);
   CHECK(fa_backward_dkdv(a, a, a, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                         FA_BF16, a, bw, nullptr) == FA_OK);
-  CHECK(g_last.bwd_passes == fa::kPassDkDv);
+                         FA_BF16, 0, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_passes == fa::kPassDkDv && g_last.bwd_dkdv_rows == 128);
+  CHECK(fa_backward_dq(a, a, a, a, a, f, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, 256, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_dq_rows == 256 && g_last.bwd_dkdv_rows == 128);
+  CHECK(fa_backward_dkdv(a, a, a, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                         FA_BF16, 64, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_dq_rows == 128 && g_last.bwd_dkdv_rows == 64);
+  CHECK(fa_backward_dkdv(a, a, a, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                         FA_BF16, 32, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
                     FA_BF16, a, bw - 1, nullptr) == FA_ERR_WORKSPACE);
   CHECK(fa_backward(a, a, a, a, a, f, nullptr, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr,
                     128, FA_BF16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
   CHECK(fa_backward_dkdv(a, a, a, a, nullptr, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                         FA_BF16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+                         FA_BF16, 0, a, bw, nullptr) == FA_ERR_INVALID_ARG);
   // ---- float32 gradients for 16-bit inputs
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_F32, a, bw, nullptr) == FA_OK);
+                       FA_BF16, FA_F32, 0, 0, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 1 && g_last.bwd_passes == fa::kPassBoth);
+  CHECK(g_last.bwd_dq_rows == 128 && g_last.bwd_dkdv_rows == 128);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_BF16, a, bw, nullptr) == FA_OK);
+                       FA_BF16, FA_BF16, 0, 0, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 0);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_F16, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+                       FA_BF16, FA_F16, 0, 0, a, bw, nullptr) == FA_ERR_INVALID_ARG);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_F32, FA_F32, a, bw, nullptr) == FA_OK);
+                       FA_F32, FA_F32, 0, 0, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 0);  // float32 inputs: float32 gradients already
+  // ---- backward tile sizes: 64, 128, 256 rows per work-group of each pass
+  for (int dqr : {0, 64, 128, 256})
+    for (int kvr : {0, 64, 128, 256}) {
+      CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr,
+                           128, FA_F16, FA_F16, dqr, kvr, a, bw, nullptr) == FA_OK);
+      CHECK(g_last.bwd_dq_rows == (dqr ? dqr : 128) && g_last.bwd_dkdv_rows == (kvr ? kvr : 128));
+    }
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_BF16, 32, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_BF16, 0, 512, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_F32, 64, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_F32, FA_F32, 0, 256, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_F32, FA_F32, 128, 128, a, bw, nullptr) == FA_OK);
+  {
+    const uint8_t* bmk = static_cast<const uint8_t*>(a);
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
+                         FA_BF16, FA_BF16, 64, 64, a, bw, nullptr) == FA_OK);
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
+                         FA_BF16, FA_BF16, 256, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
+                         FA_BF16, FA_BF16, 0, 256, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  }
+  // (the sizes are checked before anything else is read, empty problems too)
+  CHECK(fa_backward_ex(nullptr, a, a, a, a, f, a, a, a, 0, 3, 100, 64, 0.1f, 1, nullptr, nullptr,
+                       128, FA_BF16, FA_BF16, 96, 0, nullptr, 0, nullptr) == FA_ERR_UNSUPPORTED);
   // ---- allocation-free backward: the library's device scratch, size-limited
   const size_t max_rows = fa_backward_noalloc_max_rows();
   CHECK(max_rows == (size_t(16) << 20) / 8);

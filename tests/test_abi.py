@@ -137,6 +137,41 @@ def test_backward_validation(lib):
     assert bwd(lib, d=80) == _binding.FA_ERR_UNSUPPORTED
 
 
+def bwd_ex(lib, dq_rows, dkdv_rows, dtype=1, gdtype=None, bm=None, dq=FAKE, B=2):
+    return lib.fa_backward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, B, 3, 100, 64,
+                              0.1, 1, None, bm, 128, dtype, dtype if gdtype is None else gdtype,
+                              dq_rows, dkdv_rows, FAKE, 1 << 30, None)
+
+
+def test_backward_ex_tile_rows_validation(lib):
+    for bad in (32, 96, 512, -128, 1):
+        assert bwd_ex(lib, bad, 0) == _binding.FA_ERR_UNSUPPORTED, bad
+        assert "dq_rows" in detail(lib)
+        assert bwd_ex(lib, 0, bad) == _binding.FA_ERR_UNSUPPORTED, bad
+        assert "dkdv_rows" in detail(lib)
+    # every height passes for 16-bit inputs and gradients (the call then
+    # fails on the null dq, before any launch)
+    for dtype in (1, 2):
+        for a in (0, 64, 128, 256):
+            for b in (0, 64, 128, 256):
+                assert bwd_ex(lib, a, b, dtype=dtype, dq=None) == _binding.FA_ERR_INVALID_ARG
+                assert "dq is NULL" in detail(lib)
+    # 64 and 256 rows: not for float32 inputs or float32 gradients
+    for a, b in ((64, 0), (0, 256)):
+        assert bwd_ex(lib, a, b, dtype=0) == _binding.FA_ERR_UNSUPPORTED
+        assert bwd_ex(lib, a, b, dtype=2, gdtype=0) == _binding.FA_ERR_UNSUPPORTED
+        assert "16-bit" in detail(lib)
+    assert bwd_ex(lib, 128, 0, dtype=0, dq=None) == _binding.FA_ERR_INVALID_ARG
+    # 256 rows span two 128-token mask blocks: not with a block mask
+    assert bwd_ex(lib, 256, 0, bm=FAKE) == _binding.FA_ERR_UNSUPPORTED
+    assert bwd_ex(lib, 0, 256, bm=FAKE) == _binding.FA_ERR_UNSUPPORTED
+    assert "block mask" in detail(lib)
+    assert bwd_ex(lib, 64, 64, bm=FAKE, dq=None) == _binding.FA_ERR_INVALID_ARG
+    # empty problem: the sizes are still checked, nothing else is
+    assert bwd_ex(lib, 96, 0, B=0) == _binding.FA_ERR_UNSUPPORTED
+    assert bwd_ex(lib, 256, 64, B=0, dq=None) == _binding.FA_OK
+
+
 def test_backward_blocksparse_split_validation(lib):
     f = lib.fa_backward_blocksparse_split
 
@@ -181,11 +216,11 @@ def test_backward_pass_validation(lib):
 
     def dq_pass(o=FAKE, lse=FAKE, dq=FAKE, ws=FAKE, ws_bytes=need):
         return lib.fa_backward_dq(FAKE, FAKE, FAKE, o, FAKE, lse, dq, 2, 3, 100, 64, 0.1, 1,
-                                  None, None, 128, 2, ws, ws_bytes, None)
+                                  None, None, 128, 2, 0, ws, ws_bytes, None)
 
     def kv_pass(dk=FAKE, dv=FAKE, ws=FAKE, ws_bytes=need, q=FAKE):
         return lib.fa_backward_dkdv(q, FAKE, FAKE, FAKE, dk, dv, 2, 3, 100, 64, 0.1, 1, None,
-                                    None, 128, 2, ws, ws_bytes, None)
+                                    None, 128, 2, 0, ws, ws_bytes, None)
 
     for bad in (dict(o=None), dict(lse=None), dict(dq=None), dict(dq=BAD_ALIGN), dict(ws=None),
                 dict(ws_bytes=need - 1)):
@@ -255,9 +290,9 @@ def test_forward_varlen_validation(lib):
     assert varlen(lib, q=None, cq=None, mq=0) == _binding.FA_OK
 
 
-def fwd_ex(lib, rows, bm=None, N=256, q=FAKE):
-    return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, N, 64, 0.1, 0, None, bm, 128, rows,
-                             2, None)
+def fwd_ex(lib, rows, bm=None, N=256, q=FAKE, keys=0, dtype=2, d=64):
+    return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, N, d, 0.1, 0, None, bm, 128, rows,
+                             keys, dtype, None)
 
 
 def test_forward_ex_block_rows_validation(lib):
@@ -281,10 +316,40 @@ def test_forward_ex_block_rows_validation(lib):
 
     def f32(rows, q=FAKE):
         return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 128, 0.1, 0, None, None,
-                                 128, rows, 0, None)
+                                 128, rows, 0, 0, None)
     assert f32(256) == _binding.FA_ERR_UNSUPPORTED
     assert "float32" in detail(lib)
     assert f32(128, q=None) == _binding.FA_ERR_INVALID_ARG
+
+
+def test_forward_ex_block_keys_validation(lib):
+    for bad in (16, 48, 96, 256, -64, 1):
+        assert fwd_ex(lib, 0, keys=bad) == _binding.FA_ERR_UNSUPPORTED, bad
+        assert "block_keys" in detail(lib)
+    # every width passes with 128-row tiles (or 0 rows), 16-bit types, dense
+    # or block-sparse; the call then fails on the null q, before any launch
+    for dtype in (1, 2):
+        for d in (64, 128):
+            for keys in (0, 32, 64, 128):
+                for rows in (0, 128):
+                    assert fwd_ex(lib, rows, keys=keys, dtype=dtype, d=d, q=None) == \
+                        _binding.FA_ERR_INVALID_ARG, (dtype, d, keys, rows)
+                    assert "q is NULL" in detail(lib)
+            assert fwd_ex(lib, 128, bm=FAKE, keys=128, dtype=dtype, d=d, q=None) == \
+                _binding.FA_ERR_INVALID_ARG
+    # other widths come with 128-row tiles only
+    for rows in (64, 256):
+        assert fwd_ex(lib, rows, keys=32) == _binding.FA_ERR_UNSUPPORTED
+        assert "128 rows only" in detail(lib)
+        assert fwd_ex(lib, rows, keys=64, q=None) == _binding.FA_ERR_INVALID_ARG  # the default
+    # float32 keeps its 32-key tiles
+    for keys in (64, 128):
+        assert fwd_ex(lib, 0, keys=keys, dtype=0) == _binding.FA_ERR_UNSUPPORTED
+        assert "float32" in detail(lib)
+    assert fwd_ex(lib, 0, keys=32, dtype=0, q=None) == _binding.FA_ERR_INVALID_ARG
+    # empty problem: the widths are still checked first
+    assert fwd_ex(lib, 0, keys=96, N=0, q=None) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, 0, keys=128, N=0, q=None) == _binding.FA_OK
 
 
 def test_forward_block_rows_automatic(lib):

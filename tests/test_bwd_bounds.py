@@ -1,7 +1,8 @@
 """Host replay of the dK/dV pass's staging indices (fa_bwd_impl.h,
 fa_bwd_dkdv_kernel): for every key tile of a head, the rows each copy into
 the LDS ring touches must lie inside the head.  The pass streams query tiles
-of BQ rows (64; 32 for fp32 at d = 128) past 128 resident keys.  Its dense
+of BQ rows (64; 32 for fp32 at d = 128) past BK resident keys (128; 64 and
+256 with the tile-height option of 16-bit inputs).  Its dense
 interior copies tile t + 2 whole, without a row check, and each of two waves
 fetches 64 LSE or D words for it; the boundary path copies any tile with
 per-row checks.  The replay mirrors the kernel's loop bounds, so a change to
@@ -11,10 +12,8 @@ import itertools
 
 import pytest
 
-BK = 128
 
-
-def dkdv_rows(N, BQ, causal, kend):
+def dkdv_rows(N, BQ, causal, kend, BK=128):
     """Rows of Q/dO read by unchecked copies and rows of the LSE/D vectors
     read by the 64-lane word copies, over every key tile of one head."""
     nqt = (N + BQ - 1) // BQ
@@ -39,15 +38,19 @@ def dkdv_rows(N, BQ, causal, kend):
     return whole_tile_rows, word_rows
 
 
-@pytest.mark.parametrize("BQ,causal", list(itertools.product((32, 64), (False, True))))
-def test_dkdv_copies_stay_inside_the_head(BQ, causal):
+CASES = ([(BQ, causal, 128) for BQ, causal in itertools.product((32, 64), (False, True))] +
+         [(64, causal, BK) for causal, BK in itertools.product((False, True), (64, 256))])
+
+
+@pytest.mark.parametrize("BQ,causal,BK", CASES)
+def test_dkdv_copies_stay_inside_the_head(BQ, causal, BK):
     sizes = sorted({1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 300, 384, 511,
-                    512, 1000, 1024, 2048 + 32, 4096})
+                    512, 513, 1000, 1024, 2048 + 32, 4096})
     for N in sizes:
         for kend in sorted({N, max(N - 1, 0), N // 2, 1, 0}):
-            rows, words = dkdv_rows(N, BQ, causal, kend)
-            assert all(0 <= r < N for r in rows), (N, BQ, causal, kend, max(rows))
-            assert all(0 <= r < N for r in words), (N, BQ, causal, kend)
+            rows, words = dkdv_rows(N, BQ, causal, kend, BK)
+            assert all(0 <= r < N for r in rows), (N, BQ, causal, kend, BK, max(rows))
+            assert all(0 <= r < N for r in words), (N, BQ, causal, kend, BK)
 
 
 def test_interior_runs_at_the_sizes_the_replay_checks():
@@ -56,3 +59,6 @@ def test_interior_runs_at_the_sizes_the_replay_checks():
     assert rows and max(rows) == 4095
     rows, _ = dkdv_rows(1024, 64, True, 1024)
     assert rows and max(rows) == 1023
+    for BK in (64, 256):
+        rows, _ = dkdv_rows(1024, 64, True, 1024, BK)
+        assert rows and max(rows) == 1023

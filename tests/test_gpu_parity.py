@@ -26,7 +26,8 @@ import torch
 
 import oracle
 from exact_io_aware_52_amd import (fa_backward, fa_forward, fa_forward_blocksparse,
-                                   fa_forward_blocksparse_split, fa_forward_ex, inputs)
+                                   fa_forward_blocksparse_split, fa_forward_ex, inputs,
+                                   fa_backward_ex, fa_backward_dq, fa_backward_dkdv)
 
 pytestmark = pytest.mark.gpu
 
@@ -48,7 +49,7 @@ def nan_like(t):
     return torch.full_like(t, float("nan"))
 
 
-def run_gpu(prob, backward=True, block_rows=None):
+def run_gpu(prob, backward=True, block_rows=None, block_keys=0):
     """Forward (and backward) through the C ABI into NaN-filled outputs."""
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
@@ -56,8 +57,9 @@ def run_gpu(prob, backward=True, block_rows=None):
     kw = dict(scale=float(prob.scale), causal=prob.causal, key_lens=kl)
     o = nan_like(q)
     lse = torch.full((prob.B, prob.H, prob.N), float("nan"), dtype=torch.float32, device="cuda")
-    if block_rows is not None:
-        fa_forward_ex(q, k, v, bm, prob.block_size, block_rows=block_rows, o=o, lse=lse, **kw)
+    if block_rows is not None or block_keys:
+        fa_forward_ex(q, k, v, bm, prob.block_size, block_rows=block_rows or 0,
+                      block_keys=block_keys, o=o, lse=lse, **kw)
     elif bm is not None:
         fa_forward_blocksparse(q, k, v, bm, prob.block_size, o=o, lse=lse, **kw)
     else:
@@ -326,6 +328,101 @@ def test_forward_block_rows(case):
     check_all_heads(prob, gpu, f"{rows} rows")
     compare(gpu, run_oracle(prob), TOL[dtype], label=f"{rows} rows {case[1:]}",
             magnitude_scaled=klr is not None and klr[0] < 4)
+
+
+KEY_CASES = [
+    # keys per K/V tile, B, H, N, d, dtype, causal, key_len_range, block_keep_p
+    (32, 1, 2, 1000, 64, "bf16", True, None, None),
+    (32, 2, 1, 777, 128, "fp16", False, (1, 777), None),
+    (32, 1, 2, 1024, 64, "fp16", False, None, 0.5),
+    (32, 1, 1, 640, 128, "bf16", True, None, None),
+    (128, 1, 2, 1000, 64, "bf16", True, None, None),
+    (128, 2, 1, 777, 128, "fp16", False, (1, 777), None),
+    (128, 1, 2, 1100, 64, "bf16", False, None, 0.5),
+    (128, 1, 1, 640, 128, "bf16", True, None, None),
+    (128, 1, 2, 300, 64, "bf16", False, (100, 300), None),
+]
+
+
+@pytest.mark.parametrize("case", KEY_CASES, ids=lambda c: "keys{}_N{}d{}_{}".format(c[0], c[3], c[4], c[5]))
+def test_forward_block_keys(case):
+    # K/V tiles of 32 and 128 keys (the key-tile width option; 128-row query
+    # tiles) against the oracle on every head: causal diagonals inside and
+    # across tiles, ragged last tiles, key lengths down to 1, block masks
+    keys, B, H, N, d, dtype, causal, klr, bkp = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=131 + keys + N, causal=causal,
+                               key_len_range=klr, block_keep_p=bkp)
+    gpu = run_gpu(prob, backward=False, block_keys=keys)
+    check_all_heads(prob, gpu, f"{keys} keys")
+    compare(gpu, run_oracle(prob, backward=False), TOL[dtype], label=f"{keys} keys {case[1:]}",
+            magnitude_scaled=klr is not None and klr[0] < 4)
+
+
+@pytest.mark.parametrize("boost", [1.5, 6.0])
+@pytest.mark.parametrize("keys", [32, 128])
+def test_forward_block_keys_far_keys(keys, boost):
+    # The unchecked sweep and its fall-back with 32- and 128-key tiles (the
+    # fixed reference still comes from each row's first 32 keys).
+    prob = inputs.make_problem(1, 2, 700, 64, "bf16", seed=653 + keys, causal=True, scale=1.0)
+    prob.k[:, :, 300:304] *= boost
+    prob.k = inputs.round_to_dtype(prob.k, "bf16")
+    gpu = run_gpu(prob, backward=False, block_keys=keys)
+    label = f"far keys x{boost} {keys} keys"
+    check_all_heads(prob, gpu, label)
+    compare(gpu, run_oracle(prob, backward=False), TOL["bf16"], label=label, magnitude_scaled=True)
+
+
+BWD_ROW_CASES = [
+    # dQ query rows, dK/dV keys per work-group, B, H, N, d, dtype, causal, key_len_range,
+    # block_keep_p
+    (64, 64, 1, 2, 1000, 64, "bf16", True, None, None),
+    (256, 256, 2, 2, 777, 64, "bf16", True, None, None),
+    (256, 64, 1, 3, 1100, 128, "fp16", False, (1, 1100), None),
+    (64, 256, 1, 2, 1024, 128, "bf16", True, None, None),
+    (64, 64, 1, 2, 1024, 64, "fp16", False, None, 0.5),
+    (64, 64, 1, 1, 900, 128, "bf16", True, (300, 900), 0.5),
+    (256, 256, 2, 4, 520, 128, "bf16", False, (100, 520), None),
+]
+
+
+@pytest.mark.parametrize("case", BWD_ROW_CASES,
+                         ids=lambda c: "dq{}_kv{}_N{}d{}_{}".format(c[0], c[1], c[4], c[5], c[6]))
+def test_backward_tile_rows(case):
+    # dQ work-groups of 64 or 256 query rows and dK/dV work-groups of 64 or
+    # 256 keys (the backward's tile-height option): each wave still owns 32
+    # rows and sweeps the same tiles in the same order, so the gradients must
+    # equal those of the default 128-row work-groups bit for bit, on every
+    # head; the default ones are compared with the oracle.
+    dqr, kvr, B, H, N, d, dtype, causal, klr, bkp = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=171 + dqr + kvr + N, causal=causal,
+                               key_len_range=klr, block_keep_p=bkp)
+    gpu = run_gpu(prob)
+    compare(gpu, run_oracle(prob), TOL[dtype], label=f"bwd rows default {case[2:]}",
+            magnitude_scaled=klr is not None and klr[0] < 4)
+    q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
+    kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
+    bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).cuda()
+    o = torch.from_numpy(gpu["o"]).to(q.dtype).cuda()
+    lse = torch.from_numpy(gpu["lse"]).float().cuda()
+    kw = dict(scale=float(prob.scale), causal=prob.causal, key_lens=kl, block_mask=bm,
+              block_size=prob.block_size)
+    grads = [nan_like(q) for _ in range(3)]
+    fa_backward_ex(q, k, v, o, do, lse, dq=grads[0], dk=grads[1], dv=grads[2], dq_rows=dqr,
+                   dkdv_rows=kvr, **kw)
+    # the separate passes with the same heights
+    sep = [nan_like(q) for _ in range(3)]
+    _, ws = fa_backward_dq(q, k, v, o, do, lse, dq=sep[0], rows=dqr, **kw)
+    fa_backward_dkdv(q, k, v, do, ws, dk=sep[1], dv=sep[2], rows=kvr, **kw)
+    torch.cuda.synchronize()
+    for n, g, g2 in zip(("dq", "dk", "dv"), grads, sep):
+        want = gpu[n + "_16"]
+        for label, t in (("fa_backward_ex", g), ("separate passes", g2)):
+            got = t.double().cpu().numpy()
+            assert not np.isnan(got).any(), f"{label} {n}: elements never written"
+            assert np.array_equal(got, want), (
+                f"{label} {n} rows {dqr}/{kvr}: {int((got != want).sum())} elements differ "
+                f"from the 128-row backward")
+    log(f"[bwd rows] {case}: gradients equal to the 128-row backward bit for bit")
 
 
 @pytest.mark.parametrize("boost", [1.5, 6.0])

@@ -24,7 +24,7 @@ def ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def run_lib(lib, prob, block_rows=0):
+def run_lib(lib, prob, block_rows=0, block_keys=0, bwd_rows=0):
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
     bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).cuda()
@@ -35,34 +35,40 @@ def run_lib(lib, prob, block_rows=0):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     common = (prob.B, prob.H, prob.N, prob.d, float(prob.scale), int(prob.causal), ptr(kl))
     st = lib.fa_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), *common, ptr(bm),
-                           prob.block_size, block_rows, CODE[prob.dtype], stream)
+                           prob.block_size, block_rows, block_keys, CODE[prob.dtype], stream)
     assert st == 0, lib.fa_last_error_detail()
-    st = lib.fa_backward(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq), ptr(dk),
-                         ptr(dv), *common, ptr(bm), prob.block_size, CODE[prob.dtype], ptr(ws),
-                         need, stream)
+    st = lib.fa_backward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq), ptr(dk),
+                            ptr(dv), *common, ptr(bm), prob.block_size, CODE[prob.dtype],
+                            CODE[prob.dtype], bwd_rows, bwd_rows, ptr(ws), need, stream)
     assert st == 0, lib.fa_last_error_detail()
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}
 
 
 CASES = [
-    ("gpt2_small", None, 0),
-    ("block_sparse", None, 0),
-    ("small", dict(B=2, H=4, N=600, d=128, dtype="bf16", seed=31, causal=True), 256),
-    ("small", dict(B=2, H=3, N=300, d=64, dtype="fp16", seed=32, key_len_range=(1, 300)), 64),
-    ("small", dict(B=1, H=2, N=333, d=128, dtype="fp32", seed=33, block_keep_p=0.5), 0),
-    ("small", dict(B=1, H=2, N=257, d=64, dtype="fp32", seed=34, causal=True), 0),
+    # workload or make_problem arguments, forward query rows and keys per tile, backward
+    # rows per work-group of both passes
+    ("gpt2_small", None, 0, 0, 0),
+    ("block_sparse", None, 0, 0, 0),
+    ("small", dict(B=2, H=4, N=600, d=128, dtype="bf16", seed=31, causal=True), 256, 0, 256),
+    ("small", dict(B=2, H=3, N=300, d=64, dtype="fp16", seed=32, key_len_range=(1, 300)), 64, 0,
+     64),
+    ("small", dict(B=1, H=2, N=333, d=128, dtype="fp32", seed=33, block_keep_p=0.5), 0, 0, 0),
+    ("small", dict(B=1, H=2, N=257, d=64, dtype="fp32", seed=34, causal=True), 0, 0, 0),
+    ("small", dict(B=2, H=4, N=1000, d=64, dtype="bf16", seed=35, causal=True), 128, 32, 256),
+    ("small", dict(B=1, H=4, N=1100, d=128, dtype="fp16", seed=36, block_keep_p=0.5), 128, 128,
+     64),
 ]
 
 
 @pytest.mark.parametrize("case", CASES, ids=lambda c: c[0] if c[1] is None else
-                         "N{N}d{d}_{dtype}".format(**c[1]))
+                         "N{N}d{d}_{dtype}_keys{k}_bwd{b}".format(k=c[3], b=c[4], **c[1]))
 def test_serialized_stages_bitwise(case):
-    name, kw, rows = case
+    name, kw, rows, keys, brows = case
     prob = inputs.workload(name) if kw is None else inputs.make_problem(**kw)
-    log(f"[race] {name} {kw} rows={rows}")
-    main = run_lib(_binding.load_library(), prob, rows)
-    serial = run_lib(_binding.open_library(build_lib.SERIAL_LIB), prob, rows)
+    log(f"[race] {name} {kw} rows={rows} keys={keys} bwd rows={brows}")
+    main = run_lib(_binding.load_library(), prob, rows, keys, brows)
+    serial = run_lib(_binding.open_library(build_lib.SERIAL_LIB), prob, rows, keys, brows)
     for n in main:
         a, b = main[n], serial[n]
         assert not torch.isnan(a).any(), n
@@ -83,7 +89,7 @@ def run_split(lib, prob, chunk_blocks):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     common = (prob.B, prob.H, prob.N, prob.d, float(prob.scale), int(prob.causal), None)
     st = lib.fa_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), *common, ptr(bm),
-                           prob.block_size, 0, CODE[prob.dtype], stream)
+                           prob.block_size, 0, 0, CODE[prob.dtype], stream)
     assert st == 0, lib.fa_last_error_detail()
     st = lib.fa_backward_blocksparse_split(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse),
                                            ptr(dq), ptr(dk), ptr(dv), *common, ptr(bm),

@@ -83,3 +83,33 @@ def test_flops_gpt2_small():
     pairs = 96 * 1024 * 1025 // 2
     assert accounting.kept_pairs(p) == pairs
     assert accounting.flops(p, "fwd+bwd") == 14 * 64 * pairs
+
+
+@pytest.mark.parametrize("kw", [
+    dict(causal=False), dict(causal=True), dict(causal=True, key_len_range=(1, 700)),
+    dict(block_keep_p=0.5), dict(causal=True, block_keep_p=0.4, key_len_range=(300, 700)),
+    dict(block_keep_p=0.3, block_band=1, block_global=1),
+])
+@pytest.mark.parametrize("rows", [64, 128, 256])
+def test_streamed_rows_match_visibility(kw, rows):
+    # The backward IO model's count of streamed rows against brute force over
+    # the visibility matrix: per work-group of `rows` rows, the keys some of
+    # its queries keep (dQ pass) or the queries that keep some of its keys
+    # (dK/dV pass).
+    p = inputs.make_problem(2, 3, 700, 64, "bf16", seed=5, **kw)
+    want = {"dq": 0, "dkdv": 0}
+    for b in range(p.B):
+        kl = None if p.key_lens is None else int(p.key_lens[b])
+        vis = oracle.visibility(p.N, causal=p.causal, key_len=kl, block_mask=p.block_mask,
+                                block_size=p.block_size)
+        for r0 in range(0, p.N, rows):
+            want["dq"] += int(vis[r0:r0 + rows].any(axis=0).sum())
+            want["dkdv"] += int(vis[:, r0:r0 + rows].any(axis=1).sum())
+    for which in ("dq", "dkdv"):
+        assert accounting.streamed_rows(p, which, rows) == p.H * want[which], which
+    # whole passes: own rows plus the streamed ones
+    s, n, d, heads = 2, p.N, p.d, p.B * p.H
+    assert accounting.tiled_backward_pass_bytes(p, "dq", rows) == \
+        heads * (4 * n * d * s + 12 * n) + p.H * want["dq"] * 2 * d * s
+    assert accounting.tiled_backward_pass_bytes(p, "dkdv", rows) == \
+        heads * 4 * n * d * s + p.H * want["dkdv"] * (2 * d * s + 8)
