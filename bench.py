@@ -40,7 +40,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import _binding  # noqa: E402
-from exact_io_aware_52_amd import (accounting, build_lib, fa_backward,  # noqa: E402
+from exact_io_aware_52_amd import (accounting, build_lib, fa_backward, fa_backward_ex,  # noqa: E402
+                                   fa_forward_key_groups_for,
                                    fa_backward_blocksparse_split,
                                    fa_backward_blocksparse_split_workspace_bytes,
                                    fa_backward_dkdv, fa_backward_dq,
@@ -463,7 +464,7 @@ def cpu_baseline_varlen(prob, budget_s):
 class Runner:
     """Device buffers and launch closures for one self-attention workload."""
 
-    def __init__(self, prob, dev, fwd_block_rows=0, fwd_block_keys=0, bwd_rows=0):
+    def __init__(self, prob, dev, fwd_block_rows=0, fwd_block_keys=0, bwd_rows=0, key_groups=0):
         self.prob = prob
         dt = TORCH_DT[prob.dtype]
         self.q, self.k, self.v, self.do = (torch.from_numpy(x).to(dt).to(dev)
@@ -482,6 +483,8 @@ class Runner:
         # Keys per K/V tile: 64 by default (16-bit); 32 and 128 run as
         # fa_fwd_keys_kernel with 128-row tiles.
         self.keys = fwd_block_keys
+        # Key groups per forward tile (0: the library's choice).
+        self.key_groups = key_groups
         # Backward tile heights (dQ query rows, dK/dV keys per work-group).
         self.dq_rows = self.dkdv_rows = bwd_rows
         other_keys = fwd_block_keys not in (0, 64)
@@ -491,7 +494,11 @@ class Runner:
         # range: its forward is split four ways over work-groups (measured best
         # of 4K, 8K and 16K keys per split at N = 32K and 64K).
         self.key_chunk = 0
-        self.fwd_kernel = "fa_fwd_keys_kernel" if other_keys else KERNEL_NAMES["fwd"]
+        self.fwd_kgroups = key_groups or (fa_forward_key_groups_for(
+            prob.B, prob.H, prob.N, prob.d, dt, prob.block_mask is not None)
+            if not (fwd_block_rows or other_keys) else 1)
+        self.fwd_kernel = ("fa_fwd_keys_kernel" if other_keys else
+                           "fa_fwd_kgroups_kernel" if self.fwd_kgroups == 2 else KERNEL_NAMES["fwd"])
         # Their backward is split by kept mask blocks, 64 per work-group (measured
         # at 32K: 911, 979 and 1217 us for 32, 64 and 128 against 1346 unsplit; at
         # 64K all within 1% of unsplit, the passes bound by HBM reads of sparse
@@ -517,7 +524,7 @@ class Runner:
                                          lse=self.lse, workspace=self.split_ws)
         else:
             fa_forward_ex(self.q, self.k, self.v, block_rows=self.rows, block_keys=self.keys,
-                          o=self.o, lse=self.lse, **self.kw)
+                          key_groups=self.key_groups, o=self.o, lse=self.lse, **self.kw)
 
     def bwd_dq(self):
         fa_backward_dq(self.q, self.k, self.v, self.o, self.do, self.lse, dq=self.dq,
@@ -630,7 +637,7 @@ def step_stamps(args, dev):
                                  ctypes.c_void_p(run.v.data_ptr()), ctypes.c_void_p(run.o.data_ptr()),
                                  ctypes.c_void_p(run.lse.data_ptr()), prob.B, prob.H, prob.N, prob.d,
                                  run.scale, int(prob.causal), kl, bm, prob.block_size, rows, 0,
-                                 code, st) == 0
+                                 1, code, st) == 0
     for _ in range(max(args.warmup, 1)):
         fwd()
     torch.cuda.synchronize()
@@ -681,6 +688,9 @@ def main():
     ap.add_argument("--fwd-block-keys", type=int, default=0, choices=[0, 32, 64, 128],
                     help="keys per forward K/V tile (B_c); 0 = the default (64); 32 and 128 "
                          "take 128-row tiles")
+    ap.add_argument("--key-groups", type=int, default=0, choices=[0, 1, 2],
+                    help="wave groups splitting each forward tile's key range; 0 = the library's "
+                         "choice")
     ap.add_argument("--bwd-rows", type=int, default=0, choices=[0, 64, 128, 256],
                     help="backward tile height: query rows per dQ work-group and keys per dK/dV "
                          "work-group; 0 = 128")
@@ -735,7 +745,8 @@ def main():
         return
 
     prob = make_workload(args)
-    run = Runner(prob, dev, args.fwd_block_rows, args.fwd_block_keys, args.bwd_rows)
+    run = Runner(prob, dev, args.fwd_block_rows, args.fwd_block_keys, args.bwd_rows,
+                 args.key_groups)
     m = measure(run, args.steps, args.warmup)
     ms_step, ms_fwd, kus = m["ms_step"], m["ms_fwd"], m["kernels_us"]
     pairs = accounting.kept_pairs(prob)
@@ -772,6 +783,7 @@ def main():
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
                    "fwd_block_rows": run.fwd_rows, "fwd_block_keys": run.keys or 64,
+                   "fwd_key_groups": run.fwd_kgroups,
                    "bwd_rows": run.dq_rows or 128,
                    "fwd_key_chunk": run.key_chunk or None,
                    "bwd_chunk_blocks": run.chunk_blocks or None,

@@ -60,7 +60,8 @@ def open_library(path):
     lib.fa_backward_noalloc_max_rows.restype = Z
     lib.fa_backward_dq.argtypes = [P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P, Z, P]
     lib.fa_backward_dkdv.argtypes = [P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, P, Z, P]
-    lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, I, P]
+    lib.fa_forward_ex.argtypes = [P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, I, I, P]
+    lib.fa_forward_key_groups_for.argtypes = [I, I, I, I, I, I]
     lib.fa_backward_blocksparse_split.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I,
                                                   P, P, I, I, I, P, Z, P]
     lib.fa_backward_blocksparse_split_workspace_bytes.argtypes = [I, I, I, I, I]
@@ -79,7 +80,8 @@ def open_library(path):
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_forward_blocksparse_split,
                lib.fa_forward_ex, lib.fa_backward, lib.fa_backward_ex, lib.fa_backward_dq,
                lib.fa_backward_dkdv, lib.fa_backward_noalloc,
-               lib.fa_forward_block_rows_for, lib.fa_forward_kv, lib.fa_forward_varlen):
+               lib.fa_forward_block_rows_for, lib.fa_forward_key_groups_for, lib.fa_forward_kv,
+               lib.fa_forward_varlen):
         fn.restype = I
     return lib
 
@@ -155,7 +157,7 @@ def _scale(scale, d):
 
 
 def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, lse,
-             block_rows=0, block_keys=0):
+             block_rows=0, block_keys=0, key_groups=0):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     o = torch.empty_like(q) if o is None else _like("o", o, q)
@@ -168,7 +170,7 @@ def _forward(name, q, k, v, scale, causal, key_lens, block_mask, block_size, o, 
         bm = _mask(block_mask, N, block_size, q.device)
         args += [_ptr(bm), int(block_size)]
     if name == "fa_forward_ex":
-        args += [int(block_rows), int(block_keys)]
+        args += [int(block_rows), int(block_keys), int(key_groups)]
     args += [_DTYPE_CODE[q.dtype], _stream(q.device)]
     _check(name, getattr(lib, name)(*args))
     return o, lse
@@ -189,12 +191,13 @@ def fa_forward_blocksparse(q, k, v, block_mask, block_size=128, scale=None, caus
 
 
 def fa_forward_ex(q, k, v, block_mask=None, block_size=128, block_rows=0, scale=None,
-                  causal=False, key_lens=None, o=None, lse=None, block_keys=0):
+                  causal=False, key_lens=None, o=None, lse=None, block_keys=0, key_groups=0):
     """Forward with the query rows per work-group (64, 128, 256; 0 = the
-    library's choice) and the keys per K/V tile (32, 64, 128; 0 = the type's
-    default) given per call; block_mask optional."""
+    library's choice), the keys per K/V tile (32, 64, 128; 0 = the type's
+    default) and the key groups per tile (1, 2; 0 = the library's choice)
+    given per call; block_mask optional."""
     return _forward("fa_forward_ex", q, k, v, scale, causal, key_lens, block_mask, block_size,
-                    o, lse, block_rows, block_keys)
+                    o, lse, block_rows, block_keys, key_groups)
 
 
 def fa_forward_blocksparse_split_workspace_bytes(B, H, N, d, key_chunk):
@@ -486,4 +489,11 @@ def fa_forward_block_rows_for(B, H, N, d, dtype, sparse=False):
     """Query rows per work-group a forward of these sizes would use."""
     return int(load_library().fa_forward_block_rows_for(int(B), int(H), int(N), int(d),
                                                         (_DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)),
+                                                        int(bool(sparse))))
+
+
+def fa_forward_key_groups_for(B, H, N, d, dtype, sparse=False):
+    """Key groups per query tile a forward of these sizes would use."""
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_forward_key_groups_for(int(B), int(H), int(N), int(d), code,
                                                         int(bool(sparse))))

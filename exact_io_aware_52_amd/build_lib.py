@@ -33,8 +33,8 @@ STAMPS_LIB = os.path.join(PKG, "libfa_stamps.so")
 # profiles/ carry the hash of the code they were taken on, and the bench
 # reports their traffic only while it matches.
 CODE_MANIFEST = os.path.join(PKG, "kernel_code.json")
-KERNELS = ("fa_fwd_kernel", "fa_fwd_keys_kernel", "fa_fwd_combine_kernel", "fa_bwd_dq_kernel",
-           "fa_bwd_dkdv_kernel")
+KERNELS = ("fa_fwd_kernel", "fa_fwd_keys_kernel", "fa_fwd_kgroups_kernel", "fa_fwd_combine_kernel",
+           "fa_bwd_dq_kernel", "fa_bwd_dkdv_kernel")
 
 SOURCES = ["fa_api.cpp", "fa_fwd.hip", "fa_bwd.hip", "fa_bwd_f32.hip"]
 # Sources compiled without the VGPR-form matrix-core option.  fp32 backward:

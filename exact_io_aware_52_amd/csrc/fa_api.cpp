@@ -42,6 +42,21 @@ int auto_fwd_rows(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
   return groups >= kAutoTallMinGroups ? 256 : 128;
 }
 
+// Two key groups per 128-row tile (fa_fwd_kgroups_kernel: 8 waves, one
+// work-group per CU) when the default grid of 16-bit dense self-attention
+// holds at most two work-groups per CU: the plain kernel then keeps no more
+// waves resident than the split one, and the longest causal tiles set its
+// time.  Measured forward times, key groups 2 against 1 (B2 H8, causal):
+// N = 2K -10% (d = 64) and -21% (d = 128), N = 4K -4% and -13%; with more
+// work-groups the split kernel's single work-group per CU costs more than
+// the shorter chains save (GPT-2 shape, 768 tiles: +44%; N = 8K: +18%, +15%).
+constexpr long long kAutoKgroupsMaxGroups = 2LL * 256;
+int auto_fwd_kgroups(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
+  if (dtype == FA_F32 || sparse || auto_fwd_rows(B, H, N, d, dtype, sparse) != 128) return 1;
+  const long long groups = (long long)B * H * ((N + 127) / 128);
+  return groups <= kAutoKgroupsMaxGroups ? 2 : 1;
+}
+
 }  // namespace
 
 namespace {
@@ -127,7 +142,7 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
                  int N, int d, float scale, int causal, const int32_t* key_lens,
                  const uint8_t* block_mask, int block_size, bool sparse, fa_dtype dtype,
                  hipStream_t stream, const SplitArgs& split = SplitArgs(), int block_rows = 0,
-                 int block_keys = 0) {
+                 int block_keys = 0, int key_groups = 0) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
@@ -149,9 +164,20 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
     return fail(FA_ERR_UNSUPPORTED,
                 "%d keys per tile with %d query rows per tile (128 rows only)", block_keys,
                 block_rows);
+  if (key_groups < 0 || key_groups > 2)
+    return fail(FA_ERR_UNSUPPORTED, "key_groups=%d (supported: 0 = automatic, 1, 2)", key_groups);
+  if (key_groups == 2 && (dtype == FA_F32 || block_mask || other_keys ||
+                          (block_rows != 0 && block_rows != 128) || split.key_chunk > 0))
+    return fail(FA_ERR_UNSUPPORTED, "key_groups=2 takes 16-bit dense self-attention with 128-row "
+                "tiles of 64 keys");
   const int rows = other_keys ? 128
                    : block_rows ? block_rows
                                 : auto_fwd_rows(B, H, N, d, dtype, block_mask != nullptr);
+  int kgroups = key_groups;
+  if (kgroups == 0)
+    kgroups = block_rows == 0 && !other_keys && split.key_chunk == 0
+                  ? auto_fwd_kgroups(B, H, N, d, dtype, block_mask != nullptr)
+                  : 1;
   if (block_mask && rows > 128)
     return fail(FA_ERR_UNSUPPORTED, "block-sparse forward with %d query rows per tile (at most 128)",
                 rows);
@@ -167,6 +193,8 @@ int forward_impl(const void* q, const void* k, const void* v, void* o, float* ls
   if (key_lens && !aligned(key_lens, 4)) return fail(FA_ERR_INVALID_ARG, "key_lens misaligned");
   fa::Problem p{B, H, N, d, scale, causal ? 1 : 0, key_lens, block_mask, (int)dtype, stream, rows};
   p.fwd_keys = other_keys ? block_keys : 0;
+  p.fwd_rows = kgroups == 2 ? 128 : p.fwd_rows;
+  p.fwd_kgroups = kgroups;
   const int splits = split.key_chunk > 0 ? sparse_splits(N, split.key_chunk) : 1;
   if (splits > 1) {
     const size_t need = split_workspace(B, H, N, d, splits);
@@ -443,13 +471,18 @@ int fa_forward_varlen(const void* q, const void* k, const void* v, void* o, floa
 int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B, int H,
                   int N, int d, float scale, int causal, const int32_t* key_lens,
                   const uint8_t* block_mask, int block_size, int block_rows, int block_keys,
-                  fa_dtype dtype, hipStream_t stream) {
+                  int key_groups, fa_dtype dtype, hipStream_t stream) {
   return forward_impl(q, k, v, o, lse, B, H, N, d, scale, causal, key_lens, block_mask,
-                      block_size, false, dtype, stream, SplitArgs(), block_rows, block_keys);
+                      block_size, false, dtype, stream, SplitArgs(), block_rows, block_keys,
+                      key_groups);
 }
 
 int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse) {
   return auto_fwd_rows(B, H, N, d, dtype, sparse != 0);
+}
+
+int fa_forward_key_groups_for(int B, int H, int N, int d, fa_dtype dtype, int sparse) {
+  return auto_fwd_kgroups(B, H, N, d, dtype, sparse != 0);
 }
 
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {

@@ -173,13 +173,22 @@ __device__ __forceinline__ float sum16(const float (&e)[16]) {
   return (a[0] + a[1]) + (a[2] + a[3]);
 }
 
-// One work-group's query tile (the body of both forward kernels below).
-template <typename T, int D, int NW, int BC>
+// One work-group's query tile (the body of the forward kernels below).
+// KG key groups: with KG = 2 the NW waves form two groups of NW / 2 that
+// share the tile's query rows and split its key range in halves, each group
+// streaming its half through its own LDS ring; the two online-softmax states
+// are merged through LDS at the end (review page, "Method": the per-block
+// states combine exactly by rescaling to a common reference).  Dense
+// self-attention only (the caller chooses it).
+template <typename T, int D, int NW, int BC, int KG = 1>
 __device__ __forceinline__ void fwd_tile(FwdParams p) {
+  static_assert(KG == 1 || KG == 2, "one or two key groups");
+  static_assert(KG == 1 || sizeof(raw_t<T>) == 2, "key groups: 16-bit types");
+  constexpr int RW = NW / KG;  // waves per key group (32 query rows each)
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef FwdCfg<T, D, NW, BC> L;
+  typedef FwdCfg<T, D, RW, BC> L;
   constexpr int BR = L::BR;
   constexpr int BT = L::BT;
   constexpr int NSUB = L::NSUB;
@@ -187,18 +196,22 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
   constexpr int LPT = L::LPT;
   constexpr int VSWZ = sizeof(raw) == 2 ? kTr : kRows;  // V^T via transposing reads
 
-  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[KG * L::NS * L::SLOT_BYTES];
   __shared__ uint8_t mask_row[kMaxMaskBlocks];
   __shared__ int wg_redo;  // unchecked sweep overflowed somewhere in the work-group
-  const uint32_t ring_lds = lds_addr(ring);
-  auto ktile = [&](int s) { return reinterpret_cast<const raw*>(ring + s * L::SLOT_BYTES); };
-  auto vtile = [&](int s) {
-    return reinterpret_cast<const raw*>(ring + s * L::SLOT_BYTES + L::TILE_BYTES);
-  };
+  __shared__ float ref_x[KG > 1 ? RW * 64 : 1];  // key group 0's fixed references
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kgrp = KG > 1 ? wg_wave / RW : 0;  // key group of this wave
+  const int w = KG > 1 ? wg_wave % RW : wg_wave;  // row wave within the group
+  char* const gring = ring + kgrp * L::NS * L::SLOT_BYTES;  // this group's ring
+  const uint32_t ring_lds = lds_addr(gring);
+  auto ktile = [&](int s) { return reinterpret_cast<const raw*>(gring + s * L::SLOT_BYTES); };
+  auto vtile = [&](int s) {
+    return reinterpret_cast<const raw*>(gring + s * L::SLOT_BYTES + L::TILE_BYTES);
+  };
   const int col = lane & 31;
   const int hh = lane >> 5;
 
@@ -213,8 +226,8 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
     __builtin_amdgcn_sched_barrier(0);
     const unsigned long long t = __builtin_readcyclecounter();
     const unsigned long long rt = __builtin_amdgcn_s_memrealtime();
-    if (stamp_slot >= 0 && w < 4 && lane == 0 && stamp_ev < kStampEvents) {
-      unsigned long long* rec = g_stamps[stamp_slot * 4 + w] + 3 * stamp_ev;
+    if (stamp_slot >= 0 && wg_wave < 4 && lane == 0 && stamp_ev < kStampEvents) {
+      unsigned long long* rec = g_stamps[stamp_slot * 4 + wg_wave] + 3 * stamp_ev;
       rec[0] = t;
       rec[1] = rt;
       rec[2] = (unsigned long long)code;
@@ -258,6 +271,14 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
   if (p.causal) kv_end = min(kv_end, i0 + BR + shift);
   const int t0 = kbeg / BT;  // first key tile of the range
   const int nkt = kv_end > kbeg ? (kv_end + BT - 1) / BT : t0;
+  // This key group's tiles [tbeg, tend): all of [t0, nkt), or its first or
+  // second half (the first group takes the extra tile of an odd count).
+  int tbeg = t0, tend = nkt;
+  if constexpr (KG > 1) {
+    const int tmid = t0 + (nkt - t0 + 1) / 2;
+    tbeg = kgrp ? tmid : t0;
+    tend = kgrp ? nkt : tmid;
+  }
   const bool sparse = p.block_mask != nullptr;
   if (sparse) {
     const uint8_t* bm = p.block_mask + (size_t)(i0 / kMaskBlock) * p.nblk;
@@ -283,8 +304,8 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
 
   // K and V of tile t into ring slot s (LPT DMA instructions per wave).  Only
   // the ragged last tile computes clamped per-lane addresses.
-  DmaPlan<raw, BT, D, kRows, NW> kplan;
-  DmaPlan<raw, BT, D, VSWZ, NW> vplan;
+  DmaPlan<raw, BT, D, kRows, RW> kplan;  // (a key group copies its own tiles)
+  DmaPlan<raw, BT, D, VSWZ, RW> vplan;
   kplan.init(w, lane);
   vplan.init(w, lane);
   auto issue = [&](int t, int s) __attribute__((always_inline)) {
@@ -419,6 +440,7 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
     }
   };
 
+  bool one_ref = false;  // the kept sweep was the unchecked one (one fixed reference)
   // Kept tiles of this work-group, in order; tl[k] is the tile of step i + k.
   int tl[4];
   tl[0] = next_kept(t0);
@@ -479,7 +501,7 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
         if (tl[0] >= nkt) break;
       }
     }
-  } else if (tl[0] < nkt) {
+  } else if (KG > 1 ? t0 < nkt : tl[0] < nkt) {
     // Without the pipeline: step i forms, exponentiates and multiplies into
     // O the scores of tile i, from ring slot i % NS, with the next NS - 1
     // tiles requested ahead (several work-groups per CU hide the latency).
@@ -499,15 +521,15 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
     auto sweep = [&](auto checked_c) {
       constexpr bool CHECKED = decltype(checked_c)::value;
       int tl[PD + 1];
-      tl[0] = next_kept(t0);
+      tl[0] = next_kept(tbeg);
 #pragma unroll
-      for (int k = 1; k <= PD; ++k) tl[k] = tl[k - 1] < nkt ? next_kept(tl[k - 1] + 1) : nkt;
+      for (int k = 1; k <= PD; ++k) tl[k] = tl[k - 1] < tend ? next_kept(tl[k - 1] + 1) : tend;
       // (tile indices are wave-uniform; the copies take them as scalars)
 #pragma unroll
       for (int k = 0; k <= PD; ++k) tl[k] = __builtin_amdgcn_readfirstlane(tl[k]);
 #pragma unroll
       for (int k = 0; k < PD; ++k)
-        if (tl[k] < nkt) issue(tl[k], k);
+        if (tl[k] < tend) issue(tl[k], k);
       FA_STAGE_FENCE();
       // The Q fragments arrived by ordinary loads issued before these copies.
       // Waiting for everything once here tells the compiler they have landed;
@@ -516,15 +538,24 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
       wait_vmcnt<0>();
       stamp(5);
       if constexpr (!CHECKED) {
-        // Reference points: sub-tile 0 of tile 0, the keys each row sees.
+        // Reference points: sub-tile 0 of tile 0, the keys each row sees
+        // (in the first key group's ring; the second group takes them from
+        // there through LDS).
         __syncthreads();
-        f32x16 sc;
-        scores(ktile(0), 0, sc);
-        apply_mask(0, 0, sc);
-        float mx = kNegInf;
+        if (kgrp == 0) {
+          f32x16 sc;
+          scores(ktile(0), 0, sc);
+          apply_mask(0, 0, sc);
+          float mx = kNegInf;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
-        ra = pair_max(mx) * c;
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[r]);
+          ra = pair_max(mx) * c;
+        }
+        if constexpr (KG > 1) {
+          if (kgrp == 0) ref_x[w * 64 + lane] = ra;
+          __syncthreads();
+          if (kgrp == 1) ra = ref_x[w * 64 + lane];
+        }
       }
       // Per sub-tile bookkeeping: the checked sweep's settle, or the sum.
       auto take = [&](const f32x16& s, frag_t<T> (&pf)[2], float rs, bool has_mask) {
@@ -559,18 +590,25 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
         }
       };
       // Dense interior: whole tiles seen in full by every wave, tile i+PD whole.
-      int lo = nkt, hi = -1;
+      int lo = tend, hi = -1;
       if (!sparse) {
-        lo = t0;
-        hi = min(min(nkt, NK / BT) - 1 - PD, kend / BT - 1);
+        lo = tbeg;
+        hi = min(min(tend, NK / BT) - 1 - PD, kend / BT - 1);
         // whole tile visible to query i0: (t + 1) BT - 1 <= i0 + shift
         if (p.causal) hi = min(hi, i0 + shift + 1 >= 0 ? (i0 + shift + 1) / BT - 1 : -1);
       }
-      for (;;) {
+      // With two key groups both take the same number of steps (the first
+      // group's tile count, the larger), so that their barriers pair up; a
+      // group past its last tile only joins the barriers.
+      const int steps = KG > 1 ? (nkt - t0 + 1) / 2 : 0;
+      for (int iter = 0;; ++iter) {
         const int t = __builtin_amdgcn_readfirstlane(tl[0]);
         const raw* Kc = ktile(cur);
         const raw* Vc = vtile(cur);
-        if (t >= lo && t <= hi) {
+        if (KG > 1 && t >= tend) {
+          __syncthreads();  // (the step's one barrier)
+          FA_STAGE_FENCE();
+        } else if (t >= lo && t <= hi) {
           stamp(1);
           wait_vmcnt<(PD - 1) * LPT>();  // tile t landed; t+1 .. t+PD-1 may be in flight
           stamp(2);
@@ -584,12 +622,12 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
           stamp(4);
 #pragma unroll
           for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
-          tl[PD] = min(t + PD + 1, nkt);
+          tl[PD] = min(t + PD + 1, tend);
         } else {
           stamp(11);
           int inflight = 0;  // later tiles requested so far (at most PD - 1)
 #pragma unroll
-          for (int k = 1; k < PD; ++k) inflight += tl[k] < nkt;
+          for (int k = 1; k < PD; ++k) inflight += tl[k] < tend;
           if constexpr (PD >= 3) {
             if (inflight >= 2) wait_vmcnt<2 * LPT>();
             else if (inflight == 1) wait_vmcnt<LPT>();
@@ -603,7 +641,7 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
           stamp(12);
           __syncthreads();  // every wave is done with step i-1: slot nxt is free
           stamp(13);
-          if (tl[PD] < nkt) issue(tl[PD], nxt);
+          if (tl[PD] < tend) issue(tl[PD], nxt);
           FA_STAGE_FENCE();
           // A tile this wave sees in full (every sub-tile active and unmasked;
           // wave-uniform) takes the interior's interleaved order.
@@ -630,12 +668,12 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
           stamp(14);
 #pragma unroll
           for (int k = 0; k < PD; ++k) tl[k] = tl[k + 1];
-          tl[PD] = __builtin_amdgcn_readfirstlane(tl[PD] < nkt ? next_kept(tl[PD] + 1) : nkt);
+          tl[PD] = __builtin_amdgcn_readfirstlane(tl[PD] < tend ? next_kept(tl[PD] + 1) : tend);
         }
         FA_STAGE_FENCE();
         cur = cur + 1 == NS ? 0 : cur + 1;
         nxt = nxt + 1 == NS ? 0 : nxt + 1;
-        if (tl[0] >= nkt) break;
+        if (KG > 1 ? iter + 1 >= steps : tl[0] >= tend) break;
       }
     };
     // (One-wave tiles, for inference with few queries, keep only the checked
@@ -644,11 +682,13 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
     if constexpr (NW > 1) {
       if (!checked) {
         sweep(std::false_type{});
+        // (with two key groups, half the bound, so that their sum stays finite)
+        constexpr float kMaxAcc = KG > 1 ? 0x1p126f : 0x1p127f;
         bool bad = !(l_run <= 0x1p64f);
 #pragma unroll
         for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) bad = bad || !(__builtin_fabsf(oacc[db][r]) <= 0x1p127f);
+          for (int r = 0; r < 16; ++r) bad = bad || !(__builtin_fabsf(oacc[db][r]) <= kMaxAcc);
         // Work-group wide: every wave is done with the ring before the flag is
         // read, and any wave's overflow sends the whole work-group back.
         if (tid == 0) wg_redo = 0;
@@ -665,6 +705,52 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
       }
     }
     if (checked) sweep(std::true_type{});
+    one_ref = !checked;
+  }
+
+  if constexpr (KG > 1) {
+    // Key group 1 hands its state (O accumulator, denominator, reference) to
+    // group 0 through the idle ring, lane for lane; group 0 merges and alone
+    // stores the tile.  Under the unchecked sweep both groups share one
+    // reference point, so the states simply add; otherwise each is rescaled
+    // to the larger reference.
+    constexpr int XF = D / 32 * 16 + 3;
+    static_assert(RW * XF * 64 * 4 <= KG * L::NS * L::SLOT_BYTES, "hand-over fits in the rings");
+    float* const xs = reinterpret_cast<float*>(ring) + w * XF * 64;
+    __syncthreads();  // every wave is done with both rings
+    if (kgrp == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(db * 16 + r) * 64 + lane] = oacc[db][r];
+      xs[(XF - 3) * 64 + lane] = l_run;
+      xs[(XF - 2) * 64 + lane] = ra;
+      xs[(XF - 1) * 64 + lane] = ref ? 1.f : 0.f;
+    }
+    __syncthreads();
+    if (kgrp == 1) return;  // (no barrier follows)
+    const float l1 = xs[(XF - 3) * 64 + lane];
+    const float ra1 = xs[(XF - 2) * 64 + lane];
+    const bool ref1 = xs[(XF - 1) * 64 + lane] != 0.f;
+    if (one_ref) {
+      l_run += l1;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) oacc[db][r] += xs[(db * 16 + r) * 64 + lane];
+    } else if (ref1) {  // (ref, ref1 are the same on both lanes of a row)
+      const float r = ref ? fmaxf(ra, ra1) : ra1;
+      const float f0 = ref ? fast_exp2(ra - r) : 0.f;
+      const float f1 = fast_exp2(ra1 - r);
+      l_run = l_run * f0 + l1 * f1;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r2 = 0; r2 < 16; ++r2)
+          oacc[db][r2] = oacc[db][r2] * f0 + xs[(db * 16 + r2) * 64 + lane] * f1;
+      ra = r;
+      ref = true;
+    }
   }
 
   stamp(20);
@@ -722,6 +808,16 @@ template <typename T, int D, int BC>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(
     FwdCfg<T, D, 4, BC>::WAVES_PER_SIMD))) void fa_fwd_keys_kernel(FwdParams p) {
   fwd_tile<T, D, 4, BC>(p);
+}
+
+// 128-row tiles whose key range two groups of four waves split (16-bit dense
+// self-attention): half the sequential steps per tile, for grids too small
+// to fill the GPU, where the longest causal tiles set the kernel's time.  Two
+// rings take one work-group (two waves per SIMD) per CU.
+template <typename T, int D>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2))) void
+fa_fwd_kgroups_kernel(FwdParams p) {
+  fwd_tile<T, D, 8, 0, 2>(p);
 }
 
 // Merge of the key-range splits of one query row (the online-softmax merge of
@@ -785,9 +881,9 @@ hipError_t launch_fwd_combine(const Problem& pb, const FwdTensors& t, int splits
   return hipGetLastError();
 }
 
-template <typename T, int D, int NW, int BC = 0>
+template <typename T, int D, int NW, int BC = 0, int KG = 1>
 hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
-  constexpr int BR = FwdCfg<T, D, NW, BC>::BR;
+  constexpr int BR = FwdCfg<T, D, NW / KG, BC>::BR;
   FwdParams p;
   p.q = t.q; p.k = t.k; p.v = t.v; p.o = t.o; p.lse = t.lse;
   p.key_lens = pb.key_lens;
@@ -814,7 +910,11 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.Tq = pb.Tq;
   p.Tk = pb.Tk;
   const unsigned grid = (unsigned)p.nq * (unsigned)p.BH;
-  if constexpr (BC != 0) {
+  if constexpr (KG == 2) {
+    static_assert(NW == 8 && BC == 0, "two key groups of four waves, 64-key tiles");
+    hipLaunchKernelGGL((fa_fwd_kgroups_kernel<T, D>), dim3(grid, splits), dim3(512), 0, pb.stream,
+                       p);
+  } else if constexpr (BC != 0) {
     static_assert(NW == 4, "other key-tile widths come with 128-row tiles");
     hipLaunchKernelGGL((fa_fwd_keys_kernel<T, D, BC>), dim3(grid, splits), dim3(256), 0,
                        pb.stream, p);
@@ -832,7 +932,9 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
 template <typename T, int D>
 hipError_t launch_fwd_rows(const Problem& pb, const FwdTensors& t) {
   if constexpr (sizeof(T) == 2) {
-    // 128-row tiles of 32 or 128 keys (checked by the caller)
+    // 128-row tiles of 32 or 128 keys, or split between two key groups
+    // (checked by the caller)
+    if (pb.fwd_kgroups == 2) return launch_fwd_t<T, D, 8, 0, 2>(pb, t);
     if (pb.fwd_keys == 32) return launch_fwd_t<T, D, 4, 32>(pb, t);
     if (pb.fwd_keys == 128) return launch_fwd_t<T, D, 4, 128>(pb, t);
   }

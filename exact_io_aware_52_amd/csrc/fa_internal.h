@@ -23,6 +23,7 @@ struct Problem {
   hipStream_t stream;
   int fwd_rows = 128;         // forward: query rows per work-group (32, 64, 128, 256)
   int fwd_keys = 0;           // forward: keys per K/V tile (0: the type's default)
+  int fwd_kgroups = 1;        // forward: wave groups splitting each tile's key range (1, 2)
   // Forward of N queries against nk keys (inference): nk < 0 means nk = N.
   int nk = -1;
   int causal_br = 0;          // causal aligned bottom-right to the visible key count

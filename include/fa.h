@@ -303,14 +303,23 @@ size_t fa_backward_blocksparse_split_workspace_bytes(int B, int H, int N, int d,
  *               128.  Widths other than the default take 16-bit types and
  *               128 query rows per tile (block_rows 0 or 128; 0 then means
  *               128); other combinations and values are FA_ERR_UNSUPPORTED.
+ *   key_groups  groups of waves that split each query tile's key range and
+ *               merge their online-softmax states on chip (review page,
+ *               "Method": per-block states combine exactly after rescaling
+ *               to a common reference): 1, 2, or 0 to let the library choose
+ *               (fa_forward_key_groups_for; only with block_rows 0 and the
+ *               default block_keys).  2 takes 16-bit types without a block
+ *               mask, 128-row tiles (block_rows 0 or 128) and the default
+ *               key-tile width; otherwise FA_ERR_UNSUPPORTED.
  * Tuning and measurement options: results agree to rounding for every
  * value.  fa_forward and fa_forward_blocksparse are this call with
- * block_rows = 0 and block_keys = 0.
+ * block_rows = 0, block_keys = 0 and key_groups = 0.
  */
 int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* lse,
                   int B, int H, int N, int d, float scale, int causal,
                   const int32_t* key_lens, const uint8_t* block_mask, int block_size,
-                  int block_rows, int block_keys, fa_dtype dtype, hipStream_t stream);
+                  int block_rows, int block_keys, int key_groups, fa_dtype dtype,
+                  hipStream_t stream);
 
 /*
  * Query rows per work-group that a forward of these sizes uses when
@@ -319,6 +328,15 @@ int fa_forward_ex(const void* q, const void* k, const void* v, void* o, float* l
  * else 128.  Host arithmetic only.
  */
 int fa_forward_block_rows_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
+
+/*
+ * Key groups (see fa_forward_ex) that a forward of these sizes uses when
+ * key_groups is 0: 2 for 16-bit dense problems whose tiles are 128 rows and
+ * whose grid holds at most 512 of them (two per compute unit: too few to keep
+ * every unit busy until the longest causal tile ends), else 1.  Host
+ * arithmetic only.
+ */
+int fa_forward_key_groups_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
 
 /*
  * fa_backward for callers that cannot allocate device memory (code under HIP

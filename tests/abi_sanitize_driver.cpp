@@ -85,29 +85,52 @@ int main() {
   CHECK(fa_forward(a, a, a, a, f, 2, 8, 4096, 128, 0.1f, 1, nullptr, FA_BF16, nullptr) == FA_OK);
   CHECK(g_last.fwd_rows == 128);
   for (int rows : {64, 128, 256}) {
-    CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, rows, 0,
+    CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, rows, 0, 0,
                         FA_F16, nullptr) == FA_OK);
     CHECK(g_last.fwd_rows == rows && g_last.fwd_keys == 0);
   }
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 32, 0, FA_F16,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 32, 0, 0, FA_F16,
                       nullptr) == FA_ERR_UNSUPPORTED);
   // key-tile widths: 32 and 128 with 128-row tiles (0 rows means 128); 64,
   // the 16-bit default, is no option at all
   for (int keys : {32, 64, 128}) {
-    CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 16384, 128, 0.1f, 1, nullptr, nullptr, 128, 0, keys,
+    CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 16384, 128, 0.1f, 1, nullptr, nullptr, 128, 0, keys, 0,
                         FA_BF16, nullptr) == FA_OK);
     CHECK(g_last.fwd_keys == (keys == 64 ? 0 : keys) && g_last.fwd_rows == (keys == 64 ? 256 : 128));
   }
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 256, 128,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 256, 128, 0,
                       FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 0, 128,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 0, 128, 0,
                       FA_F32, nullptr) == FA_ERR_UNSUPPORTED);
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 0, 256,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, nullptr, 128, 0, 256, 0,
+                      FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
+  // key groups: automatic for small 16-bit dense grids (at most 512 tiles of 128 rows)
+  CHECK(fa_forward(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 2 && g_last.fwd_rows == 128);
+  CHECK(fa_forward(a, a, a, a, f, 2, 8, 16384, 64, 0.1f, 1, nullptr, FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 1 && g_last.fwd_rows == 128);
+  CHECK(fa_forward(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, FA_F32, nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 1);
+  CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, nullptr, 128, 128, 0, 0,
+                      FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 1);  // an explicit height: no automatic key groups
+  CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, nullptr, 128, 0, 0, 1,
+                      FA_BF16, nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 1);
+  CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 16384, 128, 0.1f, 1, nullptr, nullptr, 128, 0, 0, 2,
+                      FA_F16, nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 2 && g_last.fwd_rows == 128);
+  CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, nullptr, 128, 0, 0, 3,
                       FA_BF16, nullptr) == FA_ERR_UNSUPPORTED);
   const uint8_t* bm = static_cast<const uint8_t*>(a);
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 256, 0, FA_F16,
+  CHECK(fa_forward_blocksparse(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, bm, 128, FA_BF16,
+                               nullptr) == FA_OK);
+  CHECK(g_last.fwd_kgroups == 1);
+  CHECK(fa_forward_ex(a, a, a, a, f, 2, 8, 4096, 64, 0.1f, 1, nullptr, bm, 128, 0, 0, 2, FA_BF16,
                       nullptr) == FA_ERR_UNSUPPORTED);
-  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 0, 32, FA_F16,
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 256, 0, 0, FA_F16,
+                      nullptr) == FA_ERR_UNSUPPORTED);
+  CHECK(fa_forward_ex(a, a, a, a, f, 1, 2, 300, 64, 0.1f, 0, nullptr, bm, 128, 0, 32, 0, FA_F16,
                       nullptr) == FA_OK);
   CHECK(g_last.fwd_keys == 32 && g_last.fwd_rows == 128 && g_last.block_mask == bm);
   CHECK(fa_forward_blocksparse(a, a, a, a, f, 1, 1, 300, 64, 0.1f, 0, nullptr, nullptr, 128,

@@ -290,9 +290,9 @@ def test_forward_varlen_validation(lib):
     assert varlen(lib, q=None, cq=None, mq=0) == _binding.FA_OK
 
 
-def fwd_ex(lib, rows, bm=None, N=256, q=FAKE, keys=0, dtype=2, d=64):
+def fwd_ex(lib, rows, bm=None, N=256, q=FAKE, keys=0, dtype=2, d=64, kg=0):
     return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, N, d, 0.1, 0, None, bm, 128, rows,
-                             keys, dtype, None)
+                             keys, kg, dtype, None)
 
 
 def test_forward_ex_block_rows_validation(lib):
@@ -316,7 +316,7 @@ def test_forward_ex_block_rows_validation(lib):
 
     def f32(rows, q=FAKE):
         return lib.fa_forward_ex(q, FAKE, FAKE, FAKE, FAKE, 1, 1, 256, 128, 0.1, 0, None, None,
-                                 128, rows, 0, 0, None)
+                                 128, rows, 0, 0, 0, None)
     assert f32(256) == _binding.FA_ERR_UNSUPPORTED
     assert "float32" in detail(lib)
     assert f32(128, q=None) == _binding.FA_ERR_INVALID_ARG
@@ -350,6 +350,43 @@ def test_forward_ex_block_keys_validation(lib):
     # empty problem: the widths are still checked first
     assert fwd_ex(lib, 0, keys=96, N=0, q=None) == _binding.FA_ERR_UNSUPPORTED
     assert fwd_ex(lib, 0, keys=128, N=0, q=None) == _binding.FA_OK
+
+
+def test_forward_ex_key_groups_validation(lib):
+    for bad in (-1, 3, 4):
+        assert fwd_ex(lib, 0, kg=bad) == _binding.FA_ERR_UNSUPPORTED, bad
+        assert "key_groups" in detail(lib)
+    # 1 and 2 pass for 16-bit dense problems with 128-row tiles of 64 keys
+    for dtype in (1, 2):
+        for d in (64, 128):
+            for kg in (0, 1, 2):
+                for rows in (0, 128):
+                    for keys in (0, 64):
+                        assert fwd_ex(lib, rows, keys=keys, dtype=dtype, d=d, kg=kg, q=None) == \
+                            _binding.FA_ERR_INVALID_ARG
+                        assert "q is NULL" in detail(lib)
+    # two key groups: not for float32, block masks, other heights or widths
+    assert fwd_ex(lib, 0, dtype=0, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, 0, bm=FAKE, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, 64, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, 256, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert fwd_ex(lib, 0, keys=32, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert "key_groups=2" in detail(lib)
+    assert fwd_ex(lib, 0, dtype=0, kg=1, q=None) == _binding.FA_ERR_INVALID_ARG
+
+
+def test_forward_key_groups_automatic(lib):
+    # two key groups for 16-bit dense grids of at most 512 128-row tiles
+    kg_for = lib.fa_forward_key_groups_for
+    assert kg_for(8, 12, 1024, 64, 2, 0) == 1      # 768 tiles
+    assert kg_for(2, 8, 4096, 64, 2, 0) == 2       # 512
+    assert kg_for(2, 8, 4097, 64, 1, 0) == 1       # 528
+    assert kg_for(2, 8, 2048, 64, 1, 0) == 2       # 256
+    assert kg_for(2, 8, 8192, 64, 2, 0) == 1       # 1024
+    assert kg_for(2, 8, 16384, 64, 2, 0) == 1      # 2048
+    assert kg_for(2, 8, 4096, 128, 2, 0) == 2      # d = 128, 128-row tiles
+    assert kg_for(2, 8, 4096, 64, 0, 0) == 1       # fp32
+    assert kg_for(2, 8, 4096, 64, 2, 1) == 1       # block mask
 
 
 def test_forward_block_rows_automatic(lib):

@@ -81,3 +81,30 @@ def test_code_hash_sees_code_not_comments(tmp_path, monkeypatch):
     b = hash_of("// a comment\n/* and another */", "2.f", "b")
     c = hash_of("", "3.f", "c")
     assert a is not None and a == b and a != c
+
+
+def test_bench_global_names_resolve():
+    # Every global name a function of bench.py (or of the package's binding)
+    # reads must exist once the module is imported: a missing import would
+    # otherwise only fail on the GPU, in the middle of a run.
+    import builtins
+    import symtable
+
+    from exact_io_aware_52_amd import _binding
+
+    for path, mod in ((os.path.join(ROOT, "bench.py"), load_bench()),
+                      (_binding.__file__, _binding)):
+        table = symtable.symtable(open(path).read(), path, "exec")
+        missing = set()
+
+        def walk(t):
+            for child in t.get_children():
+                for sym in child.get_symbols():
+                    if sym.is_referenced() and (sym.is_global() or
+                                                (sym.is_free() and t.get_type() == "module")):
+                        name = sym.get_name()
+                        if not hasattr(mod, name) and not hasattr(builtins, name):
+                            missing.add((child.get_name(), name))
+                walk(child)
+        walk(table)
+        assert not missing, f"{os.path.basename(path)}: unresolved global names {sorted(missing)}"

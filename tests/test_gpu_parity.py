@@ -49,7 +49,7 @@ def nan_like(t):
     return torch.full_like(t, float("nan"))
 
 
-def run_gpu(prob, backward=True, block_rows=None, block_keys=0):
+def run_gpu(prob, backward=True, block_rows=None, block_keys=0, key_groups=0):
     """Forward (and backward) through the C ABI into NaN-filled outputs."""
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
@@ -57,9 +57,9 @@ def run_gpu(prob, backward=True, block_rows=None, block_keys=0):
     kw = dict(scale=float(prob.scale), causal=prob.causal, key_lens=kl)
     o = nan_like(q)
     lse = torch.full((prob.B, prob.H, prob.N), float("nan"), dtype=torch.float32, device="cuda")
-    if block_rows is not None or block_keys:
+    if block_rows is not None or block_keys or key_groups:
         fa_forward_ex(q, k, v, bm, prob.block_size, block_rows=block_rows or 0,
-                      block_keys=block_keys, o=o, lse=lse, **kw)
+                      block_keys=block_keys, key_groups=key_groups, o=o, lse=lse, **kw)
     elif bm is not None:
         fa_forward_blocksparse(q, k, v, bm, prob.block_size, o=o, lse=lse, **kw)
     else:
@@ -370,6 +370,52 @@ def test_forward_block_keys_far_keys(keys, boost):
     label = f"far keys x{boost} {keys} keys"
     check_all_heads(prob, gpu, label)
     compare(gpu, run_oracle(prob, backward=False), TOL["bf16"], label=label, magnitude_scaled=True)
+
+
+KG_CASES = [
+    # B, H, N, d, dtype, causal, key_len_range
+    (1, 2, 1000, 64, "bf16", True, None),
+    (2, 1, 777, 128, "fp16", False, (1, 777)),
+    (2, 3, 1100, 128, "bf16", True, (0, 1100)),     # batch 0 without keys
+    (2, 2, 100, 64, "bf16", True, None),            # one tile of two key tiles
+    (1, 2, 64, 64, "fp16", False, None),            # one key tile: group 1 idle
+    (1, 1, 200, 64, "bf16", False, (1, 40)),
+    (2, 4, 2048, 64, "bf16", True, None),
+]
+
+
+@pytest.mark.parametrize("kg", [1, 2])
+@pytest.mark.parametrize("case", KG_CASES, ids=lambda c: "N{}d{}_{}".format(c[2], c[3], c[4]))
+def test_forward_key_groups(case, kg):
+    # Each tile's key range in one sweep (1) or split between two groups of
+    # four waves whose online-softmax states merge on chip (2), against the
+    # oracle on every head.
+    B, H, N, d, dtype, causal, klr = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=191 + N + d, causal=causal,
+                               key_len_range=klr)
+    if klr is not None and klr[0] == 0:
+        prob.key_lens[0] = 0
+    gpu = run_gpu(prob, backward=False, key_groups=kg)
+    check_all_heads(prob, gpu, f"{kg} key groups")
+    compare(gpu, run_oracle(prob, backward=False), TOL[dtype], label=f"{kg} key groups {case}",
+            magnitude_scaled=klr is not None and klr[0] < 4)
+
+
+@pytest.mark.parametrize("boost", [1.5, 6.0])
+@pytest.mark.parametrize("dtype,d", [("bf16", 64), ("fp16", 128)])
+def test_forward_key_groups_far_keys(dtype, d, boost):
+    # Two key groups with scores far above the fixed reference: planted keys
+    # in the first group's half (300..303) and in the second's (1000..1003);
+    # the unchecked sweep keeps them or the work-group falls back to the
+    # checked sweep, whose two states are merged by rescaling.
+    prob = inputs.make_problem(1, 2, 1200, d, dtype, seed=677 + d, causal=True, scale=1.0)
+    for j in (300, 1000):
+        prob.k[:, :, j:j + 4] *= boost
+    prob.k = inputs.round_to_dtype(prob.k, dtype)
+    gpu = run_gpu(prob, backward=False, key_groups=2)
+    label = f"key groups far keys x{boost} {dtype} d{d}"
+    check_all_heads(prob, gpu, label)
+    compare(gpu, run_oracle(prob, backward=False), TOL[dtype], label=label, magnitude_scaled=True)
 
 
 BWD_ROW_CASES = [

@@ -24,7 +24,7 @@ def ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def run_lib(lib, prob, block_rows=0, block_keys=0, bwd_rows=0):
+def run_lib(lib, prob, block_rows=0, block_keys=0, bwd_rows=0, key_groups=0):
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
     bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).cuda()
@@ -35,7 +35,8 @@ def run_lib(lib, prob, block_rows=0, block_keys=0, bwd_rows=0):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     common = (prob.B, prob.H, prob.N, prob.d, float(prob.scale), int(prob.causal), ptr(kl))
     st = lib.fa_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), *common, ptr(bm),
-                           prob.block_size, block_rows, block_keys, CODE[prob.dtype], stream)
+                           prob.block_size, block_rows, block_keys, key_groups, CODE[prob.dtype],
+                           stream)
     assert st == 0, lib.fa_last_error_detail()
     st = lib.fa_backward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq), ptr(dk),
                             ptr(dv), *common, ptr(bm), prob.block_size, CODE[prob.dtype],
@@ -58,6 +59,9 @@ CASES = [
     ("small", dict(B=2, H=4, N=1000, d=64, dtype="bf16", seed=35, causal=True), 128, 32, 256),
     ("small", dict(B=1, H=4, N=1100, d=128, dtype="fp16", seed=36, block_keep_p=0.5), 128, 128,
      64),
+    # two key groups (chosen automatically for grids this small), d = 128, ragged
+    ("small", dict(B=2, H=2, N=1500, d=128, dtype="bf16", seed=37, causal=True,
+                   key_len_range=(700, 1500)), 0, 0, 0),
 ]
 
 
@@ -89,7 +93,7 @@ def run_split(lib, prob, chunk_blocks):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     common = (prob.B, prob.H, prob.N, prob.d, float(prob.scale), int(prob.causal), None)
     st = lib.fa_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), *common, ptr(bm),
-                           prob.block_size, 0, 0, CODE[prob.dtype], stream)
+                           prob.block_size, 0, 0, 0, CODE[prob.dtype], stream)
     assert st == 0, lib.fa_last_error_detail()
     st = lib.fa_backward_blocksparse_split(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse),
                                            ptr(dq), ptr(dk), ptr(dv), *common, ptr(bm),

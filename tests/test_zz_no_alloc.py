@@ -31,7 +31,7 @@ def both_backwards(lib, prob):
     stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
     common = (prob.B, prob.H, prob.N, prob.d, float(prob.scale), int(prob.causal), ptr(kl))
     assert lib.fa_forward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(lse), *common, ptr(bm),
-                             prob.block_size, 0, 0, CODE[prob.dtype], stream) == 0
+                             prob.block_size, 0, 0, 0, CODE[prob.dtype], stream) == 0
     ref = [torch.full_like(q, float("nan")) for _ in range(3)]
     need = lib.fa_backward_workspace_bytes(prob.B, prob.H, prob.N, prob.d)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
