@@ -13,7 +13,8 @@ import pytest
 import torch
 
 import oracle
-from exact_io_aware_52_amd import (fa_forward, fa_forward_kv, fa_forward_kv_workspace_bytes,
+from exact_io_aware_52_amd import (fa_forward, fa_forward_ex, fa_forward_kv,
+                                   fa_forward_kv_workspace_bytes,
                                    inputs)
 from test_gpu_parity import TOL, compare, dev, log
 
@@ -74,12 +75,13 @@ def test_kv_small(case):
 @pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "fp16"), (64, "fp32")])
 def test_kv_full_cache_equals_self_attention(d, dtype):
     # Nq = Nk with a full cache: bottom-right is top-left, and the same
-    # 128-row kernel runs, so the result is fa_forward's causal result bit
-    # for bit.
+    # 128-row kernel runs, so the result is the causal self-attention
+    # forward's bit for bit (that forward with one key group per tile: a
+    # grid this small otherwise takes two, which add in another order).
     prob = inputs.make_kv_problem(2, 2, 333, 333, d, dtype, seed=41, causal=True)
     q, k, v = (dev(x, dtype) for x in (prob.q, prob.k, prob.v))
     o1, l1 = fa_forward_kv(q, k, v, scale=float(prob.scale), causal=True)
-    o2, l2 = fa_forward(q, k, v, scale=float(prob.scale), causal=True)
+    o2, l2 = fa_forward_ex(q, k, v, scale=float(prob.scale), causal=True, key_groups=1)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(l1, l2)
 
@@ -167,12 +169,14 @@ def test_varlen_rows_outside_sequences_untouched():
 
 @pytest.mark.parametrize("d,dtype", [(64, "bf16"), (128, "fp16")])
 def test_varlen_equal_lengths_equal_batched(d, dtype):
-    # Equal lengths: the packed problem is fa_forward's batched one, bit for bit.
+    # Equal lengths: the packed problem is the batched forward's, bit for bit
+    # (that forward with one key group per tile, as the packed one runs).
     B, H, n = 3, 2, 200
     prob = inputs.make_varlen_problem(H, d, dtype, seed=62, lens_q=[n] * B, causal=True)
     q, k, v = (dev(x, dtype) for x in (prob.q, prob.k, prob.v))
     unpack = lambda t: t.reshape(H, B, n, d).transpose(0, 1).contiguous()
-    o, lse = fa_forward(unpack(q), unpack(k), unpack(v), scale=float(prob.scale), causal=True)
+    o, lse = fa_forward_ex(unpack(q), unpack(k), unpack(v), scale=float(prob.scale), causal=True,
+                           key_groups=1)
     got = run_gpu_varlen(prob)
     ob = o.transpose(0, 1).reshape(H, B * n, d).double().cpu().numpy()
     lb = lse.transpose(0, 1).reshape(H, B * n).double().cpu().numpy()

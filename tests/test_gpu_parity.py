@@ -677,7 +677,8 @@ def test_blocksparse_split(case):
 
 def test_blocksparse_split_edge_cases():
     # key_chunk >= N: one split, no workspace, the unsplit forward's results;
-    # an all-ones block mask through the split path equals the dense forward.
+    # an all-ones block mask through the split path equals the dense forward
+    # (with one key group per tile, as the block-sparse forward runs).
     prob = inputs.make_problem(1, 2, 520, 64, "bf16", seed=503, causal=True)
     q, k, v = (dev(x, "bf16") for x in (prob.q, prob.k, prob.v))
     nb = (520 + 127) // 128
@@ -685,7 +686,7 @@ def test_blocksparse_split_edge_cases():
     kw = dict(scale=float(prob.scale), causal=True)
     o1, l1 = fa_forward_blocksparse_split(q, k, v, ones, 128, key_chunk=1024, **kw)
     o2, l2 = fa_forward_blocksparse_split(q, k, v, ones, 128, key_chunk=192, **kw)
-    od, ld = fa_forward(q, k, v, **kw)
+    od, ld = fa_forward_ex(q, k, v, key_groups=1, **kw)
     torch.cuda.synchronize()
     dense = {"o": od.double().cpu().numpy(), "lse": ld.double().cpu().numpy()}
     one = {"o": o1.double().cpu().numpy(), "lse": l1.double().cpu().numpy()}
