@@ -41,7 +41,7 @@ sys.path.insert(0, ROOT)
 
 from exact_io_aware_52_amd import _binding  # noqa: E402
 from exact_io_aware_52_amd import (accounting, build_lib, fa_backward, fa_backward_ex,  # noqa: E402
-                                   fa_forward_key_groups_for,
+                                   fa_forward_key_groups_for, fa_backward_key_groups_for,
                                    fa_backward_blocksparse_split,
                                    fa_backward_blocksparse_split_workspace_bytes,
                                    fa_backward_dkdv, fa_backward_dq,
@@ -485,8 +485,11 @@ class Runner:
         self.keys = fwd_block_keys
         # Key groups per forward tile (0: the library's choice).
         self.key_groups = key_groups
-        # Backward tile heights (dQ query rows, dK/dV keys per work-group).
+        # Backward tile heights (dQ query rows, dK/dV keys per work-group) and
+        # the key groups the library then chooses.
         self.dq_rows = self.dkdv_rows = bwd_rows
+        self.bwd_kgroups = 1 if bwd_rows not in (0, 128) else fa_backward_key_groups_for(
+            prob.B, prob.H, prob.N, prob.d, dt, prob.block_mask is not None)
         other_keys = fwd_block_keys not in (0, 64)
         if other_keys:
             self.fwd_rows = 128
@@ -783,7 +786,7 @@ def main():
                    "key_padding": prob.key_lens is not None,
                    "block_sparse": prob.block_mask is not None,
                    "fwd_block_rows": run.fwd_rows, "fwd_block_keys": run.keys or 64,
-                   "fwd_key_groups": run.fwd_kgroups,
+                   "fwd_key_groups": run.fwd_kgroups, "bwd_key_groups": run.bwd_kgroups,
                    "bwd_rows": run.dq_rows or 128,
                    "fwd_key_chunk": run.key_chunk or None,
                    "bwd_chunk_blocks": run.chunk_blocks or None,

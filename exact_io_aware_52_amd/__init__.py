@@ -14,7 +14,7 @@ from ._binding import (  # noqa: F401
     fa_forward_blocksparse_split, fa_forward_blocksparse_split_workspace_bytes, fa_backward,
     fa_backward_ex, fa_backward_dq, fa_backward_dkdv, fa_backward_workspace_bytes,
     fa_backward_noalloc, fa_backward_noalloc_max_rows,
-    fa_forward_block_rows_for, fa_forward_key_groups_for,
+    fa_forward_block_rows_for, fa_forward_key_groups_for, fa_backward_key_groups_for,
     fa_backward_blocksparse_split, fa_backward_blocksparse_split_workspace_bytes,
     fa_forward_kv, fa_forward_kv_workspace_bytes, fa_forward_varlen,
 )

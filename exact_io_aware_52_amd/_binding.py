@@ -53,7 +53,8 @@ def open_library(path):
     lib.fa_forward_blocksparse_split_workspace_bytes.restype = Z
     lib.fa_backward.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, P, Z, P]
     lib.fa_backward_ex.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I, I, I,
-                                   I, P, Z, P]
+                                   I, I, P, Z, P]
+    lib.fa_backward_key_groups_for.argtypes = [I, I, I, I, I, I]
     lib.fa_backward_noalloc.argtypes = [P, P, P, P, P, P, P, P, P, I, I, I, I, F, I, P, P, I, I,
                                         P]
     lib.fa_backward_noalloc_max_rows.argtypes = []
@@ -80,8 +81,8 @@ def open_library(path):
     for fn in (lib.fa_forward, lib.fa_forward_blocksparse, lib.fa_forward_blocksparse_split,
                lib.fa_forward_ex, lib.fa_backward, lib.fa_backward_ex, lib.fa_backward_dq,
                lib.fa_backward_dkdv, lib.fa_backward_noalloc,
-               lib.fa_forward_block_rows_for, lib.fa_forward_key_groups_for, lib.fa_forward_kv,
-               lib.fa_forward_varlen):
+               lib.fa_forward_block_rows_for, lib.fa_forward_key_groups_for,
+               lib.fa_backward_key_groups_for, lib.fa_forward_kv, lib.fa_forward_varlen):
         fn.restype = I
     return lib
 
@@ -330,7 +331,7 @@ def fa_backward_workspace_bytes(B, H, N, d):
 
 
 def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, block_size,
-              dq, dk, dv, workspace, grad_dtype=None, dq_rows=0, dkdv_rows=0):
+              dq, dk, dv, workspace, grad_dtype=None, dq_rows=0, dkdv_rows=0, key_groups=0):
     lib = load_library()
     B, H, N, d = _shape(q, k, v)
     _like("dout", dout, q)
@@ -340,7 +341,7 @@ def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, 
     gdt = q.dtype if grad_dtype is None else grad_dtype
     if gdt not in (q.dtype, torch.float32):
         raise ValueError(f"grad_dtype must be {q.dtype} or torch.float32")
-    if name == "fa_backward" and (gdt != q.dtype or dq_rows or dkdv_rows):
+    if name == "fa_backward" and (gdt != q.dtype or dq_rows or dkdv_rows or key_groups):
         name = "fa_backward_ex"
 
     def grad(t, nm):
@@ -362,7 +363,7 @@ def _backward(name, q, k, v, o, dout, lse, scale, causal, key_lens, block_mask, 
     tail = [B, H, N, d, _scale(scale, d), int(bool(causal)), _ptr(kl), _ptr(bm),
             int(block_size), _DTYPE_CODE[q.dtype]]
     if name == "fa_backward_ex":
-        tail += [_DTYPE_CODE[gdt], int(dq_rows), int(dkdv_rows)]
+        tail += [_DTYPE_CODE[gdt], int(dq_rows), int(dkdv_rows), int(key_groups)]
     elif name in ("fa_backward_dq", "fa_backward_dkdv"):
         tail.append(int(dq_rows if name == "fa_backward_dq" else dkdv_rows))
     tail += [_ptr(workspace), workspace.numel() * workspace.element_size(), _stream(q.device)]
@@ -390,13 +391,14 @@ def fa_backward(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
 
 def fa_backward_ex(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=None,
                    block_mask=None, block_size=128, dq=None, dk=None, dv=None, workspace=None,
-                   grad_dtype=None, dq_rows=0, dkdv_rows=0):
-    """Backward with the gradients' dtype (q.dtype or torch.float32) and the
+                   grad_dtype=None, dq_rows=0, dkdv_rows=0, key_groups=0):
+    """Backward with the gradients' dtype (q.dtype or torch.float32), the
     tile sizes (query rows per dQ work-group, keys per dK/dV work-group: 64,
-    128, 256; 0 = 128) given per call: returns (dQ, dK, dV)."""
+    128, 256; 0 = 128) and the key groups (1, 2; 0 = the library's choice)
+    given per call: returns (dQ, dK, dV)."""
     dq, dk, dv, _ = _backward("fa_backward_ex", q, k, v, o, dout, lse, scale, causal, key_lens,
                               block_mask, block_size, dq, dk, dv, workspace, grad_dtype,
-                              dq_rows, dkdv_rows)
+                              dq_rows, dkdv_rows, key_groups)
     return dq, dk, dv
 
 
@@ -497,3 +499,10 @@ def fa_forward_key_groups_for(B, H, N, d, dtype, sparse=False):
     code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(load_library().fa_forward_key_groups_for(int(B), int(H), int(N), int(d), code,
                                                         int(bool(sparse))))
+
+
+def fa_backward_key_groups_for(B, H, N, d, dtype, sparse=False):
+    """Key groups per work-group a backward of these sizes would use."""
+    code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    return int(load_library().fa_backward_key_groups_for(int(B), int(H), int(N), int(d), code,
+                                                         int(bool(sparse))))

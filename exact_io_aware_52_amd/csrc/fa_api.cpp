@@ -57,6 +57,18 @@ int auto_fwd_kgroups(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
   return groups <= kAutoKgroupsMaxGroups ? 2 : 1;
 }
 
+// The backward's two passes: their 4-slot rings already hold them to two
+// 4-wave work-groups per CU, so one 8-wave work-group per CU keeps as many
+// waves and halves the chains.  Measured backward times, key groups 2
+// against 1 (B2 H8, causal): N = 2K -15% (d = 64) and -8% (d = 128, where
+// only the dQ pass splits), N = 4K -4% and +1%; N = 8K +4%, +3%; the GPT-2
+// shape (768 tiles) +26%.  So at most 512 tiles at d = 64, 256 at d = 128.
+int auto_bwd_kgroups(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
+  if (dtype == FA_F32 || sparse) return 1;
+  const long long groups = (long long)B * H * ((N + 127) / 128);
+  return groups <= (d == 64 ? kAutoKgroupsMaxGroups : kAutoKgroupsMaxGroups / 2) ? 2 : 1;
+}
+
 }  // namespace
 
 namespace {
@@ -281,7 +293,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
                   float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
                   int block_size, fa_dtype dtype, void* workspace, size_t workspace_bytes,
                   hipStream_t stream, int passes, fa_dtype grad_dtype, int chunk_blocks = 0,
-                  int dq_rows = 0, int dkdv_rows = 0) {
+                  int dq_rows = 0, int dkdv_rows = 0, int key_groups = 0) {
   g_detail[0] = 0;
   bool empty = false;
   int st = check_common(B, H, N, d, scale, dtype, &empty);
@@ -304,6 +316,16 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
     if (rows == 256 && block_mask)
       return fail(FA_ERR_UNSUPPORTED, "%s=256 with a block mask (at most 128)", name);
   }
+  const bool rows128 = (dq_rows == 0 || dq_rows == 128) && (dkdv_rows == 0 || dkdv_rows == 128);
+  if (key_groups < 0 || key_groups > 2)
+    return fail(FA_ERR_UNSUPPORTED, "key_groups=%d (supported: 0 = automatic, 1, 2)", key_groups);
+  if (key_groups == 2 && (dtype == FA_F32 || block_mask || !rows128 || chunk_blocks > 0))
+    return fail(FA_ERR_UNSUPPORTED, "key_groups=2 takes 16-bit dense problems with 128-row "
+                "tiles");
+  const int kgroups = key_groups ? key_groups
+                      : rows128 && chunk_blocks == 0
+                          ? auto_bwd_kgroups(B, H, N, d, dtype, block_mask != nullptr)
+                          : 1;
   if ((st = check_block(block_mask, block_size, N, false)) != FA_OK) return st;
   if (empty) return FA_OK;
   const bool pdq = (passes & fa::kPassDq) != 0, pkv = (passes & fa::kPassDkDv) != 0;
@@ -327,6 +349,7 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   p.grad_f32 = grad_dtype == FA_F32 && dtype != FA_F32;
   p.bwd_dq_rows = dq_rows ? dq_rows : 128;
   p.bwd_dkdv_rows = dkdv_rows ? dkdv_rows : 128;
+  p.bwd_kgroups = kgroups;
   if (chunk_blocks > 0) {
     const size_t base = fa_backward_workspace_bytes(B, H, N, d);
     const size_t part = bwd_split_part_bytes(B, H, N, d, chunk_blocks);
@@ -485,6 +508,10 @@ int fa_forward_key_groups_for(int B, int H, int N, int d, fa_dtype dtype, int sp
   return auto_fwd_kgroups(B, H, N, d, dtype, sparse != 0);
 }
 
+int fa_backward_key_groups_for(int B, int H, int N, int d, fa_dtype dtype, int sparse) {
+  return auto_bwd_kgroups(B, H, N, d, dtype, sparse != 0);
+}
+
 size_t fa_backward_workspace_bytes(int B, int H, int N, int d) {
   if (B <= 0 || H <= 0 || N <= 0 || d <= 0) return 0;
   return round_up(2 * (size_t)B * H * N * sizeof(float), 256);
@@ -504,10 +531,11 @@ int fa_backward_ex(const void* q, const void* k, const void* v, const void* o, c
                    const float* lse, void* dq, void* dk, void* dv, int B, int H, int N, int d,
                    float scale, int causal, const int32_t* key_lens, const uint8_t* block_mask,
                    int block_size, fa_dtype dtype, fa_dtype grad_dtype, int dq_rows,
-                   int dkdv_rows, void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                   int dkdv_rows, int key_groups, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream) {
   return backward_impl(q, k, v, o, dout, lse, dq, dk, dv, B, H, N, d, scale, causal, key_lens,
                        block_mask, block_size, dtype, workspace, workspace_bytes, stream,
-                       fa::kPassBoth, grad_dtype, 0, dq_rows, dkdv_rows);
+                       fa::kPassBoth, grad_dtype, 0, dq_rows, dkdv_rows, key_groups);
 }
 
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* o, const void* dout,

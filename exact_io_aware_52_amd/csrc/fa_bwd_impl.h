@@ -182,25 +182,35 @@ struct DkDvCfg {
 // GF32: store dK, dV as float32 (16-bit inputs; an option for exact
 // comparisons, compiled as separate instances so that the usual instances'
 // register allocation is untouched).
-template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4>
+//
+// KG = 2 (dense problems at d = 64, chosen by the caller): the NW waves form
+// two key groups of NW / 2 that share the keys and sweep the first and
+// second half of the query tiles, each through its own ring; group 1 adds
+// its dK, dV accumulators into group 0's through LDS.
+template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4, int KG = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
-    DkDvCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
+    DkDvCfg<T, D, NW / KG>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
+  static_assert(KG == 1 || (KG == 2 && !SPLIT), "key groups: unsplit passes");
+  constexpr int RW = NW / KG;  // waves per key group (32 keys each)
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef DkDvCfg<T, D, NW> L;
+  typedef DkDvCfg<T, D, RW> L;
   constexpr int BQ = L::BQ;
-  constexpr int BK = 32 * NW;  // keys of this work-group (at most one mask block)
+  constexpr int BK = 32 * RW;  // keys of this work-group (at most one mask block)
   static_assert(BK <= kMaskBlock || !SPLIT, "split columns come in whole mask blocks");
   constexpr int LPT = L::LPT;
 
-  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[KG * L::NS * L::SLOT_BYTES];
   __shared__ uint8_t mask_col[kMaxMaskBlocks];
-  const uint32_t ring_lds = lds_addr(ring);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kgrp = KG > 1 ? wg_wave / RW : 0;        // key group of this wave
+  const int w = KG > 1 ? wg_wave % RW : wg_wave;     // key wave within the group
+  char* const gring = ring + kgrp * L::NS * L::SLOT_BYTES;  // this group's ring
+  const uint32_t ring_lds = lds_addr(gring);
   const int col = lane & 31;
   const int hh = lane >> 5;
   const int N = p.N;
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     return t;
   };
 
-  DmaPlan<raw, BQ, D, kBoth, NW> plan;
+  DmaPlan<raw, BQ, D, kBoth, RW> plan;  // (a key group copies its own tiles)
   plan.init(w, lane);
   // Q, dO rows of tile t, plus (waves 0 and 1) its LSE2 and D words.
   auto issue = [&](int t, int s) {
@@ -450,7 +460,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         }
     }
   };
-  auto slot_of = [&](int s) { return ring + (s & 3) * L::SLOT_BYTES; };
+  auto slot_of = [&](int s) { return gring + (s & 3) * L::SLOT_BYTES; };
   // Query tile t reaches this wave's keys (under a causal mask the first
   // tiles may not; once a tile does, every later one does).
   auto active = [&](int t) { return !p.causal || kw0 <= t * BQ + BQ - 1; };
@@ -567,16 +577,28 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   // The split instances (long sparse masks, whose tiles come from HBM rather
   // than L2) request tiles three steps ahead, using the ring's fourth slot;
   // the others two.
+  //
+  // This key group's query tiles [tb, te): all of [t_begin, t_end), or its
+  // first or second half (the first group takes the extra tile of an odd
+  // count).  With two key groups the loop's condition is the work-group's,
+  // and both groups take the first group's number of steps, so that their
+  // barriers pair up; a group past its last tile only joins the barriers.
+  int tb = t_begin, te = t_end;
+  if constexpr (KG > 1) {
+    const int tmid = t_begin + (t_end - t_begin + 1) / 2;
+    tb = kgrp ? tmid : t_begin;
+    te = kgrp ? t_end : tmid;
+  }
   constexpr bool LA3 = SPLIT;
   int tl[4];
-  tl[0] = t_begin < t_end ? next_kept(t_begin) : t_end;
-  tl[1] = tl[0] < t_end ? next_kept(tl[0] + 1) : t_end;
-  tl[2] = tl[1] < t_end ? next_kept(tl[1] + 1) : t_end;
-  tl[3] = LA3 && tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
-  if (tl[0] < t_end) {
-    issue(tl[0], 0);
-    if (tl[1] < t_end) issue(tl[1], 1);
-    if (LA3 && tl[2] < t_end) issue(tl[2], 2);
+  tl[0] = tb < te ? next_kept(tb) : te;
+  tl[1] = tl[0] < te ? next_kept(tl[0] + 1) : te;
+  tl[2] = tl[1] < te ? next_kept(tl[1] + 1) : te;
+  tl[3] = LA3 && tl[2] < te ? next_kept(tl[2] + 1) : te;
+  if (KG > 1 ? t_begin < t_end : tl[0] < te) {
+    if (tl[0] < te) issue(tl[0], 0);
+    if (tl[1] < te) issue(tl[1], 1);
+    if (LA3 && tl[2] < te) issue(tl[2], 2);
     FA_STAGE_FENCE();
     // The K and V fragments arrived by ordinary loads issued before these
     // copies.  Waiting for everything once here tells the compiler they have
@@ -586,15 +608,19 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     wait_vmcnt<0>();
     // Dense interior: every wave's keys see tile t in full, and tiles t+1,
     // t+2 are whole.
-    int lo = t_end, hi = -1;
+    int lo = te, hi = -1;
     if (!sparse && j0 + BK <= kend) {
-      lo = p.causal ? (j0 + BK - 1 + BQ - 1) / BQ : t_begin;
-      hi = min(N / BQ - 3, t_end - 3);
+      lo = p.causal ? (j0 + BK - 1 + BQ - 1) / BQ : tb;
+      hi = min(N / BQ - 3, te - 3);
     }
+    const int steps = KG > 1 ? (t_end - t_begin + 1) / 2 : 0;
     int step = 0;
     while (true) {
       const int t = tl[0];
-      if (t >= lo && t <= hi) {
+      if (KG > 1 && t >= te) {
+        __syncthreads();  // (the step's one barrier)
+        FA_STAGE_FENCE();
+      } else if (t >= lo && t <= hi) {
         wait_tiles(1);    // tile t landed; t+1 may be in flight
         __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
         const uint32_t base = ring_lds + ((step + 2) & 3) * L::SLOT_BYTES;
@@ -620,16 +646,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         }
         tl[0] = t + 1;
         tl[1] = t + 2;
-        tl[2] = min(t + 3, t_end);
+        tl[2] = min(t + 3, te);
       } else {
         if constexpr (LA3) {
-          wait_tiles((tl[1] < t_end) + (tl[2] < t_end));  // tile t landed
+          wait_tiles((tl[1] < te) + (tl[2] < te));  // tile t landed
           __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
-          if (tl[3] < t_end) issue(tl[3], (step + 3) & 3);
+          if (tl[3] < te) issue(tl[3], (step + 3) & 3);
         } else {
-          wait_tiles(tl[1] < t_end ? 1 : 0);  // tile t landed; tl[1] may be in flight
+          wait_tiles(tl[1] < te ? 1 : 0);  // tile t landed; tl[1] may be in flight
           __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
-          if (tl[2] < t_end) issue(tl[2], (step + 2) & 3);
+          if (tl[2] < te) issue(tl[2], (step + 2) & 3);
         }
         FA_STAGE_FENCE();
         if (active(t)) {
@@ -648,14 +674,42 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
         tl[1] = tl[2];
         if constexpr (LA3) {
           tl[2] = tl[3];
-          tl[3] = tl[3] < t_end ? next_kept(tl[3] + 1) : t_end;
+          tl[3] = tl[3] < te ? next_kept(tl[3] + 1) : te;
         } else {
-          tl[2] = tl[2] < t_end ? next_kept(tl[2] + 1) : t_end;
+          tl[2] = tl[2] < te ? next_kept(tl[2] + 1) : te;
         }
       }
       FA_STAGE_FENCE();
       ++step;
-      if (tl[0] >= t_end) break;
+      if (KG > 1 ? step >= steps : tl[0] >= te) break;
+    }
+  }
+  if constexpr (KG > 1) {
+    // Key group 1 adds its dK, dV accumulators into group 0's through the
+    // idle rings, lane for lane; group 0 alone stores them (group 1 stays for
+    // the staged store's barriers).
+    constexpr int XF = 2 * (D / 32) * 16;
+    static_assert(RW * XF * 64 * 4 <= KG * L::NS * L::SLOT_BYTES, "hand-over fits in the rings");
+    float* const xs = reinterpret_cast<float*>(ring) + w * XF * 64;
+    __syncthreads();  // every wave is done with both rings
+    if (kgrp == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          xs[(db * 16 + r) * 64 + lane] = dk_acc[db][r];
+          xs[((D / 32 + db) * 16 + r) * 64 + lane] = dv_acc[db][r];
+        }
+    }
+    __syncthreads();
+    if (kgrp == 0) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          dk_acc[db][r] += xs[(db * 16 + r) * 64 + lane];
+          dv_acc[db][r] += xs[((D / 32 + db) * 16 + r) * 64 + lane];
+        }
     }
   }
 
@@ -693,7 +747,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   // complete rows.  With float32 gradients requested (an option for exact
   // comparisons, not a fast path), each lane stores its fp32 values directly.
   if constexpr (GF32) {
-    if (myk < N) {
+    if (myk < N && kgrp == 0) {
       float* const dkg = reinterpret_cast<float*>(p.dk) + head + (size_t)myk * D;
       float* const dvg = reinterpret_cast<float*>(p.dv) + head + (size_t)myk * D;
 #pragma unroll
@@ -715,29 +769,32 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     constexpr int RS = RB + 16;               // padded LDS row stride
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;             // rows per store instruction
-    static_assert(NW * 32 * RS <= L::NS * L::SLOT_BYTES, "staging fits in the ring");
+    static_assert(RW * 32 * RS <= L::NS * L::SLOT_BYTES, "staging fits in the ring");
     char* const stage = ring + w * 32 * RS;
+    // (with two key groups, group 0 stores; group 1 joins the barriers)
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       __syncthreads();  // no wave reads the ring (or the previous tensor) any more
+      if (kgrp == 0) {
 #pragma unroll
-      for (int db = 0; db < D / 32; ++db)
+        for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          raw4 r4;
+          for (int g = 0; g < 4; ++g) {
+            raw4 r4;
 #pragma unroll
-          for (int u = 0; u < 4; ++u)
-            r4[u] = __builtin_bit_cast(raw, t == 0 ? (T)(dk_acc[db][4 * g + u] * p.scale)
-                                                   : (T)dv_acc[db][4 * g + u]);
-          *reinterpret_cast<raw4*>(stage + col * RS + (db * 32 + 8 * g + 4 * hh) * (int)sizeof(raw)) =
-              r4;
-        }
+            for (int u = 0; u < 4; ++u)
+              r4[u] = __builtin_bit_cast(raw, t == 0 ? (T)(dk_acc[db][4 * g + u] * p.scale)
+                                                     : (T)dv_acc[db][4 * g + u]);
+            *reinterpret_cast<raw4*>(stage + col * RS +
+                                     (db * 32 + 8 * g + 4 * hh) * (int)sizeof(raw)) = r4;
+          }
+      }
       __syncthreads();
       char* const out = reinterpret_cast<char*>(t == 0 ? p.dk : p.dv) + head * sizeof(raw);
 #pragma unroll
       for (int r0 = 0; r0 < 32; r0 += RPI) {
         const int r = r0 + lane / CPR, c = lane % CPR;
-        if (kw0 + r < N)
+        if (kgrp == 0 && kw0 + r < N)
           *reinterpret_cast<uint4*>(out + (size_t)(kw0 + r) * RB + c * 16) =
               *reinterpret_cast<const uint4*>(stage + r * RS + c * 16);
       }
@@ -765,26 +822,34 @@ struct DqCfg {
 };
 
 // Work-group: NW waves x 32 queries (4 by default; 2 and 8 are a tile-size
-// option); key tiles of BC rows.
-template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4>
+// option); key tiles of BC rows.  KG = 2 (dense problems, chosen by the
+// caller): the NW waves form two key groups of NW / 2 that share the query
+// rows and sweep the first and second half of the key tiles, each through
+// its own ring; group 1 adds its dQ accumulator into group 0's through LDS.
+template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4, int KG = 1>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
-    DqCfg<T, D, NW>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
+    DqCfg<T, D, NW / KG>::WAVES_PER_SIMD))) void fa_bwd_dq_kernel(BwdParams p) {
+  static_assert(KG == 1 || (KG == 2 && !SPLIT), "key groups: unsplit passes");
+  constexpr int RW = NW / KG;  // waves per key group (32 query rows each)
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef DqCfg<T, D, NW> L;
+  typedef DqCfg<T, D, RW> L;
   constexpr int BC = L::BC;
-  constexpr int BR = 32 * NW;  // queries of this work-group (at most one mask block)
+  constexpr int BR = 32 * RW;  // queries of this work-group (at most one mask block)
   static_assert(BR <= kMaskBlock || !SPLIT, "split rows come in whole mask blocks");
   constexpr int LPT = L::LPT;
 
-  __shared__ __attribute__((aligned(1024))) char ring[L::NS * L::SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[KG * L::NS * L::SLOT_BYTES];
   __shared__ uint8_t mask_row[kMaxMaskBlocks];
-  const uint32_t ring_lds = lds_addr(ring);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wg_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kgrp = KG > 1 ? wg_wave / RW : 0;        // key group of this wave
+  const int w = KG > 1 ? wg_wave % RW : wg_wave;     // row wave within the group
+  char* const gring = ring + kgrp * L::NS * L::SLOT_BYTES;  // this group's ring
+  const uint32_t ring_lds = lds_addr(gring);
   const int col = lane & 31;
   const int hh = lane >> 5;
   const int N = p.N;
@@ -842,7 +907,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     lse2 = l == kNegInf ? __builtin_inff() : l * kLog2e;
   }
   const float dneg = -pair_sum(part);  // -D
-  if (myq < N && hh == 0 && (!SPLIT || blockIdx.y == 0)) {
+  if (myq < N && hh == 0 && (!SPLIT || blockIdx.y == 0) && kgrp == 0) {
     p.dvec[(size_t)bh * N + myq] = dneg;
     p.lse2[(size_t)bh * N + myq] = lse2;
   }
@@ -877,8 +942,8 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) dq_acc[db] = zero16();
 
-  DmaPlan<raw, BC, D, kBoth, NW> kplan;
-  DmaPlan<raw, BC, D, kRows, NW> vplan;
+  DmaPlan<raw, BC, D, kBoth, RW> kplan;  // (a key group copies its own tiles)
+  DmaPlan<raw, BC, D, kRows, RW> vplan;
   kplan.init(w, lane);
   vplan.init(w, lane);
   auto issue = [&](int t, int s) {
@@ -970,48 +1035,81 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
+  // This key group's tiles [tb, te): all of [kt_first, nkt), or its first or
+  // second half (the first group takes the extra tile of an odd count).
+  int tb = kt_first, te = nkt;
+  if constexpr (KG > 1) {
+    const int tmid = kt_first + (nkt - kt_first + 1) / 2;
+    tb = kgrp ? tmid : kt_first;
+    te = kgrp ? nkt : tmid;
+  }
   // As in the dK/dV pass: three tiles ahead in the split instances.
   constexpr bool LA3 = SPLIT;
   int tl[4];
-  tl[0] = kt_first < nkt ? next_kept(kt_first) : nkt;
-  tl[1] = tl[0] < nkt ? next_kept(tl[0] + 1) : nkt;
-  tl[2] = tl[1] < nkt ? next_kept(tl[1] + 1) : nkt;
-  tl[3] = LA3 && tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
-  if (tl[0] < nkt) {
-    issue(tl[0], 0);
-    if (tl[1] < nkt) issue(tl[1], 1);
-    if (tl[2] < nkt) issue(tl[2], 2);
-    if (LA3 && tl[3] < nkt) issue(tl[3], 3);
+  tl[0] = tb < te ? next_kept(tb) : te;
+  tl[1] = tl[0] < te ? next_kept(tl[0] + 1) : te;
+  tl[2] = tl[1] < te ? next_kept(tl[1] + 1) : te;
+  tl[3] = LA3 && tl[2] < te ? next_kept(tl[2] + 1) : te;
+  // (With two key groups the condition is the work-group's, and both groups
+  // take the first group's number of steps, so that their barriers pair up;
+  // a group past its last tile only joins the barriers.)
+  if (KG > 1 ? kt_first < nkt : tl[0] < te) {
+    if (tl[0] < te) issue(tl[0], 0);
+    if (tl[1] < te) issue(tl[1], 1);
+    if (tl[2] < te) issue(tl[2], 2);
+    if (LA3 && tl[3] < te) issue(tl[3], 3);
     FA_STAGE_FENCE();
     // As in the dK/dV pass: the Q and dO fragments came by ordinary loads;
     // wait for them here, once, rather than inside the loop.
     wait_vmcnt<0>();
+    const int steps = KG > 1 ? (nkt - kt_first + 1) / 2 : 0;
     int step = 0;
     while (true) {
       if constexpr (LA3) {
-        wait_tiles((tl[1] < nkt) + (tl[2] < nkt));
+        wait_tiles((tl[1] < te) + (tl[2] < te));
         __syncthreads();  // every wave is done with step i-1
-        if (step > 0 && tl[3] < nkt) issue(tl[3], (step + 3) & 3);
+        if (step > 0 && tl[3] < te) issue(tl[3], (step + 3) & 3);
       } else {
-        wait_tiles((tl[1] < nkt) + (step == 0 && tl[2] < nkt));
+        wait_tiles((tl[1] < te) + (step == 0 && tl[2] < te));
         __syncthreads();  // every wave is done with step i-1
-        if (step > 0 && tl[2] < nkt) issue(tl[2], (step + 2) & 3);
+        if (step > 0 && tl[2] < te) issue(tl[2], (step + 2) & 3);
       }
       FA_STAGE_FENCE();
       const int kt0 = tl[0] * BC;
-      if (!p.causal || kt0 <= qw0 + 31) step_math(ring + (step & 3) * L::SLOT_BYTES, kt0);
+      if ((KG == 1 || tl[0] < te) && (!p.causal || kt0 <= qw0 + 31))
+        step_math(gring + (step & 3) * L::SLOT_BYTES, kt0);
       tl[0] = tl[1];
       tl[1] = tl[2];
       if constexpr (LA3) {
         tl[2] = tl[3];
-        tl[3] = tl[3] < nkt ? next_kept(tl[3] + 1) : nkt;
+        tl[3] = tl[3] < te ? next_kept(tl[3] + 1) : te;
       } else {
-        tl[2] = tl[2] < nkt ? next_kept(tl[2] + 1) : nkt;
+        tl[2] = tl[2] < te ? next_kept(tl[2] + 1) : te;
       }
       FA_STAGE_FENCE();
       ++step;
-      if (tl[0] >= nkt) break;
+      if (KG > 1 ? step >= steps : tl[0] >= te) break;
     }
+  }
+  if constexpr (KG > 1) {
+    // Key group 1 adds its dQ accumulator into group 0's through the idle
+    // rings, lane for lane; group 0 alone stores.
+    constexpr int XF = D / 32 * 16;
+    static_assert(RW * XF * 64 * 4 <= KG * L::NS * L::SLOT_BYTES, "hand-over fits in the rings");
+    float* const xs = reinterpret_cast<float*>(ring) + w * XF * 64;
+    __syncthreads();  // every wave is done with both rings
+    if (kgrp == 1) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xs[(db * 16 + r) * 64 + lane] = dq_acc[db][r];
+    }
+    __syncthreads();
+    if (kgrp == 1) return;  // (no barrier follows)
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dq_acc[db][r] += xs[(db * 16 + r) * 64 + lane];
   }
 
   if (SPLIT && multi) {
@@ -1118,18 +1216,20 @@ __global__ __launch_bounds__(256) void fa_bwd_split_reduce_kernel(BwdParams p) {
 
 // SPLIT: the split instances, launched with one work-group per item
 // (gridDim.y = pb.split_items), each pass followed by its reduce kernel.
-// One pass with NW waves (32 NW rows) per work-group.
-template <typename T, int D, bool GF32, bool SPLIT, int NW>
+// One pass with NW waves in KG key groups (32 NW / KG rows) per work-group.
+template <typename T, int D, bool GF32, bool SPLIT, int NW, int KG = 1>
 hipError_t launch_dq_pass(const BwdParams& p, const Problem& pb, unsigned items) {
-  const unsigned tiles = (unsigned)((pb.N + 32 * NW - 1) / (32 * NW));
-  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32, SPLIT, NW>), dim3(tiles * p.BH, items),
+  constexpr int BR = 32 * NW / KG;
+  const unsigned tiles = (unsigned)((pb.N + BR - 1) / BR);
+  hipLaunchKernelGGL((fa_bwd_dq_kernel<T, D, GF32, SPLIT, NW, KG>), dim3(tiles * p.BH, items),
                      dim3(64 * NW), 0, pb.stream, p);
   return hipGetLastError();
 }
-template <typename T, int D, bool GF32, bool SPLIT, int NW>
+template <typename T, int D, bool GF32, bool SPLIT, int NW, int KG = 1>
 hipError_t launch_dkdv_pass(const BwdParams& p, const Problem& pb, unsigned items) {
-  const unsigned tiles = (unsigned)((pb.N + 32 * NW - 1) / (32 * NW));
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT, NW>), dim3(tiles * p.BH, items),
+  constexpr int BK = 32 * NW / KG;
+  const unsigned tiles = (unsigned)((pb.N + BK - 1) / BK);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT, NW, KG>), dim3(tiles * p.BH, items),
                      dim3(64 * NW), 0, pb.stream, p);
   return hipGetLastError();
 }
@@ -1169,16 +1269,21 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   }
   const unsigned items = SPLIT ? (unsigned)pb.split_items : 1u;
   hipError_t e = hipSuccess;
-  // Other tile heights than 128 rows: 16-bit inputs and gradients, unsplit
-  // (checked by the caller).
-  constexpr bool kRowsOption = sizeof(T) == 2 && !GF32 && !SPLIT;
+  // Run-time choices among the unsplit 16-bit instances (checked by the
+  // caller): two key groups (128 rows; the dK/dV pass only at d = 64, where
+  // its per-wave state leaves room for two waves per SIMD), or other tile
+  // heights than 128 rows (gradients in the input type).
+  const bool two_groups = pb.bwd_kgroups == 2;
   if (pb.bwd_passes & kPassDq) {
-    if constexpr (kRowsOption) {
-      e = pb.bwd_dq_rows == 64    ? launch_dq_pass<T, D, false, false, 2>(p, pb, items)
-          : pb.bwd_dq_rows == 256 ? launch_dq_pass<T, D, false, false, 8>(p, pb, items)
-                                  : launch_dq_pass<T, D, false, false, 4>(p, pb, items);
-    } else {
+    if constexpr (SPLIT || sizeof(T) == 4) {
       e = launch_dq_pass<T, D, GF32, SPLIT, 4>(p, pb, items);
+    } else if (two_groups) {
+      e = launch_dq_pass<T, D, GF32, false, 8, 2>(p, pb, items);
+    } else if (GF32 || pb.bwd_dq_rows == 128) {
+      e = launch_dq_pass<T, D, GF32, false, 4>(p, pb, items);
+    } else {
+      e = pb.bwd_dq_rows == 64 ? launch_dq_pass<T, D, false, false, 2>(p, pb, items)
+                               : launch_dq_pass<T, D, false, false, 8>(p, pb, items);
     }
     if (e != hipSuccess) return e;
     if constexpr (SPLIT) {
@@ -1189,12 +1294,15 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
     }
   }
   if (pb.bwd_passes & kPassDkDv) {
-    if constexpr (kRowsOption) {
-      e = pb.bwd_dkdv_rows == 64    ? launch_dkdv_pass<T, D, false, false, 2>(p, pb, items)
-          : pb.bwd_dkdv_rows == 256 ? launch_dkdv_pass<T, D, false, false, 8>(p, pb, items)
-                                    : launch_dkdv_pass<T, D, false, false, 4>(p, pb, items);
-    } else {
+    if constexpr (SPLIT || sizeof(T) == 4) {
       e = launch_dkdv_pass<T, D, GF32, SPLIT, 4>(p, pb, items);
+    } else if (two_groups && D == 64) {
+      if constexpr (D == 64) e = launch_dkdv_pass<T, D, GF32, false, 8, 2>(p, pb, items);
+    } else if (GF32 || pb.bwd_dkdv_rows == 128) {
+      e = launch_dkdv_pass<T, D, GF32, false, 4>(p, pb, items);
+    } else {
+      e = pb.bwd_dkdv_rows == 64 ? launch_dkdv_pass<T, D, false, false, 2>(p, pb, items)
+                                 : launch_dkdv_pass<T, D, false, false, 8>(p, pb, items);
     }
     if (e != hipSuccess) return e;
     if constexpr (SPLIT) {

@@ -40,6 +40,7 @@ struct Problem {
   int grad_f32 = 0;            // backward, 16-bit inputs: float32 dQ, dK, dV
   int bwd_dq_rows = 128;       // backward: query rows per dQ work-group (64, 128, 256)
   int bwd_dkdv_rows = 128;     // backward: keys per dK/dV work-group (64, 128, 256)
+  int bwd_kgroups = 1;         // backward: wave groups splitting each tile's sweep (1, 2)
   // Block-sparse backward split by kept mask blocks (chunk_blocks > 0): items
   // of chunk_blocks kept blocks per mask row (dQ) or column (dK, dV), at most
   // split_items per tile; fp32 partials [split_items][B*H][N][d] each.

@@ -210,13 +210,31 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
  *               FA_ERR_UNSUPPORTED.  Results agree to rounding for every
  *               value (the accumulation order over tiles is unchanged, so
  *               they are in fact bitwise equal).
+ *   key_groups  groups of waves per work-group that split each tile's sweep
+ *               (the dQ pass's key tiles, the dK/dV pass's query tiles) in
+ *               halves and add their partial gradients on chip: 1, 2, or 0
+ *               to let the library choose (fa_backward_key_groups_for; with
+ *               128-row tiles only).  2 takes 16-bit inputs, no block mask
+ *               and 128-row tiles, else FA_ERR_UNSUPPORTED; the dK/dV pass
+ *               keeps one group at d = 128 (its per-wave state needs a
+ *               SIMD's registers).  Results agree to rounding (the halves
+ *               are added in another order).
  */
 int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
                    int B, int H, int N, int d, float scale, int causal,
                    const int32_t* key_lens, const uint8_t* block_mask, int block_size,
                    fa_dtype dtype, fa_dtype grad_dtype, int dq_rows, int dkdv_rows,
-                   void* workspace, size_t workspace_bytes, hipStream_t stream);
+                   int key_groups, void* workspace, size_t workspace_bytes,
+                   hipStream_t stream);
+
+/*
+ * Key groups (see fa_backward_ex) that a backward of these sizes uses when
+ * key_groups is 0 and the tiles are 128 rows: 2 for 16-bit dense problems
+ * whose grid holds at most 512 tiles at d = 64 (two per compute unit) or 256
+ * at d = 128 (where only the dQ pass splits), else 1.  Host arithmetic only.
+ */
+int fa_backward_key_groups_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
 
 /*
  * The two passes of fa_backward, for callers that schedule them separately
@@ -231,7 +249,8 @@ int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
  *                     since).  It may be called again on that workspace.
  *   rows              the pass's tile height: dq_rows or dkdv_rows of
  *                     fa_backward_ex (0 = 128), under the same rules; the
- *                     workspace does not depend on it.
+ *                     workspace does not depend on it.  Key groups as
+ *                     fa_backward_ex with key_groups 0.
  * Other arguments, validation and errors as fa_backward.
  */
 int fa_backward_dq(const void* q, const void* k, const void* v, const void* o,

@@ -206,46 +206,73 @@ int main() {
                          FA_BF16, 0, a, bw, nullptr) == FA_ERR_INVALID_ARG);
   // ---- float32 gradients for 16-bit inputs
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_F32, 0, 0, a, bw, nullptr) == FA_OK);
+                       FA_BF16, FA_F32, 0, 0, 0, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 1 && g_last.bwd_passes == fa::kPassBoth);
   CHECK(g_last.bwd_dq_rows == 128 && g_last.bwd_dkdv_rows == 128);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_BF16, 0, 0, a, bw, nullptr) == FA_OK);
+                       FA_BF16, FA_BF16, 0, 0, 0, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 0);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_F16, 0, 0, a, bw, nullptr) == FA_ERR_INVALID_ARG);
+                       FA_BF16, FA_F16, 0, 0, 0, a, bw, nullptr) == FA_ERR_INVALID_ARG);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_F32, FA_F32, 0, 0, a, bw, nullptr) == FA_OK);
+                       FA_F32, FA_F32, 0, 0, 0, a, bw, nullptr) == FA_OK);
   CHECK(g_last.grad_f32 == 0);  // float32 inputs: float32 gradients already
   // ---- backward tile sizes: 64, 128, 256 rows per work-group of each pass
   for (int dqr : {0, 64, 128, 256})
     for (int kvr : {0, 64, 128, 256}) {
       CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr,
-                           128, FA_F16, FA_F16, dqr, kvr, a, bw, nullptr) == FA_OK);
+                           128, FA_F16, FA_F16, dqr, kvr, 0, a, bw, nullptr) == FA_OK);
       CHECK(g_last.bwd_dq_rows == (dqr ? dqr : 128) && g_last.bwd_dkdv_rows == (kvr ? kvr : 128));
     }
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_BF16, 32, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+                       FA_BF16, FA_BF16, 32, 0, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_BF16, 0, 512, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+                       FA_BF16, FA_BF16, 0, 512, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_BF16, FA_F32, 64, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+                       FA_BF16, FA_F32, 64, 0, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_F32, FA_F32, 0, 256, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+                       FA_F32, FA_F32, 0, 256, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
   CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
-                       FA_F32, FA_F32, 128, 128, a, bw, nullptr) == FA_OK);
+                       FA_F32, FA_F32, 128, 128, 0, a, bw, nullptr) == FA_OK);
   {
     const uint8_t* bmk = static_cast<const uint8_t*>(a);
     CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
-                         FA_BF16, FA_BF16, 64, 64, a, bw, nullptr) == FA_OK);
+                         FA_BF16, FA_BF16, 64, 64, 0, a, bw, nullptr) == FA_OK);
     CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
-                         FA_BF16, FA_BF16, 256, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+                         FA_BF16, FA_BF16, 256, 0, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
     CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
-                         FA_BF16, FA_BF16, 0, 256, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+                         FA_BF16, FA_BF16, 0, 256, 0, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  }
+  // ---- backward key groups: automatic for 16-bit dense grids of at most 512 tiles
+  CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                    FA_BF16, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_kgroups == 2);
+  CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                    FA_F32, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_kgroups == 1);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_F32, 0, 0, 0, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_kgroups == 2 && g_last.grad_f32 == 1);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_BF16, 64, 0, 0, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_kgroups == 1);  // another height: one group
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_BF16, 0, 0, 1, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_kgroups == 1);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_BF16, FA_BF16, 128, 0, 2, a, bw, nullptr) == FA_OK);
+  CHECK(g_last.bwd_kgroups == 2);
+  CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                       FA_F32, FA_F32, 0, 0, 2, a, bw, nullptr) == FA_ERR_UNSUPPORTED);
+  {
+    const uint8_t* bmk = static_cast<const uint8_t*>(a);
+    CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
+                      FA_BF16, a, bw, nullptr) == FA_OK);
+    CHECK(g_last.bwd_kgroups == 1);
   }
   // (the sizes are checked before anything else is read, empty problems too)
   CHECK(fa_backward_ex(nullptr, a, a, a, a, f, a, a, a, 0, 3, 100, 64, 0.1f, 1, nullptr, nullptr,
-                       128, FA_BF16, FA_BF16, 96, 0, nullptr, 0, nullptr) == FA_ERR_UNSUPPORTED);
+                       128, FA_BF16, FA_BF16, 96, 0, 0, nullptr, 0, nullptr) == FA_ERR_UNSUPPORTED);
   // ---- allocation-free backward: the library's device scratch, size-limited
   const size_t max_rows = fa_backward_noalloc_max_rows();
   CHECK(max_rows == (size_t(16) << 20) / 8);

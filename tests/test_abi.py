@@ -137,10 +137,10 @@ def test_backward_validation(lib):
     assert bwd(lib, d=80) == _binding.FA_ERR_UNSUPPORTED
 
 
-def bwd_ex(lib, dq_rows, dkdv_rows, dtype=1, gdtype=None, bm=None, dq=FAKE, B=2):
+def bwd_ex(lib, dq_rows, dkdv_rows, dtype=1, gdtype=None, bm=None, dq=FAKE, B=2, kg=0):
     return lib.fa_backward_ex(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, dq, FAKE, FAKE, B, 3, 100, 64,
                               0.1, 1, None, bm, 128, dtype, dtype if gdtype is None else gdtype,
-                              dq_rows, dkdv_rows, FAKE, 1 << 30, None)
+                              dq_rows, dkdv_rows, kg, FAKE, 1 << 30, None)
 
 
 def test_backward_ex_tile_rows_validation(lib):
@@ -170,6 +170,29 @@ def test_backward_ex_tile_rows_validation(lib):
     # empty problem: the sizes are still checked, nothing else is
     assert bwd_ex(lib, 96, 0, B=0) == _binding.FA_ERR_UNSUPPORTED
     assert bwd_ex(lib, 256, 64, B=0, dq=None) == _binding.FA_OK
+
+
+def test_backward_ex_key_groups_validation(lib):
+    for bad in (-1, 3):
+        assert bwd_ex(lib, 0, 0, kg=bad) == _binding.FA_ERR_UNSUPPORTED
+        assert "key_groups" in detail(lib)
+    for dtype in (1, 2):
+        for kg in (0, 1, 2):
+            for gd in (dtype, 0):  # 16-bit or float32 gradients
+                assert bwd_ex(lib, 0, 128, dtype=dtype, gdtype=gd, kg=kg, dq=None) == \
+                    _binding.FA_ERR_INVALID_ARG
+    assert bwd_ex(lib, 0, 0, dtype=0, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert bwd_ex(lib, 0, 0, bm=FAKE, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert bwd_ex(lib, 64, 0, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert bwd_ex(lib, 0, 256, kg=2) == _binding.FA_ERR_UNSUPPORTED
+    assert "key_groups=2" in detail(lib)
+    # other heights keep one group when the library chooses
+    assert bwd_ex(lib, 64, 256, kg=0, dq=None) == _binding.FA_ERR_INVALID_ARG
+    kg_for = lib.fa_backward_key_groups_for
+    assert kg_for(2, 8, 4096, 64, 2, 0) == 2 and kg_for(2, 8, 4096, 128, 1, 0) == 1
+    assert kg_for(2, 8, 2048, 128, 1, 0) == 2 and kg_for(2, 8, 2049, 128, 2, 0) == 1
+    assert kg_for(2, 8, 4097, 64, 2, 0) == 1 and kg_for(8, 12, 1024, 64, 2, 0) == 1
+    assert kg_for(2, 8, 4096, 64, 0, 0) == 1 and kg_for(2, 8, 4096, 64, 2, 1) == 1
 
 
 def test_backward_blocksparse_split_validation(lib):

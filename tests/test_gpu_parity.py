@@ -49,8 +49,9 @@ def nan_like(t):
     return torch.full_like(t, float("nan"))
 
 
-def run_gpu(prob, backward=True, block_rows=None, block_keys=0, key_groups=0):
-    """Forward (and backward) through the C ABI into NaN-filled outputs."""
+def run_gpu(prob, backward=True, block_rows=None, block_keys=0, key_groups=0, bwd_key_groups=0):
+    """Forward (and backward) through the C ABI into NaN-filled outputs
+    (key groups 0: the library's choice)."""
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))
     kl = None if prob.key_lens is None else torch.from_numpy(prob.key_lens).cuda()
     bm = None if prob.block_mask is None else torch.from_numpy(prob.block_mask).cuda()
@@ -67,16 +68,16 @@ def run_gpu(prob, backward=True, block_rows=None, block_keys=0, key_groups=0):
     out = {"o": o, "lse": lse}
     if backward:
         dq, dk, dv = (nan_like(q) for _ in range(3))
-        fa_backward(q, k, v, o, do, lse, block_mask=bm, block_size=prob.block_size, dq=dq, dk=dk,
-                    dv=dv, **kw)
+        fa_backward_ex(q, k, v, o, do, lse, block_mask=bm, block_size=prob.block_size, dq=dq,
+                       dk=dk, dv=dv, key_groups=bwd_key_groups, **kw)
         out.update(dq=dq, dk=dk, dv=dv)
         if prob.dtype != "fp32":
             # The same backward with float32 gradients: the 16-bit gradients
             # above must be exactly their round-to-nearest-even, and the
             # float32 ones are what the oracle comparison measures (the
             # computation's error apart from the output's own rounding).
-            g32 = fa_backward(q, k, v, o, do, lse, block_mask=bm, block_size=prob.block_size,
-                              grad_dtype=torch.float32, **kw)
+            g32 = fa_backward_ex(q, k, v, o, do, lse, block_mask=bm, block_size=prob.block_size,
+                                 grad_dtype=torch.float32, key_groups=bwd_key_groups, **kw)
             torch.cuda.synchronize()
             for n, g in zip(("dq", "dk", "dv"), g32):
                 g = g.cpu().numpy()
@@ -418,6 +419,24 @@ def test_forward_key_groups_far_keys(dtype, d, boost):
     compare(gpu, run_oracle(prob, backward=False), TOL[dtype], label=label, magnitude_scaled=True)
 
 
+@pytest.mark.parametrize("kg", [1, 2])
+@pytest.mark.parametrize("case", KG_CASES, ids=lambda c: "N{}d{}_{}".format(c[2], c[3], c[4]))
+def test_backward_key_groups(case, kg):
+    # Both backward passes with each tile's sweep in one group of waves (1)
+    # or split between two whose partial gradients add on chip (2; the dK/dV
+    # pass keeps one group at d = 128), against the oracle on every head; the
+    # 16-bit gradients are the rounding of the float32 ones (run_gpu).
+    B, H, N, d, dtype, causal, klr = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=211 + N + d, causal=causal,
+                               key_len_range=klr)
+    if klr is not None and klr[0] == 0:
+        prob.key_lens[0] = 0
+    gpu = run_gpu(prob, key_groups=1, bwd_key_groups=kg)
+    check_all_heads(prob, gpu, f"{kg} key groups backward")
+    compare(gpu, run_oracle(prob), TOL[dtype], label=f"{kg} key groups backward {case}",
+            magnitude_scaled=klr is not None and klr[0] < 4)
+
+
 BWD_ROW_CASES = [
     # dQ query rows, dK/dV keys per work-group, B, H, N, d, dtype, causal, key_len_range,
     # block_keep_p
@@ -437,12 +456,12 @@ def test_backward_tile_rows(case):
     # dQ work-groups of 64 or 256 query rows and dK/dV work-groups of 64 or
     # 256 keys (the backward's tile-height option): each wave still owns 32
     # rows and sweeps the same tiles in the same order, so the gradients must
-    # equal those of the default 128-row work-groups bit for bit, on every
-    # head; the default ones are compared with the oracle.
+    # equal those of 128-row work-groups (one key group) bit for bit, on
+    # every head; those are compared with the oracle.
     dqr, kvr, B, H, N, d, dtype, causal, klr, bkp = case
     prob = inputs.make_problem(B, H, N, d, dtype, seed=171 + dqr + kvr + N, causal=causal,
                                key_len_range=klr, block_keep_p=bkp)
-    gpu = run_gpu(prob)
+    gpu = run_gpu(prob, bwd_key_groups=1)
     compare(gpu, run_oracle(prob), TOL[dtype], label=f"bwd rows default {case[2:]}",
             magnitude_scaled=klr is not None and klr[0] < 4)
     q, k, v, do = (dev(x, prob.dtype) for x in (prob.q, prob.k, prob.v, prob.do))

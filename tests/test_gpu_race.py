@@ -40,7 +40,7 @@ def run_lib(lib, prob, block_rows=0, block_keys=0, bwd_rows=0, key_groups=0):
     assert st == 0, lib.fa_last_error_detail()
     st = lib.fa_backward_ex(ptr(q), ptr(k), ptr(v), ptr(o), ptr(do), ptr(lse), ptr(dq), ptr(dk),
                             ptr(dv), *common, ptr(bm), prob.block_size, CODE[prob.dtype],
-                            CODE[prob.dtype], bwd_rows, bwd_rows, ptr(ws), need, stream)
+                            CODE[prob.dtype], bwd_rows, bwd_rows, 0, ptr(ws), need, stream)
     assert st == 0, lib.fa_last_error_detail()
     torch.cuda.synchronize()
     return {n: t.cpu() for n, t in (("o", o), ("lse", lse), ("dq", dq), ("dk", dk), ("dv", dv))}

@@ -78,12 +78,13 @@ def test_split_backward(case):
 
 def test_split_backward_one_item_is_the_unsplit_backward():
     # chunk_blocks at least the blocks per row: every row and column is one
-    # item, no partials, and the gradients are the unsplit backward's, bit
-    # for bit.  The workspace is then only the unsplit one plus three
-    # one-item partial arrays.
+    # item, no partials, and the gradients are the unsplit backward's (with
+    # one key group, as the split instances run), bit for bit.  The
+    # workspace is then only the unsplit one plus three one-item partial
+    # arrays.
     prob = inputs.make_problem(1, 2, 900, 64, "bf16", seed=933, causal=True, block_keep_p=0.5,
                                block_band=1, block_global=1)
-    gpu = run_gpu(prob)
+    gpu = run_gpu(prob, bwd_key_groups=1)
     split = split_backward(prob, 8, gpu["o"], gpu["lse"])
     for n in GRADS:
         assert np.array_equal(split[n], gpu[n + "_16"]), n
