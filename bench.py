@@ -675,6 +675,117 @@ def step_stamps(args, dev):
                       "kernel_us_stamps_build": round(kernel_us, 2), "timeline": out}))
 
 
+RATE_OPS = [  # (op code, name, matrix products and vector instructions per wave per iteration)
+    (0, "mfma_32x32x16_bf16", 4, 0), (1, "v_exp_f32", 0, 16), (2, "v_fma_f32", 0, 16),
+    (3, "v_add_f32", 0, 16), (4, "v_cvt_pk_bf16_f32", 0, 16),
+    (5, "mfma + 4 v_exp_f32 each, one wave", 4, 16), (6, "mfma waves beside v_exp_f32 waves", 4, 16)]
+
+
+def simd_key(rec):
+    """(XCD, shader engine, shader array, CU, SIMD) of a wave from its
+    recorded XCC_ID << 32 | HW_ID word (HW_ID: SIMD bits 5:4, CU 11:8, shader
+    array 12, shader engine 15:13)."""
+    h = int(rec) & 0xFFFFFFFF
+    return (int(rec) >> 32, (h >> 13) & 7, (h >> 12) & 1, (h >> 8) & 15, (h >> 4) & 3)
+
+
+def unit_rates(args, dev):
+    """Instruction issue rates from libfa_rates.so: SIMD cycles per wave
+    instruction of each kind the attention steps use, at 1, 2 and 4 waves per
+    SIMD, with the shader clock the run saw; then a few seconds of matrix
+    products alone, launch after launch, for the rate and clock they sustain.
+    A SIMD's rate is its waves' instructions over the span from its first
+    wave's start to its last wave's end (waves grouped by their hardware
+    ids)."""
+    if not os.path.exists(build_lib.RATES_LIB):
+        raise RuntimeError(f"{build_lib.RATES_LIB} is missing: build it with "
+                           "`python -m exact_io_aware_52_amd.build_lib`")
+    lib = ctypes.CDLL(build_lib.RATES_LIB)
+    lib.fa_rates_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                 ctypes.c_void_p, ctypes.c_void_p]
+    props = torch.cuda.get_device_properties(dev)
+    cus = props.multi_processor_count
+    st = torch.cuda.current_stream()
+
+    def run(op, groups_per_cu, iters):
+        wpg = 8 if op == 6 else 4
+        grid = cus * groups_per_cu
+        sink = torch.empty(grid * 64 * wpg, dtype=torch.float32, device=dev)
+        clocks = torch.zeros(grid * wpg * 5, dtype=torch.int64, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        rc = lib.fa_rates_run(op, grid, iters, ctypes.c_void_p(sink.data_ptr()),
+                              ctypes.c_void_p(clocks.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+        assert rc == 0, rc
+        e1.record(st)
+        e1.synchronize()
+        c = clocks.view(-1, 5).cpu().numpy().astype(np.int64)
+        cyc = c[:, 1] - c[:, 0]
+        wall_ns = 10 * (c[:, 3] - c[:, 2])
+        mfma_wave = (np.arange(len(c)) % wpg) < 4 if op == 6 else np.full(len(c), op in (0, 5))
+        simds = {}
+        for i, rec in enumerate(c[:, 4]):
+            simds.setdefault(simd_key(rec), []).append(i)
+        return {"grid": grid, "c": c, "cycles": cyc, "simds": simds, "mfma_wave": mfma_wave,
+                "kernel_ms": e0.elapsed_time(e1),
+                "ghz": float(np.median(cyc / np.maximum(wall_ns, 1)))}
+
+    def simd_rate(r, iters, n_per_iter, select=None):
+        """Median over SIMDs of span cycles per wave instruction, and the
+        median number of (selected) waves per SIMD."""
+        c = r["c"]
+        per, waves = [], []
+        for idx in r["simds"].values():
+            idx = [i for i in idx if select is None or select[i]]
+            if not idx:
+                continue
+            span = c[idx, 1].max() - c[idx, 0].min()
+            per.append(span / (len(idx) * iters * n_per_iter))
+            waves.append(len(idx))
+        return round(float(np.median(per)), 3), float(np.median(waves))
+
+    rows = []
+    for op, name, n_mfma, n_valu in RATE_OPS:
+        for per_cu in ([1, 2, 4] if op not in (5, 6) else [1, 2]):
+            wps = per_cu * (2 if op == 6 else 1)  # waves per SIMD if spread evenly
+            iters = max(2000, 160000 // wps)
+            run(op, per_cu, 64)  # warm-up launch
+            r = run(op, per_cu, iters)
+            row = {"op": name, "work_groups_per_cu": per_cu, "iters": iters,
+                   "kernel_ms": round(r["kernel_ms"], 3), "clock_ghz": round(r["ghz"], 3),
+                   "simds": len(r["simds"])}
+            if op == 6:
+                row["mfma_cycles_per_inst"], row["mfma_waves_per_simd"] = simd_rate(
+                    r, iters, 4, r["mfma_wave"])
+                row["exp_cycles_per_inst"], row["exp_waves_per_simd"] = simd_rate(
+                    r, iters, 16, ~r["mfma_wave"])
+            elif op == 5:
+                row["cycles_per_iter"], row["waves_per_simd"] = simd_rate(r, iters, 1)
+            else:
+                row["cycles_per_inst"], row["waves_per_simd"] = simd_rate(r, iters,
+                                                                          n_mfma or n_valu)
+                if op == 0:
+                    flops = r["grid"] * 4 * iters * 4 * 32 * 32 * 16 * 2
+                    row["tflops"] = round(flops / (r["kernel_ms"] * 1e-3) / 1e12, 1)
+            rows.append(row)
+            print(json.dumps(row), flush=True)
+    # matrix products alone for a few seconds: the rate and clock they sustain
+    sustained = []
+    t_end = time.time() + args.rates_seconds
+    while time.time() < t_end:
+        r = run(0, 2, 300000)
+        flops = r["grid"] * 4 * 300000 * 4 * 32 * 32 * 16 * 2
+        sustained.append({"tflops": round(flops / (r["kernel_ms"] * 1e-3) / 1e12, 1),
+                          "clock_ghz": round(r["ghz"], 3), "kernel_ms": round(r["kernel_ms"], 2)})
+    print(json.dumps({"unit_rates": rows, "compute_units": cus,
+                      "mfma_sustained": {"launches": len(sustained), "first": sustained[0],
+                                         "last": sustained[-1],
+                                         "median_tflops": float(np.median(
+                                             [x["tflops"] for x in sustained])),
+                                         "median_clock_ghz": float(np.median(
+                                             [x["clock_ghz"] for x in sustained]))}}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -710,6 +821,11 @@ def main():
                     help="with --standard: run only the standard attention (counter runs)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="run only a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--unit-rates", action="store_true",
+                    help="instruction issue rates and the sustained matrix-core rate "
+                         "(libfa_rates.so)")
+    ap.add_argument("--rates-seconds", type=float, default=4.0,
+                    help="with --unit-rates: seconds of back-to-back matrix-product launches")
     ap.add_argument("--step-stamps", action="store_true",
                     help="forward step timeline of chosen work-groups from the stamps build "
                          "(libfa_stamps.so)")
@@ -733,6 +849,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calib_bytes_read": 1 << 30, "copy_calib_bytes_written": 1 << 30}))
+        return
+    if args.unit_rates:
+        unit_rates(args, dev)
         return
     if args.step_stamps:
         step_stamps(args, dev)

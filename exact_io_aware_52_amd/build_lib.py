@@ -28,6 +28,10 @@ SERIAL_LIB = os.path.join(PKG, "libfa_serial.so")
 # Step timeline build: the forward with FA_STEP_STAMPS (per-step clock stamps
 # of chosen work-groups, read by bench.py --step-stamps), the rest as libfa.so.
 STAMPS_LIB = os.path.join(PKG, "libfa_stamps.so")
+# Unit-rate build: instruction-rate kernels (matrix products, exponentials,
+# fp32 fma/add, bf16 packing, and their overlap) for the step cost model,
+# read by bench.py --unit-rates; no attention code.
+RATES_LIB = os.path.join(PKG, "libfa_rates.so")
 # Hash of each kernel's gfx950 machine code (all instances of one kernel
 # template together), written at every build.  Counter summaries under
 # profiles/ carry the hash of the code they were taken on, and the bench
@@ -158,12 +162,12 @@ def kernel_code_hashes(objects):
 
 
 def build(verbose=False):
-    """Compile libfa.so, the race-check build libfa_serial.so and the step
-    timeline build libfa_stamps.so."""
-    for var in ("serial", "stamps"):
+    """Compile libfa.so, the race-check build libfa_serial.so, the step
+    timeline build libfa_stamps.so and the unit-rate library libfa_rates.so."""
+    for var in ("serial", "stamps", "rates"):
         os.makedirs(os.path.join(BUILD, var), exist_ok=True)
     jobs = ([(src, "") for src in SOURCES] + [(src, "serial") for src in SOURCES] +
-            [("fa_fwd.hip", "stamps")])
+            [("fa_fwd.hip", "stamps"), ("fa_rates.hip", "rates")])
     with ThreadPoolExecutor(max_workers=min(9, len(jobs))) as ex:
         results = list(ex.map(lambda j: _compile(*j), jobs))
     for obj, err in results:
@@ -172,14 +176,16 @@ def build(verbose=False):
     main = [o for (o, _), (_, var) in zip(results, jobs) if not var]
     serial = [o for (o, _), (_, var) in zip(results, jobs) if var == "serial"]
     stamps_fwd = [o for (o, _), (_, var) in zip(results, jobs) if var == "stamps"]
+    rates = [o for (o, _), (_, var) in zip(results, jobs) if var == "rates"]
     _link(main, LIB)
     _link(serial, SERIAL_LIB)
     _link([o for o in main if not o.endswith("fa_fwd.o")] + stamps_fwd, STAMPS_LIB)
+    _link(rates, RATES_LIB)
     hashes = kernel_code_hashes(main)
     with open(CODE_MANIFEST, "w") as fh:
         json.dump(hashes, fh, indent=1, sort_keys=True)
     if verbose:
-        print(f"built {LIB}, {SERIAL_LIB} and {STAMPS_LIB}")
+        print(f"built {LIB}, {SERIAL_LIB}, {STAMPS_LIB} and {RATES_LIB}")
         print(f"kernel code hashes: { {k: v for k, v in hashes.items() if ':' not in k} }")
     return LIB
 
