@@ -678,7 +678,9 @@ def step_stamps(args, dev):
 RATE_OPS = [  # (op code, name, matrix products and vector instructions per wave per iteration)
     (0, "mfma_32x32x16_bf16", 4, 0), (1, "v_exp_f32", 0, 16), (2, "v_fma_f32", 0, 16),
     (3, "v_add_f32", 0, 16), (4, "v_cvt_pk_bf16_f32", 0, 16),
-    (5, "mfma + 4 v_exp_f32 each, one wave", 4, 16), (6, "mfma waves beside v_exp_f32 waves", 4, 16)]
+    (5, "mfma + 4 v_exp_f32 each, one wave", 4, 16), (6, "mfma waves beside v_exp_f32 waves", 4, 16),
+    (7, "ds_read_b128", 0, 16), (8, "ds_read_b64_tr_b16", 0, 16)]
+LDS_READ_BYTES = {7: 1024, 8: 512}  # per wave instruction
 
 
 def simd_key(rec):
@@ -730,6 +732,17 @@ def unit_rates(args, dev):
                 "kernel_ms": e0.elapsed_time(e1),
                 "ghz": float(np.median(cyc / np.maximum(wall_ns, 1)))}
 
+    def cu_lds_rate(r, iters, op):
+        """Median over CUs of LDS bytes read per cycle (span from the CU's
+        first wave start to its last wave end)."""
+        c = r["c"]
+        cus_ = {}
+        for key, idx in r["simds"].items():
+            cus_.setdefault(key[:4], []).extend(idx)
+        per = [len(idx) * iters * 16 * LDS_READ_BYTES[op] /
+               (c[idx, 1].max() - c[idx, 0].min()) for idx in cus_.values()]
+        return round(float(np.median(per)), 1)
+
     def simd_rate(r, iters, n_per_iter, select=None):
         """Median over SIMDs of span cycles per wave instruction, and the
         median number of (selected) waves per SIMD."""
@@ -764,6 +777,8 @@ def unit_rates(args, dev):
             else:
                 row["cycles_per_inst"], row["waves_per_simd"] = simd_rate(r, iters,
                                                                           n_mfma or n_valu)
+                if op in LDS_READ_BYTES:
+                    row["lds_bytes_per_cu_cycle"] = cu_lds_rate(r, iters, op)
                 if op == 0:
                     flops = r["grid"] * 4 * iters * 4 * 32 * 32 * 16 * 2
                     row["tflops"] = round(flops / (r["kernel_ms"] * 1e-3) / 1e12, 1)

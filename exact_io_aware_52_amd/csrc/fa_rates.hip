@@ -28,7 +28,10 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
-enum Op { kMfma = 0, kExp = 1, kFma = 2, kAdd = 3, kCvt = 4, kMixSelf = 5, kMixWaves = 6 };
+enum Op {
+  kMfma = 0, kExp = 1, kFma = 2, kAdd = 3, kCvt = 4, kMixSelf = 5, kMixWaves = 6,
+  kLds128 = 7, kLdsTr = 8
+};
 
 constexpr int kChains = 16;  // independent vector chains per lane
 constexpr int kAccs = 4;     // independent matrix accumulators per wave
@@ -65,6 +68,18 @@ __device__ __forceinline__ void exp_iter(float (&x)[kChains]) {
   for (int j = 0; j < kChains; ++j) x[j] = __builtin_amdgcn_exp2f(x[j]);
 }
 
+// LDS reads: each wave reads its work-group's LDS buffer, 16 reads per
+// iteration: ds_read_b128 (16 contiguous bytes per lane, 1 KB per read) or
+// ds_read_b64_tr_b16 (the transposing read the attention kernels use for the
+// V^T, dO^T and Q^T operands; 8 contiguous bytes addressed per lane, 512
+// bytes per read), and folds every element read into a running xor so that
+// no read is dead.
+constexpr int kLdsBytes = 17408;  // 16 KB read per iteration from a base that moves by 512 B
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) u32x4 lds_u4;
+
 // Waves per work-group: 4, or 8 for kMixWaves.
 template <int OP> constexpr int waves_per_group() { return OP == kMixWaves ? 8 : 4; }
 
@@ -92,6 +107,14 @@ __global__ __launch_bounds__(64 * waves_per_group<OP>()) void rates_kernel(
   const float m = 1.0f - 0.5f * seed;  // (wave-uniform: a scalar operand)
   const float add = 0.25f * base;      // (a vector operand)
   const bool mfma_wave = (threadIdx.x >> 6) < 4;  // (kMixWaves)
+  __shared__ __attribute__((aligned(1024))) char lds[OP == kLds128 || OP == kLdsTr ? kLdsBytes : 4];
+  unsigned fold = 0;
+  __attribute__((address_space(3))) char* const lb = (__attribute__((address_space(3))) char*)lds;
+  if constexpr (OP == kLds128 || OP == kLdsTr) {
+    for (int i = threadIdx.x; i < kLdsBytes / 4; i += 64 * WPG)
+      reinterpret_cast<unsigned*>(lds)[i] = (unsigned)i * 2654435761u;
+    __syncthreads();
+  }
 
   __builtin_amdgcn_sched_barrier(0);
   const unsigned long long t0 = __builtin_readcyclecounter();
@@ -123,6 +146,24 @@ __global__ __launch_bounds__(64 * waves_per_group<OP>()) void rates_kernel(
         const bf16x2 p = {(__bf16)x[j], (__bf16)x[j]};
         x[j] = __builtin_bit_cast(float, p);
       }
+    } else if constexpr (OP == kLds128) {
+      // lane l reads bytes 16 l .. 16 l + 15 of each 1 KB row j, from a base
+      // that alternates between 0 and 512 so that no read is loop-invariant
+      const __attribute__((address_space(3))) char* const b = lb + (it & 1) * 512 + lane * 16;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const u32x4 v = *(const lds_u4*)(b + j * 1024);
+        fold ^= v[0] ^ v[1] ^ v[2] ^ v[3];
+      }
+    } else if constexpr (OP == kLdsTr) {
+      // lane l addresses bytes 8 l .. 8 l + 7 of each 1 KB row j (512 bytes
+      // per read; the hardware regroups the 16-bit elements across lanes)
+      const __attribute__((address_space(3))) char* const b = lb + (it & 1) * 512 + lane * 8;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + j * 1024));
+        fold ^= (unsigned)(unsigned short)(v[0] ^ v[1] ^ v[2] ^ v[3]);
+      }
     } else if constexpr (OP == kMixSelf) {
       // per iteration kAccs products and kChains exponentials, issued as
       // one product then four exponentials (the order held by scheduling
@@ -148,6 +189,7 @@ __global__ __launch_bounds__(64 * waves_per_group<OP>()) void rates_kernel(
     for (int r = 0; r < 16; ++r) s += acc[j][r];
 #pragma unroll
   for (int j = 0; j < kChains; ++j) s += x[j];
+  s += (float)(fold & 1);
   __builtin_amdgcn_sched_barrier(0);
   const unsigned long long t1 = __builtin_readcyclecounter();
   const unsigned long long r1 = __builtin_amdgcn_s_memrealtime();
@@ -167,15 +209,16 @@ hipError_t launch(int grid, int iters, float* sink, unsigned long long* clocks,
 
 // Runs one rates kernel (op: 0 matrix products, 1 exponentials, 2 fma, 3 add,
 // 4 bf16 packing, 5 products and exponentials in one wave, 6 in separate
-// waves): `grid` work-groups of W waves (W = 4, or 8 for op 6; the dispatcher
+// waves, 7 ds_read_b128, 8 ds_read_b64_tr_b16): `grid` work-groups of W waves (W = 4, or 8 for op 6; the dispatcher
 // spreads a work-group's waves over the CU's four SIMDs), each wave `iters`
-// loop iterations of 4 matrix products or 16 vector instructions (op 5: both).
+// loop iterations of 4 matrix products, 16 vector instructions (op 5: both)
+// or 16 KB of LDS reads per wave (ops 7, 8).
 // sink: grid * 64 * W floats (device); clocks: grid * W * 5 uint64 (device):
 // per wave (shader clock start, end, wall clock start, end, XCD << 32 |
 // HW_ID).  Asynchronous on
 // `stream`.  Returns 0, 1 for arguments out of range, or 2 + the HIP error.
 extern "C" int fa_rates_run(int op, int grid, int iters, void* sink, void* clocks, void* stream) {
-  if (op < 0 || op > kMixWaves || grid <= 0 || grid > (1 << 16) || iters <= 0 || !sink || !clocks)
+  if (op < 0 || op > kLdsTr || grid <= 0 || grid > (1 << 16) || iters <= 0 || !sink || !clocks)
     return 1;
   float* s = static_cast<float*>(sink);
   unsigned long long* c = static_cast<unsigned long long*>(clocks);
@@ -189,6 +232,8 @@ extern "C" int fa_rates_run(int op, int grid, int iters, void* sink, void* clock
     case kCvt: e = launch<kCvt>(grid, iters, s, c, st); break;
     case kMixSelf: e = launch<kMixSelf>(grid, iters, s, c, st); break;
     case kMixWaves: e = launch<kMixWaves>(grid, iters, s, c, st); break;
+    case kLds128: e = launch<kLds128>(grid, iters, s, c, st); break;
+    case kLdsTr: e = launch<kLdsTr>(grid, iters, s, c, st); break;
   }
   return e == hipSuccess ? 0 : 2 + (int)e;
 }

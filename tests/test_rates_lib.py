@@ -11,7 +11,7 @@ import torch
 
 from exact_io_aware_52_amd import build_lib
 
-OPS = range(7)
+OPS = range(9)
 
 
 @pytest.fixture(scope="module")
@@ -27,7 +27,7 @@ def rates():
 def test_rates_argument_checks(rates):
     buf = ctypes.c_void_p(1)  # never dereferenced: every call below is refused first
     assert rates.fa_rates_run(-1, 1, 1, buf, buf, None) == 1
-    assert rates.fa_rates_run(7, 1, 1, buf, buf, None) == 1
+    assert rates.fa_rates_run(9, 1, 1, buf, buf, None) == 1
     assert rates.fa_rates_run(0, 0, 1, buf, buf, None) == 1
     assert rates.fa_rates_run(0, (1 << 16) + 1, 1, buf, buf, None) == 1
     assert rates.fa_rates_run(0, 1, 0, buf, buf, None) == 1
