@@ -63,6 +63,8 @@ int auto_fwd_kgroups(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
 // against 1 (B2 H8, causal): N = 2K -15% (d = 64) and -8% (d = 128, where
 // only the dQ pass splits), N = 4K -4% and +1%; N = 8K +4%, +3%; the GPT-2
 // shape (768 tiles) +26%.  So at most 512 tiles at d = 64, 256 at d = 128.
+// (At d = 128 the dK/dV pass takes its own two-group form whatever this
+// returns: see backward_impl.)
 int auto_bwd_kgroups(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
   if (dtype == FA_F32 || sparse) return 1;
   const long long groups = (long long)B * H * ((N + 127) / 128);
@@ -350,6 +352,12 @@ int backward_impl(const void* q, const void* k, const void* v, const void* o, co
   p.bwd_dq_rows = dq_rows ? dq_rows : 128;
   p.bwd_dkdv_rows = dkdv_rows ? dkdv_rows : 128;
   p.bwd_kgroups = kgroups;
+  // At d = 128 the dK/dV pass (16-bit inputs, 128-key tiles, unsplit) runs
+  // two wave groups on each query tile unless one group is asked for: each
+  // group's waves hold half the queries' products, which leaves room for two
+  // waves per SIMD.
+  p.bwd_dkdv_qs = dtype != FA_F32 && d == 128 && p.bwd_dkdv_rows == 128 && chunk_blocks == 0 &&
+                  key_groups != 1;
   if (chunk_blocks > 0) {
     const size_t base = fa_backward_workspace_bytes(B, H, N, d);
     const size_t part = bwd_split_part_bytes(B, H, N, d, chunk_blocks);

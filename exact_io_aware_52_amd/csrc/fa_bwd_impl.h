@@ -153,7 +153,11 @@ __device__ __forceinline__ int kth_kept(const uint8_t* m, int lo, int hi, int ra
 // ----------------------------------------------------------------------------
 // dK, dV.  Work-group: NW waves x 32 keys (4 by default; 2 and 8 are a
 // tile-size option); query tiles of BQ rows.
-template <typename T, int D, int NW = 4>
+//
+// QS (16-bit, d = 128, 8 waves): the two waves of each 32-key block share
+// every query tile, one 32-query half each, so that two waves per SIMD fit:
+// K and V are read from LDS rather than held in registers.
+template <typename T, int D, int NW = 4, bool QS = false>
 struct DkDvCfg {
   typedef raw_t<T> raw;
   static constexpr int BQ = (sizeof(raw) == 4 && D == 128) ? 32 : 64;
@@ -164,7 +168,7 @@ struct DkDvCfg {
   static constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);       // 16-byte DMAs per wave per tile
   // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
   // accumulators: 192 VGPRs) only fits one wave per SIMD.
-  static constexpr int WAVES_PER_SIMD = D == 128 ? 1 : 2;
+  static constexpr int WAVES_PER_SIMD = D == 128 && !QS ? 1 : 2;
   // Read each group of matrix operands one group ahead of its products
   // (explicit, fenced with scheduling barriers): the compiler otherwise reads
   // each operand just before its product.  Groups of GK k-steps: 4 at
@@ -176,7 +180,7 @@ struct DkDvCfg {
   // softmax with matrix work, so the step interleaves them itself (the
   // softmax of query block 0 beside the score products of block 1, that of
   // block 1 beside the first gradient products).
-  static constexpr bool ILV = D == 128 && sizeof(raw) == 2;
+  static constexpr bool ILV = D == 128 && sizeof(raw) == 2 && !QS;
 };
 
 // GF32: store dK, dV as float32 (16-bit inputs; an option for exact
@@ -187,21 +191,33 @@ struct DkDvCfg {
 // two key groups of NW / 2 that share the keys and sweep the first and
 // second half of the query tiles, each through its own ring; group 1 adds
 // its dK, dV accumulators into group 0's through LDS.
-template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4, int KG = 1>
+//
+// QS (with KG = 2, 16-bit, d = 128): the groups split every query tile
+// instead of the tile range: group g takes query block g (32 of the tile's
+// 64 queries) of each tile, from one 2-slot ring that both read; K and V of
+// the work-group's 128 keys sit in LDS beside it (64 KB), which frees the 64
+// registers per wave that hold them otherwise, so two waves per SIMD fit.
+template <typename T, int D, bool GF32 = false, bool SPLIT = false, int NW = 4, int KG = 1,
+          bool QS = false>
 __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
-    DkDvCfg<T, D, NW / KG>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
+    DkDvCfg<T, D, NW / KG, QS>::WAVES_PER_SIMD))) void fa_bwd_dkdv_kernel(BwdParams p) {
   static_assert(KG == 1 || (KG == 2 && !SPLIT), "key groups: unsplit passes");
+  static_assert(!QS || (KG == 2 && sizeof(raw_t<T>) == 2), "split query tiles: two groups, 16-bit");
   constexpr int RW = NW / KG;  // waves per key group (32 keys each)
   typedef raw_t<T> raw;
   typedef raw4_t<T> raw4;
   typedef Traits<T> Tr;
-  typedef DkDvCfg<T, D, RW> L;
+  typedef DkDvCfg<T, D, RW, QS> L;
   constexpr int BQ = L::BQ;
   constexpr int BK = 32 * RW;  // keys of this work-group (at most one mask block)
   static_assert(BK <= kMaskBlock || !SPLIT, "split columns come in whole mask blocks");
   constexpr int LPT = L::LPT;
+  // QS: one 2-slot ring shared by both groups, then K and V (row-major).
+  constexpr int NSL = QS ? 2 : L::NS;
+  constexpr int RING_BYTES = (QS ? 1 : KG) * NSL * L::SLOT_BYTES;
+  constexpr int KV_TILE = QS ? BK * D * (int)sizeof(raw) : 0;
 
-  __shared__ __attribute__((aligned(1024))) char ring[KG * L::NS * L::SLOT_BYTES];
+  __shared__ __attribute__((aligned(1024))) char ring[RING_BYTES + 2 * KV_TILE];
   __shared__ uint8_t mask_col[kMaxMaskBlocks];
 
   const int tid = threadIdx.x;
@@ -209,7 +225,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   const int wg_wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kgrp = KG > 1 ? wg_wave / RW : 0;        // key group of this wave
   const int w = KG > 1 ? wg_wave % RW : wg_wave;     // key wave within the group
-  char* const gring = ring + kgrp * L::NS * L::SLOT_BYTES;  // this group's ring
+  char* const gring = ring + (QS ? 0 : kgrp * L::NS * L::SLOT_BYTES);  // this group's ring
   const uint32_t ring_lds = lds_addr(gring);
   const int col = lane & 31;
   const int hh = lane >> 5;
@@ -258,11 +274,23 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
   }
   // K and V of this wave's keys as B operands (contiguous slot map over d).
   frag_t<T> kf[D / 16], vf[D / 16];
+  if constexpr (!QS) {
 #pragma unroll
-  for (int kc = 0; kc < D / 16; ++kc) {
-    const bool ok = myk < N;
-    kf[kc] = ok ? load_frag<T>(Kg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
-    vf[kc] = ok ? load_frag<T>(Vg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const bool ok = myk < N;
+      kf[kc] = ok ? load_frag<T>(Kg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+      vf[kc] = ok ? load_frag<T>(Vg + (size_t)myk * D + kc * 16 + hh * 8) : zero_frag<T>();
+    }
+  }
+  // QS: K and V rows of the work-group's keys in LDS (copied by all waves;
+  // rows past N repeat row N-1, and no key past N is stored).
+  const raw* const Kt = reinterpret_cast<const raw*>(ring + RING_BYTES);
+  const raw* const Vt = Kt + BK * D;
+  if constexpr (QS) {
+    DmaPlan<raw, BK, D, kRows, NW> kvplan;
+    kvplan.init(wg_wave, lane);
+    kvplan.copy(Kg, j0, N, lds_addr(ring) + RING_BYTES, lane);
+    kvplan.copy(Vg, j0, N, lds_addr(ring) + RING_BYTES + KV_TILE, lane);
   }
   __syncthreads();  // mask_col visible
 
@@ -289,15 +317,16 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     return t;
   };
 
-  DmaPlan<raw, BQ, D, kBoth, RW> plan;  // (a key group copies its own tiles)
-  plan.init(w, lane);
+  // (a key group copies its own tiles; with QS all waves copy the shared ones)
+  DmaPlan<raw, BQ, D, kBoth, QS ? NW : RW> plan;
+  plan.init(QS ? wg_wave : w, lane);
   // Q, dO rows of tile t, plus (waves 0 and 1) its LSE2 and D words.
   auto issue = [&](int t, int s) {
     const uint32_t base = ring_lds + s * L::SLOT_BYTES;
     const int qi0 = t * BQ;
     plan.copy(Qg, qi0, N, base, lane);
     plan.copy(dOg, qi0, N, base + L::TILE_BYTES, lane);
-    if (w < 2) {
+    if ((QS ? wg_wave : w) < 2) {
       const uint32_t voff = (uint32_t)min(qi0 + lane, N - 1) * 4u;
       dma4s(voff, w == 0 ? (const void*)lse2g : (const void*)dvecg,
             base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
@@ -572,124 +601,200 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     }
   };
 
-  // Kept query tiles in order; tl[k] is the tile of step i + k.  Step i
-  // forms S and dP of tile i, its softmax, then the dV, dK products.
-  // The split instances (long sparse masks, whose tiles come from HBM rather
-  // than L2) request tiles three steps ahead, using the ring's fourth slot;
-  // the others two.
-  //
-  // This key group's query tiles [tb, te): all of [t_begin, t_end), or its
-  // first or second half (the first group takes the extra tile of an odd
-  // count).  With two key groups the loop's condition is the work-group's,
-  // and both groups take the first group's number of steps, so that their
-  // barriers pair up; a group past its last tile only joins the barriers.
-  int tb = t_begin, te = t_end;
-  if constexpr (KG > 1) {
-    const int tmid = t_begin + (t_end - t_begin + 1) / 2;
-    tb = kgrp ? tmid : t_begin;
-    te = kgrp ? t_end : tmid;
-  }
-  constexpr bool LA3 = SPLIT;
-  int tl[4];
-  tl[0] = tb < te ? next_kept(tb) : te;
-  tl[1] = tl[0] < te ? next_kept(tl[0] + 1) : te;
-  tl[2] = tl[1] < te ? next_kept(tl[1] + 1) : te;
-  tl[3] = LA3 && tl[2] < te ? next_kept(tl[2] + 1) : te;
-  if (KG > 1 ? t_begin < t_end : tl[0] < te) {
-    if (tl[0] < te) issue(tl[0], 0);
-    if (tl[1] < te) issue(tl[1], 1);
-    if (LA3 && tl[2] < te) issue(tl[2], 2);
-    FA_STAGE_FENCE();
-    // The K and V fragments arrived by ordinary loads issued before these
-    // copies.  Waiting for everything once here tells the compiler they have
-    // landed; otherwise it waits for them (vmcnt(0)) at their first use
-    // inside the loop, on every step, which also stalls on the tile just
-    // requested.
-    wait_vmcnt<0>();
-    // Dense interior: every wave's keys see tile t in full, and tiles t+1,
-    // t+2 are whole.
-    int lo = te, hi = -1;
-    if (!sparse && j0 + BK <= kend) {
-      lo = p.causal ? (j0 + BK - 1 + BQ - 1) / BQ : tb;
-      hi = min(N / BQ - 3, te - 3);
+  // QS: one query block (this wave's group) of the tile in `slot`: S and dP
+  // with the K and V operands read from LDS, the softmax, then dV and dK
+  // over the block's two 16-query chunks.
+  auto step_qs = [&](const char* slot, int qi0, bool msk) {
+    const raw* Qs = reinterpret_cast<const raw*>(slot);
+    const raw* dOs = reinterpret_cast<const raw*>(slot + L::TILE_BYTES);
+    const float* lse2s = reinterpret_cast<const float*>(slot + 2 * L::TILE_BYTES);
+    const int qb = kgrp;
+    f32x16 sacc, pacc;
+    const f32x16 dneg = dneg_of(slot, qb);
+#pragma unroll
+    for (int kc = 0; kc < D / 16; ++kc) {
+      const frag_t<T> aq = load_frag_swz<T, D, kBoth>(Qs, qb * 32 + col, kc * 16 + hh * 8);
+      const frag_t<T> bk = load_frag_swz<T, D, kRows>(Kt, w * 32 + col, kc * 16 + hh * 8);
+      sacc = Tr::mma(aq, bk, kc == 0 ? zero16() : sacc);
+      const frag_t<T> ad = load_frag_swz<T, D, kBoth>(dOs, qb * 32 + col, kc * 16 + hh * 8);
+      const frag_t<T> bv = load_frag_swz<T, D, kRows>(Vt, w * 32 + col, kc * 16 + hh * 8);
+      pacc = Tr::mma(ad, bv, kc == 0 ? dneg : pacc);  // dP - D
     }
-    const int steps = KG > 1 ? (t_end - t_begin + 1) / 2 : 0;
-    int step = 0;
-    while (true) {
-      const int t = tl[0];
-      if (KG > 1 && t >= te) {
-        __syncthreads();  // (the step's one barrier)
-        FA_STAGE_FENCE();
-      } else if (t >= lo && t <= hi) {
-        wait_tiles(1);    // tile t landed; t+1 may be in flight
-        __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
-        const uint32_t base = ring_lds + ((step + 2) & 3) * L::SLOT_BYTES;
-        const int qn = (t + 2) * BQ;
-        plan.issue(Qg + (size_t)qn * D, base);
-        plan.issue(dOg + (size_t)qn * D, base + L::TILE_BYTES);
-        // 64 words per copy; with 32-row tiles (fp32, d = 128) lanes 32..63
-        // would reach past the head, so the row is clamped as in issue().
-        if (w < 2)
-          dma4s((uint32_t)min(qn + lane, N - 1) * 4u,
-                w == 0 ? (const void*)lse2g : (const void*)dvecg,
-                base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
-        FA_STAGE_FENCE();
-        if constexpr (L::ILV) {
-          step_ilv(slot_of(step), t * BQ, false);
-        } else {
-          qblk sacc, pacc;
-          qfrag pf, sf;
-          sdp(slot_of(step), sacc, pacc);
-          soft(slot_of(step), t * BQ, false, sacc, pacc);
-          to_frags(sacc, pacc, pf, sf);
-          grads(slot_of(step), pf, sf);
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
+      const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int r = 4 * g + u;
+        float pr = fast_exp2(fmaf(sacc[r], c, -lv[u]));
+        if (msk) {  // selects only: no branch per element
+          const int qi = qi0 + r0 + u;
+          pr = (qi >= qlo) & (qi < qhi) ? pr : 0.f;
         }
-        tl[0] = t + 1;
-        tl[1] = t + 2;
-        tl[2] = min(t + 3, te);
-      } else {
-        if constexpr (LA3) {
-          wait_tiles((tl[1] < te) + (tl[2] < te));  // tile t landed
-          __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
-          if (tl[3] < te) issue(tl[3], (step + 3) & 3);
-        } else {
-          wait_tiles(tl[1] < te ? 1 : 0);  // tile t landed; tl[1] may be in flight
+        sacc[r] = pr;            // P
+        pacc[r] = pr * pacc[r];  // dS = P (dP - D)
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const frag_t<T> pf = acc_to_frag<T>(sacc, t);
+      const frag_t<T> sf = acc_to_frag<T>(pacc, t);
+      const int qc = 2 * qb + t;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const frag_t<T> ado = load_frag_tr<T, D, kBoth>(dOs, qc * 16, db * 32, lane);
+        dv_acc[db] = Tr::mma(ado, pf, dv_acc[db]);
+        const frag_t<T> aqt = load_frag_tr<T, D, kBoth>(Qs, qc * 16, db * 32, lane);
+        dk_acc[db] = Tr::mma(aqt, sf, dk_acc[db]);
+      }
+    }
+  };
+
+  if constexpr (QS) {
+    // Both groups walk the same kept tiles [t_begin, t_end), one tile ahead
+    // in the 2-slot ring: step i waits for tile i (slot i % 2; on the first
+    // step also K and V), and once the barrier shows every wave done with
+    // step i - 1 requests the next kept tile into the other slot.
+    int t = t_begin < t_end ? next_kept(t_begin) : t_end;
+    if (t < t_end) {
+      issue(t, 0);
+      FA_STAGE_FENCE();
+      for (int step = 0;; ++step) {
+        wait_vmcnt<0>();
+        __syncthreads();
+        const int tn = t + 1 < t_end ? next_kept(t + 1) : t_end;
+        if (tn < t_end) issue(tn, (step + 1) & 1);
+        FA_STAGE_FENCE();
+        if (active(t)) step_qs(gring + (step & 1) * L::SLOT_BYTES, t * BQ, masked(t));
+        FA_STAGE_FENCE();
+        t = tn;
+        if (t >= t_end) break;
+      }
+    }
+    wait_vmcnt<0>();  // (no copy may still land in LDS once it is reused below)
+  } else {
+    // Kept query tiles in order; tl[k] is the tile of step i + k.  Step i
+    // forms S and dP of tile i, its softmax, then the dV, dK products.
+    // The split instances (long sparse masks, whose tiles come from HBM rather
+    // than L2) request tiles three steps ahead, using the ring's fourth slot;
+    // the others two.
+    //
+    // This key group's query tiles [tb, te): all of [t_begin, t_end), or its
+    // first or second half (the first group takes the extra tile of an odd
+    // count).  With two key groups the loop's condition is the work-group's,
+    // and both groups take the first group's number of steps, so that their
+    // barriers pair up; a group past its last tile only joins the barriers.
+    int tb = t_begin, te = t_end;
+    if constexpr (KG > 1) {
+      const int tmid = t_begin + (t_end - t_begin + 1) / 2;
+      tb = kgrp ? tmid : t_begin;
+      te = kgrp ? t_end : tmid;
+    }
+    constexpr bool LA3 = SPLIT;
+    int tl[4];
+    tl[0] = tb < te ? next_kept(tb) : te;
+    tl[1] = tl[0] < te ? next_kept(tl[0] + 1) : te;
+    tl[2] = tl[1] < te ? next_kept(tl[1] + 1) : te;
+    tl[3] = LA3 && tl[2] < te ? next_kept(tl[2] + 1) : te;
+    if (KG > 1 ? t_begin < t_end : tl[0] < te) {
+      if (tl[0] < te) issue(tl[0], 0);
+      if (tl[1] < te) issue(tl[1], 1);
+      if (LA3 && tl[2] < te) issue(tl[2], 2);
+      FA_STAGE_FENCE();
+      // The K and V fragments arrived by ordinary loads issued before these
+      // copies.  Waiting for everything once here tells the compiler they have
+      // landed; otherwise it waits for them (vmcnt(0)) at their first use
+      // inside the loop, on every step, which also stalls on the tile just
+      // requested.
+      wait_vmcnt<0>();
+      // Dense interior: every wave's keys see tile t in full, and tiles t+1,
+      // t+2 are whole.
+      int lo = te, hi = -1;
+      if (!sparse && j0 + BK <= kend) {
+        lo = p.causal ? (j0 + BK - 1 + BQ - 1) / BQ : tb;
+        hi = min(N / BQ - 3, te - 3);
+      }
+      const int steps = KG > 1 ? (t_end - t_begin + 1) / 2 : 0;
+      int step = 0;
+      while (true) {
+        const int t = tl[0];
+        if (KG > 1 && t >= te) {
+          __syncthreads();  // (the step's one barrier)
+          FA_STAGE_FENCE();
+        } else if (t >= lo && t <= hi) {
+          wait_tiles(1);    // tile t landed; t+1 may be in flight
           __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
-          if (tl[2] < te) issue(tl[2], (step + 2) & 3);
-        }
-        FA_STAGE_FENCE();
-        if (active(t)) {
+          const uint32_t base = ring_lds + ((step + 2) & 3) * L::SLOT_BYTES;
+          const int qn = (t + 2) * BQ;
+          plan.issue(Qg + (size_t)qn * D, base);
+          plan.issue(dOg + (size_t)qn * D, base + L::TILE_BYTES);
+          // 64 words per copy; with 32-row tiles (fp32, d = 128) lanes 32..63
+          // would reach past the head, so the row is clamped as in issue().
+          if (w < 2)
+            dma4s((uint32_t)min(qn + lane, N - 1) * 4u,
+                  w == 0 ? (const void*)lse2g : (const void*)dvecg,
+                  base + 2 * L::TILE_BYTES + w * L::ROWV_BYTES);
+          FA_STAGE_FENCE();
           if constexpr (L::ILV) {
-            step_ilv(slot_of(step), t * BQ, masked(t));
+            step_ilv(slot_of(step), t * BQ, false);
           } else {
             qblk sacc, pacc;
             qfrag pf, sf;
             sdp(slot_of(step), sacc, pacc);
-            soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
+            soft(slot_of(step), t * BQ, false, sacc, pacc);
             to_frags(sacc, pacc, pf, sf);
             grads(slot_of(step), pf, sf);
           }
-        }
-        tl[0] = tl[1];
-        tl[1] = tl[2];
-        if constexpr (LA3) {
-          tl[2] = tl[3];
-          tl[3] = tl[3] < te ? next_kept(tl[3] + 1) : te;
+          tl[0] = t + 1;
+          tl[1] = t + 2;
+          tl[2] = min(t + 3, te);
         } else {
-          tl[2] = tl[2] < te ? next_kept(tl[2] + 1) : te;
+          if constexpr (LA3) {
+            wait_tiles((tl[1] < te) + (tl[2] < te));  // tile t landed
+            __syncthreads();  // every wave is done with step i-1: slot (i+3)%4 is free
+            if (tl[3] < te) issue(tl[3], (step + 3) & 3);
+          } else {
+            wait_tiles(tl[1] < te ? 1 : 0);  // tile t landed; tl[1] may be in flight
+            __syncthreads();  // every wave is done with step i-1: slot (i+2)%4 is free
+            if (tl[2] < te) issue(tl[2], (step + 2) & 3);
+          }
+          FA_STAGE_FENCE();
+          if (active(t)) {
+            if constexpr (L::ILV) {
+              step_ilv(slot_of(step), t * BQ, masked(t));
+            } else {
+              qblk sacc, pacc;
+              qfrag pf, sf;
+              sdp(slot_of(step), sacc, pacc);
+              soft(slot_of(step), t * BQ, masked(t), sacc, pacc);
+              to_frags(sacc, pacc, pf, sf);
+              grads(slot_of(step), pf, sf);
+            }
+          }
+          tl[0] = tl[1];
+          tl[1] = tl[2];
+          if constexpr (LA3) {
+            tl[2] = tl[3];
+            tl[3] = tl[3] < te ? next_kept(tl[3] + 1) : te;
+          } else {
+            tl[2] = tl[2] < te ? next_kept(tl[2] + 1) : te;
+          }
         }
+        FA_STAGE_FENCE();
+        ++step;
+        if (KG > 1 ? step >= steps : tl[0] >= te) break;
       }
-      FA_STAGE_FENCE();
-      ++step;
-      if (KG > 1 ? step >= steps : tl[0] >= te) break;
     }
   }
+
   if constexpr (KG > 1) {
     // Key group 1 adds its dK, dV accumulators into group 0's through the
     // idle rings, lane for lane; group 0 alone stores them (group 1 stays for
     // the staged store's barriers).
     constexpr int XF = 2 * (D / 32) * 16;
-    static_assert(RW * XF * 64 * 4 <= KG * L::NS * L::SLOT_BYTES, "hand-over fits in the rings");
+    static_assert(RW * XF * 64 * 4 <= (int)sizeof(ring), "hand-over fits in the rings");
     float* const xs = reinterpret_cast<float*>(ring) + w * XF * 64;
     __syncthreads();  // every wave is done with both rings
     if (kgrp == 1) {
@@ -769,7 +874,7 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
     constexpr int RS = RB + 16;               // padded LDS row stride
     constexpr int CPR = RB / 16;              // 16-byte chunks per row
     constexpr int RPI = 64 / CPR;             // rows per store instruction
-    static_assert(RW * 32 * RS <= L::NS * L::SLOT_BYTES, "staging fits in the ring");
+    static_assert(RW * 32 * RS <= (int)sizeof(ring), "staging fits in the ring");
     char* const stage = ring + w * 32 * RS;
     // (with two key groups, group 0 stores; group 1 joins the barriers)
 #pragma unroll
@@ -1225,12 +1330,12 @@ hipError_t launch_dq_pass(const BwdParams& p, const Problem& pb, unsigned items)
                      dim3(64 * NW), 0, pb.stream, p);
   return hipGetLastError();
 }
-template <typename T, int D, bool GF32, bool SPLIT, int NW, int KG = 1>
+template <typename T, int D, bool GF32, bool SPLIT, int NW, int KG = 1, bool QS = false>
 hipError_t launch_dkdv_pass(const BwdParams& p, const Problem& pb, unsigned items) {
   constexpr int BK = 32 * NW / KG;
   const unsigned tiles = (unsigned)((pb.N + BK - 1) / BK);
-  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT, NW, KG>), dim3(tiles * p.BH, items),
-                     dim3(64 * NW), 0, pb.stream, p);
+  hipLaunchKernelGGL((fa_bwd_dkdv_kernel<T, D, GF32, SPLIT, NW, KG, QS>),
+                     dim3(tiles * p.BH, items), dim3(64 * NW), 0, pb.stream, p);
   return hipGetLastError();
 }
 
@@ -1270,9 +1375,9 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
   const unsigned items = SPLIT ? (unsigned)pb.split_items : 1u;
   hipError_t e = hipSuccess;
   // Run-time choices among the unsplit 16-bit instances (checked by the
-  // caller): two key groups (128 rows; the dK/dV pass only at d = 64, where
-  // its per-wave state leaves room for two waves per SIMD), or other tile
-  // heights than 128 rows (gradients in the input type).
+  // caller): two key groups (128 rows; the dK/dV pass at d = 64 splits the
+  // tile range, at d = 128 each tile's queries, with K and V in LDS), or
+  // other tile heights than 128 rows (gradients in the input type).
   const bool two_groups = pb.bwd_kgroups == 2;
   if (pb.bwd_passes & kPassDq) {
     if constexpr (SPLIT || sizeof(T) == 4) {
@@ -1298,6 +1403,8 @@ hipError_t launch_bwd_t(const Problem& pb, const BwdTensors& t) {
       e = launch_dkdv_pass<T, D, GF32, SPLIT, 4>(p, pb, items);
     } else if (two_groups && D == 64) {
       if constexpr (D == 64) e = launch_dkdv_pass<T, D, GF32, false, 8, 2>(p, pb, items);
+    } else if (D == 128 && pb.bwd_dkdv_qs) {
+      if constexpr (D == 128) e = launch_dkdv_pass<T, D, GF32, false, 8, 2, true>(p, pb, items);
     } else if (GF32 || pb.bwd_dkdv_rows == 128) {
       e = launch_dkdv_pass<T, D, GF32, false, 4>(p, pb, items);
     } else {

@@ -41,6 +41,9 @@ struct Problem {
   int bwd_dq_rows = 128;       // backward: query rows per dQ work-group (64, 128, 256)
   int bwd_dkdv_rows = 128;     // backward: keys per dK/dV work-group (64, 128, 256)
   int bwd_kgroups = 1;         // backward: wave groups splitting each tile's sweep (1, 2)
+  // backward, d = 128: the dK/dV pass splits each query tile between two wave
+  // groups (one 32-query half each, K and V in LDS)
+  bool bwd_dkdv_qs = false;
   // Block-sparse backward split by kept mask blocks (chunk_blocks > 0): items
   // of chunk_blocks kept blocks per mask row (dQ) or column (dK, dV), at most
   // split_items per tile; fp32 partials [split_items][B*H][N][d] each.

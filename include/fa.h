@@ -215,10 +215,13 @@ int fa_backward(const void* q, const void* k, const void* v, const void* o,
  *               halves and add their partial gradients on chip: 1, 2, or 0
  *               to let the library choose (fa_backward_key_groups_for; with
  *               128-row tiles only).  2 takes 16-bit inputs, no block mask
- *               and 128-row tiles, else FA_ERR_UNSUPPORTED; the dK/dV pass
- *               keeps one group at d = 128 (its per-wave state needs a
- *               SIMD's registers).  Results agree to rounding (the halves
- *               are added in another order).
+ *               and 128-row tiles, else FA_ERR_UNSUPPORTED.  At d = 128 the
+ *               dK/dV pass (16-bit inputs, 128-key tiles, any mask)
+ *               splits every query tile between two groups, one
+ *               32-query half each, with K and V read from LDS, whenever
+ *               key_groups is not 1; with 1 it keeps one group, one wave
+ *               per SIMD.  Results agree to rounding (the halves are added
+ *               in another order).
  */
 int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
                    const void* dout, const float* lse, void* dq, void* dk, void* dv,
@@ -232,7 +235,9 @@ int fa_backward_ex(const void* q, const void* k, const void* v, const void* o,
  * Key groups (see fa_backward_ex) that a backward of these sizes uses when
  * key_groups is 0 and the tiles are 128 rows: 2 for 16-bit dense problems
  * whose grid holds at most 512 tiles at d = 64 (two per compute unit) or 256
- * at d = 128 (where only the dQ pass splits), else 1.  Host arithmetic only.
+ * at d = 128, else 1.  (At d = 128 this is the dQ pass's choice; the dK/dV
+ * pass splits its query tiles whenever key_groups is not 1.)  Host
+ * arithmetic only.
  */
 int fa_backward_key_groups_for(int B, int H, int N, int d, fa_dtype dtype, int sparse);
 

@@ -268,7 +268,36 @@ int main() {
     const uint8_t* bmk = static_cast<const uint8_t*>(a);
     CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, bmk, 128,
                       FA_BF16, a, bw, nullptr) == FA_OK);
-    CHECK(g_last.bwd_kgroups == 1);
+    CHECK(g_last.bwd_kgroups == 1 && !g_last.bwd_dkdv_qs);
+  }
+  // ---- the d = 128 dK/dV pass splits its query tiles unless one group is asked for
+  {
+    const size_t bw128 = fa_backward_workspace_bytes(2, 3, 100, 128);
+    const uint8_t* bmk = static_cast<const uint8_t*>(a);
+    CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, nullptr, 128,
+                      FA_BF16, a, bw128, nullptr) == FA_OK);
+    CHECK(g_last.bwd_dkdv_qs);
+    CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, bmk, 128,
+                      FA_F16, a, bw128, nullptr) == FA_OK);
+    CHECK(g_last.bwd_dkdv_qs);  // block masks too
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, nullptr,
+                         128, FA_BF16, FA_BF16, 0, 0, 1, a, bw128, nullptr) == FA_OK);
+    CHECK(!g_last.bwd_dkdv_qs);  // one group asked for
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, nullptr,
+                         128, FA_BF16, FA_BF16, 0, 0, 2, a, bw128, nullptr) == FA_OK);
+    CHECK(g_last.bwd_dkdv_qs);
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, nullptr,
+                         128, FA_BF16, FA_F32, 0, 0, 0, a, bw128, nullptr) == FA_OK);
+    CHECK(g_last.bwd_dkdv_qs && g_last.grad_f32);  // float32 gradients: the same sums
+    CHECK(fa_backward_ex(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, nullptr,
+                         128, FA_BF16, FA_BF16, 0, 64, 0, a, bw128, nullptr) == FA_OK);
+    CHECK(!g_last.bwd_dkdv_qs);  // another tile height
+    CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 128, 0.1f, 1, nullptr, nullptr, 128,
+                      FA_F32, a, bw128, nullptr) == FA_OK);
+    CHECK(!g_last.bwd_dkdv_qs);
+    CHECK(fa_backward(a, a, a, a, a, f, a, a, a, 2, 3, 100, 64, 0.1f, 1, nullptr, nullptr, 128,
+                      FA_BF16, a, bw, nullptr) == FA_OK);
+    CHECK(!g_last.bwd_dkdv_qs);  // d = 64
   }
   // (the sizes are checked before anything else is read, empty problems too)
   CHECK(fa_backward_ex(nullptr, a, a, a, a, f, a, a, a, 0, 3, 100, 64, 0.1f, 1, nullptr, nullptr,

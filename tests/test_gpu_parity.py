@@ -437,6 +437,41 @@ def test_backward_key_groups(case, kg):
             magnitude_scaled=klr is not None and klr[0] < 4)
 
 
+QS_CASES = [
+    # B, H, N, d, dtype, causal, key_len_range, block_keep_p
+    (1, 2, 1000, 128, "bf16", True, None, None),
+    (2, 2, 700, 128, "fp16", False, (1, 700), None),
+    (1, 3, 1100, 128, "bf16", False, None, 0.5),
+    (1, 2, 100, 128, "bf16", True, None, None),        # one work-group, keys past N
+    (2, 1, 1536, 128, "bf16", True, (600, 1536), 0.5),
+    (8, 4, 256, 128, "fp16", True, None, None),        # 32 heads: the XCD-grouped schedule
+]
+
+
+@pytest.mark.parametrize("case", QS_CASES, ids=lambda c: "N{}d{}_{}_c{}".format(c[2], c[3], c[4],
+                                                                                int(c[5])))
+def test_backward_dkdv_query_halves(case):
+    # At d = 128 the dK/dV pass splits every query tile between two groups of
+    # waves (one 32-query half each, K and V read from LDS) unless one group is
+    # asked for.  Both forms against the oracle on every head, and against
+    # each other: the same products, added in another order, so within a few
+    # units in the last place of the float32 gradients.
+    B, H, N, d, dtype, causal, klr, bkp = case
+    prob = inputs.make_problem(B, H, N, d, dtype, seed=233 + N, causal=causal, key_len_range=klr,
+                               block_keep_p=bkp)
+    split = run_gpu(prob)
+    one = run_gpu(prob, bwd_key_groups=1)
+    check_all_heads(prob, split, "dK/dV query halves")
+    ref = run_oracle(prob)
+    compare(split, ref, TOL[dtype], label=f"dK/dV query halves {case}")
+    compare(one, ref, TOL[dtype], label=f"dK/dV one group {case}")
+    for n in ("dk", "dv"):
+        a, b = split[n], one[n]
+        scale = max(np.abs(b).max(), 1e-30)
+        assert np.abs(a - b).max() <= 1e-5 * scale, (n, float(np.abs(a - b).max()), scale)
+    log(f"[dkdv halves] {case}: both forms agree")
+
+
 BWD_ROW_CASES = [
     # dQ query rows, dK/dV keys per work-group, B, H, N, d, dtype, causal, key_len_range,
     # block_keep_p
