@@ -315,6 +315,9 @@ ROW_CASES = [
     (256, 1, 2, 600, 64, "bf16", True, None, None),
     (256, 2, 1, 520, 128, "bf16", False, (100, 520), None),
     (256, 1, 1, 300, 64, "fp32", True, None, None),
+    # 256-row d = 128 tiles stage V transposed once per work-group
+    (256, 1, 2, 1100, 128, "bf16", True, None, None),
+    (256, 2, 2, 777, 128, "fp16", True, (300, 777), None),
 ]
 
 
