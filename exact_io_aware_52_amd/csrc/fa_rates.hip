@@ -22,6 +22,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "fa_common.h"  // (the attention kernels' LDS operand reads, for op 8)
+
 namespace {
 
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -71,10 +73,10 @@ __device__ __forceinline__ void exp_iter(float (&x)[kChains]) {
 // LDS reads: each wave reads its work-group's LDS buffer, 16 reads per
 // iteration: ds_read_b128 (16 contiguous bytes per lane, 1 KB per read) or
 // ds_read_b64_tr_b16 (the transposing read the attention kernels use for the
-// V^T, dO^T and Q^T operands; 8 contiguous bytes addressed per lane, 512
-// bytes per read), and folds every element read into a running xor so that
-// no read is dead.
-constexpr int kLdsBytes = 17408;  // 16 KB read per iteration from a base that moves by 512 B
+// V^T, dO^T and Q^T operands, 512 bytes per read) addressed exactly as the
+// kernels address a swizzled tile, and folds every element read into a
+// running xor so that no read is dead.
+constexpr int kLdsBytes = 32768;  // two 16 KB tiles (op 8); op 7 reads 17 KB of it
 typedef short s16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
@@ -156,13 +158,16 @@ __global__ __launch_bounds__(64 * waves_per_group<OP>()) void rates_kernel(
         fold ^= v[0] ^ v[1] ^ v[2] ^ v[3];
       }
     } else if constexpr (OP == kLdsTr) {
-      // lane l addresses bytes 8 l .. 8 l + 7 of each 1 KB row j (512 bytes
-      // per read; the hardware regroups the 16-bit elements across lanes)
-      const __attribute__((address_space(3))) char* const b = lb + (it & 1) * 512 + lane * 8;
+      // the V^T operand reads of the forward: eight 32 x 16 fragments of a
+      // 64-key x 128-d bf16 tile stored with the transposed-read swizzle,
+      // each two ds_read_b64_tr_b16 (512 bytes each), from one of two tiles
+      const uint16_t* tile = reinterpret_cast<const uint16_t*>(lds) + (it & 1) * 64 * 128;
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const s16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(b + j * 1024));
-        fold ^= (unsigned)(unsigned short)(v[0] ^ v[1] ^ v[2] ^ v[3]);
+      for (int j = 0; j < 8; ++j) {
+        const fa::frag_t<__bf16> v =
+            fa::load_frag_tr<__bf16, 128, fa::kTr>(tile, 16 * (j & 3), 32 * (j >> 2), lane);
+        const uint32_t* w = reinterpret_cast<const uint32_t*>(&v);
+        fold ^= w[0] ^ w[1] ^ w[2] ^ w[3];
       }
     } else if constexpr (OP == kMixSelf) {
       // per iteration kAccs products and kChains exponentials, issued as
