@@ -518,6 +518,11 @@ class Runner:
                 device=dev)
         self.kw = dict(scale=self.scale, causal=prob.causal, key_lens=self.kl,
                        block_mask=self.bm, block_size=prob.block_size)
+        # At d = 128 the dK/dV pass (16-bit, 128-key tiles, unsplit) splits
+        # every query tile between two wave groups (key groups left to the
+        # library here, so never 1).
+        self.dkdv_split_queries = (prob.dtype != "fp32" and prob.d == 128 and
+                                   bwd_rows in (0, 128) and not self.chunk_blocks)
 
     def fwd(self):
         if self.key_chunk:
@@ -795,10 +800,10 @@ def unit_rates(args, dev):
     print(json.dumps({"unit_rates": rows, "compute_units": cus,
                       "mfma_sustained": {"launches": len(sustained), "first": sustained[0],
                                          "last": sustained[-1],
-                                         "median_tflops": float(np.median(
-                                             [x["tflops"] for x in sustained])),
-                                         "median_clock_ghz": float(np.median(
-                                             [x["clock_ghz"] for x in sustained]))}}))
+                                         "median_tflops": round(float(np.median(
+                                             [x["tflops"] for x in sustained])), 1),
+                                         "median_clock_ghz": round(float(np.median(
+                                             [x["clock_ghz"] for x in sustained])), 3)}}))
 
 
 def main():
@@ -921,6 +926,7 @@ def main():
                    "block_sparse": prob.block_mask is not None,
                    "fwd_block_rows": run.fwd_rows, "fwd_block_keys": run.keys or 64,
                    "fwd_key_groups": run.fwd_kgroups, "bwd_key_groups": run.bwd_kgroups,
+                   "bwd_dkdv_split_queries": run.dkdv_split_queries,
                    "bwd_rows": run.dq_rows or 128,
                    "fwd_key_chunk": run.key_chunk or None,
                    "bwd_chunk_blocks": run.chunk_blocks or None,
