@@ -60,8 +60,8 @@ int auto_fwd_kgroups(int B, int H, int N, int d, fa_dtype dtype, bool sparse) {
 // The backward's two passes: their 4-slot rings already hold them to two
 // 4-wave work-groups per CU, so one 8-wave work-group per CU keeps as many
 // waves and halves the chains.  Measured backward times, key groups 2
-// against 1 (B2 H8, causal): N = 2K -15% (d = 64) and -8% (d = 128, where
-// only the dQ pass splits), N = 4K -4% and +1%; N = 8K +4%, +3%; the GPT-2
+// against 1 (B2 H8, causal): N = 2K -15% (d = 64) and -8% (d = 128, measured
+// with only the dQ pass split), N = 4K -4% and +1%; N = 8K +4%, +3%; the GPT-2
 // shape (768 tiles) +26%.  So at most 512 tiles at d = 64, 256 at d = 128.
 // (At d = 128 the dK/dV pass takes its own two-group form whatever this
 // returns: see backward_impl.)

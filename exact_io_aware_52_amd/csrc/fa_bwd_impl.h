@@ -20,6 +20,9 @@
 //      tile is formed with queries as accumulator rows, so P and dS are the B
 //      operands of dV^T += dO^T P and dK^T += Q^T dS straight from registers;
 //      dO^T and Q^T come from the row-major tiles by transposing LDS reads.
+//      At d = 128 those registers would allow one wave per SIMD, so by
+//      default eight waves share each query tile instead (two per 32-key
+//      block, one 32-query half each) and read K and V from LDS.
 // Splitting dQ into its own pass recomputes S and dP once more (6 d flops per
 // pair on top of the 8 d of the dK/dV pass) but needs no atomics, keeps every
 // accumulator in registers and makes the result deterministic.
@@ -167,7 +170,8 @@ struct DkDvCfg {
   static constexpr int SLOT_BYTES = 2 * TILE_BYTES + 2 * ROWV_BYTES;
   static constexpr int LPT = 2 * TILE_BYTES / (1024 * NW);       // 16-byte DMAs per wave per tile
   // At d = 128 the persistent per-wave state (K, V operands and the dK, dV
-  // accumulators: 192 VGPRs) only fits one wave per SIMD.
+  // accumulators: 192 VGPRs) only fits one wave per SIMD; with QS the K and
+  // V operands come from LDS and two waves fit.
   static constexpr int WAVES_PER_SIMD = D == 128 && !QS ? 1 : 2;
   // Read each group of matrix operands one group ahead of its products
   // (explicit, fenced with scheduling barriers): the compiler otherwise reads
