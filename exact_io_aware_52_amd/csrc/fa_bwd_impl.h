@@ -50,6 +50,8 @@
 #pragma once
 
 #include "fa_common.h"
+
+#include <type_traits>
 #include "fa_internal.h"
 
 namespace fa {
@@ -624,23 +626,31 @@ __global__ __launch_bounds__(64 * NW) __attribute__((amdgpu_waves_per_eu(
       const frag_t<T> bv = load_frag_swz<T, D, kRows>(Vt, w * 32 + col, kc * 16 + hh * 8);
       pacc = Tr::mma(ad, bv, kc == 0 ? dneg : pacc);  // dP - D
     }
+    // P = exp2(c S - LSE2) and dS = P (dP - D); boundary tiles only select
+    // masked elements to 0 (one copy of the loop each, behind one
+    // wave-uniform branch).
+    auto soft_qs = [&](auto masked_c) {
+      constexpr bool M = decltype(masked_c)::value;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
-      const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
-      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      for (int g = 0; g < 4; ++g) {
+        const int r0 = qb * 32 + 8 * g + 4 * hh;  // first of 4 consecutive query rows
+        const float4 l4 = *reinterpret_cast<const float4*>(lse2s + r0);
+        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int r = 4 * g + u;
-        float pr = fast_exp2(fmaf(sacc[r], c, -lv[u]));
-        if (msk) {  // selects only: no branch per element
-          const int qi = qi0 + r0 + u;
-          pr = (qi >= qlo) & (qi < qhi) ? pr : 0.f;
+        for (int u = 0; u < 4; ++u) {
+          const int r = 4 * g + u;
+          float pr = fast_exp2(fmaf(sacc[r], c, -lv[u]));
+          if constexpr (M) {
+            const int qi = qi0 + r0 + u;
+            pr = (qi >= qlo) & (qi < qhi) ? pr : 0.f;
+          }
+          sacc[r] = pr;            // P
+          pacc[r] = pr * pacc[r];  // dS = P (dP - D)
         }
-        sacc[r] = pr;            // P
-        pacc[r] = pr * pacc[r];  // dS = P (dP - D)
       }
-    }
+    };
+    if (msk) soft_qs(std::true_type{});
+    else soft_qs(std::false_type{});
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
       const frag_t<T> pf = acc_to_frag<T>(sacc, t);
