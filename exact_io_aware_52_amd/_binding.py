@@ -395,7 +395,9 @@ def fa_backward_ex(q, k, v, o, dout, lse, scale=None, causal=False, key_lens=Non
     """Backward with the gradients' dtype (q.dtype or torch.float32), the
     tile sizes (query rows per dQ work-group, keys per dK/dV work-group: 64,
     128, 256; 0 = 128) and the key groups (1, 2; 0 = the library's choice)
-    given per call: returns (dQ, dK, dV)."""
+    given per call: returns (dQ, dK, dV).  At d = 128 the dK/dV pass of
+    16-bit inputs with 128-key tiles splits each query tile between two wave
+    groups unless key_groups is 1."""
     dq, dk, dv, _ = _backward("fa_backward_ex", q, k, v, o, dout, lse, scale, causal, key_lens,
                               block_mask, block_size, dq, dk, dv, workspace, grad_dtype,
                               dq_rows, dkdv_rows, key_groups)
@@ -502,7 +504,9 @@ def fa_forward_key_groups_for(B, H, N, d, dtype, sparse=False):
 
 
 def fa_backward_key_groups_for(B, H, N, d, dtype, sparse=False):
-    """Key groups per work-group a backward of these sizes would use."""
+    """Key groups per work-group a backward of these sizes would use (at
+    d = 128, the dQ pass's; the dK/dV pass splits its query tiles whenever
+    key_groups is not 1)."""
     code = _DTYPE_CODE[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     return int(load_library().fa_backward_key_groups_for(int(B), int(H), int(N), int(d), code,
                                                          int(bool(sparse))))
