@@ -62,6 +62,9 @@ CASES = [
     # two key groups (chosen automatically for grids this small), d = 128, ragged
     ("small", dict(B=2, H=2, N=1500, d=128, dtype="bf16", seed=37, causal=True,
                    key_len_range=(700, 1500)), 0, 0, 0),
+    # d = 128 with a block mask: the dK/dV pass's split query tiles (two-slot ring, K and V in
+    # LDS) over skipped tiles
+    ("small", dict(B=1, H=3, N=777, d=128, dtype="bf16", seed=38, block_keep_p=0.5), 0, 0, 0),
 ]
 
 
