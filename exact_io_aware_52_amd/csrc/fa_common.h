@@ -338,8 +338,9 @@ constexpr int kCusPerXcd = 32;
 // round shares a CU with the lightest of the next (causal dQ pass: 3.5-5%
 // faster at N = 2K-4K, within 1% elsewhere; the forward measured up to 19%
 // slower on grids of several rounds, whose heaviest-first order it breaks, and
-// the dK/dV pass slower too, so only the dQ pass uses it).  Whole rounds
-// only: the slot stays a bijection on [0, ntiles * BH / 8).
+// the dK/dV pass slower too, so the dQ pass uses it, and the forward only
+// when its whole grid is resident at once).  Whole rounds only: the slot stays
+// a bijection on [0, ntiles * BH / 8).
 __device__ __forceinline__ void map_tile(int bid, int ntiles, int BH, bool reverse, int group,
                                          int& tile, int& bh, bool snake = false) {
   int ti;

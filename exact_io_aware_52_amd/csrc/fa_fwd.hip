@@ -74,6 +74,7 @@ struct FwdParams {
   const uint8_t* block_mask;
   int H, N, BH, nq, nblk;  // N: query rows per head; nq: query tiles per head
   int hgroup;              // heads per XCD dispatched together (map_tile)
+  int snake;               // map_tile's snake order (causal grids of one round)
   int nk;                  // key (and value) rows per head: N for self-attention
   float scale;
   float c;  // scale * log2(e): exponents are taken base 2
@@ -216,7 +217,7 @@ __device__ __forceinline__ void fwd_tile(FwdParams p) {
   const int hh = lane >> 5;
 
   int qt, bh;
-  map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, p.hgroup, qt, bh);
+  map_tile(blockIdx.x, p.nq, p.BH, p.causal != 0, p.hgroup, qt, bh, p.snake != 0);
 #ifdef FA_STEP_STAMPS
   int stamp_slot = -1;
   for (int i = 0; i < kStampWgs; ++i)
@@ -896,6 +897,12 @@ hipError_t launch_fwd_t(const Problem& pb, const FwdTensors& t) {
   p.hgroup = head_group(p.BH, 2LL * (pb.cu_q ? (pb.Tk + pb.B - 1) / std::max(pb.B, 1) : p.nk) * D *
                                   (long long)sizeof(raw_t<T>));
   p.nq = (pb.N + BR - 1) / BR;
+  // Causal grids that the chip holds in one round (three work-groups per CU
+  // for this instance's ring and registers) are all resident from the start,
+  // so the snake order pairs heavy and light tiles on each CU instead of
+  // three of similar weight (GPT-2 shape, 768 tiles: 3.5-6.5% faster).
+  p.snake = D == 64 && NW == 4 && BC == 0 && KG == 1 && pb.causal && !pb.cu_q &&
+            (long long)p.nq * p.BH <= 3 * 256;
   p.nblk = (pb.N + kMaskBlock - 1) / kMaskBlock;
   p.scale = pb.scale;
   p.c = pb.scale * kLog2e;

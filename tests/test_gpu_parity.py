@@ -586,6 +586,16 @@ def test_deterministic():
         assert np.array_equal(a[n], b[n], equal_nan=True), n
 
 
+# Causal 128-row grids small enough to be resident at once take the snake tile
+# order: one whole reversed round of 32 slots per XCD (B4 H16), a whole and a
+# partial one (B5 H16), and none (B3 H16, 54 slots per XCD), ragged tails.
+@pytest.mark.parametrize("B,H,N", [(4, 16, 1000), (5, 16, 1000), (3, 16, 1100)])
+def test_forward_one_round_tile_orders(B, H, N):
+    prob = inputs.make_problem(B, H, N, 64, "bf16", seed=90 + B, causal=True)
+    gpu = run_gpu(prob, backward=False)
+    compare(gpu, run_oracle(prob, backward=False), TOL["bf16"], label=f"B{B} H{H} N{N}")
+
+
 # ----------------------------------------------------------------------------- the five workloads
 
 def test_config_tiny_full():
